@@ -1,0 +1,186 @@
+"""fp64 CPU oracle for the HSTU layer forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding) never imports, links or calls it, and it shares no code with that
+path.  The arithmetic lives in ``hstu_oracle.c`` (plain loops in double); this
+module only marshals numpy arrays into it and adds the two pieces that are a
+single line of numpy (the embedding sum and the layer stack loop).
+
+Sources, by page title and section:
+  "Actions Speak Louder than Words" reading notes, §3.1 eqs. (1)-(3), §3.2;
+  "4.4 推荐模型的 Scaling", section "HSTU 层" and the toy HSTULayer ("代码");
+  GenRank article (joto.ai), "(1) item-action组织" and "(2) 位置 & 时间偏差".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hstu_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+BIAS_NONE, BIAS_RAB_PT, BIAS_ALIBI = 0, 1, 2
+
+
+def build(force: bool = False) -> str:
+    """Compile hstu_oracle.c with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        _lib.oracle_pos_bucket.argtypes = [i64, i32]
+        _lib.oracle_pos_bucket.restype = i32
+        _lib.oracle_time_bucket.argtypes = [i64, i32]
+        _lib.oracle_time_bucket.restype = i32
+        _lib.oracle_attention.argtypes = [i32, i32, i32, i32, P, P, i64, P, i64, P, i64, i32, P,
+                                          P, i32, i64, P, i32, i64, P, f64, f64, P]
+        _lib.oracle_attention.restype = None
+        _lib.oracle_attention_rows.argtypes = [i32, i32, i32, i32, P, P, i64, P, i64, P, i64, i32,
+                                               P, P, i32, i64, P, i32, i64, P, f64, f64, i64, P, P,
+                                               P]
+        _lib.oracle_attention_rows.restype = None
+        _lib.oracle_layer.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, P, P, i32, P,
+                                      P, i32, i64, P, i32, i64, P, f64, i32, P, P, P]
+        _lib.oracle_layer.restype = None
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def pos_bucket(i_minus_j: int, num_pos: int) -> int:
+    return int(_L().oracle_pos_bucket(int(i_minus_j), int(num_pos)))
+
+
+def time_bucket(dt: int, num_time: int) -> int:
+    return int(_L().oracle_time_bucket(int(dt), int(num_time)))
+
+
+class Bias:
+    """Relative attention bias description (host numpy arrays).
+
+    kind: BIAS_NONE, BIAS_RAB_PT (position + log2 time-delta tables) or
+    BIAS_ALIBI (per-head slopes, bias = -slope_h * (i - j)).
+    w_pos is [P] (shared over heads) or [H, P]; likewise w_time.
+    """
+
+    def __init__(self, kind=BIAS_NONE, timestamps=None, w_pos=None, w_time=None, slopes=None):
+        self.kind = kind
+        self.ts = None if timestamps is None else np.ascontiguousarray(timestamps, dtype=np.int64)
+        self.w_pos = None if w_pos is None else _f64(w_pos)
+        self.w_time = None if w_time is None else _f64(w_time)
+        self.slopes = None if slopes is None else _f64(slopes)
+
+    def args(self):
+        if self.kind == BIAS_RAB_PT:
+            wp, wt = self.w_pos, self.w_time
+            P = wp.shape[-1]
+            NT = wt.shape[-1]
+            sp = P if wp.ndim == 2 else 0
+            st = NT if wt.ndim == 2 else 0
+            return (self.kind, _ptr(self.ts), _ptr(wp), P, sp, _ptr(wt), NT, st, None)
+        if self.kind == BIAS_ALIBI:
+            return (self.kind, None, None, 0, 0, None, 0, 0, _ptr(self.slopes))
+        return (BIAS_NONE, None, None, 0, 0, None, 0, 0, None)
+
+
+def alibi_slopes(H: int) -> np.ndarray:
+    """Slopes 2^(-8 (h+1) / H) for 0-based head h (the ALiBi geometric series
+    2^-8/H ... 2^-8); GenRank article, part (2) names ALiBi without a formula."""
+    return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float64)
+
+
+def attention(offsets, q, k, v, bias: Bias, alpha: float, out_scale: float = 1.0):
+    """Eq. (2) on a jagged batch. q, k: [T, H, dqk]; v: [T, H, dv]. Returns [T, H, dv] fp64."""
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, H, dqk = q.shape
+    dv = v.shape[2]
+    B = len(offs) - 1
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    if T == 0 or B == 0:
+        return o
+    _L().oracle_attention(B, H, dqk, dv, _ptr(offs), _ptr(q), H * dqk, _ptr(k), H * dqk, _ptr(v),
+                          H * dv, *bias.args(), float(alpha), float(out_scale), _ptr(o))
+    return o
+
+
+def attention_rows(offsets, q, k, v, bias: Bias, alpha: float, tokens, heads,
+                   out_scale: float = 1.0):
+    """Eq. (2) for selected (token, head) rows only; returns [R, dv] fp64."""
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, H, dqk = q.shape
+    dv = v.shape[2]
+    B = len(offs) - 1
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    hd = np.ascontiguousarray(heads, dtype=np.int32)
+    R = len(tok)
+    out = np.zeros((R, dv), dtype=np.float64)
+    if R == 0:
+        return out
+    _L().oracle_attention_rows(B, H, dqk, dv, _ptr(offs), _ptr(q), H * dqk, _ptr(k), H * dqk,
+                               _ptr(v), H * dv, *bias.args(), float(alpha), float(out_scale), R,
+                               _ptr(tok), _ptr(hd), _ptr(out))
+    return out
+
+
+def layer(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float, H: int, dqk: int,
+          dv: int, residual: bool = False, ln_eps: float = 1e-5, return_intermediates=False):
+    """One HSTU layer, eqs. (1)-(3). x: [T, D]; w1: [2H(dqk+dv), D]; w2: [D, H dv]."""
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    x = _f64(x)
+    T, D = x.shape
+    B = len(offs) - 1
+    N1 = 2 * H * (dqk + dv)
+    y = np.zeros((T, D), dtype=np.float64)
+    z = np.zeros((T, N1), dtype=np.float64)
+    o = np.zeros((T, H * dv), dtype=np.float64)
+    if T > 0 and B > 0:
+        w1, b1, w2, b2 = _f64(w1), _f64(b1), _f64(w2), _f64(b2)
+        gamma, beta = _f64(gamma), _f64(beta)
+        _L().oracle_layer(B, D, H, dqk, dv, _ptr(offs), _ptr(x), _ptr(w1), _ptr(b1), _ptr(gamma),
+                          _ptr(beta), float(ln_eps), _ptr(w2), _ptr(b2), *bias.args(),
+                          float(alpha), int(bool(residual)), _ptr(y), _ptr(z), _ptr(o))
+    if return_intermediates:
+        return y, z, o
+    return y
+
+
+def embed_sum(item_table, action_table, item_ids, action_ids):
+    """GenRank action-oriented token: item embedding + action embedding
+    (GenRank article, part (1))."""
+    return _f64(item_table)[np.asarray(item_ids)] + _f64(action_table)[np.asarray(action_ids)]
+
+
+def stack(offsets, x, layers, bias_per_layer, alpha, H, dqk, dv, ln_eps=1e-5):
+    """Layers stacked with residual connections ("Actions Speak Louder than
+    Words" §3.1: identical layers joined by residuals). layers: list of dicts
+    with w1, b1, gamma, beta, w2, b2."""
+    h = _f64(x)
+    for L, bias in zip(layers, bias_per_layer):
+        h = layer(offsets, h, L["w1"], L["b1"], L["gamma"], L["beta"], L["w2"], L["b2"], bias,
+                  alpha, H, dqk, dv, residual=True, ln_eps=ln_eps)
+    return h

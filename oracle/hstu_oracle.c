@@ -1,0 +1,213 @@
+/*
+ * hstu_oracle.c -- plain, slow, fp64 CPU definition of the HSTU layer forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+ * its Python binding) may include, link, load or call this file; only the
+ * tests, the smoke check and the benchmark's CPU-baseline leg use it.  It
+ * shares no source with the GPU path.
+ *
+ * Every value is widened to double on entry and nothing is rounded in
+ * between: the result is the exact real-valued definition up to fp64
+ * summation order.  Loops are written in the most direct form on purpose.
+ *
+ * Sources (page title, section):
+ *  [AS]  "Actions Speak Louder than Words" reading notes (paper-archivist.com),
+ *        §3.1 eqs. (1)-(3) and the list under them, §3.2 pointwise aggregated
+ *        attention.
+ *  [SC]  "4.4 推荐模型的 Scaling" (llm-learning-path), section "HSTU 层" and the
+ *        toy HSTULayer in section "代码" (chunk order u,v,q,k; per-head split;
+ *        lower-triangular mask including the diagonal; SiLU then mask).
+ *  [GR]  GenRank article (joto.ai), "工业场景中的高效生成式排序GenRank",
+ *        part (2): ALiBi as the relative position/time bias.
+ *  The bucketed rab^{p,t} form (position offset table + log2 time-delta
+ *  table) is the one the workload definition states; the pages only say the
+ *  real implementation buckets relative position and time ([SC], remark after
+ *  the toy code).
+ *
+ * Readings where the pages are silent (also listed in the design notes):
+ *  - alpha multiplies Q K^T inside the SiLU; out_scale multiplies the sum
+ *    afterwards (1 by default, 1/n reproduces the toy's division).
+ *  - time delta < 0 falls in bucket 0; the bucket is floor(log2(1+dt))
+ *    clipped to [0, NT-1], computed on integers.
+ *  - ALiBi bias is -slope_h * (i - j).
+ *  - positions i, j are 0-based and local to the user's sequence.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <math.h>
+#include <string.h>
+
+enum { ORACLE_BIAS_NONE = 0, ORACLE_BIAS_RAB_PT = 1, ORACLE_BIAS_ALIBI = 2 };
+
+/* SiLU(x) = x * sigmoid(x) = x / (1 + e^{-x})   [AS §3.1: phi1 = phi2 = SiLU] */
+static double silu(double x) { return x / (1.0 + exp(-x)); }
+
+/* Position bucket: the offset i - j clipped to [0, P-1]. */
+int32_t oracle_pos_bucket(int64_t i_minus_j, int32_t num_pos_buckets) {
+  if (i_minus_j < 0) return 0;
+  if (i_minus_j > (int64_t)num_pos_buckets - 1) return num_pos_buckets - 1;
+  return (int32_t)i_minus_j;
+}
+
+/* Time bucket: floor(log2(1 + dt)) clipped to [0, NT-1], on integers.
+ * floor(log2(u)) for an integer u >= 1 is the number of times u can be halved
+ * before it reaches 1. */
+int32_t oracle_time_bucket(int64_t dt, int32_t num_time_buckets) {
+  if (dt < 0) dt = 0;
+  uint64_t u = (uint64_t)dt + 1u;
+  int32_t e = 0;
+  while (u > 1u) { u >>= 1; e++; }
+  if (e > num_time_buckets - 1) e = num_time_buckets - 1;
+  return e;
+}
+
+typedef struct {
+  int32_t kind;
+  const int64_t* ts;      /* [T] timestamps (RAB_PT)                        */
+  const double* w_pos;    /* [H_tab * stride_p] position table              */
+  const double* w_time;   /* [H_tab * stride_t] time table                  */
+  int32_t num_pos, num_time;
+  int64_t head_stride_pos, head_stride_time; /* 0 = one table for all heads */
+  const double* slopes;   /* [H] ALiBi slopes                               */
+} oracle_bias;
+
+/* rab^{p,t}(i, j) for head h of a user whose first token is token `base`. */
+static double bias_value(const oracle_bias* bs, int h, int64_t base, int64_t i, int64_t j) {
+  if (bs->kind == ORACLE_BIAS_RAB_PT) {
+    int32_t pb = oracle_pos_bucket(i - j, bs->num_pos);
+    int32_t tb = oracle_time_bucket(bs->ts[base + i] - bs->ts[base + j], bs->num_time);
+    return bs->w_pos[h * bs->head_stride_pos + pb] + bs->w_time[h * bs->head_stride_time + tb];
+  }
+  if (bs->kind == ORACLE_BIAS_ALIBI) {
+    return -bs->slopes[h] * (double)(i - j);
+  }
+  return 0.0;
+}
+
+/* One output row of eq. (2) for user b, head h, local row i:
+ *   O[i,:] = out_scale * sum_{j <= i} SiLU(alpha * <q_i, k_j> + rab(i,j)) * v_j
+ * q, k, v are [T, H, d] with token row strides (in elements). */
+static void attn_row(int64_t base, int h, int64_t i, int H, int dqk, int dv,
+                     const double* q, int64_t qs, const double* k, int64_t ks,
+                     const double* v, int64_t vs, const oracle_bias* bs,
+                     double alpha, double out_scale, double* out /* [dv] */) {
+  for (int c = 0; c < dv; c++) out[c] = 0.0;
+  const double* qi = q + (base + i) * qs + (int64_t)h * dqk;
+  for (int64_t j = 0; j <= i; j++) {
+    const double* kj = k + (base + j) * ks + (int64_t)h * dqk;
+    const double* vj = v + (base + j) * vs + (int64_t)h * dv;
+    double s = 0.0;
+    for (int c = 0; c < dqk; c++) s += qi[c] * kj[c];
+    double a = silu(alpha * s + bias_value(bs, h, base, i, j));
+    for (int c = 0; c < dv; c++) out[c] += a * vj[c];
+  }
+  for (int c = 0; c < dv; c++) out[c] *= out_scale;
+  (void)H;
+}
+
+/* Full jagged attention: o is [T, H, dv] contiguous. */
+void oracle_attention(int32_t B, int32_t H, int32_t dqk, int32_t dv, const int64_t* offsets,
+                      const double* q, int64_t q_stride, const double* k, int64_t k_stride,
+                      const double* v, int64_t v_stride, int32_t bias_kind, const int64_t* ts,
+                      const double* w_pos, int32_t num_pos, int64_t head_stride_pos,
+                      const double* w_time, int32_t num_time, int64_t head_stride_time,
+                      const double* slopes, double alpha, double out_scale, double* o) {
+  oracle_bias bs = {bias_kind, ts, w_pos, w_time, num_pos, num_time,
+                    head_stride_pos, head_stride_time, slopes};
+  int64_t n_items = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t it = 0; it < n_items; it++) {
+    int32_t b = (int32_t)(it / H), h = (int32_t)(it % H);
+    int64_t base = offsets[b], n = offsets[b + 1] - offsets[b];
+    for (int64_t i = 0; i < n; i++)
+      attn_row(base, h, i, H, dqk, dv, q, q_stride, k, k_stride, v, v_stride, &bs, alpha,
+               out_scale, o + ((base + i) * H + h) * (int64_t)dv);
+  }
+}
+
+/* Selected rows only: rows[r] = (token t, head h); out is [R, dv].
+ * Used to check outputs at full workload sizes one row at a time. */
+void oracle_attention_rows(int32_t B, int32_t H, int32_t dqk, int32_t dv, const int64_t* offsets,
+                           const double* q, int64_t q_stride, const double* k, int64_t k_stride,
+                           const double* v, int64_t v_stride, int32_t bias_kind, const int64_t* ts,
+                           const double* w_pos, int32_t num_pos, int64_t head_stride_pos,
+                           const double* w_time, int32_t num_time, int64_t head_stride_time,
+                           const double* slopes, double alpha, double out_scale, int64_t R,
+                           const int64_t* row_token, const int32_t* row_head, double* out) {
+  oracle_bias bs = {bias_kind, ts, w_pos, w_time, num_pos, num_time,
+                    head_stride_pos, head_stride_time, slopes};
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t r = 0; r < R; r++) {
+    int64_t t = row_token[r];
+    int32_t b = 0;
+    while (b < B && offsets[b + 1] <= t) b++; /* user that owns token t */
+    int64_t base = offsets[b];
+    attn_row(base, row_head[r], t - base, H, dqk, dv, q, q_stride, k, k_stride, v, v_stride,
+             &bs, alpha, out_scale, out + r * (int64_t)dv);
+  }
+}
+
+/* One HSTU layer [AS §3.1 eqs. (1)-(3)]:
+ *   Z = SiLU(X W1^T + b1);  U | V | Q | K = column blocks of Z (widths H*dv, H*dv,
+ *       H*dqk, H*dqk; head h owns columns [h*d, (h+1)*d) of each block);
+ *   O = eq. (2) on Q, K, V;
+ *   Y = (LayerNorm(O) * U) W2^T + b2   (+ X when residual != 0)
+ * LayerNorm runs over the H*dv features of a token, biased variance, then
+ * gamma/beta.  W1 is [2H(dqk+dv), D], W2 is [D, H*dv] (row = output feature).
+ * z_out [T, 2H(dqk+dv)] and o_out [T, H*dv] are optional (may be NULL). */
+void oracle_layer(int32_t B, int32_t D, int32_t H, int32_t dqk, int32_t dv, const int64_t* offsets,
+                  const double* x, const double* w1, const double* b1, const double* gamma,
+                  const double* beta, double ln_eps, const double* w2, const double* b2,
+                  int32_t bias_kind, const int64_t* ts, const double* w_pos, int32_t num_pos,
+                  int64_t head_stride_pos, const double* w_time, int32_t num_time,
+                  int64_t head_stride_time, const double* slopes, double alpha, int32_t residual,
+                  double* y, double* z_out, double* o_out) {
+  int64_t T = offsets[B];
+  int64_t N1 = 2LL * H * (dqk + dv);
+  int64_t HV = (int64_t)H * dv;
+  double* z = z_out ? z_out : (double*)malloc(sizeof(double) * (size_t)(T * N1 + 1));
+  double* o = o_out ? o_out : (double*)malloc(sizeof(double) * (size_t)(T * HV + 1));
+
+  /* eq. (1): pointwise projection with SiLU */
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; t++) {
+    for (int64_t n = 0; n < N1; n++) {
+      double acc = b1[n];
+      for (int64_t c = 0; c < D; c++) acc += x[t * D + c] * w1[n * D + c];
+      z[t * N1 + n] = silu(acc);
+    }
+  }
+  /* Split: U = cols [0, HV), V = [HV, 2HV), Q = [2HV, 2HV + H dqk), K = rest */
+  const double* U = z;
+  const double* V = z + HV;
+  const double* Q = z + 2 * HV;
+  const double* K = z + 2 * HV + (int64_t)H * dqk;
+
+  /* eq. (2) */
+  oracle_attention(B, H, dqk, dv, offsets, Q, N1, K, N1, V, N1, bias_kind, ts, w_pos, num_pos,
+                   head_stride_pos, w_time, num_time, head_stride_time, slopes, alpha, 1.0, o);
+
+  /* eq. (3) */
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; t++) {
+    const double* ot = o + t * HV;
+    double mean = 0.0, var = 0.0;
+    for (int64_t c = 0; c < HV; c++) mean += ot[c];
+    mean /= (double)HV;
+    for (int64_t c = 0; c < HV; c++) var += (ot[c] - mean) * (ot[c] - mean);
+    var /= (double)HV;
+    double rstd = 1.0 / sqrt(var + ln_eps);
+    double* g = (double*)malloc(sizeof(double) * (size_t)HV);
+    for (int64_t c = 0; c < HV; c++)
+      g[c] = ((ot[c] - mean) * rstd * gamma[c] + beta[c]) * U[t * N1 + c];
+    for (int64_t n = 0; n < D; n++) {
+      double acc = b2[n];
+      for (int64_t c = 0; c < HV; c++) acc += g[c] * w2[n * HV + c];
+      if (residual) acc += x[t * D + n];
+      y[t * D + n] = acc;
+    }
+    free(g);
+  }
+  if (!z_out) free(z);
+  if (!o_out) free(o);
+}
