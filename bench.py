@@ -1,0 +1,180 @@
+#!/usr/bin/env python3
+"""Benchmark: HSTU jagged causal pointwise attention on one MI355X.
+
+Workload: the long-sequence bf16 attention batch -- 16 users with lognormal
+lengths (median 2048) clipped to [256, 8192], H = 8 heads, d_qk = d_v = 64,
+alpha = 1/8192, relative bias from 256 position buckets and 32 log2 time-delta
+buckets, Q, K, V ~ N(0, 1) (seed 1002).  One step = the jagged scheduler plus
+the attention kernel over the whole batch, inputs resident in device memory.
+
+Prints one JSON line: causal TFLOP/s (FLOPs = sum_b H n_b (n_b + 1) / 2 * 2 (d_qk + d_v)),
+tokens/s, the attention kernel's roofline figures (HIP events around its launches)
+and the fp64 CPU oracle timed on a bounded sample of the same rows.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+METRIC = "HSTU jagged causal attn TFLOP/s + tokens/s on 1 MI355X; % of bf16 MFMA peak"
+COUNTERS = os.path.join(ROOT, "profiles", "attn_long_hbm_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "hstu_sequential_transduction_jagged_amd", "csrc", "attention.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def causal_flops(lengths, H, dqk, dv):
+    return float(sum(H * int(n) * (int(n) + 1) // 2 * 2 * (dqk + dv) for n in lengths))
+
+
+def traffic_from_profile(launch_bytes_alg):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs, or None when
+    none were taken or the kernel source changed since."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, seconds=15.0, seed=7):
+    """The fp64 oracle (as it stands) on a random sample of (token, head) rows of the
+    same workload, sized to about `seconds` of CPU time; rate in causal TFLOP/s."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(seed)
+    offs = inp.offsets.astype(np.int64)
+    b = oracle.Bias(oracle.BIAS_RAB_PT, inp.ts, inp.bias.w_pos, inp.bias.w_time)
+
+    def run(R):
+        toks = rng.integers(0, inp.T, size=R)
+        heads = rng.integers(0, inp.H, size=R)
+        bi = np.searchsorted(offs, toks, side="right") - 1
+        fl = float(((toks - offs[bi] + 1) * 2 * (inp.dqk + inp.dv)).sum())
+        t0 = time.perf_counter()
+        oracle.attention_rows(inp.offsets, inp.q, inp.k, inp.v, b, inp.alpha, toks, heads)
+        return fl, time.perf_counter() - t0
+
+    fl, dt = run(500)
+    R = int(min(inp.T * inp.H, max(500, 500 * seconds / max(dt, 1e-3))))
+    fl, dt = run(R)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d random (token, head) rows of the attn_long batch (%.3g causal FLOP), "
+                      "fp64, %.1f s" % (R, fl, dt),
+            "tokens_per_s_equiv": None}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention shards by user with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from hstu_sequential_transduction_jagged_amd import binding, synth
+    if not os.path.exists(binding.LIB_PATH):
+        from hstu_sequential_transduction_jagged_amd import build as _b
+        _b.build()
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = synth.attn_long()
+    lengths = np.diff(inp.offsets.astype(np.int64))
+    bf = torch.bfloat16
+    q = torch.from_numpy(inp.q).to(dev, bf)
+    k = torch.from_numpy(inp.k).to(dev, bf)
+    v = torch.from_numpy(inp.v).to(dev, bf)
+    offs = torch.from_numpy(inp.offsets.astype(np.int32)).to(dev)
+    ts = torch.from_numpy(inp.ts).to(dev)
+    wp = torch.from_numpy(inp.bias.w_pos).to(dev)
+    wt = torch.from_numpy(inp.bias.w_time).to(dev)
+    bias = binding.make_bias(binding.BIAS_RAB_PT, ts, wp, wt)
+    out = torch.empty((inp.T, inp.H, inp.dv), dtype=bf, device=dev)
+    ws = torch.empty(binding.attn_workspace_bytes(inp.B, inp.H, inp.max_seqlen), dtype=torch.uint8,
+                     device=dev)
+
+    def step(ev=None):
+        binding.hstu_attn_plan(binding.DTYPE_BF16, inp.B, inp.H, inp.dqk, offs, inp.max_seqlen, ws)
+        if ev is not None:
+            ev[0].record()
+        binding.hstu_attn_fwd_planned(q, k, v, offs, inp.max_seqlen, ws, bias, inp.alpha, 1.0,
+                                      out=out)
+        if ev is not None:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_s = float(np.mean(kern_ms)) / 1e3
+
+    flops = causal_flops(lengths, inp.H, inp.dqk, inp.dv)
+    T = int(inp.T)
+    value = flops / step_s / 1e12
+    achieved = flops / kern_s / 1e12
+    # algorithmic bytes per launch: q, k, v read once, o written once, timestamps, tables
+    alg_bytes = T * inp.H * (inp.dqk * 2 + inp.dv * 2) * 2 + T * 8 + (256 + 32) * 4
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attn_long", "B": inp.B, "H": inp.H, "d_qk": inp.dqk,
+                   "d_v": inp.dv, "N_max": 8192, "max_len": int(lengths.max()), "T": T,
+                   "causal_pairs": int(sum(int(n) * (int(n) + 1) // 2 for n in lengths)),
+                   "bias": "rab_pt P=256 NT=32", "alpha": inp.alpha, "seed": inp.seed},
+        "tokens_per_s": round(T / step_s, 1),
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(alg_bytes),
+                     "kernel": "attn_bf16_d64_kernel", "kernel_ms": round(kern_s * 1e3, 4),
+                     "flop_per_launch": flops, "algorithmic_bytes_per_launch": alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp)
+        res["cpu_baseline"].pop("tokens_per_s_equiv", None)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

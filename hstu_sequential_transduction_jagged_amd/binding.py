@@ -1,0 +1,276 @@
+"""ctypes binding of libhstu (declared in include/hstu.h).
+
+Argument marshalling only: tensors are PyTorch device tensors, their data
+pointers and the current HIP stream are passed through the C ABI, and every
+step of the computation runs in the library's kernels.  Workspaces are
+allocated here with PyTorch (the library itself never allocates).  If the
+shared library is missing this module raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhstu.so")
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+BIAS_NONE, BIAS_RAB_PT, BIAS_ALIBI = 0, 1, 2
+
+_P = ctypes.c_void_p
+_i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class HstuBias(ctypes.Structure):
+    _fields_ = [("kind", _i32), ("timestamps", _P), ("w_pos", _P), ("w_time", _P),
+                ("num_pos_buckets", _i32), ("num_time_buckets", _i32),
+                ("pos_head_stride", _i32), ("time_head_stride", _i32), ("alibi_slopes", _P)]
+
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "hstu_attn_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "hstu_attn_fwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P, _i64, _P,
+                             _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P, _P, _sz, _P]),
+    "hstu_attn_block_rows": (_i32, [_i32, _i32]),
+    "hstu_attn_plan": (_i32, [_i32, _i32, _i32, _i32, _P, _i32, _P, _sz, _P]),
+    "hstu_attn_fwd_planned": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P,
+                                     _i64, _P, _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P, _P,
+                                     _sz, _P]),
+    "hstu_layer_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
+    "hstu_layer_fwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _P, _P, _P,
+                              _P, _f32, _P, _P, ctypes.POINTER(HstuBias), _f32, _i32, _P, _P, _sz,
+                              _P]),
+    "hstu_layer_workspace_offsets": (None, [_i64, _i32, _i32, _i32, ctypes.POINTER(_sz),
+                                            ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "hstu_embed_sum_fwd": (_i32, [_i64, _i32, _P, _i64, _P, _i32, _P, _P, _P, _P]),
+    "hstu_validate_offsets": (_i32, [_i32, _P, _i64, _i32, _P, _P]),
+    "hstu_debug_buckets": (_i32, [_i32, _P, _P, _i32, _i32, _i64, _P, _P, _P, _P, _P]),
+    "hstu_status_string": (ctypes.c_char_p, [_i32]),
+    "hstu_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libhstu.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libhstu.so not found at %s: build it with "
+                               "hstu_sequential_transduction_jagged_amd/build.py" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+class HstuError(RuntimeError):
+    pass
+
+
+def _check(name, status):
+    if status != 0:
+        L = lib()
+        raise HstuError("%s failed: %s (%s)" % (name, L.hstu_status_string(status).decode(),
+                                                L.hstu_last_error().decode()))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise HstuError("unsupported dtype %s" % t.dtype)
+
+
+def make_bias(kind=BIAS_NONE, timestamps=None, w_pos=None, w_time=None, alibi_slopes=None):
+    """Build the hstu_bias struct from device tensors.  w_pos/w_time may be [P] (shared
+    across heads) or [H, P] (per head)."""
+    b = HstuBias()
+    b.kind = kind
+    keep = []
+    if kind == BIAS_RAB_PT:
+        for t in (timestamps, w_pos, w_time):
+            if t is None or not t.is_cuda:
+                raise HstuError("rab_pt bias needs device timestamps, w_pos and w_time")
+        if timestamps.dtype != torch.int64 or w_pos.dtype != torch.float32 or \
+                w_time.dtype != torch.float32:
+            raise HstuError("timestamps must be int64, tables float32")
+        w_pos, w_time, timestamps = w_pos.contiguous(), w_time.contiguous(), timestamps.contiguous()
+        b.timestamps, b.w_pos, b.w_time = _ptr(timestamps), _ptr(w_pos), _ptr(w_time)
+        b.num_pos_buckets = w_pos.shape[-1]
+        b.num_time_buckets = w_time.shape[-1]
+        b.pos_head_stride = w_pos.shape[-1] if w_pos.dim() == 2 else 0
+        b.time_head_stride = w_time.shape[-1] if w_time.dim() == 2 else 0
+        keep = [timestamps, w_pos, w_time]
+    elif kind == BIAS_ALIBI:
+        if alibi_slopes is not None:
+            alibi_slopes = alibi_slopes.contiguous()
+            if alibi_slopes.dtype != torch.float32:
+                raise HstuError("alibi slopes must be float32")
+            b.alibi_slopes = _ptr(alibi_slopes)
+            keep = [alibi_slopes]
+    b._keep = keep  # keep tensors alive as long as the struct
+    return b
+
+
+def attn_workspace_bytes(B, H, max_seqlen):
+    return int(lib().hstu_attn_workspace_bytes(B, H, max_seqlen))
+
+
+def attn_block_rows(dtype_code, d):
+    return int(lib().hstu_attn_block_rows(dtype_code, d))
+
+
+def _rows(t: torch.Tensor, name: str):
+    """[T, H, d] tensor (possibly a strided view) -> (row stride, H, d)."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise HstuError("%s must be [T, H, d] with contiguous heads" % name)
+    return t.stride(0), t.shape[1], t.shape[2]
+
+
+def hstu_attn_fwd(q, k, v, offsets, max_seqlen, bias: Optional[HstuBias] = None, alpha=1.0,
+                  out_scale=1.0, out=None, workspace=None):
+    """Jagged causal pointwise attention.  q, k, v: [T, H, d] device tensors (bf16 or fp32,
+    row-strided views allowed); offsets: int32 [B+1] on the device.  Returns o [T, H, d]."""
+    if not q.is_cuda:
+        raise HstuError("inputs must be device tensors")
+    dt = _dtype_code(q)
+    qs, H, d = _rows(q, "q")
+    ks, _, _ = _rows(k, "k")
+    vs, _, dv = _rows(v, "v")
+    T = q.shape[0]
+    B = offsets.numel() - 1
+    if offsets.dtype != torch.int32:
+        raise HstuError("offsets must be int32")
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    need = attn_workspace_bytes(B, H, max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    bias = bias if bias is not None else make_bias(BIAS_NONE)
+    st = lib().hstu_attn_fwd(dt, B, H, d, dv, _ptr(offsets), int(max_seqlen), T, _ptr(q), qs,
+                             _ptr(k), ks, _ptr(v), vs, ctypes.byref(bias), float(alpha),
+                             float(out_scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                             _stream(q.device))
+    _check("hstu_attn_fwd", st)
+    return out
+
+
+def hstu_attn_plan(dtype_code, B, H, d, offsets, max_seqlen, workspace):
+    """Run the jagged scheduler only, writing the work list into `workspace`."""
+    st = lib().hstu_attn_plan(dtype_code, B, H, d, _ptr(offsets), int(max_seqlen), _ptr(workspace),
+                              workspace.numel(), _stream(workspace.device))
+    _check("hstu_attn_plan", st)
+    return workspace
+
+
+def hstu_attn_fwd_planned(q, k, v, offsets, max_seqlen, workspace, bias=None, alpha=1.0,
+                          out_scale=1.0, out=None):
+    """Attention on a work list that hstu_attn_plan wrote into `workspace`."""
+    dt = _dtype_code(q)
+    qs, H, d = _rows(q, "q")
+    ks, _, _ = _rows(k, "k")
+    vs, _, dv = _rows(v, "v")
+    T = q.shape[0]
+    B = offsets.numel() - 1
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    bias = bias if bias is not None else make_bias(BIAS_NONE)
+    st = lib().hstu_attn_fwd_planned(dt, B, H, d, dv, _ptr(offsets), int(max_seqlen), T, _ptr(q),
+                                     qs, _ptr(k), ks, _ptr(v), vs, ctypes.byref(bias),
+                                     float(alpha), float(out_scale), _ptr(out), _ptr(workspace),
+                                     workspace.numel(), _stream(q.device))
+    _check("hstu_attn_fwd_planned", st)
+    return out
+
+
+def layer_workspace_bytes(B, T, D, H, dqk, dv, max_seqlen):
+    return int(lib().hstu_layer_workspace_bytes(B, T, D, H, dqk, dv, max_seqlen))
+
+
+def layer_workspace_offsets(T, H, dqk, dv):
+    z, o, a = _sz(), _sz(), _sz()
+    lib().hstu_layer_workspace_offsets(T, H, dqk, dv, ctypes.byref(z), ctypes.byref(o),
+                                       ctypes.byref(a))
+    return z.value, o.value, a.value
+
+
+def hstu_layer_fwd(x, offsets, max_seqlen, w1, b1, ln_gamma, ln_beta, w2, b2, H, dqk, dv,
+                   bias: Optional[HstuBias] = None, alpha=1.0, residual=False, ln_eps=1e-5,
+                   out=None, workspace=None):
+    """One HSTU layer forward (bf16).  x: [T, D]; w1: [2H(dqk+dv), D]; w2: [D, H dv];
+    b1, b2, ln_gamma, ln_beta: fp32 or None.  Returns y [T, D]."""
+    if x.dtype != torch.bfloat16:
+        raise HstuError("the layer runs in bf16")
+    T, D = x.shape
+    B = offsets.numel() - 1
+    if out is None:
+        out = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    need = layer_workspace_bytes(B, T, D, H, dqk, dv, max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    bias = bias if bias is not None else make_bias(BIAS_NONE)
+    for name, t in (("x", x), ("w1", w1), ("w2", w2), ("b1", b1), ("b2", b2),
+                    ("ln_gamma", ln_gamma), ("ln_beta", ln_beta)):
+        if t is not None and not t.is_contiguous():
+            raise HstuError("%s must be contiguous" % name)
+    st = lib().hstu_layer_fwd(DTYPE_BF16, B, D, H, dqk, dv, _ptr(offsets), int(max_seqlen), T,
+                              _ptr(x), _ptr(w1), _ptr(b1),
+                              _ptr(ln_gamma), _ptr(ln_beta), float(ln_eps), _ptr(w2),
+                              _ptr(b2), ctypes.byref(bias), float(alpha), int(bool(residual)),
+                              _ptr(out), _ptr(workspace), workspace.numel(), _stream(x.device))
+    _check("hstu_layer_fwd", st)
+    return out
+
+
+def hstu_embed_sum_fwd(item_table, action_table, item_ids, action_ids, out=None):
+    """GenRank action-oriented tokens: x[t] = item_table[item_ids[t]] + action_table[action_ids[t]]."""
+    T = item_ids.numel()
+    dim = item_table.shape[1]
+    if out is None:
+        out = torch.empty((T, dim), dtype=torch.bfloat16, device=item_table.device)
+    st = lib().hstu_embed_sum_fwd(T, dim, _ptr(item_table), item_table.shape[0],
+                                  _ptr(action_table), action_table.shape[0], _ptr(item_ids),
+                                  _ptr(action_ids), _ptr(out), _stream(item_table.device))
+    _check("hstu_embed_sum_fwd", st)
+    return out
+
+
+def hstu_validate_offsets(offsets, total_tokens, max_seqlen):
+    flags = torch.zeros(1, dtype=torch.int32, device=offsets.device)
+    st = lib().hstu_validate_offsets(offsets.numel() - 1, _ptr(offsets), int(total_tokens),
+                                     int(max_seqlen), _ptr(flags), _stream(offsets.device))
+    _check("hstu_validate_offsets", st)
+    return flags
+
+
+def hstu_debug_buckets(offsets, timestamps, num_pos, num_time, token_i, token_j):
+    R = token_i.numel()
+    pb = torch.empty(R, dtype=torch.int32, device=offsets.device)
+    tb = torch.empty(R, dtype=torch.int32, device=offsets.device)
+    st = lib().hstu_debug_buckets(offsets.numel() - 1, _ptr(offsets), _ptr(timestamps), num_pos,
+                                  num_time, R, _ptr(token_i), _ptr(token_j), _ptr(pb), _ptr(tb),
+                                  _stream(offsets.device))
+    _check("hstu_debug_buckets", st)
+    return pb, tb
+
+
+def status_string(code):
+    return lib().hstu_status_string(code).decode()

@@ -1,0 +1,367 @@
+// C ABI of libhstu: argument checks, workspace carving and kernel launches.
+// Every entry point only enqueues work on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/hstu.h"
+#include "hstu_internal.h"
+
+using namespace hstu;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+hstu_status fail(hstu_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+hstu_status fail(hstu_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+hstu_status check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return HSTU_OK;
+  return fail(HSTU_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kHeader = 256;
+constexpr int kMinBlockRows = 128;  // smallest query tile of any attention kernel
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+hstu_status check_bias(const hstu_bias* bias, int32_t H, BiasArgs* out) {
+  *out = BiasArgs{};
+  if (!bias || bias->kind == HSTU_BIAS_NONE) {
+    out->kind = 0;
+    return HSTU_OK;
+  }
+  if (bias->kind == HSTU_BIAS_RAB_PT) {
+    if (!bias->timestamps || !bias->w_pos || !bias->w_time)
+      return fail(HSTU_ERR_INVALID_ARG, "rab_pt bias needs timestamps, w_pos and w_time");
+    if (bias->num_pos_buckets < 1 || bias->num_pos_buckets > kMaxPosBuckets)
+      return fail(HSTU_ERR_UNSUPPORTED, "num_pos_buckets must be in [1, %d]", kMaxPosBuckets);
+    if (bias->num_time_buckets < 1 || bias->num_time_buckets > kMaxTimeBuckets)
+      return fail(HSTU_ERR_UNSUPPORTED, "num_time_buckets must be in [1, %d]", kMaxTimeBuckets);
+    if (bias->pos_head_stride < 0 || bias->time_head_stride < 0)
+      return fail(HSTU_ERR_INVALID_ARG, "table head strides must be >= 0");
+    if ((bias->pos_head_stride && bias->pos_head_stride < bias->num_pos_buckets) ||
+        (bias->time_head_stride && bias->time_head_stride < bias->num_time_buckets))
+      return fail(HSTU_ERR_INVALID_ARG, "a nonzero table head stride must cover the table");
+    out->kind = 1;
+    out->ts = bias->timestamps;
+    out->w_pos = bias->w_pos;
+    out->w_time = bias->w_time;
+    out->num_pos = bias->num_pos_buckets;
+    out->num_time = bias->num_time_buckets;
+    out->pos_stride = bias->pos_head_stride;
+    out->time_stride = bias->time_head_stride;
+    return HSTU_OK;
+  }
+  if (bias->kind == HSTU_BIAS_ALIBI) {
+    out->kind = 2;
+    out->slopes = bias->alibi_slopes;
+    return HSTU_OK;
+  }
+  (void)H;
+  return fail(HSTU_ERR_INVALID_ARG, "unknown bias kind %d", bias->kind);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hstu_status_string(int32_t status) {
+  switch (status) {
+    case HSTU_OK: return "ok";
+    case HSTU_ERR_INVALID_ARG: return "invalid argument";
+    case HSTU_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case HSTU_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case HSTU_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* hstu_last_error(void) { return g_last_error; }
+
+size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen) {
+  if (B < 0 || H < 0 || max_seqlen < 0) return 0;
+  const int64_t items = (int64_t)B * H * ceil_div(max_seqlen, kMinBlockRows);
+  return kHeader + align256((size_t)items * sizeof(WorkItem));
+}
+
+int32_t hstu_attn_block_rows(int32_t dt, int32_t d) {
+  if (dt == HSTU_DTYPE_BF16) return attn_block_rows_bf16(d);
+  if (dt == HSTU_DTYPE_F32) return attn_block_rows_f32(d);
+  return 0;
+}
+
+static hstu_status attn_check(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                              int32_t max_seqlen, int64_t total_tokens, int* block_rows) {
+  if (dt != HSTU_DTYPE_BF16 && dt != HSTU_DTYPE_F32)
+    return fail(HSTU_ERR_INVALID_ARG, "unknown dtype %d", dt);
+  if (B < 0 || H < 1 || max_seqlen < 0 || total_tokens < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "negative size (B=%d H=%d max_seqlen=%d T=%lld)", B, H,
+                max_seqlen, (long long)total_tokens);
+  if (d_qk != d_v) return fail(HSTU_ERR_UNSUPPORTED, "d_qk != d_v is not supported");
+  *block_rows = hstu_attn_block_rows(dt, d_qk);
+  if (*block_rows == 0)
+    return fail(HSTU_ERR_UNSUPPORTED, "head dim %d unsupported for dtype %d", d_qk, dt);
+  if (max_seqlen > 65536) return fail(HSTU_ERR_UNSUPPORTED, "max_seqlen above 65536");
+  if (H > 65535) return fail(HSTU_ERR_UNSUPPORTED, "H above 65535");
+  return HSTU_OK;
+}
+
+static hstu_status workspace_check(const void* workspace, size_t workspace_bytes, int32_t B,
+                                   int32_t H, int32_t max_seqlen) {
+  const size_t need = hstu_attn_workspace_bytes(B, H, max_seqlen);
+  if (!workspace) return fail(HSTU_ERR_INVALID_ARG, "null workspace");
+  if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(HSTU_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  return HSTU_OK;
+}
+
+hstu_status hstu_attn_plan(int32_t dt, int32_t B, int32_t H, int32_t d, const int32_t* offsets,
+                           int32_t max_seqlen, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  g_last_error[0] = 0;
+  int block_rows = 0;
+  hstu_status st = attn_check(dt, B, H, d, d, max_seqlen, 0, &block_rows);
+  if (st != HSTU_OK) return st;
+  if (B == 0 || max_seqlen == 0) return HSTU_OK;
+  if (!offsets) return fail(HSTU_ERR_INVALID_ARG, "null offsets");
+  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen);
+  if (st != HSTU_OK) return st;
+  const int32_t max_tiles = (int32_t)ceil_div(max_seqlen, block_rows);
+  return check_hip(launch_schedule(offsets, B, H, block_rows, max_tiles, (int32_t*)workspace,
+                                   (WorkItem*)((char*)workspace + kHeader), stream),
+                   "scheduler launch");
+}
+
+static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                                const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
+                                const void* q, int64_t q_row_stride, const void* k,
+                                int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                                const hstu_bias* bias, float alpha, float out_scale, void* o,
+                                bool o_f32, const void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  int block_rows = 0;
+  hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
+  if (st != HSTU_OK) return st;
+  BiasArgs ba;
+  st = check_bias(bias, H, &ba);
+  if (st != HSTU_OK) return st;
+  if (B == 0 || total_tokens == 0 || max_seqlen == 0) return HSTU_OK;
+  if (!offsets || !q || !k || !v || !o) return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  const int64_t rowlen = (int64_t)H * d_qk;
+  if (q_row_stride < rowlen || k_row_stride < rowlen || v_row_stride < rowlen)
+    return fail(HSTU_ERR_INVALID_ARG, "row stride smaller than H*d");
+  const int elem = dt == HSTU_DTYPE_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (q_row_stride * elem) % 16 || (k_row_stride * elem) % 16 || (v_row_stride * elem) % 16)
+    return fail(HSTU_ERR_INVALID_ARG, "q/k/v/o rows must be 16-byte aligned");
+  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen);
+  if (st != HSTU_OK) return st;
+
+  const int32_t max_tiles = (int32_t)ceil_div(max_seqlen, block_rows);
+  AttnArgs a{};
+  a.offsets = offsets;
+  a.work_count = (const int32_t*)workspace;
+  a.work = (const WorkItem*)((const char*)workspace + kHeader);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.q_stride = q_row_stride;
+  a.k_stride = k_row_stride;
+  a.v_stride = v_row_stride;
+  a.H = H;
+  a.o_f32 = o_f32 ? 1 : 0;
+  a.bias = ba;
+  a.alpha = alpha;
+  a.out_scale = out_scale;
+  const int64_t grid = (int64_t)B * H * max_tiles;
+  if (grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
+  hipError_t e = dt == HSTU_DTYPE_BF16 ? launch_attn_bf16(d_qk, a, (int)grid, stream)
+                                       : launch_attn_f32(d_qk, a, (int)grid, stream);
+  return check_hip(e, "attention launch");
+}
+
+hstu_status hstu_attn_fwd_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                                  const int32_t* offsets, int32_t max_seqlen,
+                                  int64_t total_tokens, const void* q, int64_t q_row_stride,
+                                  const void* k, int64_t k_row_stride, const void* v,
+                                  int64_t v_row_stride, const hstu_bias* bias, float alpha,
+                                  float out_scale, void* o, const void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  return attn_planned(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q, q_row_stride, k,
+                      k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, false, workspace,
+                      workspace_bytes, stream);
+}
+
+hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                          const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
+                          const void* q, int64_t q_row_stride, const void* k,
+                          int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                          const hstu_bias* bias, float alpha, float out_scale, void* o,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  int block_rows = 0;
+  hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
+  if (st != HSTU_OK) return st;
+  BiasArgs ba;
+  st = check_bias(bias, H, &ba);
+  if (st != HSTU_OK) return st;
+  if (B == 0 || total_tokens == 0 || max_seqlen == 0) return HSTU_OK;
+  if (!offsets || !q || !k || !v || !o || !workspace)
+    return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  // argument checks of the attention half first, so that nothing is enqueued on error
+  const int64_t rowlen = (int64_t)H * d_qk;
+  if (q_row_stride < rowlen || k_row_stride < rowlen || v_row_stride < rowlen)
+    return fail(HSTU_ERR_INVALID_ARG, "row stride smaller than H*d");
+  const int elem = dt == HSTU_DTYPE_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (q_row_stride * elem) % 16 || (k_row_stride * elem) % 16 || (v_row_stride * elem) % 16)
+    return fail(HSTU_ERR_INVALID_ARG, "q/k/v/o rows must be 16-byte aligned");
+  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen);
+  if (st != HSTU_OK) return st;
+  st = hstu_attn_plan(dt, B, H, d_qk, offsets, max_seqlen, workspace, workspace_bytes, stream);
+  if (st != HSTU_OK) return st;
+  return hstu_attn_fwd_planned(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q,
+                               q_row_stride, k, k_row_stride, v, v_row_stride, bias, alpha,
+                               out_scale, o, workspace, workspace_bytes, stream);
+}
+
+void hstu_layer_workspace_offsets(int64_t total_tokens, int32_t H, int32_t d_qk, int32_t d_v,
+                                  size_t* z_offset, size_t* o_offset, size_t* attn_offset) {
+  const int64_t N1 = 2LL * H * (d_qk + d_v);
+  const size_t z_bytes = align256((size_t)(total_tokens * N1 * 2));
+  const size_t o_bytes = align256((size_t)(total_tokens * H * d_v * 4));
+  if (z_offset) *z_offset = 0;
+  if (o_offset) *o_offset = z_bytes;
+  if (attn_offset) *attn_offset = z_bytes + o_bytes;
+}
+
+size_t hstu_layer_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_model, int32_t H,
+                                  int32_t d_qk, int32_t d_v, int32_t max_seqlen) {
+  (void)d_model;
+  if (B < 0 || total_tokens < 0 || H < 1 || d_qk < 1 || d_v < 1) return 0;
+  size_t attn_off = 0;
+  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, nullptr, nullptr, &attn_off);
+  return attn_off + hstu_attn_workspace_bytes(B, H, max_seqlen);
+}
+
+hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,
+                           int32_t d_v, const int32_t* offsets, int32_t max_seqlen,
+                           int64_t total_tokens, const void* x, const void* w1, const float* b1,
+                           const float* ln_gamma, const float* ln_beta, float ln_eps,
+                           const void* w2, const float* b2, const hstu_bias* bias, float alpha,
+                           int32_t residual, void* y, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (dt != HSTU_DTYPE_BF16) return fail(HSTU_ERR_UNSUPPORTED, "the layer runs in bf16 only");
+  if (B < 0 || total_tokens < 0 || d_model < 1 || H < 1 || max_seqlen < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "bad sizes");
+  if (d_qk != d_v || d_qk != 64) return fail(HSTU_ERR_UNSUPPORTED, "layer needs d_qk = d_v = 64");
+  const int32_t N1 = 2 * H * (d_qk + d_v);
+  const int32_t HV = H * d_v;
+  if (d_model % 128 || N1 % 128 || HV % 64 || HV > 1024)
+    return fail(HSTU_ERR_UNSUPPORTED,
+                "layer needs d_model %% 128 == 0, 2H(dqk+dv) %% 128 == 0, H dv <= 1024");
+  if (!(ln_eps > 0.f)) return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be > 0");
+  BiasArgs ba;
+  hstu_status st = check_bias(bias, H, &ba);
+  if (st != HSTU_OK) return st;
+  if (B == 0 || total_tokens == 0) return HSTU_OK;
+  if (!offsets || !x || !w1 || !w2 || !y || !workspace)
+    return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(y))
+    return fail(HSTU_ERR_INVALID_ARG, "x, w1, w2 and y must be 16-byte aligned");
+  if (x == y) return fail(HSTU_ERR_INVALID_ARG, "y may not alias x");
+  const size_t need = hstu_layer_workspace_bytes(B, total_tokens, d_model, H, d_qk, d_v, max_seqlen);
+  if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(HSTU_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  size_t zo, oo, ao;
+  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, &zo, &oo, &ao);
+  bf16* z = (bf16*)((char*)workspace + zo);
+  float* obuf = (float*)((char*)workspace + oo);
+  void* aws = (char*)workspace + ao;
+  const size_t aws_bytes = workspace_bytes - ao;
+
+  st = check_hip(launch_f1_gemm_silu((const bf16*)x, (const bf16*)w1, b1, z, total_tokens, N1,
+                                     d_model, stream),
+                 "f1 launch");
+  if (st != HSTU_OK) return st;
+  // Split: U | V | Q | K column blocks of Z
+  const bf16* U = z;
+  const bf16* V = z + HV;
+  const bf16* Q = z + 2 * HV;
+  const bf16* K = z + 2 * HV + H * d_qk;
+  st = hstu_attn_plan(HSTU_DTYPE_BF16, B, H, d_qk, offsets, max_seqlen, aws, aws_bytes, stream);
+  if (st != HSTU_OK) return st;
+  st = attn_planned(HSTU_DTYPE_BF16, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, Q, N1, K,
+                    N1, V, N1, bias, alpha, 1.0f, obuf, true, aws, aws_bytes, stream);
+  if (st != HSTU_OK) return st;
+  return check_hip(launch_ln_gate_f2(obuf, U, N1, ln_gamma, ln_beta, ln_eps, (const bf16*)w2, b2,
+                                     residual ? (const bf16*)x : nullptr, (bf16*)y, total_tokens,
+                                     d_model, HV, stream),
+                   "f2 launch");
+}
+
+hstu_status hstu_embed_sum_fwd(int64_t total_tokens, int32_t dim, const void* item_table,
+                               int64_t num_items, const void* action_table, int32_t num_actions,
+                               const int32_t* item_ids, const int32_t* action_ids, void* x,
+                               hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (total_tokens < 0 || dim < 1 || num_items < 0 || num_actions < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "bad sizes");
+  if (dim % 8) return fail(HSTU_ERR_UNSUPPORTED, "dim must be a multiple of 8");
+  if (total_tokens == 0) return HSTU_OK;
+  if (!item_table || !action_table || !item_ids || !action_ids || !x)
+    return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(item_table) || !aligned16(action_table) || !aligned16(x))
+    return fail(HSTU_ERR_INVALID_ARG, "tables and x must be 16-byte aligned");
+  return check_hip(launch_embed_sum(total_tokens, dim, (const bf16*)item_table, num_items,
+                                    (const bf16*)action_table, num_actions, item_ids, action_ids,
+                                    (bf16*)x, stream),
+                   "embed launch");
+}
+
+hstu_status hstu_validate_offsets(int32_t B, const int32_t* offsets, int64_t total_tokens,
+                                  int32_t max_seqlen, int32_t* flags_out, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (B < 0) return fail(HSTU_ERR_INVALID_ARG, "B < 0");
+  if (!offsets || !flags_out) return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  return check_hip(launch_validate_offsets(B, offsets, total_tokens, max_seqlen, flags_out, stream),
+                   "validate launch");
+}
+
+hstu_status hstu_debug_buckets(int32_t B, const int32_t* offsets, const int64_t* timestamps,
+                               int32_t num_pos_buckets, int32_t num_time_buckets, int64_t R,
+                               const int64_t* token_i, const int64_t* token_j,
+                               int32_t* pos_bucket_out, int32_t* time_bucket_out,
+                               hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (B < 1 || R < 0 || num_pos_buckets < 1 || num_time_buckets < 1 || num_time_buckets > 64)
+    return fail(HSTU_ERR_INVALID_ARG, "bad sizes");
+  if (R == 0) return HSTU_OK;
+  if (!offsets || !timestamps || !token_i || !token_j || !pos_bucket_out || !time_bucket_out)
+    return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  return check_hip(launch_debug_buckets(B, offsets, timestamps, num_pos_buckets, num_time_buckets,
+                                        R, token_i, token_j, pos_bucket_out, time_bucket_out,
+                                        stream),
+                   "debug launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,523 @@
+// Jagged causal pointwise aggregated attention for gfx950.
+//
+// Computes, per user b, head h and local row i,
+//     O[i] = out_scale * sum_{j <= i} SiLU(alpha <q_i, k_j> + rab_h(i, j)) v_j
+// ("Actions Speak Louder than Words" reading notes §3.1 eq. (2) and §3.2: SiLU
+// applied element-wise, no softmax; causal mask including the diagonal as in
+// the toy layer of "4.4 推荐模型的 Scaling").
+//
+// Formulation used on the matrix cores.  Scores are produced transposed,
+// S^T = K Q^T, so that the accumulator of a 32x32 MFMA tile holds one query
+// per lane and 16 keys per lane in registers; that register set is exactly the
+// B operand of the next MFMA, O^T += V^T P^T, so the probabilities never leave
+// registers.  The key order inside a 16-key PV step is a fixed permutation of
+// the accumulator's row order, and V^T is stored in LDS in that permuted order.
+//
+// SiLU is evaluated in base-2 units: with y = -log2(e) x,
+//     SiLU(x) = x / (1 + e^-x) = -ln(2) * y / (1 + 2^y),
+// so the loop needs one fma (y = -log2(e) alpha s + bias_y), one exp2, one add,
+// one reciprocal and one multiply per score, and -ln(2) out_scale is applied
+// once per output.  (Folding -log2(e) alpha into Q instead would save the fma
+// but round the scaled Q to bf16, which doubles the output error.)
+//
+// Bias: rab_h(i, j) = w_pos[min(i-j, P-1)] + w_time[min(floor(log2(1+max(t_i-t_j,0))), NT-1)]
+// (tables per head or shared), or ALiBi -slope_h (i - j) (GenRank article, part
+// (2)).  Tables sit in LDS; for a 32x32 tile whose position bucket is saturated
+// and whose time-delta range falls in one bucket (decided exactly from the
+// tile's timestamp minima and maxima) the bias is one scalar, otherwise it is
+// gathered per element.  The n x n bias is never materialised.
+#include "hstu_internal.h"
+
+namespace hstu {
+namespace {
+
+// Key (0..31) of a 32x32 accumulator's register r in lane half hf: rows
+// 8*(r/4) + 4*hf + r%4 of the MFMA output layout.
+__device__ __forceinline__ int acc_key(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
+
+// MFMA k slot of key k16 (0..15) within a 16-key PV step (inverse of the
+// accumulator row order restricted to registers 8m..8m+7).
+__device__ __forceinline__ int pv_slot(int k16) {
+  int g = k16 >> 3, w = k16 & 7;
+  return 8 * (w >> 2) + 4 * g + (w & 3);
+}
+
+__device__ __forceinline__ int64_t shfl_xor_i64(int64_t v, int m) {
+  int lo = __shfl_xor((int)(uint32_t)(uint64_t)v, m, 64);
+  int hi = __shfl_xor((int)(uint32_t)((uint64_t)v >> 32), m, 64);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
+// min / max over each 32-lane half of the wave.
+__device__ __forceinline__ void half_minmax(int64_t& mn, int64_t& mx) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    int64_t a = shfl_xor_i64(mn, m), b = shfl_xor_i64(mx, m);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+}
+
+constexpr int64_t kTMax = 0x7fffffffffffffffLL;
+constexpr int64_t kTMin = -kTMax - 1;
+
+// ============================================================================================
+// bf16, d = 64: 4 waves x 64 queries = 256 query rows per work item, 64 keys per LDS stage.
+// ============================================================================================
+constexpr int kWaves = 4;
+constexpr int kQW = 64;
+constexpr int kBR = kWaves * kQW;
+constexpr int kKB = 64;
+constexpr int kD = 64;
+
+struct SmemBf16 {
+  bf16 k[2][kKB * kD];   // row = key, 8 chunks of 16 B, chunk c stored at c ^ (row & 7)
+  bf16 vt[2][kD * kKB];  // row = d, 64 keys in PV slot order, chunk c at c ^ ((d + d/8) & 7)
+  int64_t tk[2][kKB];
+  int64_t tkst[2][4];    // per 32-key half: min, max of valid key timestamps
+  float wpos[kMaxPosBuckets];   // -log2(e) * w_pos[h]
+  float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
+};
+
+__device__ __forceinline__ int k_off(int row, int chunk) { return row * kD + ((chunk ^ (row & 7)) << 3); }
+__device__ __forceinline__ int vt_off(int d, int chunk) { return d * kKB + ((chunk ^ ((d + (d >> 3)) & 7)) << 3); }
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
+  __shared__ SmemBf16 sm;
+  const int item = blockIdx.x;
+  if (item >= *a.work_count) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const WorkItem wi = a.work[item];
+  const int b = wi.b, h = wi.h, H = a.H;
+  const int64_t tok0 = a.offsets[b];
+  const int n = a.offsets[b + 1] - a.offsets[b];
+  const int q0 = wi.qt * kBR;
+  if (q0 >= n) return;
+  const int q_end = min(q0 + kBR, n);
+  const int n_tiles = (q_end + kKB - 1) / kKB;
+  const int qw0 = q0 + wave * kQW;
+  const int wq_last = min(qw0 + kQW, q_end) - 1;  // < qw0 when the wave has no rows
+
+  const bf16* __restrict__ qp = (const bf16*)a.q;
+  const bf16* __restrict__ kp = (const bf16*)a.k;
+  const bf16* __restrict__ vp = (const bf16*)a.v;
+  const int kind = a.bias.kind;
+  const int64_t* __restrict__ ts = a.bias.ts;
+
+  if (kind == 1) {
+    for (int i = tid; i < a.bias.num_pos; i += 256)
+      sm.wpos[i] = -kLog2e * a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i];
+    for (int i = tid; i < a.bias.num_time; i += 256)
+      sm.wtime[i] = -kLog2e * a.bias.w_time[(int64_t)h * a.bias.time_stride + i];
+  }
+  const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
+  float slope_y = 0.f;
+  if (kind == 2) slope_y = kLog2e * (a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H));
+
+  // ---- Q fragments (B operand of S^T = K Q^T), unscaled ----
+  const float cq = -a.alpha * kLog2e;
+  bf16x8 qop[2][4];
+  int64_t tq[2], tqmin[2], tqmax[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qw0 + 32 * qb + l32;
+    const bool valid = row <= wq_last;
+    const bf16* src = qp + (tok0 + row) * a.q_stride + (int64_t)h * kD + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (valid) raw = *(const u32x4*)(src + 16 * ks);
+      qop[qb][ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+    tq[qb] = 0;
+    tqmin[qb] = kTMax;
+    tqmax[qb] = kTMin;
+    if (kind == 1 && valid) {
+      tq[qb] = ts[tok0 + row];
+      tqmin[qb] = tq[qb];
+      tqmax[qb] = tq[qb];
+    }
+    if (kind == 1) half_minmax(tqmin[qb], tqmax[qb]);
+  }
+
+  f32x16 oacc[2][2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
+
+  // ---- staging: global -> registers -> LDS ----
+  u32x4 kreg[2], vreg[2];
+  int64_t treg = kTMax;
+  auto gload = [&](int t) {
+    const int j0 = t * kKB;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + 256 * u, row = c >> 3, chunk = c & 7;
+      const int key = j0 + row;
+      kreg[u] = u32x4{0u, 0u, 0u, 0u};
+      if (key < q_end) kreg[u] = *(const u32x4*)(kp + (tok0 + key) * a.k_stride + (int64_t)h * kD + 8 * chunk);
+    }
+    {
+      const int kpair = tid >> 3, ch = tid & 7;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = j0 + 2 * kpair + u;
+        vreg[u] = u32x4{0u, 0u, 0u, 0u};
+        if (key < q_end) vreg[u] = *(const u32x4*)(vp + (tok0 + key) * a.v_stride + (int64_t)h * kD + 8 * ch);
+      }
+    }
+    if (kind == 1 && tid < kKB) {
+      const int key = j0 + tid;
+      treg = key < q_end ? ts[tok0 + key] : kTMax;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + 256 * u, row = c >> 3, chunk = c & 7;
+      *(u32x4*)(&sm.k[buf][k_off(row, chunk)]) = kreg[u];
+    }
+    {
+      const int kpair = tid >> 3, ch = tid & 7;
+      const int key = 2 * kpair;
+      const int pos = 16 * (key >> 4) + pv_slot(key & 15);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * ch + e;
+        const uint32_t wa = vreg[0][e >> 1], wb = vreg[1][e >> 1];
+        // element e of each 16-byte row chunk: low half of word e/2 when e is even
+        const uint32_t lo = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
+        const uint32_t hi = (e & 1) ? (wb >> 16) : (wb & 0xffffu);
+        *(uint32_t*)(&sm.vt[buf][vt_off(d, pos >> 3) + (pos & 7)]) = lo | (hi << 16);
+      }
+    }
+    if (kind == 1 && tid < 64) {
+      sm.tk[buf][tid] = treg;
+      int64_t mn = treg, mx = treg == kTMax ? kTMin : treg;
+      half_minmax(mn, mx);
+      if (l32 == 0) {
+        sm.tkst[buf][2 * hf] = mn;
+        sm.tkst[buf][2 * hf + 1] = mx;
+      }
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) gload(t + 1);
+    const int j0 = t * kKB;
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+      const int j0h = j0 + 32 * hk;
+      if (j0h > wq_last) continue;
+      bf16x8 kop[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kop[ks] = *(const bf16x8*)(&sm.k[buf][k_off(32 * hk + l32, hf + 2 * ks)]);
+      bf16x8 pop[2][2];
+      bool act[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qb0 = qw0 + 32 * qb;
+        act[qb] = (qb0 <= wq_last) && (j0h <= min(qb0 + 31, wq_last));
+        if (!act[qb]) continue;
+        const int base = qb0 - j0h + l32;  // i - j = base - acc_key(r, hf)
+        f32x16 c;
+        if (kind == 1) {
+          const bool pconst = (qb0 - (j0h + 31)) >= Pm1;
+          const int64_t kmn = sm.tkst[buf][2 * hk], kmx = sm.tkst[buf][2 * hk + 1];
+          const int tb_lo = time_bucket(tqmin[qb] - kmx, NTm1);
+          const int tb_hi = time_bucket(tqmax[qb] - kmn, NTm1);
+          if (pconst && tb_lo == tb_hi) {
+            const float cb = sm.wpos[Pm1] + sm.wtime[tb_lo];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c[r] = cb;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kr = acc_key(r, hf);
+              const int pb = pos_bucket(base - kr, Pm1);
+              const int tb = time_bucket(tq[qb] - sm.tk[buf][32 * hk + kr], NTm1);
+              c[r] = sm.wpos[pb] + sm.wtime[tb];
+            }
+          }
+        } else if (kind == 2) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c[r] = slope_y * (float)(base - acc_key(r, hf));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c[r] = 0.f;
+        }
+        f32x16 s = {};
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[qb][0], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[1], qop[qb][1], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[2], qop[qb][2], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[3], qop[qb][3], s, 0, 0, 0);
+        f32x8 p0, p1;
+        const bool diag = (j0h + 31) > qb0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float y = __builtin_fmaf(s[r], cq, c[r]);
+          const float e = __builtin_amdgcn_exp2f(y);
+          float av = y * __builtin_amdgcn_rcpf(1.0f + e);
+          if (diag && (base - acc_key(r, hf)) < 0) av = 0.f;
+          if (r < 8) p0[r] = av; else p1[r - 8] = av;
+        }
+        pop[qb][0] = __builtin_convertvector(p0, bf16x8);
+        pop[qb][1] = __builtin_convertvector(p1, bf16x8);
+      }
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const bf16x8 vop = *(const bf16x8*)(&sm.vt[buf][vt_off(32 * db + l32, 4 * hk + 2 * m + hf)]);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            if (act[qb]) oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[qb][m], oacc[db][qb], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < n_tiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O^T accumulators -> O rows, scaled by -ln(2) out_scale ----
+  const float osc = -kLn2 * a.out_scale;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = qw0 + 32 * qb + l32;
+    if (row > wq_last) continue;
+    const int64_t base = ((tok0 + row) * H + h) * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4 = {oacc[db][qb][4 * g] * osc, oacc[db][qb][4 * g + 1] * osc,
+                    oacc[db][qb][4 * g + 2] * osc, oacc[db][qb][4 * g + 3] * osc};
+        const int d0 = 32 * db + 8 * g + 4 * hf;
+        if (OUT_F32)
+          *(f32x4*)((float*)a.o + base + d0) = v4;
+        else
+          *(bf16x4*)((bf16*)a.o + base + d0) = __builtin_convertvector(v4, bf16x4);
+      }
+  }
+}
+
+// ============================================================================================
+// fp32, d in {32, 64}: 4 waves x 32 queries = 128 query rows per work item, 32 keys per stage,
+// v_mfma_f32_32x32x2_f32 for both products.
+// ============================================================================================
+constexpr int kBRf = 128;
+constexpr int kKBf = 32;
+
+template <int D>
+struct SmemF32 {
+  float k[2][kKBf][D + 1];
+  float vt[2][D][kKBf + 1];
+  int64_t tk[2][kKBf];
+  int64_t tkst[2][2];
+  float wpos[kMaxPosBuckets];
+  float wtime[kMaxTimeBuckets];
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
+  __shared__ SmemF32<D> sm;
+  constexpr int NDB = D / 32;       // 32-row blocks of O^T
+  constexpr int NC = D / 4;         // 16-byte chunks per row
+  constexpr int NLD = (kKBf * NC) / 256;  // chunks per thread per tile
+  const int item = blockIdx.x;
+  if (item >= *a.work_count) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const WorkItem wi = a.work[item];
+  const int b = wi.b, h = wi.h, H = a.H;
+  const int64_t tok0 = a.offsets[b];
+  const int n = a.offsets[b + 1] - a.offsets[b];
+  const int q0 = wi.qt * kBRf;
+  if (q0 >= n) return;
+  const int q_end = min(q0 + kBRf, n);
+  const int n_tiles = (q_end + kKBf - 1) / kKBf;
+  const int qw0 = q0 + wave * 32;
+  const int wq_last = min(qw0 + 32, q_end) - 1;
+
+  const float* __restrict__ qp = (const float*)a.q;
+  const float* __restrict__ kp = (const float*)a.k;
+  const float* __restrict__ vp = (const float*)a.v;
+  const int kind = a.bias.kind;
+  const int64_t* __restrict__ ts = a.bias.ts;
+  if (kind == 1) {
+    for (int i = tid; i < a.bias.num_pos; i += 256)
+      sm.wpos[i] = -kLog2e * a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i];
+    for (int i = tid; i < a.bias.num_time; i += 256)
+      sm.wtime[i] = -kLog2e * a.bias.w_time[(int64_t)h * a.bias.time_stride + i];
+  }
+  const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
+  float slope_y = 0.f;
+  if (kind == 2) slope_y = kLog2e * (a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H));
+
+  const float cq = -a.alpha * kLog2e;
+  float qop[D / 2];
+  const int row_q = qw0 + l32;
+  const bool qvalid = row_q <= wq_last;
+#pragma unroll
+  for (int ks = 0; ks < D / 2; ++ks)
+    qop[ks] = qvalid ? qp[(tok0 + row_q) * a.q_stride + (int64_t)h * D + 2 * ks + hf] * cq : 0.f;
+  int64_t tq = 0, tqmin = kTMax, tqmax = kTMin;
+  if (kind == 1 && qvalid) {
+    tq = ts[tok0 + row_q];
+    tqmin = tq;
+    tqmax = tq;
+  }
+  if (kind == 1) half_minmax(tqmin, tqmax);
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+
+  f32x4 kreg[NLD], vreg[NLD];
+  int64_t treg = kTMax;
+  auto gload = [&](int t) {
+    const int j0 = t * kKBf;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int c = tid + 256 * u, row = c / NC, chunk = c % NC;
+      const int key = j0 + row;
+      kreg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      vreg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (key < q_end) {
+        kreg[u] = *(const f32x4*)(kp + (tok0 + key) * a.k_stride + (int64_t)h * D + 4 * chunk);
+        vreg[u] = *(const f32x4*)(vp + (tok0 + key) * a.v_stride + (int64_t)h * D + 4 * chunk);
+      }
+    }
+    if (kind == 1 && tid < kKBf) {
+      const int key = j0 + tid;
+      treg = key < q_end ? ts[tok0 + key] : kTMax;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int c = tid + 256 * u, row = c / NC, chunk = c % NC;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm.k[buf][row][4 * chunk + e] = kreg[u][e];
+        sm.vt[buf][4 * chunk + e][row] = vreg[u][e];
+      }
+    }
+    if (kind == 1 && tid < 64) {
+      if (tid < kKBf) sm.tk[buf][tid] = treg;
+      int64_t mn = treg, mx = treg == kTMax ? kTMin : treg;
+      half_minmax(mn, mx);
+      if (lane == 0) {
+        sm.tkst[buf][0] = mn;
+        sm.tkst[buf][1] = mx;
+      }
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) gload(t + 1);
+    const int j0 = t * kKBf;
+    if (j0 <= wq_last) {
+      const int base = qw0 - j0 + l32;
+      f32x16 c;
+      if (kind == 1) {
+        const bool pconst = (qw0 - (j0 + 31)) >= Pm1;
+        const int tb_lo = time_bucket(tqmin - sm.tkst[buf][1], NTm1);
+        const int tb_hi = time_bucket(tqmax - sm.tkst[buf][0], NTm1);
+        if (pconst && tb_lo == tb_hi) {
+          const float cb = sm.wpos[Pm1] + sm.wtime[tb_lo];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c[r] = cb;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kr = acc_key(r, hf);
+            c[r] = sm.wpos[pos_bucket(base - kr, Pm1)] + sm.wtime[time_bucket(tq - sm.tk[buf][kr], NTm1)];
+          }
+        }
+      } else if (kind == 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[r] = slope_y * (float)(base - acc_key(r, hf));
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c[r] = 0.f;
+      }
+      f32x16 s = c;
+#pragma unroll
+      for (int ks = 0; ks < D / 2; ++ks)
+        s = __builtin_amdgcn_mfma_f32_32x32x2f32(sm.k[buf][l32][2 * ks + hf], qop[ks], s, 0, 0, 0);
+      const bool diag = (j0 + 31) > qw0;
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float y = s[r];
+        const float e = __builtin_amdgcn_exp2f(y);
+        float av = y * __builtin_amdgcn_rcpf(1.0f + e);
+        if (diag && (base - acc_key(r, hf)) < 0) av = 0.f;
+        p[r] = av;
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(sm.vt[buf][32 * db + l32][acc_key(m, hf)], p[m], oacc[db], 0, 0, 0);
+    }
+    if (t + 1 < n_tiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (qvalid) {
+    const float osc = -kLn2 * a.out_scale;
+    float* dst = (float*)a.o + ((tok0 + row_q) * H + h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4 = {oacc[db][4 * g] * osc, oacc[db][4 * g + 1] * osc, oacc[db][4 * g + 2] * osc,
+                    oacc[db][4 * g + 3] * osc};
+        *(f32x4*)(dst + 32 * db + 8 * g + 4 * hf) = v4;
+      }
+  }
+}
+
+}  // namespace
+
+int attn_block_rows_bf16(int d) { return d == 64 ? kBR : 0; }
+int attn_block_rows_f32(int d) { return (d == 32 || d == 64) ? kBRf : 0; }
+
+hipError_t launch_attn_bf16(int d, const AttnArgs& a, int grid, hipStream_t stream) {
+  if (d != 64) return hipErrorInvalidValue;
+  if (grid <= 0) return hipSuccess;
+  if (a.o_f32)
+    hipLaunchKernelGGL(attn_bf16_d64_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_bf16_d64_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(int d, const AttnArgs& a, int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (d == 32) hipLaunchKernelGGL(attn_f32_kernel<32>, dim3(grid), dim3(256), 0, stream, a);
+  else if (d == 64) hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace hstu

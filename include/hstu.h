@@ -1,0 +1,181 @@
+/*
+ * hstu.h -- C ABI of the HSTU pointwise aggregated attention / layer forward
+ * library for AMD MI355X (gfx950).
+ *
+ * What is computed (page title, section):
+ *  - "Actions Speak Louder than Words" reading notes, §3.1 eqs. (1)-(3):
+ *      U, V, Q, K = Split(SiLU(f1(X)))                                  (1)
+ *      A V        = SiLU(Q K^T + rab^{p,t}) V   (no softmax, §3.2)      (2)
+ *      Y          = f2(LayerNorm(A V) * U)                              (3)
+ *    with f1, f2 single linear layers W x + b, and layers stacked with
+ *    residual connections.
+ *  - "4.4 推荐模型的 Scaling", section "HSTU 层" and its toy layer: chunk order
+ *    U, V, Q, K; head h owns columns [h d, (h+1) d) of each chunk; causal mask
+ *    j <= i including the diagonal; an optional normalising constant.
+ *  - rab^{p,t}: bias from the relative position and the timestamp difference
+ *    (§3.1 of the first page).  Bucketed form used here:
+ *      rab(i, j) = w_pos[min(i - j, P - 1)] + w_time[min(floor(log2(1 + max(t_i - t_j, 0))), NT - 1)]
+ *  - GenRank article (joto.ai), part (2): ALiBi in place of the learned bias,
+ *      rab(i, j) = -slope_h * (i - j).
+ *
+ * The attention computes, for every user b, head h and local row i < n_b,
+ *      O[i] = out_scale * sum_{j <= i} SiLU(alpha * <q_i, k_j> + rab_h(i, j)) * v_j .
+ *
+ * Conventions shared by all entry points:
+ *  - Every pointer argument named as "device" must be a device allocation on
+ *    the current HIP device; the caller owns all memory.  The library never
+ *    allocates, frees or synchronises: every call only enqueues kernels on
+ *    `stream` and returns.
+ *  - Jagged batches: `offsets` is a device int32 array [B + 1], offsets[0] = 0,
+ *    non-decreasing, offsets[B] = total_tokens; user b owns tokens
+ *    [offsets[b], offsets[b+1]).  Empty users are allowed.  Every user length
+ *    must be <= max_seqlen (the scheduler sizes its work list from it).
+ *  - Row strides are in elements and must keep every row 16-byte aligned.
+ *  - Errors detectable on the host return a negative hstu_status and enqueue
+ *    nothing; a failed launch returns HSTU_ERR_HIP.  A thread-local message is
+ *    available from hstu_last_error().  Device-side contract violations
+ *    (non-monotone offsets, lengths above max_seqlen) are not checked by the
+ *    fast path; hstu_validate_offsets() detects them.
+ */
+#ifndef HSTU_H_
+#define HSTU_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HSTU_OK = 0,
+  HSTU_ERR_INVALID_ARG = -1,
+  HSTU_ERR_UNSUPPORTED = -2,
+  HSTU_ERR_WORKSPACE = -3,
+  HSTU_ERR_HIP = -4
+} hstu_status;
+
+typedef enum { HSTU_DTYPE_F32 = 0, HSTU_DTYPE_BF16 = 1 } hstu_dtype;
+
+typedef enum { HSTU_BIAS_NONE = 0, HSTU_BIAS_RAB_PT = 1, HSTU_BIAS_ALIBI = 2 } hstu_bias_kind;
+
+/* Relative attention bias.  Host struct; the arrays it points to are device memory.
+ *  RAB_PT: timestamps [T] int64 (any unit; only differences are used);
+ *          w_pos [H_tab][pos_head_stride] and w_time [H_tab][time_head_stride] fp32,
+ *          with num_pos_buckets in [1, 1024] and num_time_buckets in [1, 64];
+ *          a head stride of 0 shares one table across heads.
+ *  ALIBI:  alibi_slopes [H] fp32, or NULL for slope_h = 2^(-8 (h+1) / H).
+ *  NONE:   rab = 0. */
+typedef struct {
+  int32_t kind;
+  const int64_t* timestamps;
+  const float* w_pos;
+  const float* w_time;
+  int32_t num_pos_buckets;
+  int32_t num_time_buckets;
+  int32_t pos_head_stride;
+  int32_t time_head_stride;
+  const float* alibi_slopes;
+} hstu_bias;
+
+/* Bytes of device workspace hstu_attn_fwd needs for B users, H heads and
+ * lengths up to max_seqlen (work list of the jagged scheduler). */
+size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen);
+
+/* Jagged causal pointwise attention, eq. (2) above.
+ *  dt          HSTU_DTYPE_BF16 (bf16 in/out, fp32 accumulation) or HSTU_DTYPE_F32.
+ *  B, H        users and heads; d_qk == d_v in {32, 64} for F32, 64 for BF16.
+ *  offsets     device int32 [B+1]; max_seqlen >= every user length, <= 65536.
+ *  q, k, v     device [T, H, d] rows with row strides q_row_stride etc.
+ *              (elements between consecutive tokens; >= H*d).
+ *  bias        host pointer to the bias description (may be NULL = NONE).
+ *  alpha       multiplies Q K^T inside the SiLU; out_scale multiplies the sum.
+ *  o           device [T, H, d_v] contiguous output.
+ *  workspace   device, >= hstu_attn_workspace_bytes(B, H, max_seqlen), 256-B aligned.
+ * Layout of the workspace after the call: int32 item_count at byte 0, then
+ * from byte 256 the scheduler's work list, one int32x4 {b, h, q_tile, 0} per
+ * item, in launch order (cost = q_tile + 1 descending, then b, h ascending). */
+hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                          const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
+                          const void* q, int64_t q_row_stride, const void* k,
+                          int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                          const hstu_bias* bias, float alpha, float out_scale, void* o,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The two halves of hstu_attn_fwd, for callers that run several attentions over one
+ * jagged batch (a layer stack) or time the kernels apart.
+ * hstu_attn_plan runs the jagged scheduler only: it writes the work list for
+ * (dt, B, H, d, offsets, max_seqlen) into `workspace` (layout as above).
+ * hstu_attn_fwd_planned runs the attention only, on a workspace that a completed
+ * or earlier-enqueued hstu_attn_plan call with the same dt, B, H, d, offsets and
+ * max_seqlen filled; all other arguments as for hstu_attn_fwd. */
+hstu_status hstu_attn_plan(int32_t dt, int32_t B, int32_t H, int32_t d, const int32_t* offsets,
+                           int32_t max_seqlen, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+hstu_status hstu_attn_fwd_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                                  const int32_t* offsets, int32_t max_seqlen,
+                                  int64_t total_tokens, const void* q, int64_t q_row_stride,
+                                  const void* k, int64_t k_row_stride, const void* v,
+                                  int64_t v_row_stride, const hstu_bias* bias, float alpha,
+                                  float out_scale, void* o, const void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Query rows per work item (q_tile granularity) of the attention kernel for a dtype/d. */
+int32_t hstu_attn_block_rows(int32_t dt, int32_t d);
+
+/* Bytes of device workspace hstu_layer_fwd needs. */
+size_t hstu_layer_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_model, int32_t H,
+                                  int32_t d_qk, int32_t d_v, int32_t max_seqlen);
+
+/* One HSTU layer forward, eqs. (1)-(3), bf16 storage with fp32 accumulation.
+ *  x        device bf16 [T, d_model]
+ *  w1       device bf16 [2H(d_qk+d_v), d_model] (row n = output feature n), b1 fp32 [2H(d_qk+d_v)] or NULL
+ *  ln_gamma, ln_beta  device fp32 [H d_v] (NULL = 1 / 0), ln_eps > 0
+ *  w2       device bf16 [d_model, H d_v], b2 fp32 [d_model] or NULL
+ *  residual nonzero: y = x + f2(...)
+ *  y        device bf16 [T, d_model]; may not alias x.
+ *  The workspace holds Z = SiLU(x W1^T + b1) as bf16 [T, 2H(d_qk+d_v)] (column blocks
+ *  U | V | Q | K) at byte 0, then the attention output O as fp32 [T, H d_v], then the
+ *  attention workspace; offsets of each are returned by hstu_layer_workspace_offsets(). */
+hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,
+                           int32_t d_v, const int32_t* offsets, int32_t max_seqlen,
+                           int64_t total_tokens, const void* x, const void* w1, const float* b1,
+                           const float* ln_gamma, const float* ln_beta, float ln_eps,
+                           const void* w2, const float* b2, const hstu_bias* bias, float alpha,
+                           int32_t residual, void* y, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Byte offsets of Z, O and the attention workspace inside the layer workspace. */
+void hstu_layer_workspace_offsets(int64_t total_tokens, int32_t H, int32_t d_qk, int32_t d_v,
+                                  size_t* z_offset, size_t* o_offset, size_t* attn_offset);
+
+/* GenRank action-oriented tokens (GenRank article, part (1)): x[t] = item_table[item_ids[t]]
+ * + action_table[action_ids[t]], bf16 in and out, fp32 add.  ids are device int32 [T];
+ * an id outside [0, num_items) or [0, num_actions) contributes a zero row.  dim % 8 == 0. */
+hstu_status hstu_embed_sum_fwd(int64_t total_tokens, int32_t dim, const void* item_table,
+                               int64_t num_items, const void* action_table, int32_t num_actions,
+                               const int32_t* item_ids, const int32_t* action_ids, void* x,
+                               hipStream_t stream);
+
+/* Checks a jagged offsets array on the device: writes int32 flags to device `flags_out`
+ * (bit 0: offsets[0] != 0, bit 1: decreasing, bit 2: offsets[B] != total_tokens,
+ * bit 3: a length above max_seqlen).  0 means valid. */
+hstu_status hstu_validate_offsets(int32_t B, const int32_t* offsets, int64_t total_tokens,
+                                  int32_t max_seqlen, int32_t* flags_out, hipStream_t stream);
+
+/* Test hook: the bias bucket indices the attention kernel uses, for R (token_i, token_j)
+ * pairs of the same user (local positions from `offsets`).  Writes device int32
+ * pos_bucket[R], time_bucket[R]. */
+hstu_status hstu_debug_buckets(int32_t B, const int32_t* offsets, const int64_t* timestamps,
+                               int32_t num_pos_buckets, int32_t num_time_buckets, int64_t R,
+                               const int64_t* token_i, const int64_t* token_j,
+                               int32_t* pos_bucket, int32_t* time_bucket, hipStream_t stream);
+
+const char* hstu_status_string(int32_t status);
+const char* hstu_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HSTU_H_ */

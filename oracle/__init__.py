@@ -59,7 +59,14 @@ def _L():
         _lib.oracle_layer.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, P, P, i32, P,
                                       P, i32, i64, P, i32, i64, P, f64, i32, P, P, P]
         _lib.oracle_layer.restype = None
+        _lib.oracle_num_threads.restype = i32
+        _lib.oracle_num_threads.argtypes = []
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(_L().oracle_num_threads())
 
 
 def _f64(a):

@@ -211,3 +211,11 @@ void oracle_layer(int32_t B, int32_t D, int32_t H, int32_t dqk, int32_t dv, cons
   if (!z_out) free(z);
   if (!o_out) free(o);
 }
+
+/* Threads the OpenMP loops above run with (reported beside timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int32_t oracle_num_threads(void) { return (int32_t)omp_get_max_threads(); }
+#else
+int32_t oracle_num_threads(void) { return 1; }
+#endif

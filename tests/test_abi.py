@@ -1,0 +1,97 @@
+"""The C-ABI library loads on the host and exports every symbol include/hstu.h declares;
+host-side argument checks answer without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hstu_sequential_transduction_jagged_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hstu.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hstu_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert "hstu_attn_fwd" in names and "hstu_layer_fwd" in names
+    L = binding.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(binding.SIGNATURES), set(names) ^ set(binding.SIGNATURES)
+
+
+def test_status_strings():
+    L = binding.lib()
+    assert L.hstu_status_string(0) == b"ok"
+    assert L.hstu_status_string(-3).startswith(b"workspace")
+    assert L.hstu_status_string(12345) == b"unknown status"
+
+
+def test_workspace_sizes():
+    L = binding.lib()
+    # 256-byte header + one 16-byte item per (user, head, 128-row tile), 256-aligned
+    assert L.hstu_attn_workspace_bytes(16, 8, 8192) == 256 + 16 * 8 * 64 * 16
+    assert L.hstu_attn_workspace_bytes(0, 8, 8192) == 256
+    assert L.hstu_attn_block_rows(1, 64) == 256
+    assert L.hstu_attn_block_rows(0, 32) == 128
+    assert L.hstu_attn_block_rows(1, 48) == 0
+    z, o, a = binding.layer_workspace_offsets(1000, 4, 64, 64)
+    assert z == 0 and o == 1000 * 1024 * 2 and a == o + 1000 * 256 * 4
+
+
+def _attn(**kw):
+    L = binding.lib()
+    args = dict(dt=1, B=2, H=2, dqk=64, dv=64, offsets=None, max_seqlen=16, T=20, q=None, qs=128,
+                k=None, ks=128, v=None, vs=128, bias=None, alpha=1.0, out_scale=1.0, o=None,
+                ws=None, wsb=0, stream=None)
+    args.update(kw)
+    return L.hstu_attn_fwd(args["dt"], args["B"], args["H"], args["dqk"], args["dv"],
+                           args["offsets"], args["max_seqlen"], args["T"], args["q"], args["qs"],
+                           args["k"], args["ks"], args["v"], args["vs"], args["bias"],
+                           args["alpha"], args["out_scale"], args["o"], args["ws"], args["wsb"],
+                           args["stream"])
+
+
+def test_host_side_errors_need_no_gpu():
+    L = binding.lib()
+    assert _attn(dt=7) == -1
+    assert _attn(H=0) == -1
+    assert _attn(dqk=64, dv=32) == -2
+    assert _attn(dt=1, dqk=32, dv=32) == -2      # bf16 needs d = 64
+    assert _attn(max_seqlen=70000) == -2
+    bad = binding.HstuBias()
+    bad.kind = 9
+    assert _attn(bias=ctypes.byref(bad)) == -1
+    rab = binding.HstuBias()
+    rab.kind = binding.BIAS_RAB_PT            # missing tables
+    assert _attn(bias=ctypes.byref(rab)) == -1
+    assert b"timestamps" in L.hstu_last_error()
+    # empty problems return OK without launching anything
+    assert _attn(B=0) == 0
+    assert _attn(T=0) == 0
+    # null pointers with work to do are rejected before any launch
+    assert _attn() == -1
+    fake = ctypes.c_void_p(0x100000)
+    assert _attn(offsets=fake, q=fake, k=fake, v=fake, o=fake, ws=fake, wsb=16) == -3
+    assert _attn(offsets=fake, q=fake, k=fake, v=fake, o=fake, ws=fake, wsb=1 << 20, qs=100) == -1
+    assert _attn(offsets=fake, q=fake, k=fake, v=fake, o=fake, ws=ctypes.c_void_p(0x100010),
+                 wsb=1 << 20) == -3
+    assert L.hstu_layer_fwd(0, 1, 256, 4, 64, 64, None, 8, 8, None, None, None, None, None, 1e-5,
+                            None, None, None, 1.0, 0, None, None, 0, None) == -2
+    assert L.hstu_layer_fwd(1, 1, 256, 4, 64, 64, None, 8, 8, None, None, None, None, None, 0.0,
+                            None, None, None, 1.0, 0, None, None, 0, None) == -1
+    assert L.hstu_embed_sum_fwd(4, 12, None, 1, None, 1, None, None, None, None) == -2
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="libhstu.so not found"):
+        binding.lib()

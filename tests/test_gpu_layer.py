@@ -1,0 +1,115 @@
+"""GPU parity of the full layer (eqs. (1)-(3)), the GenRank token construction and the
+residual stack against the fp64 oracle, through the C ABI.  bf16 outputs: max error
+<= 2e-2 of the reference RMS beyond each element's own bf16 rounding (err_stored)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hstu_sequential_transduction_jagged_amd import binding, synth
+from tests.hstu_testutil import TOL, DevLayer, err_rms, err_stored, oracle_layer, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_layer(inp, x=None, **kw):
+    d = DevLayer(inp)
+    xx = d.x if x is None else x
+    y = d.run_layer(xx, **kw)
+    torch.cuda.synchronize()
+    return d, y
+
+
+@pytest.mark.parametrize("affine", [False, True])
+def test_layer_small_workload(affine):
+    inp = synth.layer_small(randomize_affine=affine)
+    d, y = _run_layer(inp)
+    ref = oracle_layer(inp)
+    yy = y.float().cpu().numpy()
+    e = err_stored(yy, ref, "bf16")
+    print("layer_small T=%d affine=%s err=%.3g (without storage allowance %.3g)"
+          % (inp.T, affine, e, err_rms(yy, ref)), flush=True)
+    assert e <= TOL["bf16"]
+
+
+def test_layer_intermediates():
+    """Z = SiLU(X W1^T + b1) with its U | V | Q | K blocks, and O, checked separately."""
+    inp = synth.make_layer("t", 40, [0, 1, 300, 257, 64], D=256, H=4, d=64, alpha=1.0 / 300,
+                           P=128, NT=32, table_std=0.5, randomize_affine=True)
+    d = DevLayer(inp)
+    ws = torch.zeros(binding.layer_workspace_bytes(inp.B, inp.T, 256, 4, 64, 64, inp.max_seqlen),
+                     dtype=torch.uint8, device="cuda")
+    y = d.run_layer(d.x, workspace=ws)
+    torch.cuda.synchronize()
+    zo, oo, _ = binding.layer_workspace_offsets(inp.T, 4, 64, 64)
+    z = ws[zo:zo + inp.T * 1024 * 2].view(torch.bfloat16).view(inp.T, 1024).float().cpu().numpy()
+    o = ws[oo:oo + inp.T * 256 * 4].view(torch.float32).view(inp.T, 256).cpu().numpy()
+    yr, zr, orf = oracle_layer(inp, return_intermediates=True)
+    for name, a, r in [("U", z[:, :256], zr[:, :256]), ("V", z[:, 256:512], zr[:, 256:512]),
+                       ("Q", z[:, 512:768], zr[:, 512:768]), ("K", z[:, 768:], zr[:, 768:]),
+                       ("O", o, orf), ("Y", y.float().cpu().numpy(), yr)]:
+        e = err_stored(a, r, "f32" if name == "O" else "bf16")
+        print(name, "err=%.3g (without storage allowance %.3g)" % (e, err_rms(a, r)), flush=True)
+        assert e <= TOL["bf16"], name
+
+
+def test_layer_residual_and_alibi():
+    inp = synth.make_layer("t", 41, [200, 3, 129], D=512, H=8, d=64, alpha=1.0 / 200,
+                           residual=True, bias_kind=synth.BIAS_ALIBI, randomize_affine=True)
+    d, y = _run_layer(inp)
+    e = err_stored(y.float().cpu().numpy(), oracle_layer(inp), "bf16")
+    assert e <= TOL["bf16"], e
+
+
+def test_embed_sum_exact():
+    g = synth.genrank(B=3, lo=40, hi=90, n_items=2000)
+    it = to_dev(g.item_table, torch.bfloat16)
+    ac = to_dev(g.action_table, torch.bfloat16)
+    ids = to_dev(g.item_ids.astype(np.int32))
+    aids = to_dev(g.action_ids.astype(np.int32))
+    x = binding.hstu_embed_sum_fwd(it, ac, ids, aids)
+    torch.cuda.synchronize()
+    # fp32 sum of the two bf16 rows, rounded once to bf16
+    ref = (torch.from_numpy(g.item_table[g.item_ids]) + torch.from_numpy(g.action_table[g.action_ids])
+           ).to(torch.bfloat16)
+    assert torch.equal(x.cpu(), ref)
+    ro = oracle.embed_sum(g.item_table, g.action_table, g.item_ids, g.action_ids)
+    assert err_stored(x.float().cpu().numpy(), ro, "bf16") <= 1e-6
+
+
+def test_genrank_layer_small():
+    g = synth.genrank(B=4, lo=100, hi=600, n_items=5000, randomize_affine=True)
+    it = to_dev(g.item_table, torch.bfloat16)
+    ac = to_dev(g.action_table, torch.bfloat16)
+    x = binding.hstu_embed_sum_fwd(it, ac, to_dev(g.item_ids.astype(np.int32)),
+                                   to_dev(g.action_ids.astype(np.int32)))
+    d = DevLayer(g)
+    y = d.run_layer(x)
+    torch.cuda.synchronize()
+    # the layer's input is the bf16-stored token sum (checked bit-exact in test_embed_sum_exact);
+    # the oracle takes the same rounding of its own fp64 sum
+    xr = synth.round_bf16(oracle.embed_sum(g.item_table, g.action_table, g.item_ids,
+                                           g.action_ids).astype(np.float32))
+    ref = oracle_layer(g, x=xr)
+    yy = y.float().cpu().numpy()
+    e = err_stored(yy, ref, "bf16")
+    print("genrank small T=%d err=%.3g (without storage allowance %.3g)" % (g.T, e, err_rms(yy, ref)),
+          flush=True)
+    assert e <= TOL["bf16"]
+
+
+def test_stack_small():
+    inp = synth.stack8(B=12, n_layers=3, hi=1500, randomize_affine=True)
+    d = DevLayer(inp)
+    h = d.x
+    for li in range(len(inp.layers)):
+        h = d.run_layer(h, li=li)
+    torch.cuda.synchronize()
+    x = inp.x.astype(np.float64)
+    for li in range(len(inp.layers)):
+        x = oracle_layer(inp, x=x, li=li)
+    hh = h.float().cpu().numpy()
+    e = err_stored(hh, x, "bf16")
+    print("stack T=%d layers=%d err=%.3g (without storage allowance %.3g)"
+          % (inp.T, len(inp.layers), e, err_rms(hh, x)), flush=True)
+    assert e <= TOL["bf16"]
