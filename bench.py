@@ -112,8 +112,8 @@ def main():
     wt = torch.from_numpy(inp.bias.w_time).to(dev)
     bias = binding.make_bias(binding.BIAS_RAB_PT, ts, wp, wt)
     out = torch.empty((inp.T, inp.H, inp.dv), dtype=bf, device=dev)
-    ws = torch.empty(binding.attn_workspace_bytes(inp.B, inp.H, inp.max_seqlen), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(binding.attn_workspace_bytes(inp.B, inp.H, inp.max_seqlen, inp.T),
+                     dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         binding.hstu_attn_plan(binding.DTYPE_BF16, inp.B, inp.H, inp.dqk, offs, inp.max_seqlen, ws)

@@ -32,7 +32,7 @@ class HstuBias(ctypes.Structure):
 
 # name -> (restype, argtypes)
 SIGNATURES = {
-    "hstu_attn_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "hstu_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i64]),
     "hstu_attn_fwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P, _i64, _P,
                              _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P, _P, _sz, _P]),
     "hstu_attn_block_rows": (_i32, [_i32, _i32]),
@@ -130,8 +130,8 @@ def make_bias(kind=BIAS_NONE, timestamps=None, w_pos=None, w_time=None, alibi_sl
     return b
 
 
-def attn_workspace_bytes(B, H, max_seqlen):
-    return int(lib().hstu_attn_workspace_bytes(B, H, max_seqlen))
+def attn_workspace_bytes(B, H, max_seqlen, total_tokens):
+    return int(lib().hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens))
 
 
 def attn_block_rows(dtype_code, d):
@@ -161,7 +161,7 @@ def hstu_attn_fwd(q, k, v, offsets, max_seqlen, bias: Optional[HstuBias] = None,
         raise HstuError("offsets must be int32")
     if out is None:
         out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
-    need = attn_workspace_bytes(B, H, max_seqlen)
+    need = attn_workspace_bytes(B, H, max_seqlen, T)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     bias = bias if bias is not None else make_bias(BIAS_NONE)

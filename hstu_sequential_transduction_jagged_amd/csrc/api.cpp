@@ -92,10 +92,16 @@ const char* hstu_status_string(int32_t status) {
 
 const char* hstu_last_error(void) { return g_last_error; }
 
-size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen) {
-  if (B < 0 || H < 0 || max_seqlen < 0) return 0;
+// Attention workspace: [count | pad to 256] [work list] [TimeStat x T] [int32 x T]
+static size_t worklist_bytes(int32_t B, int32_t H, int32_t max_seqlen) {
   const int64_t items = (int64_t)B * H * ceil_div(max_seqlen, kMinBlockRows);
   return kHeader + align256((size_t)items * sizeof(WorkItem));
+}
+
+size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64_t total_tokens) {
+  if (B < 0 || H < 0 || max_seqlen < 0 || total_tokens < 0) return 0;
+  return worklist_bytes(B, H, max_seqlen) + align256((size_t)total_tokens * sizeof(TimeStat)) +
+         align256((size_t)total_tokens * sizeof(int32_t));
 }
 
 int32_t hstu_attn_block_rows(int32_t dt, int32_t d) {
@@ -121,8 +127,8 @@ static hstu_status attn_check(int32_t dt, int32_t B, int32_t H, int32_t d_qk, in
 }
 
 static hstu_status workspace_check(const void* workspace, size_t workspace_bytes, int32_t B,
-                                   int32_t H, int32_t max_seqlen) {
-  const size_t need = hstu_attn_workspace_bytes(B, H, max_seqlen);
+                                   int32_t H, int32_t max_seqlen, int64_t total_tokens) {
+  const size_t need = hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens);
   if (!workspace) return fail(HSTU_ERR_INVALID_ARG, "null workspace");
   if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
     return fail(HSTU_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
@@ -139,7 +145,7 @@ hstu_status hstu_attn_plan(int32_t dt, int32_t B, int32_t H, int32_t d, const in
   if (st != HSTU_OK) return st;
   if (B == 0 || max_seqlen == 0) return HSTU_OK;
   if (!offsets) return fail(HSTU_ERR_INVALID_ARG, "null offsets");
-  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen);
+  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen, 0);
   if (st != HSTU_OK) return st;
   const int32_t max_tiles = (int32_t)ceil_div(max_seqlen, block_rows);
   return check_hip(launch_schedule(offsets, B, H, block_rows, max_tiles, (int32_t*)workspace,
@@ -152,7 +158,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
                                 const void* q, int64_t q_row_stride, const void* k,
                                 int64_t k_row_stride, const void* v, int64_t v_row_stride,
                                 const hstu_bias* bias, float alpha, float out_scale, void* o,
-                                bool o_f32, const void* workspace, size_t workspace_bytes,
+                                bool o_f32, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
   int block_rows = 0;
   hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
@@ -169,11 +175,19 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (q_row_stride * elem) % 16 || (k_row_stride * elem) % 16 || (v_row_stride * elem) % 16)
     return fail(HSTU_ERR_INVALID_ARG, "q/k/v/o rows must be 16-byte aligned");
-  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen);
+  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen, total_tokens);
   if (st != HSTU_OK) return st;
 
   const int32_t max_tiles = (int32_t)ceil_div(max_seqlen, block_rows);
+  TimeStat* tstat = (TimeStat*)((char*)workspace + worklist_bytes(B, H, max_seqlen));
+  int32_t* trel = (int32_t*)((char*)tstat + align256((size_t)total_tokens * sizeof(TimeStat)));
+  if (dt == HSTU_DTYPE_BF16 && ba.kind == 1) {
+    st = check_hip(launch_time_stats(B, offsets, ba.ts, tstat, trel, stream), "time stats launch");
+    if (st != HSTU_OK) return st;
+  }
   AttnArgs a{};
+  a.tstat = tstat;
+  a.trel = trel;
   a.offsets = offsets;
   a.work_count = (const int32_t*)workspace;
   a.work = (const WorkItem*)((const char*)workspace + kHeader);
@@ -201,7 +215,7 @@ hstu_status hstu_attn_fwd_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk
                                   int64_t total_tokens, const void* q, int64_t q_row_stride,
                                   const void* k, int64_t k_row_stride, const void* v,
                                   int64_t v_row_stride, const hstu_bias* bias, float alpha,
-                                  float out_scale, void* o, const void* workspace,
+                                  float out_scale, void* o, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
   return attn_planned(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q, q_row_stride, k,
@@ -233,7 +247,7 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (q_row_stride * elem) % 16 || (k_row_stride * elem) % 16 || (v_row_stride * elem) % 16)
     return fail(HSTU_ERR_INVALID_ARG, "q/k/v/o rows must be 16-byte aligned");
-  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen);
+  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen, total_tokens);
   if (st != HSTU_OK) return st;
   st = hstu_attn_plan(dt, B, H, d_qk, offsets, max_seqlen, workspace, workspace_bytes, stream);
   if (st != HSTU_OK) return st;
@@ -258,7 +272,7 @@ size_t hstu_layer_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_mod
   if (B < 0 || total_tokens < 0 || H < 1 || d_qk < 1 || d_v < 1) return 0;
   size_t attn_off = 0;
   hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, nullptr, nullptr, &attn_off);
-  return attn_off + hstu_attn_workspace_bytes(B, H, max_seqlen);
+  return attn_off + hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens);
 }
 
 hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,

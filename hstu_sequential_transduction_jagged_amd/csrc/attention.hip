@@ -58,8 +58,45 @@ __device__ __forceinline__ void half_minmax(int64_t& mn, int64_t& mx) {
   }
 }
 
+// Values the whole wave holds in common, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, v)));
+}
+
 constexpr int64_t kTMax = 0x7fffffffffffffffLL;
 constexpr int64_t kTMin = -kTMax - 1;
+
+// ============================================================================================
+// Timestamp statistics: for every 32-token block of a user (blocks start at the user's first
+// token), the min and max timestamp, stored at the block's first token; and for every token
+// its offset from its block's minimum as int32 (saturated; only read where the block spans
+// at most 2^30).  One workgroup per user.
+// ============================================================================================
+__global__ __launch_bounds__(256) void time_stats_kernel(const int32_t* __restrict__ offsets,
+                                                        const int64_t* __restrict__ ts,
+                                                        TimeStat* __restrict__ stats,
+                                                        int32_t* __restrict__ rel) {
+  const int b = blockIdx.x;
+  const int64_t s = offsets[b];
+  const int n = offsets[b + 1] - offsets[b];
+  const int lane = threadIdx.x & 63, l32 = lane & 31;
+  for (int j = threadIdx.x; j < ((n + 63) & ~63); j += 256) {
+    const bool valid = j < n;
+    const int64_t t = valid ? ts[s + j] : 0;
+    int64_t mn = valid ? t : kTMax, mx = valid ? t : kTMin;
+    half_minmax(mn, mx);
+    if (valid) {
+      const int64_t d = t - mn;
+      rel[s + j] = d > 0x7fffffffLL ? 0x7fffffff : (int32_t)d;
+      if (l32 == 0) stats[s + j] = TimeStat{mn, mx};
+    }
+  }
+}
 
 // ============================================================================================
 // bf16, d = 64: 4 waves x 64 queries = 256 query rows per work item, 64 keys per LDS stage.
@@ -73,10 +110,11 @@ constexpr int kD = 64;
 struct SmemBf16 {
   bf16 k[2][kKB * kD];   // row = key, 8 chunks of 16 B, chunk c stored at c ^ (row & 7)
   bf16 vt[2][kD * kKB];  // row = d, 64 keys in PV slot order, chunk c at c ^ ((d + d/8) & 7)
-  int64_t tk[2][kKB];
-  int64_t tkst[2][4];    // per 32-key half: min, max of valid key timestamps
+  int32_t krel[2][kKB];  // key timestamp minus its 32-key block's minimum (0 past the end)
   float wpos[kMaxPosBuckets];   // -log2(e) * w_pos[h]
   float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
+  float wtime_lz[32];           // wtime[min(31 - lz, NT - 1)]: time bias by leading zeros of dt + 1
+  float cbuf[kWaves][16][64];   // per-wave bias staging of the 64-bit timestamp path
 };
 
 __device__ __forceinline__ int k_off(int row, int chunk) { return row * kD + ((chunk ^ (row & 7)) << 3); }
@@ -87,7 +125,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
   __shared__ SmemBf16 sm;
   const int item = blockIdx.x;
   if (item >= *a.work_count) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = a.work[item];
   const int b = wi.b, h = wi.h, H = a.H;
@@ -105,24 +144,31 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
   const bf16* __restrict__ vp = (const bf16*)a.v;
   const int kind = a.bias.kind;
   const int64_t* __restrict__ ts = a.bias.ts;
+  const TimeStat* __restrict__ tstat = a.tstat;
 
   if (kind == 1) {
     for (int i = tid; i < a.bias.num_pos; i += 256)
       sm.wpos[i] = -kLog2e * a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i];
     for (int i = tid; i < a.bias.num_time; i += 256)
       sm.wtime[i] = -kLog2e * a.bias.w_time[(int64_t)h * a.bias.time_stride + i];
+    if (tid < 32) {
+      const int tb = min(31 - tid, a.bias.num_time - 1);
+      sm.wtime_lz[tid] = -kLog2e * a.bias.w_time[(int64_t)h * a.bias.time_stride + tb];
+    }
   }
   const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
   float slope_y = 0.f;
   if (kind == 2) slope_y = kLog2e * (a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H));
 
-  // ---- Q fragments (B operand of S^T = K Q^T), unscaled ----
+  // ---- Q fragments (B operand of S^T = K Q^T), unscaled; query timestamps ----
   const float cq = -a.alpha * kLog2e;
   bf16x8 qop[2][4];
-  int64_t tq[2], tqmin[2], tqmax[2];
+  int64_t tq[2];
+  int64_t tqmin[2] = {0, 0}, tqmax[2] = {0, 0};
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int row = qw0 + 32 * qb + l32;
+    const int qb0 = qw0 + 32 * qb;
+    const int row = qb0 + l32;
     const bool valid = row <= wq_last;
     const bf16* src = qp + (tok0 + row) * a.q_stride + (int64_t)h * kD + 8 * hf;
 #pragma unroll
@@ -132,14 +178,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
       qop[qb][ks] = __builtin_bit_cast(bf16x8, raw);
     }
     tq[qb] = 0;
-    tqmin[qb] = kTMax;
-    tqmax[qb] = kTMin;
-    if (kind == 1 && valid) {
-      tq[qb] = ts[tok0 + row];
-      tqmin[qb] = tq[qb];
-      tqmax[qb] = tq[qb];
+    if (kind == 1 && qb0 <= wq_last) {
+      const TimeStat st = tstat[tok0 + qb0];
+      tqmin[qb] = st.mn;
+      tqmax[qb] = st.mx;
+      tq[qb] = valid ? ts[tok0 + row] : st.mn;
     }
-    if (kind == 1) half_minmax(tqmin[qb], tqmax[qb]);
   }
 
   f32x16 oacc[2][2];
@@ -151,60 +195,55 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
 
   // ---- staging: global -> registers -> LDS ----
+  const int krow0 = tid >> 3, kchunk = tid & 7;       // K rows krow0 and krow0 + 32
+  const int vpair = tid >> 3, vch = tid & 7;          // V keys 2 vpair, 2 vpair + 1; d chunk vch
+  const bf16* kbase = kp + (tok0 + krow0) * a.k_stride + (int64_t)h * kD + 8 * kchunk;
+  const bf16* vbase = vp + (tok0 + 2 * vpair) * a.v_stride + (int64_t)h * kD + 8 * vch;
+  // V^T store: element e of the chunk (d = 8 vch + e) goes to row d at key slot vpos; the
+  // swizzled 16-byte chunk index of row d is (vpos / 8) ^ ((e + vch) & 7)
+  const int vpos = 16 * ((2 * vpair) >> 4) + pv_slot((2 * vpair) & 15);
+  uint32_t vsw = 0;  // 8 nibbles: swizzled chunk for e = 0..7
+#pragma unroll
+  for (int e = 0; e < 8; ++e) vsw |= (uint32_t)(((vpos >> 3) ^ ((e + vch) & 7)) & 7) << (4 * e);
+  const int vdst0 = 8 * vch * kKB + (vpos & 7);
   u32x4 kreg[2], vreg[2];
-  int64_t treg = kTMax;
+  i32x4 rreg = {0, 0, 0, 0};
   auto gload = [&](int t) {
     const int j0 = t * kKB;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int c = tid + 256 * u, row = c >> 3, chunk = c & 7;
-      const int key = j0 + row;
+      const int key = j0 + krow0 + 32 * u;
       kreg[u] = u32x4{0u, 0u, 0u, 0u};
-      if (key < q_end) kreg[u] = *(const u32x4*)(kp + (tok0 + key) * a.k_stride + (int64_t)h * kD + 8 * chunk);
+      if (key < q_end) kreg[u] = *(const u32x4*)(kbase + (int64_t)(j0 + 32 * u) * a.k_stride);
+      const int vkey = j0 + 2 * vpair + u;
+      vreg[u] = u32x4{0u, 0u, 0u, 0u};
+      if (vkey < q_end) vreg[u] = *(const u32x4*)(vbase + (int64_t)(j0 + u) * a.v_stride);
     }
-    {
-      const int kpair = tid >> 3, ch = tid & 7;
+    if (kind == 1 && tid < kKB / 4) {
+      const int key = j0 + 4 * tid;
+      rreg = i32x4{0, 0, 0, 0};
+      if (key + 3 < q_end) {
+        rreg = *(const i32x4*)(a.trel + tok0 + key);
+      } else {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int key = j0 + 2 * kpair + u;
-        vreg[u] = u32x4{0u, 0u, 0u, 0u};
-        if (key < q_end) vreg[u] = *(const u32x4*)(vp + (tok0 + key) * a.v_stride + (int64_t)h * kD + 8 * ch);
+        for (int e = 0; e < 4; ++e)
+          if (key + e < q_end) rreg[e] = a.trel[tok0 + key + e];
       }
-    }
-    if (kind == 1 && tid < kKB) {
-      const int key = j0 + tid;
-      treg = key < q_end ? ts[tok0 + key] : kTMax;
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + 256 * u, row = c >> 3, chunk = c & 7;
-      *(u32x4*)(&sm.k[buf][k_off(row, chunk)]) = kreg[u];
-    }
-    {
-      const int kpair = tid >> 3, ch = tid & 7;
-      const int key = 2 * kpair;
-      const int pos = 16 * (key >> 4) + pv_slot(key & 15);
+    for (int u = 0; u < 2; ++u)
+      *(u32x4*)(&sm.k[buf][k_off(krow0 + 32 * u, kchunk)]) = kreg[u];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * ch + e;
-        const uint32_t wa = vreg[0][e >> 1], wb = vreg[1][e >> 1];
-        // element e of each 16-byte row chunk: low half of word e/2 when e is even
-        const uint32_t lo = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
-        const uint32_t hi = (e & 1) ? (wb >> 16) : (wb & 0xffffu);
-        *(uint32_t*)(&sm.vt[buf][vt_off(d, pos >> 3) + (pos & 7)]) = lo | (hi << 16);
-      }
+    for (int e = 0; e < 8; ++e) {
+      // element e of both key rows: low (e even) or high (e odd) half of word e / 2
+      const uint32_t wa = vreg[0][e >> 1], wb = vreg[1][e >> 1];
+      const uint32_t pk = __builtin_amdgcn_perm(wb, wa, (e & 1) ? 0x07060302u : 0x05040100u);
+      const int chunk = (vsw >> (4 * e)) & 7;
+      *(uint32_t*)(&sm.vt[buf][vdst0 + e * kKB + (chunk << 3)]) = pk;
     }
-    if (kind == 1 && tid < 64) {
-      sm.tk[buf][tid] = treg;
-      int64_t mn = treg, mx = treg == kTMax ? kTMin : treg;
-      half_minmax(mn, mx);
-      if (l32 == 0) {
-        sm.tkst[buf][2 * hf] = mn;
-        sm.tkst[buf][2 * hf + 1] = mx;
-      }
-    }
+    if (kind == 1 && tid < kKB / 4) *(i32x4*)(&sm.krel[buf][4 * tid]) = rreg;
   };
 
   gload(0);
@@ -219,71 +258,187 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
     for (int hk = 0; hk < 2; ++hk) {
       const int j0h = j0 + 32 * hk;
       if (j0h > wq_last) continue;
-      bf16x8 kop[4];
+      // K operands of this 32-key step (V operands are read after the SiLU)
+      bf16x8 kop[4], vop[2][2];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         kop[ks] = *(const bf16x8*)(&sm.k[buf][k_off(32 * hk + l32, hf + 2 * ks)]);
-      bf16x8 pop[2][2];
-      bool act[2];
+
+      // ---- classification of the two 32x32 sub-tiles, all in scalar registers ----
+      // mode 0: inactive, 1: scalar bias, 2: two time buckets (one compare per element),
+      // 3: per-element bias (gather on 32-bit time offsets, ALiBi, or none with the mask),
+      // 4: per-element gather on 64-bit times
+      int mode[2], thi2[2];
+      float cb[2], chi[2];
+      bool diag[2];
+      int64_t kmn = 0, kmx = 0;
+      if (kind == 1) {
+        const TimeStat ks = tstat[tok0 + j0h];
+        kmn = ks.mn;
+        kmx = ks.mx;
+      }
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qb0 = qw0 + 32 * qb;
-        act[qb] = (qb0 <= wq_last) && (j0h <= min(qb0 + 31, wq_last));
-        if (!act[qb]) continue;
-        const int base = qb0 - j0h + l32;  // i - j = base - acc_key(r, hf)
-        f32x16 c;
-        if (kind == 1) {
-          const bool pconst = (qb0 - (j0h + 31)) >= Pm1;
-          const int64_t kmn = sm.tkst[buf][2 * hk], kmx = sm.tkst[buf][2 * hk + 1];
-          const int tb_lo = time_bucket(tqmin[qb] - kmx, NTm1);
-          const int tb_hi = time_bucket(tqmax[qb] - kmn, NTm1);
-          if (pconst && tb_lo == tb_hi) {
-            const float cb = sm.wpos[Pm1] + sm.wtime[tb_lo];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) c[r] = cb;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kr = acc_key(r, hf);
-              const int pb = pos_bucket(base - kr, Pm1);
-              const int tb = time_bucket(tq[qb] - sm.tk[buf][32 * hk + kr], NTm1);
-              c[r] = sm.wpos[pb] + sm.wtime[tb];
-            }
-          }
-        } else if (kind == 2) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) c[r] = slope_y * (float)(base - acc_key(r, hf));
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) c[r] = 0.f;
+        const bool act = (qb0 <= wq_last) && (j0h <= min(qb0 + 31, wq_last));
+        const bool dg = (j0h + 31) > qb0;
+        int md = 3, th = 0;
+        float c0 = 0.f, c1 = 0.f;
+        if (kind == 0) {
+          md = dg ? 3 : 1;
+        } else if (kind == 1) {
+          const bool pconst = (qb0 - (j0h + 31)) >= Pm1;  // implies !dg
+          const int tlo = time_bucket(tqmin[qb] - kmx, NTm1);
+          const int thi = time_bucket(tqmax[qb] - kmn, NTm1);
+          const int64_t lim30 = 1LL << 30;
+          const bool fits32 = (kmx - kmn) <= lim30 && (tqmax[qb] - kmn) <= lim30 &&
+                              (tqmin[qb] - kmn) >= -lim30;
+          c0 = sm.wpos[Pm1] + sm.wtime[tlo];
+          c1 = sm.wpos[Pm1] + sm.wtime[thi];
+          th = thi;
+          md = (pconst && tlo == thi) ? 1 : (pconst && thi == tlo + 1 && fits32) ? 2 : fits32 ? 3 : 4;
         }
-        f32x16 s = {};
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[qb][0], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[1], qop[qb][1], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[2], qop[qb][2], s, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[3], qop[qb][3], s, 0, 0, 0);
-        f32x8 p0, p1;
-        const bool diag = (j0h + 31) > qb0;
+        mode[qb] = act ? md : 0;
+        thi2[qb] = th;
+        diag[qb] = dg;
+        cb[qb] = uniform_f32(c0);
+        chi[qb] = uniform_f32(c1);
+      }
+
+      auto qk = [&](int qb) {
+        f32x16 sacc = {};
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[qb][0], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[1], qop[qb][1], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[2], qop[qb][2], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[3], qop[qb][3], sacc, 0, 0, 0);
+        return sacc;
+      };
+      // y = -log2(e) (alpha s + bias), a = y / (1 + 2^y) = -log2(e) SiLU(alpha s + bias)
+      auto silu_scalar = [&](const f32x16& sacc, float c, bf16x8& p0, bf16x8& p1) {
+        f32x8 a0, a1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float y = __builtin_fmaf(s[r], cq, c[r]);
-          const float e = __builtin_amdgcn_exp2f(y);
-          float av = y * __builtin_amdgcn_rcpf(1.0f + e);
-          if (diag && (base - acc_key(r, hf)) < 0) av = 0.f;
-          if (r < 8) p0[r] = av; else p1[r - 8] = av;
+          const float y = __builtin_fmaf(sacc[r], cq, c);
+          const float av = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+          if (r < 8) a0[r] = av; else a1[r - 8] = av;
         }
-        pop[qb][0] = __builtin_convertvector(p0, bf16x8);
-        pop[qb][1] = __builtin_convertvector(p1, bf16x8);
+        p0 = __builtin_convertvector(a0, bf16x8);
+        p1 = __builtin_convertvector(a1, bf16x8);
+      };
+      auto silu_vector = [&](const f32x16& sacc, const f32x16& c, bool mask, int base, bf16x8& p0,
+                             bf16x8& p1) {
+        f32x8 a0, a1;
+        if (mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float y = __builtin_fmaf(sacc[r], cq, c[r]);
+            float av = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+            av = (base - acc_key(r, hf)) < 0 ? 0.f : av;
+            if (r < 8) a0[r] = av; else a1[r - 8] = av;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float y = __builtin_fmaf(sacc[r], cq, c[r]);
+            const float av = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+            if (r < 8) a0[r] = av; else a1[r - 8] = av;
+          }
+        }
+        p0 = __builtin_convertvector(a0, bf16x8);
+        p1 = __builtin_convertvector(a1, bf16x8);
+      };
+      // per-element bias (y units) of sub-tile qb
+      auto bias_vector = [&](int qb, int m, int base) {
+        f32x16 c;
+        if (kind == 2) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c[r] = slope_y * (float)(base - acc_key(r, hf));
+        } else if (kind == 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c[r] = 0.f;
+        } else if (m == 2 || m == 3) {
+          i32x4 rel4[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) rel4[g] = *(const i32x4*)(&sm.krel[buf][32 * hk + 8 * g + 4 * hf]);
+          if (m == 2) {
+            // two time buckets: dt >= 2^thi - 1  <=>  rel_j <= (t_i - kmin) - (2^thi - 1)
+            const int64_t lim64 = (tq[qb] - kmn) - ((1LL << thi2[qb]) - 1);
+            const int lim = lim64 < -1 ? -1 : (lim64 > 0x7fffffffLL ? 0x7fffffff : (int)lim64);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) c[r] = rel4[r >> 2][r & 3] <= lim ? chi[qb] : cb[qb];
+          } else {
+            const int ti1 = (int)(tq[qb] - kmn) + 1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int u = max(ti1 - rel4[r >> 2][r & 3], 1);  // max(dt, 0) + 1
+              const int pb = min(max(base - acc_key(r, hf), 0), Pm1);
+              c[r] = sm.wpos[pb] + sm.wtime_lz[__builtin_clz((uint32_t)u)];
+            }
+          }
+        } else {
+          // timestamps spread beyond 2^30 within the sub-tile: exact 64-bit deltas, one
+          // element at a time through LDS to keep register use flat
+#pragma unroll 1
+          for (int r = 0; r < 16; ++r) {
+            const int kr = acc_key(r, hf);
+            const int key = min(j0h + kr, n - 1);
+            sm.cbuf[wave][r][lane] = sm.wpos[pos_bucket(base - kr, Pm1)] +
+                                     sm.wtime[time_bucket(tq[qb] - ts[tok0 + key], NTm1)];
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c[r] = sm.cbuf[wave][r][lane];
+        }
+        return c;
+      };
+
+      bf16x8 pop[2][2];
+      if (mode[0] == 1 && mode[1] == 1) {
+        const f32x16 s0 = qk(0);
+        const f32x16 s1 = qk(1);
+        silu_scalar(s0, cb[0], pop[0][0], pop[0][1]);
+        silu_scalar(s1, cb[1], pop[1][0], pop[1][1]);
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (mode[qb] == 0) continue;
+          const int qb0 = qw0 + 32 * qb;
+          if (mode[qb] == 1) {
+            const f32x16 sacc = qk(qb);
+            silu_scalar(sacc, cb[qb], pop[qb][0], pop[qb][1]);
+          } else {
+            // bias first, then the scores: fewer registers live at once
+            const int base = qb0 - j0h + l32;  // i - j = base - acc_key(r, hf)
+            const f32x16 c = bias_vector(qb, mode[qb], base);
+            const f32x16 sacc = qk(qb);
+            silu_vector(sacc, c, diag[qb], base, pop[qb][0], pop[qb][1]);
+          }
+        }
       }
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8 vop = *(const bf16x8*)(&sm.vt[buf][vt_off(32 * db + l32, 4 * hk + 2 * m + hf)]);
+        for (int m = 0; m < 2; ++m)
+          vop[db][m] = *(const bf16x8*)(&sm.vt[buf][vt_off(32 * db + l32, 4 * hk + 2 * m + hf)]);
+      if (mode[0] != 0 && mode[1] != 0) {
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            if (act[qb]) oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[qb][m], oacc[db][qb], 0, 0, 0);
-        }
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+              oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[qb][m], oacc[db][qb], 0, 0, 0);
+      } else if (mode[0] != 0) {
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[0][m], oacc[db][0], 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[1][m], oacc[db][1], 0, 0, 0);
       }
     }
     if (t + 1 < n_tiles) lstore(buf ^ 1);
@@ -501,6 +656,13 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
 
 int attn_block_rows_bf16(int d) { return d == 64 ? kBR : 0; }
 int attn_block_rows_f32(int d) { return (d == 32 || d == 64) ? kBRf : 0; }
+
+hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts, TimeStat* stats,
+                             int32_t* rel, hipStream_t stream) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(time_stats_kernel, dim3(B), dim3(256), 0, stream, offsets, ts, stats, rel);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_bf16(int d, const AttnArgs& a, int grid, hipStream_t stream) {
   if (d != 64) return hipErrorInvalidValue;

@@ -34,6 +34,11 @@ struct BiasArgs {
   const float* slopes;  // may be null: 2^(-8 (h+1) / H)
 };
 
+// Min and max timestamp of a 32-token block.
+struct TimeStat {
+  int64_t mn, mx;
+};
+
 struct AttnArgs {
   const int32_t* offsets;
   const int32_t* work_count;
@@ -46,6 +51,8 @@ struct AttnArgs {
   int32_t H;
   int32_t o_f32;  // bf16 inputs only: write O as fp32 instead of bf16
   BiasArgs bias;
+  const TimeStat* tstat;  // per token: stats of the 32-token block starting there (bf16 path)
+  const int32_t* trel;    // per token: timestamp minus its block's minimum (bf16 path)
   float alpha, out_scale;
 };
 
@@ -75,6 +82,8 @@ __device__ __forceinline__ float default_alibi_slope(int h, int H) {
 hipError_t launch_schedule(const int32_t* offsets, int32_t B, int32_t H, int32_t block_rows,
                            int32_t max_tiles, int32_t* work_count, WorkItem* work,
                            hipStream_t stream);
+hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts, TimeStat* stats,
+                             int32_t* rel, hipStream_t stream);
 hipError_t launch_attn_bf16(int d, const AttnArgs& a, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(int d, const AttnArgs& a, int grid, hipStream_t stream);
 int attn_block_rows_bf16(int d);

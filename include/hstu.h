@@ -79,9 +79,10 @@ typedef struct {
   const float* alibi_slopes;
 } hstu_bias;
 
-/* Bytes of device workspace hstu_attn_fwd needs for B users, H heads and
- * lengths up to max_seqlen (work list of the jagged scheduler). */
-size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen);
+/* Bytes of device workspace hstu_attn_fwd needs for B users, H heads, lengths up to
+ * max_seqlen and total_tokens tokens (work list of the jagged scheduler, plus per-token
+ * timestamp statistics of the relative bias). */
+size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64_t total_tokens);
 
 /* Jagged causal pointwise attention, eq. (2) above.
  *  dt          HSTU_DTYPE_BF16 (bf16 in/out, fp32 accumulation) or HSTU_DTYPE_F32.
@@ -92,10 +93,12 @@ size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen);
  *  bias        host pointer to the bias description (may be NULL = NONE).
  *  alpha       multiplies Q K^T inside the SiLU; out_scale multiplies the sum.
  *  o           device [T, H, d_v] contiguous output.
- *  workspace   device, >= hstu_attn_workspace_bytes(B, H, max_seqlen), 256-B aligned.
+ *  workspace   device, >= hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens),
+ *              256-B aligned.
  * Layout of the workspace after the call: int32 item_count at byte 0, then
  * from byte 256 the scheduler's work list, one int32x4 {b, h, q_tile, 0} per
- * item, in launch order (cost = q_tile + 1 descending, then b, h ascending). */
+ * item, in launch order (cost = q_tile + 1 descending, then b, h ascending);
+ * after it (256-aligned) per-token timestamp statistics of the bias. */
 hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
                           const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
                           const void* q, int64_t q_row_stride, const void* k,
@@ -109,7 +112,8 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
  * (dt, B, H, d, offsets, max_seqlen) into `workspace` (layout as above).
  * hstu_attn_fwd_planned runs the attention only, on a workspace that a completed
  * or earlier-enqueued hstu_attn_plan call with the same dt, B, H, d, offsets and
- * max_seqlen filled; all other arguments as for hstu_attn_fwd. */
+ * max_seqlen filled (it rewrites only the timestamp statistics after the work
+ * list); all other arguments as for hstu_attn_fwd. */
 hstu_status hstu_attn_plan(int32_t dt, int32_t B, int32_t H, int32_t d, const int32_t* offsets,
                            int32_t max_seqlen, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
@@ -118,7 +122,7 @@ hstu_status hstu_attn_fwd_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk
                                   int64_t total_tokens, const void* q, int64_t q_row_stride,
                                   const void* k, int64_t k_row_stride, const void* v,
                                   int64_t v_row_stride, const hstu_bias* bias, float alpha,
-                                  float out_scale, void* o, const void* workspace,
+                                  float out_scale, void* o, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
 /* Query rows per work item (q_tile granularity) of the attention kernel for a dtype/d. */

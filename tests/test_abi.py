@@ -37,8 +37,10 @@ def test_status_strings():
 def test_workspace_sizes():
     L = binding.lib()
     # 256-byte header + one 16-byte item per (user, head, 128-row tile), 256-aligned
-    assert L.hstu_attn_workspace_bytes(16, 8, 8192) == 256 + 16 * 8 * 64 * 16
-    assert L.hstu_attn_workspace_bytes(0, 8, 8192) == 256
+    # + per-token timestamp statistics (16 B) and offsets (4 B), each region 256-aligned
+    assert L.hstu_attn_workspace_bytes(16, 8, 8192, 0) == 256 + 16 * 8 * 64 * 16
+    assert L.hstu_attn_workspace_bytes(0, 8, 8192, 0) == 256
+    assert L.hstu_attn_workspace_bytes(16, 8, 8192, 1000) == 256 + 16 * 8 * 64 * 16 + 16128 + 4096
     assert L.hstu_attn_block_rows(1, 64) == 256
     assert L.hstu_attn_block_rows(0, 32) == 128
     assert L.hstu_attn_block_rows(1, 48) == 0

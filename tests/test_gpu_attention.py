@@ -227,8 +227,8 @@ def test_schedule_bit_exact(dtype, d):
     H = 3
     inp = _case(dtype, lengths, H=H, d=d)
     dev = DevAttn(inp)
-    ws = torch.zeros(binding.attn_workspace_bytes(inp.B, H, inp.max_seqlen), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.zeros(binding.attn_workspace_bytes(inp.B, H, inp.max_seqlen, inp.T),
+                     dtype=torch.uint8, device="cuda")
     dev.run(workspace=ws)
     torch.cuda.synchronize()
     w = ws.cpu().numpy()
