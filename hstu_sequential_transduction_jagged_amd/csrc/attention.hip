@@ -14,11 +14,16 @@
 // the accumulator's row order, and V^T is stored in LDS in that permuted order.
 //
 // SiLU is evaluated in base-2 units: with y = -log2(e) x,
-//     SiLU(x) = x / (1 + e^-x) = -ln(2) * y / (1 + 2^y),
-// so the loop needs one fma (y = -log2(e) alpha s + bias_y), one exp2, one add,
-// one reciprocal and one multiply per score, and -ln(2) out_scale is applied
-// once per output.  (Folding -log2(e) alpha into Q instead would save the fma
-// but round the scaled Q to bf16, which doubles the output error.)
+//     SiLU(x) = x / (1 + e^-x) = -(ln 2 / 2) * w(y),   w(y) = 2 y / (1 + 2^y),
+// and the matrix cores accumulate w; -(ln 2 / 2) out_scale is applied once per
+// output.  y = -log2(e) alpha s + bias_y costs one fma per score (folding the
+// scale into Q instead would round the scaled Q to bf16 and double the output
+// error).  w is computed either exactly, w = y / (0.5 + 0.5 * 2^y) (exp2 and
+// reciprocal), or -- when a per-tile bound shows |y| <= 2 for every score of
+// the tile -- by the odd polynomial w = y - y^2 P(y^2) (three fmas, no
+// transcendental; relative error of 1/(1+2^y) below 7.5e-5, far under the bf16
+// rounding of w).  The bound is |y| <= |alpha log2 e| max|q| max|k| + max|bias_y|
+// with max-norms of the tile's query and key rows (Cauchy-Schwarz).
 //
 // Bias: rab_h(i, j) = w_pos[min(i-j, P-1)] + w_time[min(floor(log2(1+max(t_i-t_j,0))), NT-1)]
 // (tables per head or shared), or ALiBi -slope_h (i - j) (GenRank article, part
@@ -68,6 +73,17 @@ __device__ __forceinline__ float uniform_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, v)));
 }
 
+// w(y) = y - y^2 (P0 + P1 y^2 + P2 y^4) on |y| <= kPolyRange (near-minimax fit of the
+// relative error of 1/(1+2^y); the fitting script sits beside this file).
+constexpr float kPolyRange = 2.0f;
+constexpr float kP0 = 0.3463683490f, kP1 = -0.0135027335f, kP2 = 0.0004785898f;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
 constexpr int64_t kTMax = 0x7fffffffffffffffLL;
 constexpr int64_t kTMin = -kTMax - 1;
 
@@ -107,17 +123,21 @@ constexpr int kBR = kWaves * kQW;
 constexpr int kKB = 64;
 constexpr int kD = 64;
 
-struct SmemBf16 {
-  bf16 k[2][kKB * kD];   // row = key, 8 chunks of 16 B, chunk c stored at c ^ (row & 7)
-  bf16 vt[2][kD * kKB];  // row = d, 64 keys in PV slot order, chunk c at c ^ ((d + d/8) & 7)
-  int32_t krel[2][kKB];  // key timestamp minus its 32-key block's minimum (0 past the end)
+struct __attribute__((aligned(16))) SmemBf16 {
+  __attribute__((aligned(16))) bf16 k[2][kKB * kD];   // row = key, 8 chunks of 16 B, chunk c stored at c ^ ((row / 2) & 7)
+  __attribute__((aligned(16))) bf16 vt[2][kD * kKB];  // row = d, 64 keys in PV slot order, chunk c at c ^ ((d + d/8) & 7)
+  __attribute__((aligned(16))) int32_t krel[2][kKB];  // key timestamp minus its 32-key block's minimum (0 past the end)
+  float knorm2[2][kWaves];      // per wave: max squared norm of the key rows it staged
   float wpos[kMaxPosBuckets];   // -log2(e) * w_pos[h]
   float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
   float wtime_lz[32];           // wtime[min(31 - lz, NT - 1)]: time bias by leading zeros of dt + 1
   float cbuf[kWaves][16][64];   // per-wave bias staging of the 64-bit timestamp path
 };
 
-__device__ __forceinline__ int k_off(int row, int chunk) { return row * kD + ((chunk ^ (row & 7)) << 3); }
+// LDS has 64 four-byte banks and serves 16 lanes of a 16-byte read per cycle: 16 lanes
+// reading the same chunk of 16 consecutive 128-byte rows hit distinct banks when the chunk
+// is XOR-ed with (row / 2) & 7 (row parity selects the bank half).
+__device__ __forceinline__ int k_off(int row, int chunk) { return row * kD + ((chunk ^ ((row >> 1) & 7)) << 3); }
 __device__ __forceinline__ int vt_off(int d, int chunk) { return d * kKB + ((chunk ^ ((d + (d >> 3)) & 7)) << 3); }
 
 template <bool OUT_F32>
@@ -186,6 +206,34 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
     }
   }
 
+  // max norm of the query rows of each 32-row block (bound of the polynomial SiLU path)
+  float qnorm[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {qop[qb][ks][2 * e], qop[qb][ks][2 * e + 1]};
+        ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
+      }
+    }
+    ss += __shfl_xor(ss, 32, 64);  // the two lane halves hold the two halves of a row
+    qnorm[qb] = uniform_f32(sqrtf(wave_max(ss)));
+  }
+  // largest |bias| the tables can produce (y units)
+  float tabmax = 0.f;
+  if (kind == 1) {
+    float mp = 0.f, mt = 0.f;
+    for (int i = lane; i < a.bias.num_pos; i += 64)
+      mp = fmaxf(mp, fabsf(a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i]));
+    for (int i = lane; i < a.bias.num_time; i += 64)
+      mt = fmaxf(mt, fabsf(a.bias.w_time[(int64_t)h * a.bias.time_stride + i]));
+    tabmax = uniform_f32(kLog2e * (wave_max(mp) + wave_max(mt)));
+  }
+  const float acq = fabsf(cq) * 1.0001f;  // rounding margin of the bound
+
   f32x16 oacc[2][2];
 #pragma unroll
   for (int db = 0; db < 2; ++db)
@@ -244,6 +292,27 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
       *(uint32_t*)(&sm.vt[buf][vdst0 + e * kKB + (chunk << 3)]) = pk;
     }
     if (kind == 1 && tid < kKB / 4) *(i32x4*)(&sm.krel[buf][4 * tid]) = rreg;
+    // max squared norm of the staged key rows: 8 threads hold the 8 chunks of a row
+    float ss[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg[u]);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
+      }
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      acc += __shfl_xor(acc, 4, 64);
+      ss[u] = acc;
+    }
+    float mx = fmaxf(ss[0], ss[1]);
+    mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (lane == 0) sm.knorm2[buf][wave] = mx;
   };
 
   gload(0);
@@ -270,7 +339,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
       // 4: per-element gather on 64-bit times
       int mode[2], thi2[2];
       float cb[2], chi[2];
-      bool diag[2];
+      bool diag[2], poly[2];
+      float kn2 = fmaxf(fmaxf(sm.knorm2[buf][0], sm.knorm2[buf][1]),
+                        fmaxf(sm.knorm2[buf][2], sm.knorm2[buf][3]));
+      const float knorm = uniform_f32(sqrtf(kn2));
       int64_t kmn = 0, kmx = 0;
       if (kind == 1) {
         const TimeStat ks = tstat[tok0 + j0h];
@@ -303,6 +375,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
         diag[qb] = dg;
         cb[qb] = uniform_f32(c0);
         chi[qb] = uniform_f32(c1);
+        // largest |bias_y| in the sub-tile, then the bound on |y|
+        float cabs = 0.f;
+        if (kind == 1) cabs = md == 1 ? fabsf(cb[qb]) : md == 2 ? fmaxf(fabsf(cb[qb]), fabsf(chi[qb])) : tabmax;
+        if (kind == 2) cabs = fabsf(slope_y) * (float)max(qb0 + 31 - j0h, 0);
+        poly[qb] = acq * qnorm[qb] * knorm + cabs <= kPolyRange;
       }
 
       auto qk = [&](int qb) {
@@ -313,35 +390,53 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[3], qop[qb][3], sacc, 0, 0, 0);
         return sacc;
       };
-      // y = -log2(e) (alpha s + bias), a = y / (1 + 2^y) = -log2(e) SiLU(alpha s + bias)
-      auto silu_scalar = [&](const f32x16& sacc, float c, bf16x8& p0, bf16x8& p1) {
-        f32x8 a0, a1;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float y = __builtin_fmaf(sacc[r], cq, c);
-          const float av = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
-          if (r < 8) a0[r] = av; else a1[r - 8] = av;
-        }
-        p0 = __builtin_convertvector(a0, bf16x8);
-        p1 = __builtin_convertvector(a1, bf16x8);
+      // y = -log2(e) (alpha s + bias); w(y) = 2 y / (1 + 2^y) = -(2 / ln 2) SiLU(alpha s + bias)
+      auto w_exact = [&](float y) {
+        return y * __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(y), 0.5f, 0.5f));
       };
-      auto silu_vector = [&](const f32x16& sacc, const f32x16& c, bool mask, int base, bf16x8& p0,
-                             bf16x8& p1) {
+      auto w_poly = [&](float y) {
+        const float u = y * y;
+        return __builtin_fmaf(-u, __builtin_fmaf(__builtin_fmaf(kP2, u, kP1), u, kP0), y);
+      };
+      auto silu_scalar = [&](const f32x16& sacc, float c, bool pl, bf16x8& p0, bf16x8& p1) {
         f32x8 a0, a1;
-        if (mask) {
+        if (pl) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float y = __builtin_fmaf(sacc[r], cq, c[r]);
-            float av = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
-            av = (base - acc_key(r, hf)) < 0 ? 0.f : av;
+            const float av = w_poly(__builtin_fmaf(sacc[r], cq, c));
             if (r < 8) a0[r] = av; else a1[r - 8] = av;
           }
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float y = __builtin_fmaf(sacc[r], cq, c[r]);
-            const float av = y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
+            const float av = w_exact(__builtin_fmaf(sacc[r], cq, c));
             if (r < 8) a0[r] = av; else a1[r - 8] = av;
+          }
+        }
+        p0 = __builtin_convertvector(a0, bf16x8);
+        p1 = __builtin_convertvector(a1, bf16x8);
+      };
+      auto silu_vector = [&](const f32x16& sacc, const f32x16& c, bool mask, bool pl, int base,
+                             bf16x8& p0, bf16x8& p1) {
+        f32x8 a0, a1;
+        if (pl) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float av = w_poly(__builtin_fmaf(sacc[r], cq, c[r]));
+            if (r < 8) a0[r] = av; else a1[r - 8] = av;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float av = w_exact(__builtin_fmaf(sacc[r], cq, c[r]));
+            if (r < 8) a0[r] = av; else a1[r - 8] = av;
+          }
+        }
+        if (mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool keep = (base - acc_key(r, hf)) >= 0;
+            if (r < 8) a0[r] = keep ? a0[r] : 0.f; else a1[r - 8] = keep ? a1[r - 8] : 0.f;
           }
         }
         p0 = __builtin_convertvector(a0, bf16x8);
@@ -391,12 +486,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
         return c;
       };
 
-      bf16x8 pop[2][2];
+      bf16x8 pop[2][2] = {{bf16x8{}, bf16x8{}}, {bf16x8{}, bf16x8{}}};
       if (mode[0] == 1 && mode[1] == 1) {
         const f32x16 s0 = qk(0);
         const f32x16 s1 = qk(1);
-        silu_scalar(s0, cb[0], pop[0][0], pop[0][1]);
-        silu_scalar(s1, cb[1], pop[1][0], pop[1][1]);
+        silu_scalar(s0, cb[0], poly[0], pop[0][0], pop[0][1]);
+        silu_scalar(s1, cb[1], poly[1], pop[1][0], pop[1][1]);
       } else {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -404,13 +499,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
           const int qb0 = qw0 + 32 * qb;
           if (mode[qb] == 1) {
             const f32x16 sacc = qk(qb);
-            silu_scalar(sacc, cb[qb], pop[qb][0], pop[qb][1]);
+            silu_scalar(sacc, cb[qb], poly[qb], pop[qb][0], pop[qb][1]);
           } else {
             // bias first, then the scores: fewer registers live at once
             const int base = qb0 - j0h + l32;  // i - j = base - acc_key(r, hf)
             const f32x16 c = bias_vector(qb, mode[qb], base);
             const f32x16 sacc = qk(qb);
-            silu_vector(sacc, c, diag[qb], base, pop[qb][0], pop[qb][1]);
+            silu_vector(sacc, c, diag[qb], poly[qb], base, pop[qb][0], pop[qb][1]);
           }
         }
       }
@@ -419,34 +514,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
           vop[db][m] = *(const bf16x8*)(&sm.vt[buf][vt_off(32 * db + l32, 4 * hk + 2 * m + hf)]);
-      if (mode[0] != 0 && mode[1] != 0) {
+      // an inactive sub-tile has P = 0 and adds nothing; issuing its MFMAs anyway keeps the
+      // accumulators out of branches (they are rare: diagonal and tail steps only)
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
-              oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[qb][m], oacc[db][qb], 0, 0, 0);
-      } else if (mode[0] != 0) {
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int m = 0; m < 2; ++m)
-            oacc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[0][m], oacc[db][0], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int m = 0; m < 2; ++m)
-            oacc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[1][m], oacc[db][1], 0, 0, 0);
-      }
+          for (int qb = 0; qb < 2; ++qb)
+            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[qb][m], oacc[db][qb], 0, 0, 0);
     }
     if (t + 1 < n_tiles) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue: O^T accumulators -> O rows, scaled by -ln(2) out_scale ----
-  const float osc = -kLn2 * a.out_scale;
+  // ---- epilogue: O^T accumulators -> O rows, scaled by -(ln 2 / 2) out_scale ----
+  const float osc = -0.5f * kLn2 * a.out_scale;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = qw0 + 32 * qb + l32;

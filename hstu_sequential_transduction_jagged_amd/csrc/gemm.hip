@@ -47,7 +47,9 @@ struct SmemGemm {
   float beta[1024];
 };
 
-__device__ __forceinline__ int t_off(int row, int chunk) { return row * kBK + ((chunk ^ (row & 7)) << 3); }
+// 64-bank LDS: 16 lanes reading one chunk of 16 consecutive 128-byte rows are conflict-free
+// when the chunk is XOR-ed with (row / 2) & 7.
+__device__ __forceinline__ int t_off(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

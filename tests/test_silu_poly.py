@@ -1,0 +1,57 @@
+"""The bf16 attention kernel replaces SiLU by an odd polynomial on tiles where a
+Cauchy-Schwarz bound keeps |y| (y = -log2(e) x) inside a fixed range.  These host checks
+read the constants from the kernel source and bound the approximation error in fp64
+against the exact SiLU; the kernel's parity tests then check the result end to end."""
+import os
+import re
+
+import numpy as np
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "hstu_sequential_transduction_jagged_amd", "csrc", "attention.hip")
+
+
+def _constants():
+    text = open(SRC).read()
+    get = lambda name: float(re.search(r"\b%s = (-?[0-9.e+-]+)f" % name, text).group(1))
+    return get("kPolyRange"), [get("kP0"), get("kP1"), get("kP2")]
+
+
+def _w_poly(y, P):
+    u = y * y
+    return y - u * (P[0] + u * (P[1] + u * P[2]))
+
+
+def test_polynomial_relative_error_bound():
+    R, P = _constants()
+    y = np.linspace(-R, R, 200001)
+    x = -y / np.log2(np.e)
+    silu = x / (1.0 + np.exp(-x))
+    approx = -(np.log(2.0) / 2.0) * _w_poly(y, P)
+    nz = y != 0
+    rel = np.abs(approx[nz] - silu[nz]) / np.abs(silu[nz])
+    # far below bf16's unit roundoff 2^-8 = 3.9e-3, which P is rounded to anyway
+    assert rel.max() < 1e-4, rel.max()
+    assert approx[~nz][0] == 0.0
+
+
+def test_polynomial_limits():
+    R, P = _constants()
+    # near 0, s(y) = 1/2 - (ln 2 / 4) y + O(y^3), so P(0) is close to ln(2) / 2 (the minimax
+    # fit trades a little accuracy there for the ends of the range)
+    assert abs(P[0] - np.log(2.0) / 2.0) < 1e-3
+    # the fit is odd in y around the SiLU's symmetric part: w(y) - w(-y) = 2 y exactly
+    y = np.linspace(0, R, 101)
+    assert np.allclose(_w_poly(y, P) - _w_poly(-y, P), 2 * y, rtol=0, atol=1e-14)
+
+
+def test_fit_script_reproduces_constants():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "fit_silu_poly", os.path.join(os.path.dirname(SRC), "fit_silu_poly.py"))
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    R, P = _constants()
+    c, err = m.fit(R)
+    assert np.allclose(c, P, rtol=1e-6, atol=1e-9), (c, P)
+    assert err < 1e-4
