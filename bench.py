@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB five times "
+                         "(calibrates the HBM byte counters against a known traffic)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -100,6 +103,17 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mib:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
+                          "launches": 5}), flush=True)
+        return
     inp = synth.attn_long()
     lengths = np.diff(inp.offsets.astype(np.int64))
     bf = torch.bfloat16
