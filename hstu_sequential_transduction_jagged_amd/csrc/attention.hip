@@ -115,33 +115,74 @@ __global__ __launch_bounds__(256) void time_stats_kernel(const int32_t* __restri
 }
 
 // ============================================================================================
-// bf16, d = 64: 4 waves x 64 queries = 256 query rows per work item, 64 keys per LDS stage.
+// bf16, d = 64: 8 waves x 32 queries = 256 query rows per work item, 64 keys per LDS stage,
+// four waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time tables,
+// 2 ALiBi).
 // ============================================================================================
-constexpr int kWaves = 4;
-constexpr int kQW = 64;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kQW = 32;
 constexpr int kBR = kWaves * kQW;
 constexpr int kKB = 64;
 constexpr int kD = 64;
 
+// Largest half-width D of a 32x32 tile's y range (y = c + delta, |delta| <= D) for which the
+// second-order Taylor expansion of w around the tile's constant bias c is used: its remainder
+// is at most max|w'''| D^3 / 6 = 0.0521 D^3 <= 8.4e-5 D, below 2^-13 of the tile's largest
+// |w| (which is at least 0.96 D for D this small).
+constexpr float kTaylorD = 0.04f;
+
+// LDS rows of 64 bf16 are padded to 144 bytes: 16 lanes reading the same 16-byte column of 16
+// consecutive rows then hit 16 distinct groups of 4 banks (row * 36 words mod 64 is a
+// permutation of the multiples of 4), and every operand read is one base address per lane
+// plus an immediate offset.
+constexpr int kRow = 72;  // bf16 elements per padded row
+
+// Classification of one 32x32 tile (one wave's 32 queries x 32 keys) for the position + time
+// bias, written by the classifier lanes while the tile is staged.
+//   mode 1: one bias value c0 for the whole tile; 2: two time buckets, c0 below the split
+//   and c1 from it on (split: key offset from the block minimum <= lim); 3: per-element
+//   gather on 32-bit time offsets; 4: per-element gather on 64-bit times.
+struct __attribute__((aligned(16))) TileClass {
+  int32_t mode, thi, dq, pad;  // dq = (query block min time) - (key block min time), modes 2, 3
+  float c0, c1, thr_taylor, thr_poly;  // thresholds on the tile's max squared key norm
+  float a0, a1, a2, pad2;       // Taylor coefficients around c0 (mode 1)
+};
+
 struct __attribute__((aligned(16))) SmemBf16 {
-  __attribute__((aligned(16))) bf16 k[2][kKB * kD];   // row = key, 8 chunks of 16 B, chunk c stored at c ^ ((row / 2) & 7)
-  __attribute__((aligned(16))) bf16 vt[2][kD * kKB];  // row = d, 64 keys in PV slot order, chunk c at c ^ ((d + d/8) & 7)
-  __attribute__((aligned(16))) int32_t krel[2][kKB];  // key timestamp minus its 32-key block's minimum (0 past the end)
-  float knorm2[2][kWaves];      // per wave: max squared norm of the key rows it staged
+  __attribute__((aligned(16))) bf16 k[2][kKB * kRow];   // row = key
+  __attribute__((aligned(16))) bf16 vt[2][kD * kRow];   // row = d, 64 keys in PV slot order
+  __attribute__((aligned(16))) int32_t krel[2][kKB];    // key time minus its 32-key block's minimum
+  __attribute__((aligned(16))) float knorm2[2][kWaves]; // per staging wave: max squared key norm
+  __attribute__((aligned(16))) TileClass cls[2][kWaves][2];
+  __attribute__((aligned(16))) float tay[kMaxTimeBuckets][4];  // per time bucket: c, a0, a1, a2
+  __attribute__((aligned(16))) int64_t qtime[kWaves][2];       // per wave: query block min, max time
+  float qbound[kWaves];
   float wpos[kMaxPosBuckets];   // -log2(e) * w_pos[h]
   float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
   float wtime_lz[32];           // wtime[min(31 - lz, NT - 1)]: time bias by leading zeros of dt + 1
-  float cbuf[kWaves][16][64];   // per-wave bias staging of the 64-bit timestamp path
+  float cbuf[kWaves][16][64];   // per-wave per-element bias of one tile
 };
 
-// LDS has 64 four-byte banks and serves 16 lanes of a 16-byte read per cycle: 16 lanes
-// reading the same chunk of 16 consecutive 128-byte rows hit distinct banks when the chunk
-// is XOR-ed with (row / 2) & 7 (row parity selects the bank half).
-__device__ __forceinline__ int k_off(int row, int chunk) { return row * kD + ((chunk ^ ((row >> 1) & 7)) << 3); }
-__device__ __forceinline__ int vt_off(int d, int chunk) { return d * kKB + ((chunk ^ ((d + (d >> 3)) & 7)) << 3); }
+// w(y) = 2y/(1+2^y) and its first two derivatives at c, as the coefficients of the expansion
+// in the raw score s (y = c + cq s): w ~ a0 + a1 s + a2 s^2.  No overflow for any finite c:
+// s = 1/(1+2^c) and o = 1 - s come from 2^-|c|.
+__device__ __forceinline__ void w_taylor_coeffs(float c, float cq, float& a0, float& a1, float& a2) {
+  const float e = exp2f(-fabsf(c));
+  const float inv = 1.0f / (1.0f + e);
+  const float s = c >= 0.f ? e * inv : inv;
+  const float o = c >= 0.f ? inv : e * inv;
+  const float g = s * o;
+  const float w0 = 2.0f * c * s;
+  const float w1 = 2.0f * s - 2.0f * kLn2 * c * g;
+  const float w2 = -4.0f * kLn2 * g + 2.0f * kLn2 * kLn2 * c * g * (o - s);
+  a0 = w0;
+  a1 = w1 * cq;
+  a2 = 0.5f * w2 * cq * cq;
+}
 
-template <bool OUT_F32>
-__global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
+template <int KIND, bool OUT_F32>
+__global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) {
   __shared__ SmemBf16 sm;
   const int item = blockIdx.x;
   if (item >= *a.work_count) return;
@@ -156,173 +197,230 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
   if (q0 >= n) return;
   const int q_end = min(q0 + kBR, n);
   const int n_tiles = (q_end + kKB - 1) / kKB;
-  const int qw0 = q0 + wave * kQW;
+  const int qw0 = q0 + wave * kQW;                // first query row of this wave
   const int wq_last = min(qw0 + kQW, q_end) - 1;  // < qw0 when the wave has no rows
 
   const bf16* __restrict__ qp = (const bf16*)a.q;
   const bf16* __restrict__ kp = (const bf16*)a.k;
   const bf16* __restrict__ vp = (const bf16*)a.v;
-  const int kind = a.bias.kind;
   const int64_t* __restrict__ ts = a.bias.ts;
   const TimeStat* __restrict__ tstat = a.tstat;
-
-  if (kind == 1) {
-    for (int i = tid; i < a.bias.num_pos; i += 256)
-      sm.wpos[i] = -kLog2e * a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i];
-    for (int i = tid; i < a.bias.num_time; i += 256)
-      sm.wtime[i] = -kLog2e * a.bias.w_time[(int64_t)h * a.bias.time_stride + i];
-    if (tid < 32) {
-      const int tb = min(31 - tid, a.bias.num_time - 1);
-      sm.wtime_lz[tid] = -kLog2e * a.bias.w_time[(int64_t)h * a.bias.time_stride + tb];
-    }
-  }
-  const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
-  float slope_y = 0.f;
-  if (kind == 2) slope_y = kLog2e * (a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H));
-
-  // ---- Q fragments (B operand of S^T = K Q^T), unscaled; query timestamps ----
   const float cq = -a.alpha * kLog2e;
-  bf16x8 qop[2][4];
-  int64_t tq[2];
-  int64_t tqmin[2] = {0, 0}, tqmax[2] = {0, 0};
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qb0 = qw0 + 32 * qb;
-    const int row = qb0 + l32;
-    const bool valid = row <= wq_last;
+  const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
+  constexpr int kClassWave = 1;  // its lanes 0..15 classify the next tile (lane = 2 wave + hk)
+
+  // ---- Q fragments (B operand of S^T = K Q^T), unscaled ----
+  bf16x8 qop[4];
+  const int row = qw0 + l32;
+  const bool qvalid = row <= wq_last;
+  {
     const bf16* src = qp + (tok0 + row) * a.q_stride + (int64_t)h * kD + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (valid) raw = *(const u32x4*)(src + 16 * ks);
-      qop[qb][ks] = __builtin_bit_cast(bf16x8, raw);
-    }
-    tq[qb] = 0;
-    if (kind == 1 && qb0 <= wq_last) {
-      const TimeStat st = tstat[tok0 + qb0];
-      tqmin[qb] = st.mn;
-      tqmax[qb] = st.mx;
-      tq[qb] = valid ? ts[tok0 + row] : st.mn;
+      if (qvalid) raw = *(const u32x4*)(src + 16 * ks);
+      qop[ks] = __builtin_bit_cast(bf16x8, raw);
     }
   }
-
-  // max norm of the query rows of each 32-row block (bound of the polynomial SiLU path)
-  float qnorm[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  // |alpha log2 e| times the max norm of the wave's query rows: with a tile's max key norm,
+  // a bound on |y - bias| over the tile (Cauchy-Schwarz)
+  float qbound;
+  {
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bf16x2 pr = {qop[qb][ks][2 * e], qop[qb][ks][2 * e + 1]};
+        const bf16x2 pr = {qop[ks][2 * e], qop[ks][2 * e + 1]};
         ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
       }
     }
     ss += __shfl_xor(ss, 32, 64);  // the two lane halves hold the two halves of a row
-    qnorm[qb] = uniform_f32(sqrtf(wave_max(ss)));
+    qbound = uniform_f32(fabsf(cq) * 1.0001f * sqrtf(wave_max(ss)));  // margin for rounding
   }
-  // largest |bias| the tables can produce (y units)
-  float tabmax = 0.f;
-  if (kind == 1) {
-    float mp = 0.f, mt = 0.f;
-    for (int i = lane; i < a.bias.num_pos; i += 64)
-      mp = fmaxf(mp, fabsf(a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i]));
-    for (int i = lane; i < a.bias.num_time; i += 64)
-      mt = fmaxf(mt, fabsf(a.bias.w_time[(int64_t)h * a.bias.time_stride + i]));
-    tabmax = uniform_f32(kLog2e * (wave_max(mp) + wave_max(mt)));
-  }
-  const float acq = fabsf(cq) * 1.0001f;  // rounding margin of the bound
 
-  f32x16 oacc[2][2];
+  // ---- bias set-up ----
+  float slope_y = 0.f, ta0 = 0.f, ta1 = 0.f, ta2 = 0.f, tabmax = 0.f;
+  int32_t tq_rel = 0;  // query time minus the wave's block minimum (32-bit paths)
+  if (KIND == 1) {
+    const float* wp = a.bias.w_pos + (int64_t)h * a.bias.pos_stride;
+    const float* wt = a.bias.w_time + (int64_t)h * a.bias.time_stride;
+    for (int i = tid; i < a.bias.num_pos; i += kThreads) sm.wpos[i] = -kLog2e * wp[i];
+    if (tid < a.bias.num_time) {
+      // per time bucket: the bias of a tile with saturated position bucket, and its Taylor
+      // coefficients
+      const float c = -kLog2e * (wp[Pm1] + wt[tid]);
+      float x0, x1, x2;
+      w_taylor_coeffs(c, cq, x0, x1, x2);
+      *(f32x4*)(&sm.tay[tid][0]) = f32x4{c, x0, x1, x2};
+      sm.wtime[tid] = -kLog2e * wt[tid];
+    }
+    if (tid < 32) sm.wtime_lz[tid] = -kLog2e * wt[min(31 - tid, NTm1)];
+    if (wave == kClassWave) {
+      float mp = 0.f, mt = 0.f;
+      for (int i = lane; i < a.bias.num_pos; i += 64) mp = fmaxf(mp, fabsf(wp[i]));
+      for (int i = lane; i < a.bias.num_time; i += 64) mt = fmaxf(mt, fabsf(wt[i]));
+      tabmax = uniform_f32(kLog2e * (wave_max(mp) + wave_max(mt)));
+    }
+    int64_t tmin = 0, tmax = 0;
+    if (qw0 <= wq_last) {
+      const TimeStat st = tstat[tok0 + qw0];
+      tmin = st.mn;
+      tmax = st.mx;
+    }
+    if (lane == 0) {
+      sm.qtime[wave][0] = tmin;
+      sm.qtime[wave][1] = tmax;
+      sm.qbound[wave] = qbound;
+    }
+    if (qvalid) {
+      const int64_t d = ts[tok0 + row] - tmin;
+      tq_rel = d > 0x7fffffffLL ? 0x7fffffff : (int32_t)d;
+    }
+  } else if (KIND == 0) {
+    w_taylor_coeffs(0.f, cq, ta0, ta1, ta2);
+  } else {
+    slope_y = kLog2e * (a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H));
+  }
+  // register r of a 32x32 accumulator holds key acc_key(r, hf) = kc(r) + 4 hf for query l32
+  const int lv = l32 - 4 * hf;
+  const float neg_slope_y = -slope_y, alibi_lane = slope_y * (float)lv;
+
+  f32x16 oacc[2];
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][qb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
   // ---- staging: global -> registers -> LDS ----
-  const int krow0 = tid >> 3, kchunk = tid & 7;       // K rows krow0 and krow0 + 32
-  const int vpair = tid >> 3, vch = tid & 7;          // V keys 2 vpair, 2 vpair + 1; d chunk vch
-  const bf16* kbase = kp + (tok0 + krow0) * a.k_stride + (int64_t)h * kD + 8 * kchunk;
-  const bf16* vbase = vp + (tok0 + 2 * vpair) * a.v_stride + (int64_t)h * kD + 8 * vch;
-  // V^T store: element e of the chunk (d = 8 vch + e) goes to row d at key slot vpos; the
-  // swizzled 16-byte chunk index of row d is (vpos / 8) ^ ((e + vch) & 7)
+  // K: thread t stages 16-byte chunk t % 8 of key row t / 8.  V: thread t stages d values
+  // 4 (t % 16) .. +3 of the key pair 2 (t / 16), 2 (t / 16) + 1, packed per d into one 32-bit
+  // word (the pair occupies two adjacent PV slots).  K and V rows are read through buffer
+  // descriptors bounded at the last key row this item needs: rows at or past q_end read as
+  // zeros without a branch.
+  const int krow = tid >> 3, kchunk = tid & 7;
+  const int vpair = tid >> 4, vq = tid & 15;
+  const uint32_t kstride_b = (uint32_t)a.k_stride * 2u, vstride_b = (uint32_t)a.v_stride * 2u;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kp + tok0 * a.k_stride + (int64_t)h * kD), (short)0,
+      (int)((uint32_t)(q_end - 1) * kstride_b + 2u * kD), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vp + tok0 * a.v_stride + (int64_t)h * kD), (short)0,
+      (int)((uint32_t)(q_end - 1) * vstride_b + 2u * kD), 0x00020000);
+  const uint32_t koff = (uint32_t)krow * kstride_b + 16u * kchunk;
+  const uint32_t voff = (uint32_t)(2 * vpair) * vstride_b + 8u * vq;
   const int vpos = 16 * ((2 * vpair) >> 4) + pv_slot((2 * vpair) & 15);
-  uint32_t vsw = 0;  // 8 nibbles: swizzled chunk for e = 0..7
-#pragma unroll
-  for (int e = 0; e < 8; ++e) vsw |= (uint32_t)(((vpos >> 3) ^ ((e + vch) & 7)) & 7) << (4 * e);
-  const int vdst0 = 8 * vch * kKB + (vpos & 7);
-  u32x4 kreg[2], vreg[2];
-  i32x4 rreg = {0, 0, 0, 0};
+  // timestamp data of the tile: wave 0 lane l stages key l's offset from its block minimum;
+  // lanes 0..7 of the classifier wave load the min / max of the tile's two 32-key blocks
+  // (one dword each)
+  const __amdgpu_buffer_rsrc_t rrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(KIND != 1 ? nullptr : wave == 0 ? (const void*)(a.trel + tok0) : (const void*)(tstat + tok0)),
+      (short)0, KIND == 1 ? q_end * (wave == 0 ? 4 : 16) : 0, 0x00020000);
+  const uint32_t roff = wave == 0 ? 4u * lane : 16u * 32u * (uint32_t)(lane >> 2) + 4u * (lane & 3);
+  u32x4 kreg;
+  u32x2 vreg[2];
+  int32_t rdw = 0;
   auto gload = [&](int t) {
     const int j0 = t * kKB;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = j0 + krow0 + 32 * u;
-      kreg[u] = u32x4{0u, 0u, 0u, 0u};
-      if (key < q_end) kreg[u] = *(const u32x4*)(kbase + (int64_t)(j0 + 32 * u) * a.k_stride);
-      const int vkey = j0 + 2 * vpair + u;
-      vreg[u] = u32x4{0u, 0u, 0u, 0u};
-      if (vkey < q_end) vreg[u] = *(const u32x4*)(vbase + (int64_t)(j0 + u) * a.v_stride);
-    }
-    if (kind == 1 && tid < kKB / 4) {
-      const int key = j0 + 4 * tid;
-      rreg = i32x4{0, 0, 0, 0};
-      if (key + 3 < q_end) {
-        rreg = *(const i32x4*)(a.trel + tok0 + key);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (key + e < q_end) rreg[e] = a.trel[tok0 + key + e];
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
+    kreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, koff, (uint32_t)j0 * kstride_b, 0));
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      *(u32x4*)(&sm.k[buf][k_off(krow0 + 32 * u, kchunk)]) = kreg[u];
+      vreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff + u * vstride_b, (uint32_t)j0 * vstride_b, 0));
+    if (KIND == 1 && (wave == 0 || (wave == kClassWave && lane < 8)))
+      rdw = __builtin_amdgcn_raw_buffer_load_b32(rrsrc, roff, (uint32_t)j0 * (wave == 0 ? 4u : 16u), 0);
+  };
+  auto lstore = [&](int buf) {
+    *(u32x4*)(&sm.k[buf][krow * kRow + 8 * kchunk]) = kreg;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // element e of both key rows: low (e even) or high (e odd) half of word e / 2
+    for (int e = 0; e < 4; ++e) {
+      // d = 4 vq + e: element e of both key rows (low half of word e / 2 for even e)
       const uint32_t wa = vreg[0][e >> 1], wb = vreg[1][e >> 1];
       const uint32_t pk = __builtin_amdgcn_perm(wb, wa, (e & 1) ? 0x07060302u : 0x05040100u);
-      const int chunk = (vsw >> (4 * e)) & 7;
-      *(uint32_t*)(&sm.vt[buf][vdst0 + e * kKB + (chunk << 3)]) = pk;
+      *(uint32_t*)(&sm.vt[buf][(4 * vq + e) * kRow + vpos]) = pk;
     }
-    if (kind == 1 && tid < kKB / 4) *(i32x4*)(&sm.krel[buf][4 * tid]) = rreg;
+    if (KIND == 1 && wave == 0) sm.krel[buf][lane] = rdw;
     // max squared norm of the staged key rows: 8 threads hold the 8 chunks of a row
-    float ss[2];
+    const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg);
+    float acc = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg[u]);
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
-        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
-      }
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      acc += __shfl_xor(acc, 4, 64);
-      ss[u] = acc;
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
+      acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
     }
-    float mx = fmaxf(ss[0], ss[1]);
-    mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (lane == 0) sm.knorm2[buf][wave] = mx;
+    acc += __shfl_xor(acc, 1, 64);
+    acc += __shfl_xor(acc, 2, 64);
+    acc += __shfl_xor(acc, 4, 64);
+    acc = wave_max(acc);
+    if (lane == 0) sm.knorm2[buf][wave] = acc;
+  };
+  // classifier: lanes 0..15 of the classifier wave classify the tile t (staged into buf) for
+  // wave (lane / 2) and its 32-key half (lane % 2).  Needs rdw of tile t, the tables and the
+  // per-wave query data in LDS.
+  auto classify = [&](int t, int buf) {
+    // key block min / max of both halves, from the dwords lanes 0..7 loaded
+    int64_t kmn_h[2], kmx_h[2];
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+      const uint32_t w0 = __builtin_amdgcn_readlane(rdw, 4 * hk), w1 = __builtin_amdgcn_readlane(rdw, 4 * hk + 1);
+      const uint32_t w2 = __builtin_amdgcn_readlane(rdw, 4 * hk + 2), w3 = __builtin_amdgcn_readlane(rdw, 4 * hk + 3);
+      kmn_h[hk] = (int64_t)(((uint64_t)w1 << 32) | w0);
+      kmx_h[hk] = (int64_t)(((uint64_t)w3 << 32) | w2);
+    }
+    if (lane < 2 * kWaves) {
+      const int w = lane >> 1, hk = lane & 1;
+      const int j0h = t * kKB + 32 * hk;
+      const int qb0 = q0 + kQW * w;
+      const int64_t kmn = hk ? kmn_h[1] : kmn_h[0], kmx = hk ? kmx_h[1] : kmx_h[0];
+      const int64_t tmin = sm.qtime[w][0], tmax = sm.qtime[w][1];
+      const float qb = sm.qbound[w];
+      const bool pconst = (qb0 - (j0h + 31)) >= Pm1;
+      const int tlo = time_bucket(tmin - kmx, NTm1);
+      const int thi = time_bucket(tmax - kmn, NTm1);
+      const int64_t lim30 = 1LL << 30;
+      const bool fits32 = (kmx - kmn) <= lim30 && (tmax - tmin) <= lim30 && (tmax - kmn) <= lim30 &&
+                          (tmin - kmn) >= -lim30;
+      const int mode = (pconst && tlo == thi) ? 1 : (pconst && thi == tlo + 1 && fits32) ? 2 : fits32 ? 3 : 4;
+      const f32x4 lo = *(const f32x4*)(&sm.tay[tlo][0]);
+      const float c1 = sm.tay[thi][0];
+      const float cabs = mode == 1 ? fabsf(lo[0]) : mode == 2 ? fmaxf(fabsf(lo[0]), fabsf(c1)) : tabmax;
+      // |y - bias| <= qb * knorm: Taylor iff qb^2 knorm^2 <= kTaylorD^2 (constant bias only),
+      // polynomial iff qb * knorm + cabs <= kPolyRange
+      const float qb2 = qb * qb;
+      const float thr_t = mode == 1 ? kTaylorD * kTaylorD / qb2 : -1.f;
+      const float room = kPolyRange - cabs;
+      const float thr_p = room >= 0.f ? room * room / qb2 : -1.f;
+      TileClass c;
+      c.mode = mode;
+      c.thi = thi;
+      c.dq = (int32_t)(tmin - kmn);
+      c.pad = 0;
+      c.c0 = lo[0];
+      c.c1 = c1;
+      c.thr_taylor = thr_t;
+      c.thr_poly = thr_p;
+      c.a0 = lo[1];
+      c.a1 = lo[2];
+      c.a2 = lo[3];
+      c.pad2 = 0.f;
+      sm.cls[buf][w][hk] = c;
+    }
   };
 
   gload(0);
   lstore(0);
+  if (KIND == 1) {
+    __syncthreads();  // tables and per-wave query data
+    if (wave == kClassWave) classify(0, 0);
+  }
   __syncthreads();
 
+  enum { kExact = 0, kPoly = 1, kTaylor = 2 };
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(t + 1);
+    const bool more = t + 1 < n_tiles;
+    if (more) gload(t + 1);
     const int j0 = t * kKB;
+    float kn2 = 0.f;
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
       const int j0h = j0 + 32 * hk;
@@ -331,65 +429,79 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
       bf16x8 kop[4], vop[2][2];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        kop[ks] = *(const bf16x8*)(&sm.k[buf][k_off(32 * hk + l32, hf + 2 * ks)]);
-
-      // ---- classification of the two 32x32 sub-tiles, all in scalar registers ----
-      // mode 0: inactive, 1: scalar bias, 2: two time buckets (one compare per element),
-      // 3: per-element bias (gather on 32-bit time offsets, ALiBi, or none with the mask),
-      // 4: per-element gather on 64-bit times
-      int mode[2], thi2[2];
-      float cb[2], chi[2];
-      bool diag[2], poly[2];
-      float kn2 = fmaxf(fmaxf(sm.knorm2[buf][0], sm.knorm2[buf][1]),
-                        fmaxf(sm.knorm2[buf][2], sm.knorm2[buf][3]));
-      const float knorm = uniform_f32(sqrtf(kn2));
-      int64_t kmn = 0, kmx = 0;
-      if (kind == 1) {
-        const TimeStat ks = tstat[tok0 + j0h];
-        kmn = ks.mn;
-        kmx = ks.mx;
+        kop[ks] = *(const bf16x8*)(&sm.k[buf][(32 * hk + l32) * kRow + 16 * ks + 8 * hf]);
+      if (hk == 0) {
+        const f32x4 k0 = *(const f32x4*)(&sm.knorm2[buf][0]);
+        const f32x4 k1 = *(const f32x4*)(&sm.knorm2[buf][4]);
+        kn2 = uniform_f32(fmaxf(fmaxf(fmaxf(k0[0], k0[1]), fmaxf(k0[2], k0[3])),
+                                fmaxf(fmaxf(k1[0], k1[1]), fmaxf(k1[2], k1[3]))));
       }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int qb0 = qw0 + 32 * qb;
-        const bool act = (qb0 <= wq_last) && (j0h <= min(qb0 + 31, wq_last));
-        const bool dg = (j0h + 31) > qb0;
-        int md = 3, th = 0;
-        float c0 = 0.f, c1 = 0.f;
-        if (kind == 0) {
-          md = dg ? 3 : 1;
-        } else if (kind == 1) {
-          const bool pconst = (qb0 - (j0h + 31)) >= Pm1;  // implies !dg
-          const int tlo = time_bucket(tqmin[qb] - kmx, NTm1);
-          const int thi = time_bucket(tqmax[qb] - kmn, NTm1);
-          const int64_t lim30 = 1LL << 30;
-          const bool fits32 = (kmx - kmn) <= lim30 && (tqmax[qb] - kmn) <= lim30 &&
-                              (tqmin[qb] - kmn) >= -lim30;
-          c0 = sm.wpos[Pm1] + sm.wtime[tlo];
-          c1 = sm.wpos[Pm1] + sm.wtime[thi];
-          th = thi;
-          md = (pconst && tlo == thi) ? 1 : (pconst && thi == tlo + 1 && fits32) ? 2 : fits32 ? 3 : 4;
+      const bool diag = (j0h + 31) > qw0;
+      // i - j of register r = dlt + lv - kc(r): a lane term, a tile term and a constant
+      const int dlt = qw0 - j0h;
+      auto kc = [](int r) { return 8 * (r >> 2) + (r & 3); };
+
+      // ---- this tile's bias mode and SiLU evaluation ----
+      int mode, path, thi = 0, dq = 0;
+      float c0 = 0.f, c1 = 0.f, A0 = ta0, A1 = ta1, A2 = ta2;
+      if (KIND == 0) {
+        mode = diag ? 3 : 1;
+        const float D2 = qbound * qbound * kn2;
+        path = D2 <= kTaylorD * kTaylorD ? kTaylor : D2 <= kPolyRange * kPolyRange ? kPoly : kExact;
+      } else if (KIND == 1) {
+        const i32x4 e0 = *(const i32x4*)(&sm.cls[buf][wave][hk].mode);
+        const f32x4 e1 = *(const f32x4*)(&sm.cls[buf][wave][hk].c0);
+        const f32x4 e2 = *(const f32x4*)(&sm.cls[buf][wave][hk].a0);
+        mode = __builtin_amdgcn_readfirstlane(e0[0]);
+        thi = __builtin_amdgcn_readfirstlane(e0[1]);
+        dq = __builtin_amdgcn_readfirstlane(e0[2]);
+        c0 = uniform_f32(e1[0]);
+        c1 = uniform_f32(e1[1]);
+        path = kn2 <= uniform_f32(e1[2]) ? kTaylor : kn2 <= uniform_f32(e1[3]) ? kPoly : kExact;
+        A0 = uniform_f32(e2[0]);
+        A1 = uniform_f32(e2[1]);
+        A2 = uniform_f32(e2[2]);
+      } else {
+        mode = 3;
+        const float room = kPolyRange - slope_y * (float)max(qw0 + 31 - j0h, 0);
+        path = (room >= 0.f && qbound * qbound * kn2 <= room * room) ? kPoly : kExact;
+      }
+
+      if (KIND == 1 && mode >= 2) {
+        // per-element bias of the tile (y units) into this wave's LDS scratch, one register
+        // at a time: these tiles are the few near the diagonal or straddling time buckets
+        if (mode == 2) {
+          // two time buckets: dt >= 2^thi - 1  <=>  rel_j <= (t_i - kmin) - (2^thi - 1)
+          const int lim = tq_rel + dq - ((1 << thi) - 1);
+#pragma unroll 1
+          for (int r = 0; r < 16; ++r)
+            sm.cbuf[wave][r][lane] = sm.krel[buf][32 * hk + kc(r) + 4 * hf] <= lim ? c1 : c0;
+        } else if (mode == 3) {
+          const int ti1 = tq_rel + dq + 1;
+#pragma unroll 1
+          for (int r = 0; r < 16; ++r) {
+            const int u = max(ti1 - sm.krel[buf][32 * hk + kc(r) + 4 * hf], 1);  // max(dt, 0) + 1
+            const int pb = min(max(lv + (dlt - kc(r)), 0), Pm1);
+            sm.cbuf[wave][r][lane] = sm.wpos[pb] + sm.wtime_lz[__builtin_clz((uint32_t)u)];
+          }
+        } else {
+          // timestamps spread beyond 2^30 within the tile: exact 64-bit deltas
+          const int64_t tq = ts[tok0 + min(row, n - 1)];
+#pragma unroll 1
+          for (int r = 0; r < 16; ++r) {
+            const int key = min(j0h + kc(r) + 4 * hf, n - 1);
+            sm.cbuf[wave][r][lane] = sm.wpos[pos_bucket(lv + (dlt - kc(r)), Pm1)] +
+                                     sm.wtime[time_bucket(tq - ts[tok0 + key], NTm1)];
+          }
         }
-        mode[qb] = act ? md : 0;
-        thi2[qb] = th;
-        diag[qb] = dg;
-        cb[qb] = uniform_f32(c0);
-        chi[qb] = uniform_f32(c1);
-        // largest |bias_y| in the sub-tile, then the bound on |y|
-        float cabs = 0.f;
-        if (kind == 1) cabs = md == 1 ? fabsf(cb[qb]) : md == 2 ? fmaxf(fabsf(cb[qb]), fabsf(chi[qb])) : tabmax;
-        if (kind == 2) cabs = fabsf(slope_y) * (float)max(qb0 + 31 - j0h, 0);
-        poly[qb] = acq * qnorm[qb] * knorm + cabs <= kPolyRange;
       }
 
-      auto qk = [&](int qb) {
-        f32x16 sacc = {};
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[0], qop[qb][0], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[1], qop[qb][1], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[2], qop[qb][2], sacc, 0, 0, 0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[3], qop[qb][3], sacc, 0, 0, 0);
-        return sacc;
-      };
+      // S^T tile: rows = keys, columns = this wave's queries
+      f32x16 sacc = {};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], sacc, 0, 0, 0);
+
       // y = -log2(e) (alpha s + bias); w(y) = 2 y / (1 + 2^y) = -(2 / ln 2) SiLU(alpha s + bias)
       auto w_exact = [&](float y) {
         return y * __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(y), 0.5f, 0.5f));
@@ -398,149 +510,81 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_d64_kernel(AttnArgs a) {
         const float u = y * y;
         return __builtin_fmaf(-u, __builtin_fmaf(__builtin_fmaf(kP2, u, kP1), u, kP0), y);
       };
-      auto silu_scalar = [&](const f32x16& sacc, float c, bool pl, bf16x8& p0, bf16x8& p1) {
-        f32x8 a0, a1;
-        if (pl) {
+      f32x16 w;
+      if (path == kTaylor && (mode == 1 || KIND == 0)) {
+        // the common case: constant bias, small |delta|
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float av = w_poly(__builtin_fmaf(sacc[r], cq, c));
-            if (r < 8) a0[r] = av; else a1[r - 8] = av;
-          }
+        for (int r = 0; r < 16; ++r) w[r] = __builtin_fmaf(__builtin_fmaf(A2, sacc[r], A1), sacc[r], A0);
+      } else if (mode == 1 || KIND == 0) {
+        if (path == kPoly) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) w[r] = w_poly(__builtin_fmaf(sacc[r], cq, c0));
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float av = w_exact(__builtin_fmaf(sacc[r], cq, c));
-            if (r < 8) a0[r] = av; else a1[r - 8] = av;
-          }
+          for (int r = 0; r < 16; ++r) w[r] = w_exact(__builtin_fmaf(sacc[r], cq, c0));
         }
-        p0 = __builtin_convertvector(a0, bf16x8);
-        p1 = __builtin_convertvector(a1, bf16x8);
-      };
-      auto silu_vector = [&](const f32x16& sacc, const f32x16& c, bool mask, bool pl, int base,
-                             bf16x8& p0, bf16x8& p1) {
-        f32x8 a0, a1;
-        if (pl) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float av = w_poly(__builtin_fmaf(sacc[r], cq, c[r]));
-            if (r < 8) a0[r] = av; else a1[r - 8] = av;
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float av = w_exact(__builtin_fmaf(sacc[r], cq, c[r]));
-            if (r < 8) a0[r] = av; else a1[r - 8] = av;
-          }
-        }
-        if (mask) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool keep = (base - acc_key(r, hf)) >= 0;
-            if (r < 8) a0[r] = keep ? a0[r] : 0.f; else a1[r - 8] = keep ? a1[r - 8] : 0.f;
-          }
-        }
-        p0 = __builtin_convertvector(a0, bf16x8);
-        p1 = __builtin_convertvector(a1, bf16x8);
-      };
-      // per-element bias (y units) of sub-tile qb
-      auto bias_vector = [&](int qb, int m, int base) {
-        f32x16 c;
-        if (kind == 2) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) c[r] = slope_y * (float)(base - acc_key(r, hf));
-        } else if (kind == 0) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) c[r] = 0.f;
-        } else if (m == 2 || m == 3) {
-          i32x4 rel4[4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) rel4[g] = *(const i32x4*)(&sm.krel[buf][32 * hk + 8 * g + 4 * hf]);
-          if (m == 2) {
-            // two time buckets: dt >= 2^thi - 1  <=>  rel_j <= (t_i - kmin) - (2^thi - 1)
-            const int64_t lim64 = (tq[qb] - kmn) - ((1LL << thi2[qb]) - 1);
-            const int lim = lim64 < -1 ? -1 : (lim64 > 0x7fffffffLL ? 0x7fffffff : (int)lim64);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) c[r] = rel4[r >> 2][r & 3] <= lim ? chi[qb] : cb[qb];
-          } else {
-            const int ti1 = (int)(tq[qb] - kmn) + 1;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int u = max(ti1 - rel4[r >> 2][r & 3], 1);  // max(dt, 0) + 1
-              const int pb = min(max(base - acc_key(r, hf), 0), Pm1);
-              c[r] = sm.wpos[pb] + sm.wtime_lz[__builtin_clz((uint32_t)u)];
-            }
-          }
-        } else {
-          // timestamps spread beyond 2^30 within the sub-tile: exact 64-bit deltas, one
-          // element at a time through LDS to keep register use flat
-#pragma unroll 1
-          for (int r = 0; r < 16; ++r) {
-            const int kr = acc_key(r, hf);
-            const int key = min(j0h + kr, n - 1);
-            sm.cbuf[wave][r][lane] = sm.wpos[pos_bucket(base - kr, Pm1)] +
-                                     sm.wtime[time_bucket(tq[qb] - ts[tok0 + key], NTm1)];
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) c[r] = sm.cbuf[wave][r][lane];
-        }
-        return c;
-      };
-
-      bf16x8 pop[2][2] = {{bf16x8{}, bf16x8{}}, {bf16x8{}, bf16x8{}}};
-      if (mode[0] == 1 && mode[1] == 1) {
-        const f32x16 s0 = qk(0);
-        const f32x16 s1 = qk(1);
-        silu_scalar(s0, cb[0], poly[0], pop[0][0], pop[0][1]);
-        silu_scalar(s1, cb[1], poly[1], pop[1][0], pop[1][1]);
       } else {
+        // per-element bias (y units), added to the scaled scores in place
+        if (KIND == 2) {
+          const float base = alibi_lane + slope_y * (float)dlt;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (mode[qb] == 0) continue;
-          const int qb0 = qw0 + 32 * qb;
-          if (mode[qb] == 1) {
-            const f32x16 sacc = qk(qb);
-            silu_scalar(sacc, cb[qb], poly[qb], pop[qb][0], pop[qb][1]);
-          } else {
-            // bias first, then the scores: fewer registers live at once
-            const int base = qb0 - j0h + l32;  // i - j = base - acc_key(r, hf)
-            const f32x16 c = bias_vector(qb, mode[qb], base);
-            const f32x16 sacc = qk(qb);
-            silu_vector(sacc, c, diag[qb], poly[qb], base, pop[qb][0], pop[qb][1]);
-          }
+          for (int r = 0; r < 16; ++r)
+            sacc[r] = __builtin_fmaf(sacc[r], cq, __builtin_fmaf(neg_slope_y, (float)kc(r), base));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[r] = __builtin_fmaf(sacc[r], cq, sm.cbuf[wave][r][lane]);
         }
+        if (path == kPoly) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) w[r] = w_poly(sacc[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) w[r] = w_exact(sacc[r]);
+        }
+      }
+      if (diag) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w[r] = lv >= kc(r) - dlt ? w[r] : 0.f;
+      }
+      bf16x8 pop[2];
+      {
+        f32x8 a0, a1;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          a0[r] = w[r];
+          a1[r] = w[r + 8];
+        }
+        pop[0] = __builtin_convertvector(a0, bf16x8);
+        pop[1] = __builtin_convertvector(a1, bf16x8);
       }
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-          vop[db][m] = *(const bf16x8*)(&sm.vt[buf][vt_off(32 * db + l32, 4 * hk + 2 * m + hf)]);
-      // an inactive sub-tile has P = 0 and adds nothing; issuing its MFMAs anyway keeps the
-      // accumulators out of branches (they are rare: diagonal and tail steps only)
+          vop[db][m] = *(const bf16x8*)(&sm.vt[buf][(32 * db + l32) * kRow + 32 * hk + 16 * m + 8 * hf]);
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            oacc[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[qb][m], oacc[db][qb], 0, 0, 0);
+        for (int db = 0; db < 2; ++db)
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[m], oacc[db], 0, 0, 0);
     }
-    if (t + 1 < n_tiles) lstore(buf ^ 1);
+    if (more) {
+      lstore(buf ^ 1);
+      if (KIND == 1 && wave == kClassWave) classify(t + 1, buf ^ 1);
+    }
     __syncthreads();
   }
 
   // ---- epilogue: O^T accumulators -> O rows, scaled by -(ln 2 / 2) out_scale ----
   const float osc = -0.5f * kLn2 * a.out_scale;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int row = qw0 + 32 * qb + l32;
-    if (row > wq_last) continue;
+  if (qvalid) {
     const int64_t base = ((tok0 + row) * H + h) * kD;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 v4 = {oacc[db][qb][4 * g] * osc, oacc[db][qb][4 * g + 1] * osc,
-                    oacc[db][qb][4 * g + 2] * osc, oacc[db][qb][4 * g + 3] * osc};
+        f32x4 v4 = {oacc[db][4 * g] * osc, oacc[db][4 * g + 1] * osc, oacc[db][4 * g + 2] * osc,
+                    oacc[db][4 * g + 3] * osc};
         const int d0 = 32 * db + 8 * g + 4 * hf;
         if (OUT_F32)
           *(f32x4*)((float*)a.o + base + d0) = v4;
@@ -750,10 +794,16 @@ hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* t
 hipError_t launch_attn_bf16(int d, const AttnArgs& a, int grid, hipStream_t stream) {
   if (d != 64) return hipErrorInvalidValue;
   if (grid <= 0) return hipSuccess;
-  if (a.o_f32)
-    hipLaunchKernelGGL(attn_bf16_d64_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_bf16_d64_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+  const dim3 g(grid), blk(kThreads);
+  switch (a.bias.kind * 2 + (a.o_f32 ? 1 : 0)) {
+    case 0: hipLaunchKernelGGL((attn_bf16_d64_kernel<0, false>), g, blk, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((attn_bf16_d64_kernel<0, true>), g, blk, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_bf16_d64_kernel<1, false>), g, blk, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((attn_bf16_d64_kernel<1, true>), g, blk, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((attn_bf16_d64_kernel<2, false>), g, blk, 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((attn_bf16_d64_kernel<2, true>), g, blk, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
