@@ -140,9 +140,10 @@ constexpr int kRow = 72;  // bf16 elements per padded row
 
 // Classification of one 32x32 tile (one wave's 32 queries x 32 keys) for the position + time
 // bias, written by the classifier lanes while the tile is staged.
-//   mode 1: one bias value c0 for the whole tile; 2: two time buckets, c0 below the split
-//   and c1 from it on (split: key offset from the block minimum <= lim); 3: per-element
-//   gather on 32-bit time offsets; 4: per-element gather on 64-bit times.
+//   mode 1: one bias value c0 for the whole tile (position bucket saturated, one time
+//   bucket); 2: position bucket saturated, two time buckets: c0 or c1 per element; 3: position
+//   bucket varies, one time bucket: position table plus c0 (the time part); 4: both vary,
+//   gathered per element on 32-bit time offsets; 5: as 4 on 64-bit times.
 struct __attribute__((aligned(16))) TileClass {
   int32_t mode, thi, dq, pad;  // dq = (query block min time) - (key block min time), modes 2, 3
   float c0, c1, thr_taylor, thr_poly;  // thresholds on the tile's max squared key norm
@@ -158,7 +159,7 @@ struct __attribute__((aligned(16))) SmemBf16 {
   __attribute__((aligned(16))) float tay[kMaxTimeBuckets][4];  // per time bucket: c, a0, a1, a2
   __attribute__((aligned(16))) int64_t qtime[kWaves][2];       // per wave: query block min, max time
   float qbound[kWaves];
-  float wpos[kMaxPosBuckets];   // -log2(e) * w_pos[h]
+  float wposx[kMaxPosBuckets + 96];  // -log2(e) * w_pos[h][clamp(i - j, 0, P - 1)] at i - j + 32
   float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
   float wtime_lz[32];           // wtime[min(31 - lz, NT - 1)]: time bias by leading zeros of dt + 1
   float cbuf[kWaves][16][64];   // per-wave per-element bias of one tile
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   if (KIND == 1) {
     const float* wp = a.bias.w_pos + (int64_t)h * a.bias.pos_stride;
     const float* wt = a.bias.w_time + (int64_t)h * a.bias.time_stride;
-    for (int i = tid; i < a.bias.num_pos; i += kThreads) sm.wpos[i] = -kLog2e * wp[i];
+    for (int i = tid; i < a.bias.num_pos + 96; i += kThreads) sm.wposx[i] = -kLog2e * wp[min(max(i - 32, 0), Pm1)];
     if (tid < a.bias.num_time) {
       // per time bucket: the bias of a tile with saturated position bucket, and its Taylor
       // coefficients
@@ -379,7 +380,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       const int64_t lim30 = 1LL << 30;
       const bool fits32 = (kmx - kmn) <= lim30 && (tmax - tmin) <= lim30 && (tmax - kmn) <= lim30 &&
                           (tmin - kmn) >= -lim30;
-      const int mode = (pconst && tlo == thi) ? 1 : (pconst && thi == tlo + 1 && fits32) ? 2 : fits32 ? 3 : 4;
+      const int mode = pconst ? (tlo == thi ? 1 : (thi == tlo + 1 && fits32) ? 2 : fits32 ? 4 : 5)
+                              : (tlo == thi ? 3 : fits32 ? 4 : 5);
       const f32x4 lo = *(const f32x4*)(&sm.tay[tlo][0]);
       const float c1 = sm.tay[thi][0];
       const float cabs = mode == 1 ? fabsf(lo[0]) : mode == 2 ? fmaxf(fabsf(lo[0]), fabsf(c1)) : tabmax;
@@ -394,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       c.thi = thi;
       c.dq = (int32_t)(tmin - kmn);
       c.pad = 0;
-      c.c0 = lo[0];
+      c.c0 = mode == 3 ? sm.wtime[tlo] : lo[0];
       c.c1 = c1;
       c.thr_taylor = thr_t;
       c.thr_poly = thr_p;
@@ -440,6 +442,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       // i - j of register r = dlt + lv - kc(r): a lane term, a tile term and a constant
       const int dlt = qw0 - j0h;
       auto kc = [](int r) { return 8 * (r >> 2) + (r & 3); };
+      // dlt capped where every position bucket of the tile saturates: then i - j + 32 indexes
+      // the extended position table within its P + 96 entries
+      const int dltc = min(dlt, Pm1 + 33);
 
       // ---- this tile's bias mode and SiLU evaluation ----
       int mode, path, thi = 0, dq = 0;
@@ -467,32 +472,15 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
         path = (room >= 0.f && qbound * qbound * kn2 <= room * room) ? kPoly : kExact;
       }
 
-      if (KIND == 1 && mode >= 2) {
-        // per-element bias of the tile (y units) into this wave's LDS scratch, one register
-        // at a time: these tiles are the few near the diagonal or straddling time buckets
-        if (mode == 2) {
-          // two time buckets: dt >= 2^thi - 1  <=>  rel_j <= (t_i - kmin) - (2^thi - 1)
-          const int lim = tq_rel + dq - ((1 << thi) - 1);
+      if (KIND == 1 && mode == 5) {
+        // timestamps spread beyond 2^30 within the tile: exact 64-bit deltas, one register at a
+        // time into this wave's LDS scratch (such spreads are rare)
+        const int64_t tq = ts[tok0 + min(row, n - 1)];
 #pragma unroll 1
-          for (int r = 0; r < 16; ++r)
-            sm.cbuf[wave][r][lane] = sm.krel[buf][32 * hk + kc(r) + 4 * hf] <= lim ? c1 : c0;
-        } else if (mode == 3) {
-          const int ti1 = tq_rel + dq + 1;
-#pragma unroll 1
-          for (int r = 0; r < 16; ++r) {
-            const int u = max(ti1 - sm.krel[buf][32 * hk + kc(r) + 4 * hf], 1);  // max(dt, 0) + 1
-            const int pb = min(max(lv + (dlt - kc(r)), 0), Pm1);
-            sm.cbuf[wave][r][lane] = sm.wpos[pb] + sm.wtime_lz[__builtin_clz((uint32_t)u)];
-          }
-        } else {
-          // timestamps spread beyond 2^30 within the tile: exact 64-bit deltas
-          const int64_t tq = ts[tok0 + min(row, n - 1)];
-#pragma unroll 1
-          for (int r = 0; r < 16; ++r) {
-            const int key = min(j0h + kc(r) + 4 * hf, n - 1);
-            sm.cbuf[wave][r][lane] = sm.wpos[pos_bucket(lv + (dlt - kc(r)), Pm1)] +
-                                     sm.wtime[time_bucket(tq - ts[tok0 + key], NTm1)];
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int key = min(j0h + kc(r) + 4 * hf, n - 1);
+          sm.cbuf[wave][r][lane] = sm.wposx[pos_bucket(lv + (dlt - kc(r)), Pm1) + 32] +
+                                   sm.wtime[time_bucket(tq - ts[tok0 + key], NTm1)];
         }
       }
 
@@ -524,22 +512,43 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
           for (int r = 0; r < 16; ++r) w[r] = w_exact(__builtin_fmaf(sacc[r], cq, c0));
         }
       } else {
-        // per-element bias (y units), added to the scaled scores in place
-        if (KIND == 2) {
-          const float base = alibi_lane + slope_y * (float)dlt;
+        // per-element bias (y units), four registers at a time
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sacc[r] = __builtin_fmaf(sacc[r], cq, __builtin_fmaf(neg_slope_y, (float)kc(r), base));
-        } else {
+        for (int g = 0; g < 4; ++g) {
+          f32x4 c4;
+          if (KIND == 2) {
+            const float base = alibi_lane + slope_y * (float)dlt;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[r] = __builtin_fmaf(sacc[r], cq, sm.cbuf[wave][r][lane]);
-        }
-        if (path == kPoly) {
+            for (int i = 0; i < 4; ++i) c4[i] = __builtin_fmaf(neg_slope_y, (float)kc(4 * g + i), base);
+          } else if (mode == 2) {
+            // two time buckets: dt >= 2^thi - 1  <=>  rel_j <= (t_i - kmin) - (2^thi - 1)
+            const int lim = tq_rel + dq - ((1 << thi) - 1);
+            const i32x4 rel4 = *(const i32x4*)(&sm.krel[buf][32 * hk + 8 * g + 4 * hf]);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) w[r] = w_poly(sacc[r]);
-        } else {
+            for (int i = 0; i < 4; ++i) c4[i] = rel4[i] <= lim ? c1 : c0;
+          } else if (mode == 3) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) w[r] = w_exact(sacc[r]);
+            for (int i = 0; i < 4; ++i) c4[i] = sm.wposx[lv + (dltc - kc(4 * g + i)) + 32] + c0;
+          } else if (mode == 4) {
+            const int ti1 = tq_rel + dq + 1;
+            const i32x4 rel4 = *(const i32x4*)(&sm.krel[buf][32 * hk + 8 * g + 4 * hf]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int u = max(ti1 - rel4[i], 1);  // max(dt, 0) + 1
+              c4[i] = sm.wposx[lv + (dltc - kc(4 * g + i)) + 32] + sm.wtime_lz[__builtin_clz((uint32_t)u)];
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c4[i] = sm.cbuf[wave][4 * g + i][lane];
+          }
+          if (path == kPoly) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[4 * g + i] = w_poly(__builtin_fmaf(sacc[4 * g + i], cq, c4[i]));
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[4 * g + i] = w_exact(__builtin_fmaf(sacc[4 * g + i], cq, c4[i]));
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       if (diag) {
