@@ -93,15 +93,24 @@ const char* hstu_status_string(int32_t status) {
 const char* hstu_last_error(void) { return g_last_error; }
 
 // Attention workspace: [count | pad to 256] [work list] [TimeStat x T] [int32 x T]
+// [tile classes: 8 bytes x max_blocks per row, rows as tclass_row0 assigns them]
 static size_t worklist_bytes(int32_t B, int32_t H, int32_t max_seqlen) {
   const int64_t items = (int64_t)B * H * ceil_div(max_seqlen, kMinBlockRows);
   return kHeader + align256((size_t)items * sizeof(WorkItem));
 }
 
+static int32_t tclass_cols(int32_t max_seqlen) { return (int32_t)ceil_div(max_seqlen, 32); }
+
+static size_t tclass_bytes(int32_t B, int32_t max_seqlen, int64_t total_tokens) {
+  const int64_t rows = (total_tokens + 31 * (int64_t)B) / 32 + 1;
+  return (size_t)rows * (size_t)tclass_cols(max_seqlen) * 8;
+}
+
 size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64_t total_tokens) {
   if (B < 0 || H < 0 || max_seqlen < 0 || total_tokens < 0) return 0;
   return worklist_bytes(B, H, max_seqlen) + align256((size_t)total_tokens * sizeof(TimeStat)) +
-         align256((size_t)total_tokens * sizeof(int32_t));
+         align256((size_t)total_tokens * sizeof(int32_t)) +
+         align256(tclass_bytes(B, max_seqlen, total_tokens));
 }
 
 int32_t hstu_attn_block_rows(int32_t dt, int32_t d) {
@@ -177,17 +186,29 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
     return fail(HSTU_ERR_INVALID_ARG, "q/k/v/o rows must be 16-byte aligned");
   st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen, total_tokens);
   if (st != HSTU_OK) return st;
+  // the bf16 kernel addresses one user's K and V rows with 32-bit byte offsets
+  const int64_t max_stride = k_row_stride > v_row_stride ? k_row_stride : v_row_stride;
+  if (dt == HSTU_DTYPE_BF16 && (int64_t)max_seqlen * max_stride * 2 >= ((int64_t)1 << 31))
+    return fail(HSTU_ERR_UNSUPPORTED, "max_seqlen x row stride reaches 2 GiB per user");
 
   const int32_t max_tiles = (int32_t)ceil_div(max_seqlen, block_rows);
   TimeStat* tstat = (TimeStat*)((char*)workspace + worklist_bytes(B, H, max_seqlen));
   int32_t* trel = (int32_t*)((char*)tstat + align256((size_t)total_tokens * sizeof(TimeStat)));
+  uint32_t* tclass = (uint32_t*)((char*)trel + align256((size_t)total_tokens * sizeof(int32_t)));
   if (dt == HSTU_DTYPE_BF16 && ba.kind == 1) {
     st = check_hip(launch_time_stats(B, offsets, ba.ts, tstat, trel, stream), "time stats launch");
+    if (st != HSTU_OK) return st;
+    st = check_hip(launch_tile_class(B, offsets, tstat, tclass_cols(max_seqlen), ba.num_pos,
+                                     ba.num_time, tclass, stream),
+                   "tile class launch");
     if (st != HSTU_OK) return st;
   }
   AttnArgs a{};
   a.tstat = tstat;
   a.trel = trel;
+  a.tclass = tclass;
+  a.tclass_cols = tclass_cols(max_seqlen);
+  a.tclass_bytes = (int64_t)tclass_bytes(B, max_seqlen, total_tokens);
   a.offsets = offsets;
   a.work_count = (const int32_t*)workspace;
   a.work = (const WorkItem*)((const char*)workspace + kHeader);

@@ -115,6 +115,45 @@ __global__ __launch_bounds__(256) void time_stats_kernel(const int32_t* __restri
 }
 
 // ============================================================================================
+// Bias class of every (32-query block, 32-key block) pair of a user with key block <= query
+// block, for the position + time bias (independent of the head: timestamps are per token):
+//   info = mode | tlo << 4 | thi << 12, and dq = (query block min time) - (key block min time)
+// with tlo / thi the smallest / largest time bucket any pair of the two blocks can have (from
+// the blocks' min / max times, exactly), and
+//   mode 1: position bucket saturated (i - j >= P - 1 for the whole tile), one time bucket;
+//   mode 2: position saturated, time buckets tlo and tlo + 1, 32-bit offsets suffice;
+//   mode 3: position varies, one time bucket;
+//   mode 4: anything else on 32-bit time offsets; mode 5: anything else.
+// 32-bit offsets suffice when the key block spans at most 2^30, the query block too, and the
+// query times lie within 2^30 of the key block's minimum.  One workgroup per (user, query
+// block), one thread per key block.
+// ============================================================================================
+__global__ __launch_bounds__(256) void tile_class_kernel(const int32_t* __restrict__ offsets,
+                                                        const TimeStat* __restrict__ stats,
+                                                        int max_blocks, int P, int NT,
+                                                        uint32_t* __restrict__ tclass) {
+  const int b = blockIdx.x, i = blockIdx.y;
+  const int64_t tok0 = offsets[b];
+  const int n = offsets[b + 1] - offsets[b];
+  if (32 * i >= n) return;
+  const TimeStat q = stats[tok0 + 32 * i];
+  uint32_t* row = tclass + 2 * ((tclass_row0(tok0, b) + i) * (int64_t)max_blocks);
+  for (int j = threadIdx.x; j <= i; j += 256) {
+    const TimeStat k = stats[tok0 + 32 * j];
+    const bool pconst = 32 * (i - j) - 31 >= P - 1;
+    const int tlo = time_bucket(q.mn - k.mx, NT - 1);
+    const int thi = time_bucket(q.mx - k.mn, NT - 1);
+    const int64_t lim = 1LL << 30;
+    const bool fits32 = (k.mx - k.mn) <= lim && (q.mx - q.mn) <= lim && (q.mx - k.mn) <= lim &&
+                        (q.mn - k.mn) >= -lim;
+    const int mode = pconst ? (tlo == thi ? 1 : (thi == tlo + 1 && fits32) ? 2 : fits32 ? 4 : 5)
+                            : (tlo == thi ? 3 : fits32 ? 4 : 5);
+    row[2 * j] = (uint32_t)mode | ((uint32_t)tlo << 4) | ((uint32_t)thi << 12);
+    row[2 * j + 1] = fits32 ? (uint32_t)(int32_t)(q.mn - k.mn) : 0u;
+  }
+}
+
+// ============================================================================================
 // bf16, d = 64: 8 waves x 32 queries = 256 query rows per work item, 64 keys per LDS stage,
 // four waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time tables,
 // 2 ALiBi).
@@ -138,31 +177,16 @@ constexpr float kTaylorD = 0.04f;
 // plus an immediate offset.
 constexpr int kRow = 72;  // bf16 elements per padded row
 
-// Classification of one 32x32 tile (one wave's 32 queries x 32 keys) for the position + time
-// bias, written by the classifier lanes while the tile is staged.
-//   mode 1: one bias value c0 for the whole tile (position bucket saturated, one time
-//   bucket); 2: position bucket saturated, two time buckets: c0 or c1 per element; 3: position
-//   bucket varies, one time bucket: position table plus c0 (the time part); 4: both vary,
-//   gathered per element on 32-bit time offsets; 5: as 4 on 64-bit times.
-struct __attribute__((aligned(16))) TileClass {
-  int32_t mode, thi, dq, pad;  // dq = (query block min time) - (key block min time), modes 2, 3
-  float c0, c1, thr_taylor, thr_poly;  // thresholds on the tile's max squared key norm
-  float a0, a1, a2, pad2;       // Taylor coefficients around c0 (mode 1)
-};
-
 struct __attribute__((aligned(16))) SmemBf16 {
   __attribute__((aligned(16))) bf16 k[2][kKB * kRow];   // row = key
   __attribute__((aligned(16))) bf16 vt[2][kD * kRow];   // row = d, 64 keys in PV slot order
   __attribute__((aligned(16))) int32_t krel[2][kKB];    // key time minus its 32-key block's minimum
   __attribute__((aligned(16))) float knorm2[2][kWaves]; // per staging wave: max squared key norm
-  __attribute__((aligned(16))) TileClass cls[2][kWaves][2];
+  __attribute__((aligned(16))) uint32_t cls[2][kWaves][2][2];  // tile class entries (info, dq)
   __attribute__((aligned(16))) float tay[kMaxTimeBuckets][4];  // per time bucket: c, a0, a1, a2
-  __attribute__((aligned(16))) int64_t qtime[kWaves][2];       // per wave: query block min, max time
-  float qbound[kWaves];
   float wposx[kMaxPosBuckets + 96];  // -log2(e) * w_pos[h][clamp(i - j, 0, P - 1)] at i - j + 32
   float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
   float wtime_lz[32];           // wtime[min(31 - lz, NT - 1)]: time bias by leading zeros of dt + 1
-  float cbuf[kWaves][16][64];   // per-wave per-element bias of one tile
 };
 
 // w(y) = 2y/(1+2^y) and its first two derivatives at c, as the coefficients of the expansion
@@ -208,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   const TimeStat* __restrict__ tstat = a.tstat;
   const float cq = -a.alpha * kLog2e;
   const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
-  constexpr int kClassWave = 1;  // its lanes 0..15 classify the next tile (lane = 2 wave + hk)
+  constexpr int kClassWave = 1;  // its lanes 0..31 stage the next tile's class entries
 
   // ---- Q fragments (B operand of S^T = K Q^T), unscaled ----
   bf16x8 qop[4];
@@ -257,23 +281,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       sm.wtime[tid] = -kLog2e * wt[tid];
     }
     if (tid < 32) sm.wtime_lz[tid] = -kLog2e * wt[min(31 - tid, NTm1)];
-    if (wave == kClassWave) {
+    {
       float mp = 0.f, mt = 0.f;
       for (int i = lane; i < a.bias.num_pos; i += 64) mp = fmaxf(mp, fabsf(wp[i]));
       for (int i = lane; i < a.bias.num_time; i += 64) mt = fmaxf(mt, fabsf(wt[i]));
       tabmax = uniform_f32(kLog2e * (wave_max(mp) + wave_max(mt)));
     }
-    int64_t tmin = 0, tmax = 0;
-    if (qw0 <= wq_last) {
-      const TimeStat st = tstat[tok0 + qw0];
-      tmin = st.mn;
-      tmax = st.mx;
-    }
-    if (lane == 0) {
-      sm.qtime[wave][0] = tmin;
-      sm.qtime[wave][1] = tmax;
-      sm.qbound[wave] = qbound;
-    }
+    int64_t tmin = 0;
+    if (qw0 <= wq_last) tmin = tstat[tok0 + qw0].mn;
     if (qvalid) {
       const int64_t d = ts[tok0 + row] - tmin;
       tq_rel = d > 0x7fffffffLL ? 0x7fffffff : (int32_t)d;
@@ -311,13 +326,19 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   const uint32_t koff = (uint32_t)krow * kstride_b + 16u * kchunk;
   const uint32_t voff = (uint32_t)(2 * vpair) * vstride_b + 8u * vq;
   const int vpos = 16 * ((2 * vpair) >> 4) + pv_slot((2 * vpair) & 15);
-  // timestamp data of the tile: wave 0 lane l stages key l's offset from its block minimum;
-  // lanes 0..7 of the classifier wave load the min / max of the tile's two 32-key blocks
-  // (one dword each)
+  // per tile: wave 0 lane l stages key l's time offset from its block minimum; lanes 0..31 of
+  // the class wave stage the class entries of the tile's (wave, 32-key half) pairs, entry
+  // dword l = (wave l / 4, half (l / 2) % 2, word l % 2)
+  const int64_t crow = tclass_row0(tok0, b) + q0 / 32;
+  const int64_t cbase = crow * a.tclass_cols * 8;  // bytes
   const __amdgpu_buffer_rsrc_t rrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(KIND != 1 ? nullptr : wave == 0 ? (const void*)(a.trel + tok0) : (const void*)(tstat + tok0)),
-      (short)0, KIND == 1 ? q_end * (wave == 0 ? 4 : 16) : 0, 0x00020000);
-  const uint32_t roff = wave == 0 ? 4u * lane : 16u * 32u * (uint32_t)(lane >> 2) + 4u * (lane & 3);
+      (void*)(KIND != 1 ? nullptr
+                        : wave == 0 ? (const void*)(a.trel + tok0)
+                                    : (const void*)((const char*)a.tclass + cbase)),
+      (short)0,
+      KIND != 1 ? 0 : wave == 0 ? q_end * 4 : (int)min(a.tclass_bytes - cbase, (int64_t)0x7fffffff),
+      0x00020000);
+  const uint32_t roff = wave == 0 ? 4u * lane : 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3);
   u32x4 kreg;
   u32x2 vreg[2];
   int32_t rdw = 0;
@@ -327,8 +348,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
 #pragma unroll
     for (int u = 0; u < 2; ++u)
       vreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff + u * vstride_b, (uint32_t)j0 * vstride_b, 0));
-    if (KIND == 1 && (wave == 0 || (wave == kClassWave && lane < 8)))
-      rdw = __builtin_amdgcn_raw_buffer_load_b32(rrsrc, roff, (uint32_t)j0 * (wave == 0 ? 4u : 16u), 0);
+    if (KIND == 1 && (wave == 0 || (wave == kClassWave && lane < 32)))
+      rdw = __builtin_amdgcn_raw_buffer_load_b32(rrsrc, roff, wave == 0 ? 4u * (uint32_t)j0 : (uint32_t)j0 / 4u, 0);
   };
   auto lstore = [&](int buf) {
     *(u32x4*)(&sm.k[buf][krow * kRow + 8 * kchunk]) = kreg;
@@ -340,6 +361,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       *(uint32_t*)(&sm.vt[buf][(4 * vq + e) * kRow + vpos]) = pk;
     }
     if (KIND == 1 && wave == 0) sm.krel[buf][lane] = rdw;
+    else if (KIND == 1 && wave == kClassWave && lane < 32) (&sm.cls[buf][0][0][0])[lane] = (uint32_t)rdw;
     // max squared norm of the staged key rows: 8 threads hold the 8 chunks of a row
     const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg);
     float acc = 0.f;
@@ -354,66 +376,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
     acc = wave_max(acc);
     if (lane == 0) sm.knorm2[buf][wave] = acc;
   };
-  // classifier: lanes 0..15 of the classifier wave classify the tile t (staged into buf) for
-  // wave (lane / 2) and its 32-key half (lane % 2).  Needs rdw of tile t, the tables and the
-  // per-wave query data in LDS.
-  auto classify = [&](int t, int buf) {
-    // key block min / max of both halves, from the dwords lanes 0..7 loaded
-    int64_t kmn_h[2], kmx_h[2];
-#pragma unroll
-    for (int hk = 0; hk < 2; ++hk) {
-      const uint32_t w0 = __builtin_amdgcn_readlane(rdw, 4 * hk), w1 = __builtin_amdgcn_readlane(rdw, 4 * hk + 1);
-      const uint32_t w2 = __builtin_amdgcn_readlane(rdw, 4 * hk + 2), w3 = __builtin_amdgcn_readlane(rdw, 4 * hk + 3);
-      kmn_h[hk] = (int64_t)(((uint64_t)w1 << 32) | w0);
-      kmx_h[hk] = (int64_t)(((uint64_t)w3 << 32) | w2);
-    }
-    if (lane < 2 * kWaves) {
-      const int w = lane >> 1, hk = lane & 1;
-      const int j0h = t * kKB + 32 * hk;
-      const int qb0 = q0 + kQW * w;
-      const int64_t kmn = hk ? kmn_h[1] : kmn_h[0], kmx = hk ? kmx_h[1] : kmx_h[0];
-      const int64_t tmin = sm.qtime[w][0], tmax = sm.qtime[w][1];
-      const float qb = sm.qbound[w];
-      const bool pconst = (qb0 - (j0h + 31)) >= Pm1;
-      const int tlo = time_bucket(tmin - kmx, NTm1);
-      const int thi = time_bucket(tmax - kmn, NTm1);
-      const int64_t lim30 = 1LL << 30;
-      const bool fits32 = (kmx - kmn) <= lim30 && (tmax - tmin) <= lim30 && (tmax - kmn) <= lim30 &&
-                          (tmin - kmn) >= -lim30;
-      const int mode = pconst ? (tlo == thi ? 1 : (thi == tlo + 1 && fits32) ? 2 : fits32 ? 4 : 5)
-                              : (tlo == thi ? 3 : fits32 ? 4 : 5);
-      const f32x4 lo = *(const f32x4*)(&sm.tay[tlo][0]);
-      const float c1 = sm.tay[thi][0];
-      const float cabs = mode == 1 ? fabsf(lo[0]) : mode == 2 ? fmaxf(fabsf(lo[0]), fabsf(c1)) : tabmax;
-      // |y - bias| <= qb * knorm: Taylor iff qb^2 knorm^2 <= kTaylorD^2 (constant bias only),
-      // polynomial iff qb * knorm + cabs <= kPolyRange
-      const float qb2 = qb * qb;
-      const float thr_t = mode == 1 ? kTaylorD * kTaylorD / qb2 : -1.f;
-      const float room = kPolyRange - cabs;
-      const float thr_p = room >= 0.f ? room * room / qb2 : -1.f;
-      TileClass c;
-      c.mode = mode;
-      c.thi = thi;
-      c.dq = (int32_t)(tmin - kmn);
-      c.pad = 0;
-      c.c0 = mode == 3 ? sm.wtime[tlo] : lo[0];
-      c.c1 = c1;
-      c.thr_taylor = thr_t;
-      c.thr_poly = thr_p;
-      c.a0 = lo[1];
-      c.a1 = lo[2];
-      c.a2 = lo[3];
-      c.pad2 = 0.f;
-      sm.cls[buf][w][hk] = c;
-    }
-  };
-
   gload(0);
   lstore(0);
-  if (KIND == 1) {
-    __syncthreads();  // tables and per-wave query data
-    if (wave == kClassWave) classify(0, 0);
-  }
   __syncthreads();
 
   enum { kExact = 0, kPoly = 1, kTaylor = 2 };
@@ -426,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
       const int j0h = j0 + 32 * hk;
-      if (j0h > wq_last) continue;
+      if (j0h > wq_last || wq_last < qw0) continue;  // past the diagonal, or the wave has no rows
       // K operands of this 32-key step (V operands are read after the SiLU)
       bf16x8 kop[4], vop[2][2];
 #pragma unroll
@@ -454,34 +418,29 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
         const float D2 = qbound * qbound * kn2;
         path = D2 <= kTaylorD * kTaylorD ? kTaylor : D2 <= kPolyRange * kPolyRange ? kPoly : kExact;
       } else if (KIND == 1) {
-        const i32x4 e0 = *(const i32x4*)(&sm.cls[buf][wave][hk].mode);
-        const f32x4 e1 = *(const f32x4*)(&sm.cls[buf][wave][hk].c0);
-        const f32x4 e2 = *(const f32x4*)(&sm.cls[buf][wave][hk].a0);
-        mode = __builtin_amdgcn_readfirstlane(e0[0]);
-        thi = __builtin_amdgcn_readfirstlane(e0[1]);
-        dq = __builtin_amdgcn_readfirstlane(e0[2]);
-        c0 = uniform_f32(e1[0]);
-        c1 = uniform_f32(e1[1]);
-        path = kn2 <= uniform_f32(e1[2]) ? kTaylor : kn2 <= uniform_f32(e1[3]) ? kPoly : kExact;
-        A0 = uniform_f32(e2[0]);
-        A1 = uniform_f32(e2[1]);
-        A2 = uniform_f32(e2[2]);
+        const u32x2 e = *(const u32x2*)(&sm.cls[buf][wave][hk][0]);
+        const uint32_t info = __builtin_amdgcn_readfirstlane(e[0]);
+        dq = (int32_t)__builtin_amdgcn_readfirstlane(e[1]);
+        mode = info & 15;
+        const int tlo = (info >> 4) & 255;
+        thi = info >> 12;
+        const f32x4 lo = *(const f32x4*)(&sm.tay[tlo][0]);
+        c0 = uniform_f32(mode == 3 ? sm.wtime[tlo] : lo[0]);
+        c1 = uniform_f32(sm.tay[thi][0]);
+        A0 = uniform_f32(lo[1]);
+        A1 = uniform_f32(lo[2]);
+        A2 = uniform_f32(lo[3]);
+        // |y - bias| <= D = qbound * knorm; Taylor iff the bias is one value and D <= kTaylorD,
+        // polynomial iff D + max|bias| <= kPolyRange
+        const float cabs = mode == 1 ? fabsf(c0) : mode == 2 ? fmaxf(fabsf(c0), fabsf(c1)) : tabmax;
+        const float D2 = qbound * qbound * kn2;
+        const float room = kPolyRange - cabs;
+        path = (mode == 1 && D2 <= kTaylorD * kTaylorD) ? kTaylor
+             : (room >= 0.f && D2 <= room * room) ? kPoly : kExact;
       } else {
         mode = 3;
         const float room = kPolyRange - slope_y * (float)max(qw0 + 31 - j0h, 0);
         path = (room >= 0.f && qbound * qbound * kn2 <= room * room) ? kPoly : kExact;
-      }
-
-      if (KIND == 1 && mode == 5) {
-        // timestamps spread beyond 2^30 within the tile: exact 64-bit deltas, one register at a
-        // time into this wave's LDS scratch (such spreads are rare)
-        const int64_t tq = ts[tok0 + min(row, n - 1)];
-#pragma unroll 1
-        for (int r = 0; r < 16; ++r) {
-          const int key = min(j0h + kc(r) + 4 * hf, n - 1);
-          sm.cbuf[wave][r][lane] = sm.wposx[pos_bucket(lv + (dlt - kc(r)), Pm1) + 32] +
-                                   sm.wtime[time_bucket(tq - ts[tok0 + key], NTm1)];
-        }
       }
 
       // S^T tile: rows = keys, columns = this wave's queries
@@ -538,8 +497,15 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
               c4[i] = sm.wposx[lv + (dltc - kc(4 * g + i)) + 32] + sm.wtime_lz[__builtin_clz((uint32_t)u)];
             }
           } else {
+            // timestamps spread beyond 2^30 within the tile (rare): exact 64-bit deltas from
+            // global memory
+            const int64_t tq = ts[tok0 + min(row, n - 1)];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) c4[i] = sm.cbuf[wave][4 * g + i][lane];
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * g + i;
+              const int64_t tk = ts[tok0 + min(j0h + kc(r) + 4 * hf, n - 1)];
+              c4[i] = sm.wposx[pos_bucket(lv + (dlt - kc(r)), Pm1) + 32] + sm.wtime[time_bucket(tq - tk, NTm1)];
+            }
           }
           if (path == kPoly) {
 #pragma unroll
@@ -577,10 +543,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
         for (int db = 0; db < 2; ++db)
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[m], oacc[db], 0, 0, 0);
     }
-    if (more) {
-      lstore(buf ^ 1);
-      if (KIND == 1 && wave == kClassWave) classify(t + 1, buf ^ 1);
-    }
+    if (more) lstore(buf ^ 1);
     __syncthreads();
   }
 
@@ -725,7 +688,7 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
     const int buf = t & 1;
     if (t + 1 < n_tiles) gload(t + 1);
     const int j0 = t * kKBf;
-    if (j0 <= wq_last) {
+    if (j0 <= wq_last && qw0 <= wq_last) {  // before the diagonal, and the wave has rows
       const int base = qw0 - j0 + l32;
       f32x16 c;
       if (kind == 1) {
@@ -797,6 +760,15 @@ hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* t
                              int32_t* rel, hipStream_t stream) {
   if (B <= 0) return hipSuccess;
   hipLaunchKernelGGL(time_stats_kernel, dim3(B), dim3(256), 0, stream, offsets, ts, stats, rel);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_class(int32_t B, const int32_t* offsets, const TimeStat* stats,
+                             int32_t max_blocks, int32_t num_pos, int32_t num_time,
+                             uint32_t* tclass, hipStream_t stream) {
+  if (B <= 0 || max_blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(tile_class_kernel, dim3(B, max_blocks), dim3(256), 0, stream, offsets, stats,
+                     max_blocks, num_pos, num_time, tclass);
   return hipGetLastError();
 }
 

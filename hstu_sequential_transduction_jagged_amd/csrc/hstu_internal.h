@@ -53,8 +53,15 @@ struct AttnArgs {
   BiasArgs bias;
   const TimeStat* tstat;  // per token: stats of the 32-token block starting there (bf16 path)
   const int32_t* trel;    // per token: timestamp minus its block's minimum (bf16 path)
+  const uint32_t* tclass; // per (query block, key block) pair: bias class (bf16 path)
+  int32_t tclass_cols;    // entries per query-block row of tclass (= blocks of the longest user)
+  int64_t tclass_bytes;
   float alpha, out_scale;
 };
+
+// Rows of the tile-class table: user b's query block i sits on row (offsets[b] + 31 b) / 32 + i,
+// which never collides with another user's rows; fewer than (T + 31 B) / 32 + 1 rows in all.
+__host__ __device__ inline int64_t tclass_row0(int64_t tok0, int64_t b) { return (tok0 + 31 * b) / 32; }
 
 constexpr int kMaxPosBuckets = 1024;
 constexpr int kMaxTimeBuckets = 64;
@@ -84,6 +91,9 @@ hipError_t launch_schedule(const int32_t* offsets, int32_t B, int32_t H, int32_t
                            hipStream_t stream);
 hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts, TimeStat* stats,
                              int32_t* rel, hipStream_t stream);
+hipError_t launch_tile_class(int32_t B, const int32_t* offsets, const TimeStat* stats,
+                             int32_t max_blocks, int32_t num_pos, int32_t num_time,
+                             uint32_t* tclass, hipStream_t stream);
 hipError_t launch_attn_bf16(int d, const AttnArgs& a, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(int d, const AttnArgs& a, int grid, hipStream_t stream);
 int attn_block_rows_bf16(int d);

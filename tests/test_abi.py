@@ -38,9 +38,14 @@ def test_workspace_sizes():
     L = binding.lib()
     # 256-byte header + one 16-byte item per (user, head, 128-row tile), 256-aligned
     # + per-token timestamp statistics (16 B) and offsets (4 B), each region 256-aligned
-    assert L.hstu_attn_workspace_bytes(16, 8, 8192, 0) == 256 + 16 * 8 * 64 * 16
-    assert L.hstu_attn_workspace_bytes(0, 8, 8192, 0) == 256
-    assert L.hstu_attn_workspace_bytes(16, 8, 8192, 1000) == 256 + 16 * 8 * 64 * 16 + 16128 + 4096
+    # + tile classes: 8 B per (query block row, key block), (T + 31 B) / 32 + 1 rows of
+    #   ceil(max_seqlen / 32) entries
+    def tclass(B, ms, T):
+        return ((T + 31 * B) // 32 + 1) * ((ms + 31) // 32) * 8
+    assert L.hstu_attn_workspace_bytes(16, 8, 8192, 0) == 256 + 16 * 8 * 64 * 16 + tclass(16, 8192, 0)
+    assert L.hstu_attn_workspace_bytes(0, 8, 8192, 0) == 256 + tclass(0, 8192, 0)
+    assert L.hstu_attn_workspace_bytes(16, 8, 8192, 1000) == \
+        256 + 16 * 8 * 64 * 16 + 16128 + 4096 + tclass(16, 8192, 1000)
     assert L.hstu_attn_block_rows(1, 64) == 256
     assert L.hstu_attn_block_rows(0, 32) == 128
     assert L.hstu_attn_block_rows(1, 48) == 0
