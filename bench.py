@@ -68,9 +68,15 @@ def cpu_baseline(inp, seconds=15.0, seed=7):
         oracle.attention_rows(inp.offsets, inp.q, inp.k, inp.v, b, inp.alpha, toks, heads)
         return fl, time.perf_counter() - t0
 
-    fl, dt = run(500)
-    R = int(min(inp.T * inp.H, max(500, 500 * seconds / max(dt, 1e-3))))
+    # grow the sample until one run takes at least a second, then scale it to `seconds`
+    R = 500
     fl, dt = run(R)
+    while dt < 1.0 and R < inp.T * inp.H:
+        R = min(inp.T * inp.H, R * 4)
+        fl, dt = run(R)
+    if dt < seconds and R < inp.T * inp.H:
+        R = int(min(inp.T * inp.H, R * seconds / max(dt, 1e-3)))
+        fl, dt = run(R)
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": "%d random (token, head) rows of the attn_long batch (%.3g causal FLOP), "
