@@ -84,6 +84,32 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Cross-lane moves inside a row of 16 lanes (DPP, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within each 16 lanes
+
+// Sum over each aligned group of 8 lanes, in all 8 lanes.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  return v + dpp<kDppHalfMirror>(v);
+}
+// Max over the 64 lanes of a wave, as a wave-uniform value.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  auto at = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+  return fmaxf(fmaxf(at(0), at(16)), fmaxf(at(32), at(48)));
+}
+
 constexpr int64_t kTMax = 0x7fffffffffffffffLL;
 constexpr int64_t kTMin = -kTMax - 1;
 
@@ -370,10 +396,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
       acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
     }
-    acc += __shfl_xor(acc, 1, 64);
-    acc += __shfl_xor(acc, 2, 64);
-    acc += __shfl_xor(acc, 4, 64);
-    acc = wave_max(acc);
+    acc = wave_max_dpp(sum8(acc));
     if (lane == 0) sm.knorm2[buf][wave] = acc;
   };
   gload(0);
