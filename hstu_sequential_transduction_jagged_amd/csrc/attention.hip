@@ -9,9 +9,10 @@
 // Formulation used on the matrix cores.  Scores are produced transposed,
 // S^T = K Q^T, so that the accumulator of a 32x32 MFMA tile holds one query
 // per lane and 16 keys per lane in registers; that register set is exactly the
-// B operand of the next MFMA, O^T += V^T P^T, so the probabilities never leave
+// B operand of the next MFMA, O^T += V^T P^T, so the SiLU weights never leave
 // registers.  The key order inside a 16-key PV step is a fixed permutation of
-// the accumulator's row order, and V^T is stored in LDS in that permuted order.
+// the accumulator's row order; the V^T operand is read in that order from the
+// row-major V tile with transposing LDS reads (bf16 path).
 //
 // SiLU is evaluated in base-2 units: with y = -log2(e) x,
 //     SiLU(x) = x / (1 + e^-x) = -(ln 2 / 2) * w(y),   w(y) = 2 y / (1 + 2^y),
@@ -39,13 +40,6 @@ namespace {
 // Key (0..31) of a 32x32 accumulator's register r in lane half hf: rows
 // 8*(r/4) + 4*hf + r%4 of the MFMA output layout.
 __device__ __forceinline__ int acc_key(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
-
-// MFMA k slot of key k16 (0..15) within a 16-key PV step (inverse of the
-// accumulator row order restricted to registers 8m..8m+7).
-__device__ __forceinline__ int pv_slot(int k16) {
-  int g = k16 >> 3, w = k16 & 7;
-  return 8 * (w >> 2) + 4 * g + (w & 3);
-}
 
 __device__ __forceinline__ int64_t shfl_xor_i64(int64_t v, int m) {
   int lo = __shfl_xor((int)(uint32_t)(uint64_t)v, m, 64);
@@ -205,7 +199,7 @@ constexpr int kRow = 72;  // bf16 elements per padded row
 
 struct __attribute__((aligned(16))) SmemBf16 {
   __attribute__((aligned(16))) bf16 k[2][kKB * kRow];   // row = key
-  __attribute__((aligned(16))) bf16 vt[2][kD * kRow];   // row = d, 64 keys in PV slot order
+  __attribute__((aligned(16))) bf16 v[2][kKB * kRow];   // row = key
   __attribute__((aligned(16))) int32_t krel[2][kKB];    // key time minus its 32-key block's minimum
   __attribute__((aligned(16))) float knorm2[2][kWaves]; // per staging wave: max squared key norm
   __attribute__((aligned(16))) uint32_t cls[2][kWaves][2][2];  // tile class entries (info, dq)
@@ -326,6 +320,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   }
   // register r of a 32x32 accumulator holds key acc_key(r, hf) = kc(r) + 4 hf for query l32
   const int lv = l32 - 4 * hf;
+  // transposing V reads: this lane's source row (key) and column (d) within a 16-key group
+  const int vtr_row0 = 4 * hf + ((lane & 15) >> 2);
+  const int vtr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const float neg_slope_y = -slope_y, alibi_lane = slope_y * (float)lv;
 
   f32x16 oacc[2];
@@ -335,13 +332,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
   // ---- staging: global -> registers -> LDS ----
-  // K: thread t stages 16-byte chunk t % 8 of key row t / 8.  V: thread t stages d values
-  // 4 (t % 16) .. +3 of the key pair 2 (t / 16), 2 (t / 16) + 1, packed per d into one 32-bit
-  // word (the pair occupies two adjacent PV slots).  K and V rows are read through buffer
-  // descriptors bounded at the last key row this item needs: rows at or past q_end read as
-  // zeros without a branch.
+  // Thread t stages 16-byte chunk t % 8 of key row t / 8 of both K and V, row-major.  K and V
+  // rows are read through buffer descriptors bounded at the last key row this item needs:
+  // rows at or past q_end read as zeros without a branch.
   const int krow = tid >> 3, kchunk = tid & 7;
-  const int vpair = tid >> 4, vq = tid & 15;
   const uint32_t kstride_b = (uint32_t)a.k_stride * 2u, vstride_b = (uint32_t)a.v_stride * 2u;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(kp + tok0 * a.k_stride + (int64_t)h * kD), (short)0,
@@ -350,8 +344,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       (void*)(vp + tok0 * a.v_stride + (int64_t)h * kD), (short)0,
       (int)((uint32_t)(q_end - 1) * vstride_b + 2u * kD), 0x00020000);
   const uint32_t koff = (uint32_t)krow * kstride_b + 16u * kchunk;
-  const uint32_t voff = (uint32_t)(2 * vpair) * vstride_b + 8u * vq;
-  const int vpos = 16 * ((2 * vpair) >> 4) + pv_slot((2 * vpair) & 15);
+  const uint32_t voff = (uint32_t)krow * vstride_b + 16u * kchunk;
   // per tile: wave 0 lane l stages key l's time offset from its block minimum; lanes 0..31 of
   // the class wave stage the class entries of the tile's (wave, 32-key half) pairs, entry
   // dword l = (wave l / 4, half (l / 2) % 2, word l % 2)
@@ -365,27 +358,18 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       KIND != 1 ? 0 : wave == 0 ? q_end * 4 : (int)min(a.tclass_bytes - cbase, (int64_t)0x7fffffff),
       0x00020000);
   const uint32_t roff = wave == 0 ? 4u * lane : 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3);
-  u32x4 kreg;
-  u32x2 vreg[2];
+  u32x4 kreg, vreg;
   int32_t rdw = 0;
   auto gload = [&](int t) {
     const int j0 = t * kKB;
     kreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, koff, (uint32_t)j0 * kstride_b, 0));
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      vreg[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrsrc, voff + u * vstride_b, (uint32_t)j0 * vstride_b, 0));
+    vreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, voff, (uint32_t)j0 * vstride_b, 0));
     if (KIND == 1 && (wave == 0 || (wave == kClassWave && lane < 32)))
       rdw = __builtin_amdgcn_raw_buffer_load_b32(rrsrc, roff, wave == 0 ? 4u * (uint32_t)j0 : (uint32_t)j0 / 4u, 0);
   };
   auto lstore = [&](int buf) {
     *(u32x4*)(&sm.k[buf][krow * kRow + 8 * kchunk]) = kreg;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // d = 4 vq + e: element e of both key rows (low half of word e / 2 for even e)
-      const uint32_t wa = vreg[0][e >> 1], wb = vreg[1][e >> 1];
-      const uint32_t pk = __builtin_amdgcn_perm(wb, wa, (e & 1) ? 0x07060302u : 0x05040100u);
-      *(uint32_t*)(&sm.vt[buf][(4 * vq + e) * kRow + vpos]) = pk;
-    }
+    *(u32x4*)(&sm.v[buf][krow * kRow + 8 * kchunk]) = vreg;
     if (KIND == 1 && wave == 0) sm.krel[buf][lane] = rdw;
     else if (KIND == 1 && wave == kClassWave && lane < 32) (&sm.cls[buf][0][0][0])[lane] = (uint32_t)rdw;
     // max squared norm of the staged key rows: 8 threads hold the 8 chunks of a row
@@ -555,11 +539,21 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
         pop[0] = __builtin_convertvector(a0, bf16x8);
         pop[1] = __builtin_convertvector(a1, bf16x8);
       }
+      // V^T operands straight from the row-major V tile with transposing LDS reads: in each
+      // 16-lane group, source lane j points at keys (row j / 4) and d (4 (j % 4) .. +3); lane i
+      // of the group then holds d = i for 4 consecutive keys.  Two reads give the 8 keys of
+      // k-slots 8 hf .. 8 hf + 7, in the key order of the Pt registers: 4 hf + {0..3} and
+      // 8 + 4 hf + {0..3} within the 16-key group m.
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-          vop[db][m] = *(const bf16x8*)(&sm.vt[buf][(32 * db + l32) * kRow + 32 * hk + 16 * m + 8 * hf]);
+        for (int m = 0; m < 2; ++m) {
+          bf16x4 half0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&sm.v[buf][vtr_row0 * kRow + (32 * hk + 16 * m) * kRow + 32 * db + vtr_col]));
+          bf16x4 half1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&sm.v[buf][vtr_row0 * kRow + (32 * hk + 16 * m + 8) * kRow + 32 * db + vtr_col]));
+          vop[db][m] = bf16x8{half0[0], half0[1], half0[2], half0[3], half1[0], half1[1], half1[2], half1[3]};
+        }
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
