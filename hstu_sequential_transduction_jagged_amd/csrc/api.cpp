@@ -289,11 +289,11 @@ void hstu_layer_workspace_offsets(int64_t total_tokens, int32_t H, int32_t d_qk,
 
 size_t hstu_layer_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_model, int32_t H,
                                   int32_t d_qk, int32_t d_v, int32_t max_seqlen) {
-  (void)d_model;
-  if (B < 0 || total_tokens < 0 || H < 1 || d_qk < 1 || d_v < 1) return 0;
+  if (B < 0 || total_tokens < 0 || d_model < 1 || H < 1 || d_qk < 1 || d_v < 1) return 0;
   size_t attn_off = 0;
   hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, nullptr, nullptr, &attn_off);
-  return attn_off + hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens);
+  return attn_off + align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens)) +
+         align256((size_t)d_model * H * d_v * 2);
 }
 
 hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,
@@ -332,7 +332,8 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   bf16* z = (bf16*)((char*)workspace + zo);
   float* obuf = (float*)((char*)workspace + oo);
   void* aws = (char*)workspace + ao;
-  const size_t aws_bytes = workspace_bytes - ao;
+  const size_t aws_bytes = align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens));
+  bf16* w2p = (bf16*)((char*)aws + aws_bytes);  // W2 in MFMA fragment order
 
   st = check_hip(launch_f1_gemm_silu((const bf16*)x, (const bf16*)w1, b1, z, total_tokens, N1,
                                      d_model, stream),
@@ -350,7 +351,7 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   if (st != HSTU_OK) return st;
   return check_hip(launch_ln_gate_f2(obuf, U, N1, ln_gamma, ln_beta, ln_eps, (const bf16*)w2, b2,
                                      residual ? (const bf16*)x : nullptr, (bf16*)y, total_tokens,
-                                     d_model, HV, stream),
+                                     d_model, HV, w2p, stream),
                    "f2 launch");
 }
 

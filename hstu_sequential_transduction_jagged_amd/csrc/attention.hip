@@ -79,14 +79,6 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Cross-lane moves inside a row of 16 lanes (DPP, no LDS round trip).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes
-constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within each 16 lanes
 
 // Sum over each aligned group of 8 lanes, in all 8 lanes.
 __device__ __forceinline__ float sum8(float v) {

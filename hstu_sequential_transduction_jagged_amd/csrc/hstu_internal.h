@@ -20,6 +20,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Lane moves within a row of 16 lanes (DPP): the value of another lane of the same row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within each 16 lanes
+
 // One unit of attention work: query tile `qt` of user `b`, head `h`.
 struct WorkItem {
   int32_t b, h, qt, pad;
@@ -104,7 +114,7 @@ hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, b
 hipError_t launch_ln_gate_f2(const float* o, const bf16* u, int64_t u_stride, const float* gamma,
                              const float* beta, float eps, const bf16* w2, const float* b2,
                              const bf16* x, bf16* y, int64_t M, int32_t D, int32_t HV,
-                             hipStream_t stream);
+                             bf16* w2_packed, hipStream_t stream);
 hipError_t launch_embed_sum(int64_t T, int32_t dim, const bf16* item, int64_t num_items,
                             const bf16* action, int32_t num_actions, const int32_t* ids,
                             const int32_t* aids, bf16* x, hipStream_t stream);

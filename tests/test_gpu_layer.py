@@ -113,3 +113,19 @@ def test_stack_small():
     print("stack T=%d layers=%d err=%.3g (without storage allowance %.3g)"
           % (inp.T, len(inp.layers), e, err_rms(hh, x)), flush=True)
     assert e <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("D,H", [(640, 12), (384, 2)])
+def test_layer_uneven_widths(D, H):
+    """Model widths whose f2 output is not a whole number of 512-feature chunks (640 = 512 + 128,
+    384 = 3 x 128) and a LayerNorm width above 512 (H dv = 768), with residual; 380 tokens cover
+    one full and one ragged 256-token f1 tile and six 64-token f2 tiles."""
+    inp = synth.make_layer("t", 42 + H, [130, 250], D=D, H=H, d=64, alpha=1.0 / 250,
+                           residual=True, randomize_affine=True)
+    d, y = _run_layer(inp)
+    yy = y.float().cpu().numpy()
+    ref = oracle_layer(inp)
+    e = err_stored(yy, ref, "bf16")
+    print("layer D=%d H=%d err=%.3g (without storage allowance %.3g)" % (D, H, e, err_rms(yy, ref)),
+          flush=True)
+    assert e <= TOL["bf16"]
