@@ -167,8 +167,8 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
                                 const void* q, int64_t q_row_stride, const void* k,
                                 int64_t k_row_stride, const void* v, int64_t v_row_stride,
                                 const hstu_bias* bias, float alpha, float out_scale, void* o,
-                                bool o_f32, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                bool o_f32, f32x2* ostats, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   int block_rows = 0;
   hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
   if (st != HSTU_OK) return st;
@@ -224,6 +224,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   a.bias = ba;
   a.alpha = alpha;
   a.out_scale = out_scale;
+  a.ostats = ostats;
   const int64_t grid = (int64_t)B * H * max_tiles;
   if (grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
   hipError_t e = dt == HSTU_DTYPE_BF16 ? launch_attn_bf16(d_qk, a, (int)grid, stream)
@@ -240,7 +241,7 @@ hstu_status hstu_attn_fwd_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk
                                   size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
   return attn_planned(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q, q_row_stride, k,
-                      k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, false, workspace,
+                      k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, false, nullptr, workspace,
                       workspace_bytes, stream);
 }
 
@@ -281,7 +282,7 @@ void hstu_layer_workspace_offsets(int64_t total_tokens, int32_t H, int32_t d_qk,
                                   size_t* z_offset, size_t* o_offset, size_t* attn_offset) {
   const int64_t N1 = 2LL * H * (d_qk + d_v);
   const size_t z_bytes = align256((size_t)(total_tokens * N1 * 2));
-  const size_t o_bytes = align256((size_t)(total_tokens * H * d_v * 4));
+  const size_t o_bytes = align256((size_t)(total_tokens * H * d_v * 2));
   if (z_offset) *z_offset = 0;
   if (o_offset) *o_offset = z_bytes;
   if (attn_offset) *attn_offset = z_bytes + o_bytes;
@@ -293,7 +294,7 @@ size_t hstu_layer_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_mod
   size_t attn_off = 0;
   hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, nullptr, nullptr, &attn_off);
   return attn_off + align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens)) +
-         align256((size_t)d_model * H * d_v * 2);
+         align256((size_t)total_tokens * H * 8);
 }
 
 hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,
@@ -330,10 +331,10 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   size_t zo, oo, ao;
   hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, &zo, &oo, &ao);
   bf16* z = (bf16*)((char*)workspace + zo);
-  float* obuf = (float*)((char*)workspace + oo);
+  bf16* obuf = (bf16*)((char*)workspace + oo);
   void* aws = (char*)workspace + ao;
   const size_t aws_bytes = align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens));
-  bf16* w2p = (bf16*)((char*)aws + aws_bytes);  // W2 in MFMA fragment order
+  f32x2* ostats = (f32x2*)((char*)aws + aws_bytes);  // per (token, head) mean and M2 of O
 
   st = check_hip(launch_f1_gemm_silu((const bf16*)x, (const bf16*)w1, b1, z, total_tokens, N1,
                                      d_model, stream),
@@ -347,11 +348,11 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   st = hstu_attn_plan(HSTU_DTYPE_BF16, B, H, d_qk, offsets, max_seqlen, aws, aws_bytes, stream);
   if (st != HSTU_OK) return st;
   st = attn_planned(HSTU_DTYPE_BF16, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, Q, N1, K,
-                    N1, V, N1, bias, alpha, 1.0f, obuf, true, aws, aws_bytes, stream);
+                    N1, V, N1, bias, alpha, 1.0f, obuf, false, ostats, aws, aws_bytes, stream);
   if (st != HSTU_OK) return st;
-  return check_hip(launch_ln_gate_f2(obuf, U, N1, ln_gamma, ln_beta, ln_eps, (const bf16*)w2, b2,
-                                     residual ? (const bf16*)x : nullptr, (bf16*)y, total_tokens,
-                                     d_model, HV, w2p, stream),
+  return check_hip(launch_ln_gate_f2(obuf, ostats, U, N1, ln_gamma, ln_beta, ln_eps,
+                                     (const bf16*)w2, b2, residual ? (const bf16*)x : nullptr,
+                                     (bf16*)y, total_tokens, d_model, H, d_v, stream),
                    "f2 launch");
 }
 

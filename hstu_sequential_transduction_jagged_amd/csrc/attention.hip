@@ -558,20 +558,50 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
 
   // ---- epilogue: O^T accumulators -> O rows, scaled by -(ln 2 / 2) out_scale ----
   const float osc = -0.5f * kLn2 * a.out_scale;
+  f32x4 ov[2][4];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[db][g][e] = oacc[db][4 * g + e] * osc;
+      // the statistics below describe the values as stored
+      if (!OUT_F32) ov[db][g] = __builtin_convertvector(__builtin_convertvector(ov[db][g], bf16x4), f32x4);
+    }
   if (qvalid) {
     const int64_t base = ((tok0 + row) * H + h) * kD;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 v4 = {oacc[db][4 * g] * osc, oacc[db][4 * g + 1] * osc, oacc[db][4 * g + 2] * osc,
-                    oacc[db][4 * g + 3] * osc};
         const int d0 = 32 * db + 8 * g + 4 * hf;
         if (OUT_F32)
-          *(f32x4*)((float*)a.o + base + d0) = v4;
+          *(f32x4*)((float*)a.o + base + d0) = ov[db][g];
         else
-          *(bf16x4*)((bf16*)a.o + base + d0) = __builtin_convertvector(v4, bf16x4);
+          *(bf16x4*)((bf16*)a.o + base + d0) = __builtin_convertvector(ov[db][g], bf16x4);
       }
+  }
+  // optional per-(token, head) statistics for a LayerNorm over the heads: mean of the row's 64
+  // values and the sum of squared deviations from it (lanes l and l + 32 hold the two halves)
+  if (a.ostats) {
+    float s = 0.f;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += ov[db][g][e];
+    s += __shfl_xor(s, 32, 64);
+    const float mh = s * (1.0f / kD);
+    float q = 0.f;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q += (ov[db][g][e] - mh) * (ov[db][g][e] - mh);
+    q += __shfl_xor(q, 32, 64);
+    if (qvalid && hf == 0) a.ostats[(tok0 + row) * H + h] = f32x2{mh, q};
   }
 }
 

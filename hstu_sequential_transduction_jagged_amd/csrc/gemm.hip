@@ -202,259 +202,227 @@ __global__ __launch_bounds__(kF1Threads, 2) void f1_kernel(F1Args g) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// f2: 64 tokens per workgroup, all output features.  Phase 1 (LayerNorm statistics, affine map,
-// U gate) writes the bf16 operand A [64 tokens][HV] to LDS; phase 2 runs C^T = W2 A^T with each
-// of the four waves owning a quarter of a 512-feature chunk.  W2 fragments come straight from
-// global memory (every W2 element is used by one wave of the workgroup, so LDS staging would not
-// be reused) through a ring of four k-steps, out of a copy of W2 in fragment order: one MFMA
-// operand is 1 KiB of contiguous bytes, eight whole cache lines per load.
+// f2: 64 tokens x (up to) 512 output features per workgroup, four waves of 128 features x 64
+// tokens, wider models in 512-feature chunks.  K (= H dv) is staged 32 deep through two LDS
+// buffers, from two register sets one slice ahead: the W2 slice (512 rows x 32) and the gated
+// operand slice (64 tokens x 32), which the staging threads compute from O and U on the way,
+// ((o - mean) rstd gamma + beta) u, so the gated activations never go to HBM.  The token's
+// LayerNorm statistics come from the attention's per-head (mean, M2) pairs (Chan et al.'s
+// pairwise combination).  The outputs leave through LDS as whole rows, the residual added there.
 
 constexpr int kF2Tok = 64;
+constexpr int kF2K = 32;
 constexpr int kF2Threads = 256;
 
 struct F2Args {
-  const float* O;      // attention output [M][HV], fp32
-  const bf16* U;       // gate, row stride u_stride
+  const bf16* O;        // attention output [M][HV]
+  const f32x2* ostats;  // [M][H]: mean and M2 of each head's d_v values of O
+  const bf16* U;        // gate, row stride u_stride
   int64_t u_stride;
-  const float* gamma;  // [HV] or null
-  const float* beta;   // [HV] or null
+  const float* gamma;   // [HV] or null
+  const float* beta;    // [HV] or null
   float eps;
-  const bf16* Wp;      // W2 [N][HV] in fragment order (pack_frag_kernel)
-  const float* bias;   // [N] or null
-  const bf16* R;       // residual [M][N] or null
-  bf16* Y;             // [M][N]
+  const bf16* W;        // [N][HV]
+  const float* bias;    // [N] or null
+  const bf16* R;        // residual [M][N] or null
+  bf16* Y;              // [M][N]
   int64_t M;
-  int32_t N, HV;
+  int32_t N, HV, H, dv;
+  int32_t n_begin, n_end;  // output features of this launch, in chunks of 128 NI
 };
 
-// Sum over the 64 lanes of a wave, as a wave-uniform value.
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += dpp<kDppXor1>(v);
-  v += dpp<kDppXor2>(v);
-  v += dpp<kDppHalfMirror>(v);
-  v += dpp<kDppMirror>(v);
-  auto at = [&](int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-  };
-  return (at(0) + at(16)) + (at(32) + at(48));
-}
-
-// One 128 NI-feature chunk of the output: wave w computes features nb + 32 NI w .. + 32 NI - 1
-// for all 64 tokens.  The LDS operand rows are HV + 8 elements apart: (HV / 8 + 1) is odd, so
-// 16 consecutive rows at one column fall in 16 distinct 16-byte bank groups.
+// NI: 32-feature blocks per wave (chunk = 128 NI features)
 template <int NI>
-__device__ __forceinline__ void f2_chunk(const F2Args& g, const bf16* sa, int nb, int64_t m0,
-                                         int lane, int wave) {
+__global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
+  constexpr int CH = 128 * NI;                  // features per chunk
+  constexpr int WEL = CH * kF2K, AEL = kF2Tok * kF2K;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (WEL + AEL)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int HV = g.HV, rs8 = HV / 8 + 1, N = g.N;
-  const int fw = nb + 32 * NI * wave;
-  // fragment (row block fw / 32 + i, k-step ks) of the packed W2, through a buffer descriptor
-  // over this wave's row blocks (fetches past the last k-step read zeros or unused fragments)
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(g.Wp + (int64_t)fw * HV), (short)0, (int)(32 * NI * HV * 2), 0x00020000);
-  const uint32_t voff = 16u * (uint32_t)lane;
-  const int nks = HV / 16;  // a multiple of 4
-  auto wload = [&](int i, int ks) {
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                          wrs, voff, (uint32_t)(i * nks + ks) * 1024u, 0));
-  };
-  f32x16 acc[NI][2];
-#pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int HV = g.HV, N = g.N;
+  const int64_t M = g.M;
+  const int64_t m0 = (int64_t)blockIdx.x * kF2Tok;
+  const uint32_t kb = 2u * (uint32_t)HV;  // bytes per O / W2 row
+  const int64_t nrow = M - m0 < kF2Tok ? M - m0 : kF2Tok;
 
-  bf16x8 wring[4][NI];
-#pragma unroll
-  for (int p = 0; p < 3; ++p)
-#pragma unroll
-    for (int i = 0; i < NI; ++i) wring[p][i] = wload(i, p);
-  for (int ks0 = 0; ks0 < nks; ks0 += 4) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int ks = ks0 + u;
-      // unconditional, so the wait counts stay exact: the last three steps fetch fragments
-      // past the end of K (the next row, or zeros past the descriptor), never used
-#pragma unroll
-      for (int i = 0; i < NI; ++i) wring[(u + 3) & 3][i] = wload(i, ks + 3);
-      bf16x8 b[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = ((const bf16x8*)sa)[(32 * j + l32) * rs8 + 2 * ks + hf];
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wring[u][i], b[j], acc[i][j], 0, 0, 0);
-      // keep each step's fetches three steps ahead of their use
-      __builtin_amdgcn_sched_barrier(0);
+  // staging roles: chunk sch of W2 rows srow + 64 u and of operand row srow (= token)
+  const int srow = tid >> 2, sch = tid & 3;
+  const int lofs = f1_off(srow, sch);  // rows srow + 64 u share the swizzle
+
+  // LayerNorm statistics of token srow: mean = mean of the head means; M2 = sum of the head M2
+  // plus dv x the squared deviations of the head means (rows past M give zeros)
+  float mean, rstd;
+  {
+    const int64_t t = m0 + srow;
+    const int H = g.H;
+    const f32x2* st = g.ostats + (t < M ? t : 0) * H;
+    float hq = 0.f, sm = 0.f;
+    for (int hh = 0; hh < H; ++hh) {
+      const f32x2 v = st[hh];
+      sm += v[0];
+      hq += v[1];
     }
+    mean = sm / (float)H;
+    float dev = 0.f;
+    for (int hh = 0; hh < H; ++hh) dev += (st[hh][0] - mean) * (st[hh][0] - mean);
+    rstd = 1.0f / sqrtf((hq + (float)g.dv * dev) / (float)HV + g.eps);
   }
+  // O and U rows through descriptors bounded at the block's last token (zeros past M)
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.O + m0 * HV), (short)0, (int)(nrow * kb), 0x00020000);
+  const __amdgpu_buffer_rsrc_t urs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.U + m0 * g.u_stride), (short)0, (int)(nrow * g.u_stride * 2), 0x00020000);
+  const uint32_t voff_o = (uint32_t)srow * kb + 16u * sch;
+  const uint32_t voff_u = (uint32_t)srow * (uint32_t)g.u_stride * 2u + 16u * sch;
+  // gamma / beta (null: 1 / 0) through descriptors: a null one reads zeros
+  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.gamma, (short)0, g.gamma ? 4 * HV : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.beta, (short)0, g.beta ? 4 * HV : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t biasrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.bias, (short)0, g.bias ? 4 * N : 0, 0x00020000);
+  const bool has_gamma = g.gamma != nullptr;
 
-  // acc[i][j] register r -> feature fw + 32 i + 8 (r / 4) + 4 hf + r % 4, token m0 + 32 j + l32
-  float bv[NI][4][4];
+  auto sw = [&](int buf) { return smem + buf * (WEL + AEL); };
+  auto sa = [&](int buf) { return smem + buf * (WEL + AEL) + WEL; };
+
+  for (int n0 = g.n_begin; n0 < g.n_end; n0 += CH) {
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(g.W + (int64_t)n0 * HV), (short)0, (int)(CH * kb), 0x00020000);
+    const int nk = HV / kF2K;
+    u32x4 wr[2 * NI], orr, urr;
+    auto gload = [&](int kt) {
+      const uint32_t k0 = 2u * (uint32_t)kt * kF2K;
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+      for (int u = 0; u < 2 * NI; ++u)
+        wr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              wrs, voff_o + 64u * u * kb, k0, 0));
+      orr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, voff_o, k0, 0));
+      urr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(urs, voff_u, k0, 0));
+    };
+    // gamma / beta of the slice's 8 k-values of this thread (small, cache-resident)
+    auto lstore = [&](int buf, int kt) {
+      const uint32_t kf = 4u * (uint32_t)(kt * kF2K + 8 * sch);
+      f32x4 gr[2], br[2];
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp)
+      for (int h2 = 0; h2 < 2; ++h2) {
+        gr[h2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(grs, kf + 16u * h2, 0, 0));
+        br[h2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, kf + 16u * h2, 0, 0));
+      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        bv[i][grp][e] = g.bias ? g.bias[fw + 32 * i + 8 * grp + 4 * hf + e] : 0.f;
-  // y may not alias the residual: all of a token block's residual loads are issued before its
-  // stores (rows past M read zeros through the descriptor and are not stored)
-  const bf16* __restrict__ R = g.R;
-  bf16* __restrict__ Y = g.Y;
-  const int64_t nrow = g.M - m0 < kF2Tok ? g.M - m0 : kF2Tok;
-  const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(R ? R + m0 * N : nullptr), (short)0, R ? (int)(nrow * N * 2) : 0, 0x00020000);
+      for (int u = 0; u < 2 * NI; ++u) *(u32x4*)(sw(buf) + lofs + 64 * u * kF2K) = wr[u];
+      const bf16x8 o8 = __builtin_bit_cast(bf16x8, orr);
+      const bf16x8 u8 = __builtin_bit_cast(bf16x8, urr);
+      f32x8 y;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int tl = 32 * j + l32;  // token within the block
-    u32x2 r4[NI][4];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp)
-        r4[i][grp] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                   rrs, (uint32_t)(tl * N + fw + 4 * hf) * 2u,
-                                                   (uint32_t)(32 * i + 8 * grp) * 2u, 0));
-    if (tl >= nrow) continue;
-    bf16* yrow = Y + (m0 + tl) * N + fw + 4 * hf;
+      for (int e = 0; e < 8; ++e) {
+        const float gm = has_gamma ? gr[e >> 2][e & 3] : 1.0f;
+        y[e] = (((float)o8[e] - mean) * rstd * gm + br[e >> 2][e & 3]) * (float)u8[e];
+      }
+      *(bf16x8*)(sa(buf) + lofs) = __builtin_convertvector(y, bf16x8);
+    };
+
+    // acc[i][j] register r -> feature n0 + 32 NI wave + 32 i + 8 (r / 4) + 4 hf + r % 4, token
+    // 32 j + l32; the accumulators start at the bias
+    f32x16 acc[NI][2];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
-        const bf16x4 rb = __builtin_bit_cast(bf16x4, r4[i][grp]);
-        f32x4 v;
+        const f32x4 b4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            biasrs, 4u * (uint32_t)(n0 + 32 * NI * wave + 4 * hf), 4u * (32 * i + 8 * grp), 0));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * grp + e] + bv[i][grp][e] + (float)rb[e];
-        *(bf16x4*)(yrow + 32 * i + 8 * grp) = __builtin_convertvector(v, bf16x4);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * grp + e] = b4[e];
       }
-  }
-}
-
-// QN: 8-feature chunks of a row per lane (HV <= 512 QN).
-template <int QN>
-__global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
-  __shared__ bf16 sa[kF2Tok * (512 * QN + 8)];
-  // the wave index is uniform: W2 descriptors built from it stay in scalar registers
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int HV = g.HV, nch = HV >> 3;
-  const int64_t m0 = (int64_t)blockIdx.x * kF2Tok;
-  const int64_t M = g.M;
-
-  // ---- phase 1: wave w normalises and gates token rows 16 w .. 16 w + 15, RB rows at a time;
-  // lane l handles the 8-feature chunks l + 64 q of each row.
-  constexpr int RB = 4 / QN;
-  f32x8 gam[QN], bet[QN];
+    auto compute = [&](int buf) {
 #pragma unroll
-  for (int q = 0; q < QN; ++q) {
-    const int c = min(lane + 64 * q, nch - 1);  // lanes past the last chunk repeat it, unused
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 a[NI], b[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      gam[q][e] = g.gamma ? g.gamma[8 * c + e] : 1.0f;
-      bet[q][e] = g.beta ? g.beta[8 * c + e] : 0.0f;
-    }
-  }
-  // O and U rows through buffer descriptors bounded at the workgroup's last token: rows past M
-  // and lanes past the row's last chunk (offset 2^31) read as zeros, without branches.
-  const int64_t nrow = M - m0 < kF2Tok ? M - m0 : kF2Tok;
-  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(g.O + m0 * HV), (short)0, (int)(nrow * HV * 4), 0x00020000);
-  const __amdgpu_buffer_rsrc_t urs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(g.U + m0 * g.u_stride), (short)0, (int)(nrow * g.u_stride * 2), 0x00020000);
-  uint32_t vo[QN], vu[QN];
+        for (int i = 0; i < NI; ++i)
+          a[i] = *(const bf16x8*)(sw(buf) + f1_off(32 * NI * wave + 32 * i + l32, 2 * ks + hf));
 #pragma unroll
-  for (int q = 0; q < QN; ++q) {
-    const int c = lane + 64 * q;
-    vo[q] = c < nch ? 32u * c : 0x80000000u;
-    vu[q] = c < nch ? 16u * c : 0x80000000u;
-  }
-  f32x4 ov[2][RB][QN][2];
-  u32x4 uv[2][RB][QN];
-  auto load = [&](int slot, int r0) {
+        for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8*)(sa(buf) + f1_off(32 * j + l32, 2 * ks + hf));
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const uint32_t row = 16 * wave + r0 + rr;
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int q = 0; q < QN; ++q) {
-        ov[slot][rr][q][0] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, vo[q], row * HV * 4u, 0));
-        ov[slot][rr][q][1] = __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, vo[q] + 16u, row * HV * 4u, 0));
-        uv[slot][rr][q] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(urs, vu[q], row * (uint32_t)g.u_stride * 2u, 0));
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
       }
+    };
+    // slice kt in LDS buffer kt % 2; slice kt + 1's loads are in flight during slice kt
+    gload(0);
+    lstore(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(buf);
+      if (kt + 1 < nk) lstore(buf ^ 1, kt + 1);
+      __syncthreads();
     }
-  };
-  const float inv_hv = 1.0f / (float)HV;
-  load(0, 0);
+
+    // epilogue through LDS in two passes of 64 NI features (waves 2 p, 2 p + 1), as an fp32 tile
+    // of 64 token rows: granule (4 features) q of row lr sits at q ^ (lr & 15).  The residual is
+    // added to the fp32 sum, so each output is rounded once.
+    const bf16* __restrict__ R = g.R;
+    bf16* __restrict__ Y = g.Y;
+    const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(R ? R + m0 * N : nullptr), (short)0, R ? (int)(nrow * N * 2) : 0, 0x00020000);
+    // output rows past M fall outside the descriptor and are dropped
+    const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Y + m0 * N), (short)0, (int)(nrow * N * 2), 0x00020000);
+    f32x4* tile = (f32x4*)smem;        // [64 rows][16 NI granules]
+    constexpr int GPR = 16 * NI;       // granules per row
+    constexpr int NPC = 64 * 8 * NI / kF2Threads;  // 8-output pieces per thread and pass
 #pragma unroll
-  for (int bi = 0; bi < 16 / RB; ++bi) {
-    const int slot = bi & 1;
-    if (bi + 1 < 16 / RB) load(slot ^ 1, (bi + 1) * RB);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int p = 0; p < 2; ++p) {
+      if ((wave >> 1) == p) {
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      float s = 0.f;
+        for (int j = 0; j < 2; ++j) {
+          const int lr = 32 * j + l32;
 #pragma unroll
-      for (int q = 0; q < QN; ++q)
+          for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += ov[slot][rr][q][e >> 2][e & 3];
-      const float mean = wave_sum_dpp(s) * inv_hv;
-      float d = 0.f;
-#pragma unroll
-      for (int q = 0; q < QN; ++q) {
-        const bool in = lane + 64 * q < nch;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float t = in ? ov[slot][rr][q][e >> 2][e & 3] - mean : 0.f;
-          d += t * t;
+            for (int grp = 0; grp < 4; ++grp) {
+              const int q = 8 * NI * (wave & 1) + 8 * i + 2 * grp + hf;
+              tile[lr * GPR + (q ^ (lr & 15))] =
+                  f32x4{acc[i][j][4 * grp], acc[i][j][4 * grp + 1], acc[i][j][4 * grp + 2],
+                        acc[i][j][4 * grp + 3]};
+            }
         }
       }
-      const float rstd = 1.0f / sqrtf(wave_sum_dpp(d) * inv_hv + g.eps);
-      const int row = 16 * wave + bi * RB + rr;
-      // lanes past the row's last chunk write the row's padding chunk, which is never read
+      __syncthreads();
+      // piece c = t + 256 k: row c / (8 NI), features 8 (c % (8 NI)) .. + 7 of the pass
+      const int fp = n0 + 64 * NI * p;
+      u32x4 rv[NPC];
 #pragma unroll
-      for (int q = 0; q < QN; ++q) {
-        const int c = lane + 64 * q;
-        const bf16x8 u8 = __builtin_bit_cast(bf16x8, uv[slot][rr][q]);
-        f32x8 y;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          y[e] = ((ov[slot][rr][q][e >> 2][e & 3] - mean) * rstd * gam[q][e] + bet[q][e]) *
-                 (float)u8[e];
-        ((bf16x8*)sa)[row * (nch + 1) + (c < nch ? c : nch)] = __builtin_convertvector(y, bf16x8);
+      for (int k = 0; k < NPC; ++k) {
+        const int c = tid + kF2Threads * k, lr = c / (8 * NI), pc = c % (8 * NI);
+        rv[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rrs, (uint32_t)(lr * N + fp + 8 * pc) * 2u, 0, 0));
       }
+#pragma unroll
+      for (int k = 0; k < NPC; ++k) {
+        const int c = tid + kF2Threads * k, lr = c / (8 * NI), pc = c % (8 * NI);
+        const f32x4 a0 = tile[lr * GPR + ((2 * pc) ^ (lr & 15))];
+        const f32x4 a1 = tile[lr * GPR + ((2 * pc + 1) ^ (lr & 15))];
+        const f32x8 r8 = __builtin_convertvector(__builtin_bit_cast(bf16x8, rv[k]), f32x8);
+        f32x8 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = a0[e] + r8[e];
+          v[e + 4] = a1[e] + r8[e + 4];
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, __builtin_convertvector(v, bf16x8)), yrs,
+            (uint32_t)(lr * N + fp + 8 * pc) * 2u, 0, 0);
+      }
+      __syncthreads();  // the tile is the next pass's / chunk's staging area
     }
-  }
-  __syncthreads();
-
-  // ---- phase 2
-  for (int nb = 0; nb < g.N; nb += 512) {
-    const int rem = g.N - nb;
-    if (rem >= 512) f2_chunk<4>(g, sa, nb, m0, lane, wave);
-    else if (rem == 384) f2_chunk<3>(g, sa, nb, m0, lane, wave);
-    else if (rem == 256) f2_chunk<2>(g, sa, nb, m0, lane, wave);
-    else f2_chunk<1>(g, sa, nb, m0, lane, wave);
-  }
-}
-
-// W [N][K] (N % 32 == 0, K % 16 == 0) rewritten in MFMA operand order: fragment (nb, ks), at
-// index nb K / 16 + ks, is 64 lanes x 8 bf16 where lane l + 32 h holds row 32 nb + l, columns
-// 16 ks + 8 h .. + 7 (the A operand of v_mfma_f32_32x32x16_bf16 for rows 32 nb .. + 31).
-__global__ void pack_frag_kernel(const bf16* __restrict__ w, bf16* __restrict__ out, int N, int K) {
-  const int64_t total = (int64_t)N * K / 8;  // 16-byte pieces
-  const int kst = K / 16;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t frag = idx >> 6;
-    const int ln = (int)(idx & 63);
-    const int64_t nb = frag / kst;
-    const int ks = (int)(frag - nb * kst);
-    const int64_t row = 32 * nb + (ln & 31);
-    ((u32x4*)out)[idx] = *(const u32x4*)(w + row * K + 16 * ks + 8 * (ln >> 5));
   }
 }
 
@@ -498,27 +466,35 @@ hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, b
   return hipGetLastError();
 }
 
-hipError_t launch_ln_gate_f2(const float* o, const bf16* u, int64_t u_stride, const float* gamma,
-                             const float* beta, float eps, const bf16* w2, const float* b2,
-                             const bf16* x, bf16* y, int64_t M, int32_t D, int32_t HV,
-                             bf16* w2_packed, hipStream_t stream) {
-  if (D % 128 || D <= 0 || HV % 64 || HV <= 0 || HV > 1024 || u_stride % 8 || u_stride < HV ||
-      u_stride > (1 << 24))
+hipError_t launch_ln_gate_f2(const bf16* o, const f32x2* ostats, const bf16* u,
+                             int64_t u_stride, const float* gamma, const float* beta, float eps,
+                             const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,
+                             int32_t D, int32_t H, int32_t dv, hipStream_t stream) {
+  const int32_t HV = H * dv;
+  if (D % 128 || D <= 0 || HV % (2 * kF2K) || HV <= 0 || u_stride % 8 || u_stride < HV)
+    return hipErrorInvalidValue;
+  if ((int64_t)kF2Tok * 2 * u_stride > 0x7fffffff || (int64_t)512 * 2 * HV > 0x7fffffff)
     return hipErrorInvalidValue;
   if (M <= 0) return hipSuccess;
-  {
-    const int64_t pieces = (int64_t)D * HV / 8;
-    hipLaunchKernelGGL(pack_frag_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0,
-                       stream, w2, w2_packed, D, HV);
-  }
   F2Args g{};
-  g.O = o; g.U = u; g.u_stride = u_stride; g.gamma = gamma; g.beta = beta; g.eps = eps;
-  g.Wp = w2_packed; g.bias = b2; g.R = x; g.Y = y; g.M = M; g.N = D; g.HV = HV;
+  g.O = o; g.ostats = ostats; g.U = u; g.u_stride = u_stride; g.gamma = gamma; g.beta = beta;
+  g.eps = eps; g.W = w2; g.bias = b2; g.R = x; g.Y = y; g.M = M; g.N = D; g.HV = HV; g.H = H;
+  g.dv = dv;
   const dim3 grid((unsigned)((M + kF2Tok - 1) / kF2Tok));
-  if (HV <= 512)
-    hipLaunchKernelGGL(f2_kernel<1>, grid, dim3(kF2Threads), 0, stream, g);
-  else
-    hipLaunchKernelGGL(f2_kernel<2>, grid, dim3(kF2Threads), 0, stream, g);
+  // chunks of 512 features, then one launch for a narrower remainder
+  const int32_t full = D / 512 * 512;
+  if (full > 0) {
+    g.n_begin = 0; g.n_end = full;
+    hipLaunchKernelGGL(f2_kernel<4>, grid, dim3(kF2Threads), 0, stream, g);
+  }
+  if (D > full) {
+    g.n_begin = full; g.n_end = D;
+    switch ((D - full) / 128) {
+      case 1: hipLaunchKernelGGL(f2_kernel<1>, grid, dim3(kF2Threads), 0, stream, g); break;
+      case 2: hipLaunchKernelGGL(f2_kernel<2>, grid, dim3(kF2Threads), 0, stream, g); break;
+      default: hipLaunchKernelGGL(f2_kernel<3>, grid, dim3(kF2Threads), 0, stream, g); break;
+    }
+  }
   return hipGetLastError();
 }
 

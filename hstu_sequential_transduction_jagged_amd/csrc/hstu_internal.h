@@ -67,6 +67,7 @@ struct AttnArgs {
   int32_t tclass_cols;    // entries per query-block row of tclass (= blocks of the longest user)
   int64_t tclass_bytes;
   float alpha, out_scale;
+  f32x2* ostats;          // bf16 path, optional: per (token, head) mean and M2 of the O row
 };
 
 // Rows of the tile-class table: user b's query block i sits on row (offsets[b] + 31 b) / 32 + i,
@@ -111,10 +112,10 @@ int attn_block_rows_f32(int d);
 
 hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, bf16* z, int64_t M,
                                int32_t N, int32_t K, hipStream_t stream);
-hipError_t launch_ln_gate_f2(const float* o, const bf16* u, int64_t u_stride, const float* gamma,
-                             const float* beta, float eps, const bf16* w2, const float* b2,
-                             const bf16* x, bf16* y, int64_t M, int32_t D, int32_t HV,
-                             bf16* w2_packed, hipStream_t stream);
+hipError_t launch_ln_gate_f2(const bf16* o, const f32x2* ostats, const bf16* u,
+                             int64_t u_stride, const float* gamma, const float* beta, float eps,
+                             const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,
+                             int32_t D, int32_t H, int32_t dv, hipStream_t stream);
 hipError_t launch_embed_sum(int64_t T, int32_t dim, const bf16* item, int64_t num_items,
                             const bf16* action, int32_t num_actions, const int32_t* ids,
                             const int32_t* aids, bf16* x, hipStream_t stream);

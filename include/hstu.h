@@ -140,9 +140,10 @@ size_t hstu_layer_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_mod
  *  residual nonzero: y = x + f2(...)
  *  y        device bf16 [T, d_model]; may not alias x.
  *  The workspace holds Z = SiLU(x W1^T + b1) as bf16 [T, 2H(d_qk+d_v)] (column blocks
- *  U | V | Q | K) at byte 0, then the attention output O as fp32 [T, H d_v], then the
+ *  U | V | Q | K) at byte 0, then the attention output O as bf16 [T, H d_v], then the
  *  attention workspace; offsets of each are returned by hstu_layer_workspace_offsets().
- *  The last d_model H d_v bf16 (256-byte aligned) hold a copy of w2 in MFMA operand order. */
+ *  The last T H fp32 pairs (256-byte aligned) hold each (token, head)'s mean of O and sum of
+ *  squared deviations from it, from which the LayerNorm statistics are combined. */
 hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,
                            int32_t d_v, const int32_t* offsets, int32_t max_seqlen,
                            int64_t total_tokens, const void* x, const void* w1, const float* b1,

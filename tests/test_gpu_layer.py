@@ -33,7 +33,8 @@ def test_layer_small_workload(affine):
 
 
 def test_layer_intermediates():
-    """Z = SiLU(X W1^T + b1) with its U | V | Q | K blocks, and O, checked separately."""
+    """Z = SiLU(X W1^T + b1) with its U | V | Q | K blocks, and O (stored in bf16 between the
+    attention and the LayerNorm), checked separately."""
     inp = synth.make_layer("t", 40, [0, 1, 300, 257, 64], D=256, H=4, d=64, alpha=1.0 / 300,
                            P=128, NT=32, table_std=0.5, randomize_affine=True)
     d = DevLayer(inp)
@@ -43,12 +44,12 @@ def test_layer_intermediates():
     torch.cuda.synchronize()
     zo, oo, _ = binding.layer_workspace_offsets(inp.T, 4, 64, 64)
     z = ws[zo:zo + inp.T * 1024 * 2].view(torch.bfloat16).view(inp.T, 1024).float().cpu().numpy()
-    o = ws[oo:oo + inp.T * 256 * 4].view(torch.float32).view(inp.T, 256).cpu().numpy()
+    o = ws[oo:oo + inp.T * 256 * 2].view(torch.bfloat16).view(inp.T, 256).float().cpu().numpy()
     yr, zr, orf = oracle_layer(inp, return_intermediates=True)
     for name, a, r in [("U", z[:, :256], zr[:, :256]), ("V", z[:, 256:512], zr[:, 256:512]),
                        ("Q", z[:, 512:768], zr[:, 512:768]), ("K", z[:, 768:], zr[:, 768:]),
                        ("O", o, orf), ("Y", y.float().cpu().numpy(), yr)]:
-        e = err_stored(a, r, "f32" if name == "O" else "bf16")
+        e = err_stored(a, r, "bf16")
         print(name, "err=%.3g (without storage allowance %.3g)" % (e, err_rms(a, r)), flush=True)
         assert e <= TOL["bf16"], name
 
