@@ -20,10 +20,11 @@ namespace hstu {
 namespace {
 
 // ---------------------------------------------------------------------------------------------
-// f1: 128 output features x 256 tokens per workgroup, four waves of 64 features x 128 tokens.
-// K is staged 32 deep through two LDS buffers from two register sets, so each slice's global
-// loads are issued two slices before their LDS write.  The bf16 results leave through LDS as
-// whole 256-byte row segments.
+// f1: 128 output features x 256 tokens per workgroup, four waves of 64 features x 128 tokens,
+// three workgroups per CU (167 registers, 48 KiB of LDS each), so that one workgroup's
+// SiLU epilogue overlaps the others' MFMA loops.  K is staged 32 deep through two LDS stages
+// filled by direct global-to-LDS transfers one slice ahead (no staging registers).  The bf16
+// results leave through LDS as whole 256-byte row segments.
 
 constexpr int kF1Feat = 128;
 constexpr int kF1Tok = 256;
@@ -42,15 +43,34 @@ struct F1Args {
 };
 
 // 64-byte LDS rows of four 16-byte chunks; chunk c of row r sits in slot c ^ ((r >> 2) & 3), so
-// 16 lanes that read one chunk of 16 consecutive rows, or write the four chunks of four
-// consecutive rows, touch 16 distinct 16-byte bank groups.
+// 16 lanes that read one chunk of 16 consecutive rows touch 16 distinct 16-byte bank groups.
 __device__ __forceinline__ int f1_off(int row, int chunk) {
   return row * kF1K + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
-__global__ __launch_bounds__(kF1Threads, 2) void f1_kernel(F1Args g) {
-  // two stages of (W slice, X slice); reused by the epilogue as a 128-token x 128-feature tile
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * (kF1WElems + kF1XElems)];
+// s_waitcnt bounding only the vector-memory counter (loads and LDS transfers still in flight)
+template <int C>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((C & 15) | (7 << 4) | (15 << 8) | ((C >> 4) << 14));
+}
+// workgroup barrier with no compiler reordering of memory operations across it (the LDS
+// transfers it publishes were waited for explicitly)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// NK: K / 32 when known at compile time (the slice loop is then straight-line code, which keeps
+// the compiler's own waits on the transfers exact), 0 for any K
+template <int NK>
+__global__ __launch_bounds__(kF1Threads, 3) void f1_kernel(F1Args g) {
+  // stage arrays of their own: the compiler then knows which stage a transfer writes
+  __shared__ __attribute__((aligned(16))) bf16 sW0[kF1WElems], sW1[kF1WElems];
+  __shared__ __attribute__((aligned(16))) bf16 sX0[kF1XElems], sX1[kF1XElems];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int wf = wave & 1, wt = wave >> 1;
@@ -75,53 +95,58 @@ __global__ __launch_bounds__(kF1Threads, 2) void f1_kernel(F1Args g) {
       (void*)(g.W + (int64_t)n0 * K), (short)0, (int)(kF1Feat * kb), 0x00020000);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.X + m0 * K), (short)0, (int)(rows * kb), 0x00020000);
-  // thread t stages chunk t % 4 of rows t / 4 + 64 u (same swizzle for every u)
-  const int srow = tid >> 2, sch = tid & 3;
-  const uint32_t voff = (uint32_t)srow * kb + 16u * sch;
-  const int lofs = f1_off(srow, sch);
-  auto sw = [&](int buf) { return smem + buf * (kF1WElems + kF1XElems); };
-  auto sx = [&](int buf) { return smem + buf * (kF1WElems + kF1XElems) + kF1WElems; };
-
-  u32x4 wr[2][2], xr[2][4];
-  const int nk = K / kF1K;  // even
-  // slices past the end reload the last one: the loads stay unconditional, so the wait counts
-  // are exact
-  auto gload = [&](int set, int kt) {
+  // A transfer instruction fills 1 KiB of a stage: lane p writes 16-byte granule 64 v + p, which
+  // is row 16 v + p / 4, slot p % 4, so the lane fetches chunk (p % 4) ^ ((row >> 2) & 3) of
+  // that row.  Wave w issues instructions v = w + 4 u (W: u < 2, X: u < 4).
+  uint32_t wvo[2], xvo[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 16 * (wave + 4 * u) + (lane >> 2);
+    const uint32_t off = (uint32_t)row * kb + 16u * (uint32_t)((lane & 3) ^ ((row >> 2) & 3));
+    if (u < 2) wvo[u] = off;
+    xvo[u] = off;
+  }
+  const int nk = NK ? NK : K / kF1K;
+  auto dma = [&](bf16* sw, bf16* sx, int kt) {
+    // the slice past the end repeats the last one into a stage no one reads again
     const uint32_t k0 = 2u * (uint32_t)(kt < nk ? kt : nk - 1) * kF1K;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      wr[set][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 wrs, voff + 64u * u * kb, k0, 0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(sw + (wave + 4 * u) * 512), 16,
+                                               wvo[u], k0, 0, 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      xr[set][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 xrs, voff + 64u * u * kb, k0, 0));
-  };
-  auto lstore = [&](int set, int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) *(u32x4*)(sw(buf) + lofs + 64 * u * kF1K) = wr[set][u];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *(u32x4*)(sx(buf) + lofs + 64 * u * kF1K) = xr[set][u];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(sx + (wave + 4 * u) * 512), 16,
+                                               xvo[u], k0, 0, 0);
   };
 
+  // acc[i][j] register r -> feature n0 + 64 wf + 32 i + 8 (r / 4) + 4 hf + r % 4, token
+  // m0 + 128 wt + 32 j + l32; the accumulators start at the bias (a null bias reads zeros)
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)g.bias, (short)0, g.bias ? 4 * N : 0, 0x00020000);
   f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 b4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          brs, 4u * (uint32_t)(n0 + 64 * wf + 4 * hf), 4u * (32 * i + 8 * grp), 0));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][j][4 * grp + e] = b4[e];
+    }
 
-  auto compute = [&](int buf) {
+  auto compute = [&](const bf16* sw, const bf16* sx) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 a[2], b[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        a[i] = *(const bf16x8*)(sw(buf) + f1_off(64 * wf + 32 * i + l32, 2 * ks + hf));
+        a[i] = *(const bf16x8*)(sw + f1_off(64 * wf + 32 * i + l32, 2 * ks + hf));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b[j] = *(const bf16x8*)(sx(buf) + f1_off(128 * wt + 32 * j + l32, 2 * ks + hf));
+        b[j] = *(const bf16x8*)(sx + f1_off(128 * wt + 32 * j + l32, 2 * ks + hf));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -129,48 +154,41 @@ __global__ __launch_bounds__(kF1Threads, 2) void f1_kernel(F1Args g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   };
-
-  // slice kt lives in register set kt % 2 and LDS buffer kt % 2
-  gload(0, 0);
-  gload(1, 1);
-  lstore(0, 0);
-  __syncthreads();
-  // (scheduling barriers pin the loads ahead of the slice's MFMAs)
-  for (int kt = 0; kt < nk; kt += 2) {
-    gload(0, kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(0);
-    lstore(1, 1);
-    __syncthreads();
-    gload(1, kt + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(1);
-    lstore(0, 0);
-    __syncthreads();
+  // slice kt lives in stage kt % 2; at slice kt the transfer of slice kt + 1 is issued into the
+  // other stage (whose readers all passed the last barrier), then slice kt is multiplied, then
+  // the transfer is waited for
+  auto step = [&](bf16* cw, bf16* cx, bf16* fw, bf16* fx, int kt) {
+    dma(fw, fx, kt + 1);
+    __builtin_amdgcn_sched_barrier(0);  // issued ahead of the slice's MFMAs
+    compute(cw, cx);
+    wait_vm<0>();
+    lds_barrier();
+  };
+  dma(sW0, sX0, 0);
+  wait_vm<0>();
+  lds_barrier();
+#pragma unroll
+  for (int kt = 0; kt < (NK ? NK : nk); kt += 2) {
+    step(sW0, sX0, sW1, sX1, kt);
+    if (kt + 1 < nk) step(sW1, sX1, sW0, sX0, kt + 1);
   }
-  // the last two gloads were the repeated last slice and are unused; the final lstore wrote
-  // buffer 0 after every read of it
+  wait_vm<0>();  // the repeated transfers past the end land before the stages are reused
+  lds_barrier();
 
-  // epilogue: acc[i][j] register r -> feature n0 + 64 wf + 32 i + 8 (r / 4) + 4 hf + r % 4,
-  // token m0 + 128 wt + 32 j + l32.  Two passes of 128 tokens (j = 2p, 2p + 1) through an LDS
-  // tile of 256-byte rows: 8-byte piece (granule q, half hf) of local row lr sits at granule
-  // q ^ (lr & 15), half hf ^ ((lr >> 4) & 1), so each 32-lane half of a write touches 32
-  // distinct 8-byte bank pairs and each 16-lane row read 16 distinct granules.
-  float bv[2][4][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        bv[i][grp][e] = g.bias ? g.bias[n0 + 64 * wf + 32 * i + 8 * grp + 4 * hf + e] : 0.f;
-  u32x2* tile = (u32x2*)smem;  // [128 rows][32 halves of 8 bytes]
+  // epilogue: SiLU of acc[i][j] (bias included).  Two passes of 128 tokens (j = 2 p, 2 p + 1) through an LDS
+  // tile of 256-byte rows (rows 0..63 in sX0, 64..127 in sX1; local row 64 wt + 32 (j - 2 p) +
+  // l32): 8-byte piece (granule q, half hf) of row r sits at granule q ^ (r & 15), half
+  // hf ^ ((r >> 4) & 1), so each 32-lane half of a write touches 32 distinct 8-byte bank pairs
+  // and each 16-lane row read 16 distinct granules.
+  // output rows past M fall outside the descriptor and are dropped
+  const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.Y + m0 * N), (short)0, (int)min(rows * N * 2, (int64_t)0x7fffffff), 0x00020000);
+  u32x2* wtile = (u32x2*)(wt ? sX1 : sX0);  // [64 rows][32 halves of 8 bytes]
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * p + jj;
-      const int lr = 64 * wt + 32 * jj + l32;
+      const int r = 32 * jj + l32;  // row within this wave's array
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -178,11 +196,11 @@ __global__ __launch_bounds__(kF1Threads, 2) void f1_kernel(F1Args g) {
           f32x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float x = acc[i][j][4 * grp + e] + bv[i][grp][e];
+            const float x = acc[i][2 * p + jj][4 * grp + e];
             v[e] = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
           }
           const int q = 8 * wf + 4 * i + grp;
-          tile[lr * 32 + 2 * (q ^ (lr & 15)) + (hf ^ ((lr >> 4) & 1))] =
+          wtile[r * 32 + 2 * (q ^ (r & 15)) + (hf ^ ((r >> 4) & 1))] =
               __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
         }
     }
@@ -191,11 +209,13 @@ __global__ __launch_bounds__(kF1Threads, 2) void f1_kernel(F1Args g) {
     const int q = tid & 15;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int lr = (tid >> 4) + 16 * k;
-      const int64_t m = m0 + 128 * (lr >> 6) + 32 * (2 * p + ((lr >> 5) & 1)) + (lr & 31);
-      const u32x4 c = *(const u32x4*)(tile + lr * 32 + 2 * (q ^ (lr & 15)));
-      const u32x4 o = ((lr >> 4) & 1) ? u32x4{c[2], c[3], c[0], c[1]} : c;
-      if (m < M) *(u32x4*)(g.Y + m * N + n0 + 8 * q) = o;
+      const int r = (tid >> 4) + 16 * k;
+      const int rl = r & 63;
+      const int tok = 128 * (r >> 6) + 32 * (2 * p + (rl >> 5)) + (rl & 31);  // within the tile
+      const u32x2* rtile = (const u32x2*)(r < 64 ? sX0 : sX1);
+      const u32x4 c = *(const u32x4*)(rtile + rl * 32 + 2 * (q ^ (rl & 15)));
+      const u32x4 o = ((rl >> 4) & 1) ? u32x4{c[2], c[3], c[0], c[1]} : c;
+      __builtin_amdgcn_raw_buffer_store_b128(o, yrs, (uint32_t)(tok * N + n0 + 8 * q) * 2u, 0, 0);
     }
     __syncthreads();
   }
@@ -453,7 +473,8 @@ __global__ void embed_sum_kernel(int64_t T, int dim, const bf16* __restrict__ it
 
 hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, bf16* z, int64_t M,
                                int32_t N, int32_t K, hipStream_t stream) {
-  if (N % kF1Feat || K % (2 * kF1K) || K <= 0) return hipErrorInvalidValue;
+  if (N % kF1Feat || K % kF1K || K <= 0) return hipErrorInvalidValue;
+  if ((int64_t)kF1Tok * N * 2 > 0x7fffffff) return hipErrorInvalidValue;
   if ((int64_t)kF1Tok * 2 * K > 0x7fffffff || (int64_t)kF1Feat * 2 * K > 0x7fffffff)
     return hipErrorInvalidValue;
   if (M <= 0) return hipSuccess;
@@ -462,7 +483,9 @@ hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, b
   F1Args g{};
   g.X = x; g.W = w1; g.bias = b1; g.Y = z; g.M = M; g.N = N; g.K = K; g.tiles = (int32_t)tiles;
   const unsigned grid = (unsigned)((tiles + 7) / 8 * 8);
-  hipLaunchKernelGGL(f1_kernel, dim3(grid), dim3(kF1Threads), 0, stream, g);
+  if (K == 512) hipLaunchKernelGGL(f1_kernel<16>, dim3(grid), dim3(kF1Threads), 0, stream, g);
+  else if (K == 256) hipLaunchKernelGGL(f1_kernel<8>, dim3(grid), dim3(kF1Threads), 0, stream, g);
+  else hipLaunchKernelGGL(f1_kernel<0>, dim3(grid), dim3(kF1Threads), 0, stream, g);
   return hipGetLastError();
 }
 
