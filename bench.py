@@ -84,12 +84,76 @@ def cpu_baseline(inp, seconds=15.0, seed=7):
             "tokens_per_s_equiv": None}
 
 
+def bench_stack8(args, dev):
+    """The 8-layer stack forward (D=512, H=8, d=64, B=128 power-law users, stochastic length
+    cap 1024, residual): one step = all 8 layers, each f1 GEMM + SiLU + split, the jagged
+    attention with the position / time bias, and the LayerNorm-gate-f2 GEMM with the residual."""
+    import numpy as np
+    import torch
+    from hstu_sequential_transduction_jagged_amd import binding, synth
+    inp = synth.stack8()
+    bf = torch.bfloat16
+    t = lambda a, d=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev, d) if d else \
+        torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x0 = t(inp.x, bf)
+    offs = t(inp.offsets.astype(np.int32))
+    ts = t(inp.ts)
+    layers = []
+    for L in inp.layers:
+        layers.append(dict(w1=t(L.w1, bf), b1=t(L.b1), gamma=t(L.gamma), beta=t(L.beta),
+                           w2=t(L.w2, bf), b2=t(L.b2),
+                           bias=binding.make_bias(binding.BIAS_RAB_PT, ts, t(L.bias.w_pos),
+                                                  t(L.bias.w_time))))
+    D = x0.shape[1]
+    ws = torch.empty(binding.layer_workspace_bytes(inp.B, inp.T, D, inp.H, inp.dqk, inp.dv,
+                                                   inp.max_seqlen), dtype=torch.uint8, device=dev)
+    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+
+    def step():
+        h = x0
+        for li, L in enumerate(layers):
+            h = binding.hstu_layer_fwd(h, offs, inp.max_seqlen, L["w1"], L["b1"], L["gamma"],
+                                       L["beta"], L["w2"], L["b2"], inp.H, inp.dqk, inp.dv,
+                                       L["bias"], inp.alpha, True, inp.ln_eps, out=bufs[li % 2],
+                                       workspace=ws)
+        return h
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    lengths = np.diff(inp.offsets.astype(np.int64))
+    T = int(inp.T)
+    N1 = 2 * inp.H * (inp.dqk + inp.dv)
+    gemm = 2.0 * T * D * N1 + 2.0 * T * inp.H * inp.dv * D
+    flops = len(layers) * (causal_flops(lengths, inp.H, inp.dqk, inp.dv) + gemm)
+    print(json.dumps({
+        "metric": "HSTU 8-layer stack forward TFLOP/s (attention causal FLOPs + f1/f2 GEMM FLOPs)",
+        "value": round(flops / step_s / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "stack8", "B": inp.B, "layers": len(layers), "D": D, "H": inp.H,
+                   "d_qk": inp.dqk, "d_v": inp.dv, "T": T, "max_len": int(lengths.max()),
+                   "bias": "rab_pt P=256 NT=32", "alpha": inp.alpha, "seed": inp.seed},
+        "tokens_per_s": round(T / step_s, 1),
+        "pct_of_bf16_peak": round(100.0 * flops / step_s / 1e12 / PEAK_BF16_TFLOPS, 2)}),
+        flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8"],
+                    help="attn_long (the headline attention batch) or stack8 (the 8-layer HSTU "
+                         "stack forward: f1 GEMM + SiLU, attention, LayerNorm-gate-f2, residual)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the HBM byte counters against a known traffic)")
@@ -119,6 +183,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
                           "launches": 5}), flush=True)
+        return
+    if args.workload == "stack8":
+        bench_stack8(args, dev)
         return
     inp = synth.attn_long()
     lengths = np.diff(inp.offsets.astype(np.int64))
