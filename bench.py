@@ -255,6 +255,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(alg_bytes),
                      "kernel": "attn_bf16_d64_kernel", "kernel_ms": round(kern_s * 1e3, 4),
+                     "kernel_ms_p10_p50_p90": [round(float(np.percentile(kern_ms, q)), 4)
+                                               for q in (10, 50, 90)],
                      "flop_per_launch": flops, "algorithmic_bytes_per_launch": alg_bytes},
     }
     if not args.no_cpu_baseline:

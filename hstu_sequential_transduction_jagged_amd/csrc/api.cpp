@@ -196,7 +196,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   int32_t* trel = (int32_t*)((char*)tstat + align256((size_t)total_tokens * sizeof(TimeStat)));
   uint32_t* tclass = (uint32_t*)((char*)trel + align256((size_t)total_tokens * sizeof(int32_t)));
   if (dt == HSTU_DTYPE_BF16 && ba.kind == 1) {
-    st = check_hip(launch_time_stats(B, offsets, ba.ts, tstat, trel, stream), "time stats launch");
+    st = check_hip(launch_time_stats(B, offsets, ba.ts, max_seqlen, tstat, trel, stream), "time stats launch");
     if (st != HSTU_OK) return st;
     st = check_hip(launch_tile_class(B, offsets, tstat, tclass_cols(max_seqlen), ba.num_pos,
                                      ba.num_time, tclass, stream),

@@ -103,7 +103,7 @@ constexpr int64_t kTMin = -kTMax - 1;
 // Timestamp statistics: for every 32-token block of a user (blocks start at the user's first
 // token), the min and max timestamp, stored at the block's first token; and for every token
 // its offset from its block's minimum as int32 (saturated; only read where the block spans
-// at most 2^30).  One workgroup per user.
+// at most 2^30).  One workgroup per (user, 256-token chunk).
 // ============================================================================================
 __global__ __launch_bounds__(256) void time_stats_kernel(const int32_t* __restrict__ offsets,
                                                         const int64_t* __restrict__ ts,
@@ -113,7 +113,9 @@ __global__ __launch_bounds__(256) void time_stats_kernel(const int32_t* __restri
   const int64_t s = offsets[b];
   const int n = offsets[b + 1] - offsets[b];
   const int lane = threadIdx.x & 63, l32 = lane & 31;
-  for (int j = threadIdx.x; j < ((n + 63) & ~63); j += 256) {
+  const int j = 256 * (int)blockIdx.y + (int)threadIdx.x;
+  if (256 * (int)blockIdx.y >= n) return;
+  {
     const bool valid = j < n;
     const int64_t t = valid ? ts[s + j] : 0;
     int64_t mn = valid ? t : kTMax, mx = valid ? t : kTMin;
@@ -795,10 +797,12 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
 int attn_block_rows_bf16(int d) { return d == 64 ? kBR : 0; }
 int attn_block_rows_f32(int d) { return (d == 32 || d == 64) ? kBRf : 0; }
 
-hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts, TimeStat* stats,
-                             int32_t* rel, hipStream_t stream) {
-  if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(time_stats_kernel, dim3(B), dim3(256), 0, stream, offsets, ts, stats, rel);
+hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts,
+                             int32_t max_seqlen, TimeStat* stats, int32_t* rel,
+                             hipStream_t stream) {
+  if (B <= 0 || max_seqlen <= 0) return hipSuccess;
+  hipLaunchKernelGGL(time_stats_kernel, dim3(B, (max_seqlen + 255) / 256), dim3(256), 0, stream,
+                     offsets, ts, stats, rel);
   return hipGetLastError();
 }
 

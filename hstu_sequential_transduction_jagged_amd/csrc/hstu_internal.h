@@ -100,8 +100,9 @@ __device__ __forceinline__ float default_alibi_slope(int h, int H) {
 hipError_t launch_schedule(const int32_t* offsets, int32_t B, int32_t H, int32_t block_rows,
                            int32_t max_tiles, int32_t* work_count, WorkItem* work,
                            hipStream_t stream);
-hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts, TimeStat* stats,
-                             int32_t* rel, hipStream_t stream);
+hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts,
+                             int32_t max_seqlen, TimeStat* stats, int32_t* rel,
+                             hipStream_t stream);
 hipError_t launch_tile_class(int32_t B, const int32_t* offsets, const TimeStat* stats,
                              int32_t max_blocks, int32_t num_pos, int32_t num_time,
                              uint32_t* tclass, hipStream_t stream);
