@@ -8,7 +8,8 @@ module only marshals numpy arrays into it and adds the two pieces that are a
 single line of numpy (the embedding sum and the layer stack loop).
 
 Sources, by page title and section:
-  "Actions Speak Louder than Words" reading notes, §3.1 eqs. (1)-(3), §3.2;
+  "Actions Speak Louder than Words" reading notes, §3.1 eqs. (1)-(3), §3.2,
+  §3.6 (M-FALCON candidate scoring);
   "4.4 推荐模型的 Scaling", section "HSTU 层" and the toy HSTULayer ("代码");
   GenRank article (joto.ai), "(1) item-action组织" and "(2) 位置 & 时间偏差".
 """
@@ -56,6 +57,10 @@ def _L():
                                                P, P, i32, i64, P, i32, i64, P, f64, f64, i64, P, P,
                                                P]
         _lib.oracle_attention_rows.restype = None
+        _lib.oracle_attention_candidates.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, i32,
+                                                     P, P, P, i32, i64, P, i32, i64, P, f64, f64,
+                                                     P]
+        _lib.oracle_attention_candidates.restype = None
         _lib.oracle_layer.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, P, P, i32, P,
                                       P, i32, i64, P, i32, i64, P, f64, i32, P, P, P]
         _lib.oracle_layer.restype = None
@@ -152,6 +157,31 @@ def attention_rows(offsets, q, k, v, bias: Bias, alpha: float, tokens, heads,
                                _ptr(v), H * dv, *bias.args(), float(alpha), float(out_scale), R,
                                _ptr(tok), _ptr(hd), _ptr(out))
     return out
+
+
+def attention_candidates(hist_offsets, cand_offsets, q_c, k_c, v_c, k_h, v_h, bias: Bias,
+                         cand_ts, alpha: float, out_scale: float = 1.0):
+    """Candidate scoring over a user history ("Actions Speak Louder than Words" §3.6, M-FALCON;
+    GenRank article part (2): candidates of one request share one position): candidate c of
+    user b sits at position n_b and attends to the whole history and to itself only.
+    q_c, k_c, v_c: [Tc, H, d]; k_h, v_h: [Th, H, d]; bias.timestamps are the history's and
+    cand_ts the candidates'.  Returns [Tc, H, dv] in float64."""
+    hist_offsets = np.ascontiguousarray(hist_offsets, np.int64)
+    cand_offsets = np.ascontiguousarray(cand_offsets, np.int64)
+    B = len(cand_offsets) - 1
+    Tc, H, dqk = q_c.shape
+    dv = v_c.shape[2]
+    q_c, k_c, v_c = _f64(q_c), _f64(k_c), _f64(v_c)
+    k_h = _f64(k_h).reshape(-1, H, dqk)
+    v_h = _f64(v_h).reshape(-1, H, dv)
+    cts = np.ascontiguousarray(cand_ts if cand_ts is not None else np.zeros(Tc), np.int64)
+    o = np.zeros((Tc, H, dv), np.float64)
+    a = bias.args()
+    _L().oracle_attention_candidates(B, H, dqk, dv, _ptr(hist_offsets), _ptr(cand_offsets),
+                                     _ptr(q_c), _ptr(k_c), _ptr(v_c), _ptr(k_h), _ptr(v_h), a[0],
+                                     a[1], _ptr(cts), *a[2:], float(alpha), float(out_scale),
+                                     _ptr(o))
+    return o
 
 
 def layer(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float, H: int, dqk: int,

@@ -147,6 +147,58 @@ void oracle_attention_rows(int32_t B, int32_t H, int32_t dqk, int32_t dv, const 
   }
 }
 
+/* Candidate scoring over a user history [AS §3.6 M-FALCON; GenRank part (2): the candidates of
+ * one request share one position].  User b: history rows [hist_off[b], hist_off[b+1]) of
+ * k_h, v_h with timestamps ts_h, positions 0 .. n_b - 1; candidate rows [cand_off[b],
+ * cand_off[b+1]) of q_c, k_c, v_c with timestamps ts_c, every candidate at position n_b.
+ * Candidate c attends to the whole history and to itself, to no other candidate:
+ *   O[c] = out_scale * ( sum_{j < n_b} SiLU(alpha <q_c,k_j> + rab(n_b - j, t_c - t_j)) v_j
+ *                        + SiLU(alpha <q_c,k_c> + rab(0, 0)) v_c ).
+ * o is [Tc, H, dv]. */
+static double cand_bias(const oracle_bias* bs, int h, int64_t pos_delta, int64_t dt) {
+  if (bs->kind == ORACLE_BIAS_RAB_PT) {
+    int32_t pb = oracle_pos_bucket(pos_delta, bs->num_pos);
+    int32_t tb = oracle_time_bucket(dt, bs->num_time);
+    return bs->w_pos[h * bs->head_stride_pos + pb] + bs->w_time[h * bs->head_stride_time + tb];
+  }
+  if (bs->kind == ORACLE_BIAS_ALIBI) return -bs->slopes[h] * (double)pos_delta;
+  return 0.0;
+}
+
+void oracle_attention_candidates(int32_t B, int32_t H, int32_t dqk, int32_t dv,
+                                 const int64_t* hist_off, const int64_t* cand_off,
+                                 const double* q_c, const double* k_c, const double* v_c,
+                                 const double* k_h, const double* v_h, int32_t bias_kind,
+                                 const int64_t* ts_h, const int64_t* ts_c, const double* w_pos,
+                                 int32_t num_pos, int64_t head_stride_pos, const double* w_time,
+                                 int32_t num_time, int64_t head_stride_time,
+                                 const double* slopes, double alpha, double out_scale,
+                                 double* o) {
+  oracle_bias bs = {bias_kind, ts_h, w_pos, w_time, num_pos, num_time,
+                    head_stride_pos, head_stride_time, slopes};
+  int64_t n_items = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t it = 0; it < n_items; it++) {
+    int32_t b = (int32_t)(it / H), h = (int32_t)(it % H);
+    int64_t hb = hist_off[b], n = hist_off[b + 1] - hist_off[b];
+    for (int64_t c = cand_off[b]; c < cand_off[b + 1]; c++) {
+      const double* qi = q_c + (c * H + h) * (int64_t)dqk;
+      double* out = o + (c * H + h) * (int64_t)dv;
+      for (int e = 0; e < dv; e++) out[e] = 0.0;
+      for (int64_t j = 0; j <= n; j++) {  /* j == n: the candidate itself */
+        const double* kj = j < n ? k_h + ((hb + j) * H + h) * (int64_t)dqk : k_c + (c * H + h) * (int64_t)dqk;
+        const double* vj = j < n ? v_h + ((hb + j) * H + h) * (int64_t)dv : v_c + (c * H + h) * (int64_t)dv;
+        double s = 0.0;
+        for (int e = 0; e < dqk; e++) s += qi[e] * kj[e];
+        int64_t dt = bias_kind == ORACLE_BIAS_RAB_PT ? ts_c[c] - (j < n ? ts_h[hb + j] : ts_c[c]) : 0;
+        double a = silu(alpha * s + cand_bias(&bs, h, n - j, dt));
+        for (int e = 0; e < dv; e++) out[e] += a * vj[e];
+      }
+      for (int e = 0; e < dv; e++) out[e] *= out_scale;
+    }
+  }
+}
+
 /* One HSTU layer [AS §3.1 eqs. (1)-(3)]:
  *   Z = SiLU(X W1^T + b1);  U | V | Q | K = column blocks of Z (widths H*dv, H*dv,
  *       H*dqk, H*dqk; head h owns columns [h*d, (h+1)*d) of each block);
