@@ -145,22 +145,83 @@ def bench_stack8(args, dev):
         flush=True)
 
 
+def bench_mfalcon(args, dev):
+    """Candidate scoring over cached histories (M-FALCON): 16 users with the attention
+    benchmark's history lengths, 1024 candidates each, H=8, d=64, position / time bias; one
+    step = one call scoring every candidate of every user against its history K / V."""
+    import numpy as np
+    import torch
+    from hstu_sequential_transduction_jagged_amd import binding, synth
+    inp = synth.mfalcon()
+    bf = torch.bfloat16
+    t = lambda a, d=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev, d) if d else \
+        torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    qc, kc, vc, kh, vh = (t(a, bf) for a in (inp.qc, inp.kc, inp.vc, inp.kh, inp.vh))
+    ho, co = t(inp.hist_offsets.astype(np.int32)), t(inp.cand_offsets.astype(np.int32))
+    ts_h, ts_c = t(inp.ts_h), t(inp.ts_c)
+    bias = binding.make_bias(binding.BIAS_RAB_PT, ts_h, t(inp.bias.w_pos), t(inp.bias.w_time))
+    out = torch.empty_like(qc)
+    ws = torch.empty(binding.candidates_workspace_bytes(inp.B, inp.H, inp.max_hist, inp.Th, inp.Tc),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.hstu_attn_candidates_fwd(qc, kc, vc, co, inp.max_cand, kh, vh, ho, inp.max_hist,
+                                         bias, ts_c, inp.alpha, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    kms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    k_avg = sum(kms) / len(kms) * 1e-3
+    hist = np.diff(inp.hist_offsets.astype(np.int64))
+    cand = np.diff(inp.cand_offsets.astype(np.int64))
+    flops = float(sum(int(m) * inp.H * (int(n) + 1) * 2 * 2 * inp.d for n, m in zip(hist, cand)))
+    tf = flops / k_avg / 1e12
+    print(json.dumps({
+        "metric": "M-FALCON candidate scoring TFLOP/s + candidates/s on 1 MI355X",
+        "value": round(flops / step_s / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mfalcon", "B": inp.B, "H": inp.H, "d": inp.d,
+                   "candidates_per_user": int(cand.max()), "hist_tokens": int(inp.Th),
+                   "max_hist": int(inp.max_hist), "bias": "rab_pt P=256 NT=32",
+                   "alpha": inp.alpha, "seed": inp.seed},
+        "candidates_per_s": round(inp.Tc / step_s, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "attn_cand_bf16_kernel",
+                     "kernel_ms_p10_p50_p90": [round(kms[int(f * (len(kms) - 1))], 4)
+                                               for f in (0.1, 0.5, 0.9)]}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8"],
-                    help="attn_long (the headline attention batch) or stack8 (the 8-layer HSTU "
-                         "stack forward: f1 GEMM + SiLU, attention, LayerNorm-gate-f2, residual)")
+    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8", "mfalcon"],
+                    help="attn_long (the headline attention batch), stack8 (the 8-layer HSTU "
+                         "stack forward: f1 GEMM + SiLU, attention, LayerNorm-gate-f2, residual) "
+                         "or mfalcon (1024 candidates per user scored over cached histories)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the HBM byte counters against a known traffic)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the attention shards by user with no communication; see the design notes)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the attention shards by user with no communication between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -186,6 +247,9 @@ def main():
         return
     if args.workload == "stack8":
         bench_stack8(args, dev)
+        return
+    if args.workload == "mfalcon":
+        bench_mfalcon(args, dev)
         return
     inp = synth.attn_long()
     lengths = np.diff(inp.offsets.astype(np.int64))

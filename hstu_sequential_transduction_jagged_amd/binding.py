@@ -46,6 +46,11 @@ SIGNATURES = {
                               _P]),
     "hstu_layer_workspace_offsets": (None, [_i64, _i32, _i32, _i32, ctypes.POINTER(_sz),
                                             ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "hstu_attn_candidates_fwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i32,
+                                        _i64, _P, _i64, _P, _i64, _P, _i64, _P, _i64, _P, _i64,
+                                        ctypes.POINTER(HstuBias), _P, _f32, _f32, _P, _P, _sz,
+                                        _P]),
+    "hstu_attn_candidates_workspace_bytes": (_sz, [_i32, _i32, _i32, _i64, _i64]),
     "hstu_embed_sum_fwd": (_i32, [_i64, _i32, _P, _i64, _P, _i32, _P, _P, _P, _P]),
     "hstu_validate_offsets": (_i32, [_i32, _P, _i64, _i32, _P, _P]),
     "hstu_debug_buckets": (_i32, [_i32, _P, _P, _i32, _i32, _i64, _P, _P, _P, _P, _P]),
@@ -140,6 +145,8 @@ def attn_block_rows(dtype_code, d):
 
 def _rows(t: torch.Tensor, name: str):
     """[T, H, d] tensor (possibly a strided view) -> (row stride, H, d)."""
+    if t.dim() == 3 and t.numel() == 0:
+        return t.shape[1] * t.shape[2], t.shape[1], t.shape[2]
     if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
         raise HstuError("%s must be [T, H, d] with contiguous heads" % name)
     return t.stride(0), t.shape[1], t.shape[2]
@@ -238,6 +245,49 @@ def hstu_layer_fwd(x, offsets, max_seqlen, w1, b1, ln_gamma, ln_beta, w2, b2, H,
                               _ptr(out), _ptr(workspace), workspace.numel(), _stream(x.device))
     _check("hstu_layer_fwd", st)
     return out
+
+
+def hstu_attn_candidates_fwd(q_cand, k_cand, v_cand, cand_offsets, max_cand, k_hist, v_hist,
+                             hist_offsets, max_hist, bias: Optional[HstuBias] = None,
+                             cand_timestamps=None, alpha=1.0, out_scale=1.0, out=None,
+                             workspace=None):
+    """Candidate scoring over a cached history (bf16, d = 64): every candidate of user b sees
+    the user's history and itself.  q/k/v_cand: [Tc, H, 64]; k/v_hist: [Th, H, 64] (row-strided
+    views allowed); offsets int32 [B+1] on the device; bias.timestamps are the history's and
+    cand_timestamps the candidates'.  Returns o [Tc, H, 64]."""
+    if q_cand.dtype != torch.bfloat16:
+        raise HstuError("candidate scoring runs in bf16")
+    qs, H, d = _rows(q_cand, "q_cand")
+    kcs, _, _ = _rows(k_cand, "k_cand")
+    vcs, _, dv = _rows(v_cand, "v_cand")
+    khs, _, _ = _rows(k_hist, "k_hist")
+    vhs, _, _ = _rows(v_hist, "v_hist")
+    Tc = q_cand.shape[0]
+    B = cand_offsets.numel() - 1
+    if hist_offsets.numel() != B + 1:
+        raise HstuError("hist_offsets and cand_offsets must have the same length")
+    if cand_offsets.dtype != torch.int32 or hist_offsets.dtype != torch.int32:
+        raise HstuError("offsets must be int32")
+    if out is None:
+        out = torch.empty((Tc, H, dv), dtype=q_cand.dtype, device=q_cand.device)
+    bias = bias if bias is not None else make_bias(BIAS_NONE)
+    Th = k_hist.shape[0]
+    need = candidates_workspace_bytes(B, H, max_hist, Th, Tc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q_cand.device)
+    st = lib().hstu_attn_candidates_fwd(
+        DTYPE_BF16, B, H, d, dv, _ptr(hist_offsets), int(max_hist), Th, _ptr(cand_offsets),
+        int(max_cand), Tc, _ptr(q_cand), qs, _ptr(k_cand), kcs, _ptr(v_cand), vcs, _ptr(k_hist),
+        khs, _ptr(v_hist), vhs, ctypes.byref(bias), _ptr(cand_timestamps), float(alpha),
+        float(out_scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q_cand.device))
+    _check("hstu_attn_candidates_fwd", st)
+    return out
+
+
+def candidates_workspace_bytes(B, H, max_hist, total_hist, total_cand):
+    return int(lib().hstu_attn_candidates_workspace_bytes(int(B), int(H), int(max_hist),
+                                                          int(total_hist), int(total_cand)))
 
 
 def hstu_embed_sum_fwd(item_table, action_table, item_ids, action_ids, out=None):

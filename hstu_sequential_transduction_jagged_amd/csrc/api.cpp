@@ -356,6 +356,69 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
                    "f2 launch");
 }
 
+size_t hstu_attn_candidates_workspace_bytes(int32_t B, int32_t H, int32_t max_hist,
+                                            int64_t total_hist, int64_t total_cand) {
+  if (B < 0 || H < 0 || max_hist < 0 || total_hist < 0 || total_cand < 0) return 0;
+  return cand_workspace_bytes(B, max_hist, total_hist, total_cand, H);
+}
+
+hstu_status hstu_attn_candidates_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                                     const int32_t* hist_offsets, int32_t max_hist,
+                                     int64_t total_hist, const int32_t* cand_offsets,
+                                     int32_t max_cand, int64_t total_cand, const void* q_cand,
+                                     int64_t q_stride,
+                                     const void* k_cand, int64_t k_cand_stride,
+                                     const void* v_cand, int64_t v_cand_stride,
+                                     const void* k_hist, int64_t k_hist_stride,
+                                     const void* v_hist, int64_t v_hist_stride,
+                                     const hstu_bias* bias, const int64_t* cand_timestamps,
+                                     float alpha, float out_scale, void* o, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (dt != HSTU_DTYPE_BF16) return fail(HSTU_ERR_UNSUPPORTED, "candidate scoring runs in bf16 only");
+  if (d_qk != 64 || d_v != 64) return fail(HSTU_ERR_UNSUPPORTED, "candidate scoring needs d = 64");
+  if (B < 0 || H < 1 || max_hist < 0 || total_hist < 0 || max_cand < 0 || total_cand < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "bad sizes");
+  BiasArgs ba;
+  hstu_status st = check_bias(bias, H, &ba);
+  if (st != HSTU_OK) return st;
+  if (B == 0 || total_cand == 0 || max_cand == 0) return HSTU_OK;
+  if (!hist_offsets || !cand_offsets || !q_cand || !k_cand || !v_cand || !o)
+    return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  if (max_hist > 0 && (!k_hist || !v_hist)) return fail(HSTU_ERR_INVALID_ARG, "null history K / V");
+  if (ba.kind == 1 && !cand_timestamps)
+    return fail(HSTU_ERR_INVALID_ARG, "rab_pt bias needs candidate timestamps");
+  const int64_t rowlen = (int64_t)H * 64;
+  if (q_stride < rowlen || k_cand_stride < rowlen || v_cand_stride < rowlen ||
+      (max_hist > 0 && (k_hist_stride < rowlen || v_hist_stride < rowlen)))
+    return fail(HSTU_ERR_INVALID_ARG, "row stride smaller than H*d");
+  if (!aligned16(q_cand) || !aligned16(k_cand) || !aligned16(v_cand) || !aligned16(o) ||
+      (max_hist > 0 && (!aligned16(k_hist) || !aligned16(v_hist))) || q_stride % 8 ||
+      k_cand_stride % 8 || v_cand_stride % 8 || k_hist_stride % 8 || v_hist_stride % 8)
+    return fail(HSTU_ERR_INVALID_ARG, "rows must be 16-byte aligned");
+  // the kernel addresses one user's history rows with 32-bit byte offsets
+  const int64_t hs = k_hist_stride > v_hist_stride ? k_hist_stride : v_hist_stride;
+  if ((int64_t)(max_hist + 64) * hs * 2 >= ((int64_t)1 << 31))
+    return fail(HSTU_ERR_UNSUPPORTED, "max_hist x row stride reaches 2 GiB per user");
+  const size_t need = cand_workspace_bytes(B, max_hist, total_hist, total_cand, H);
+  if ((!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)))
+    return fail(HSTU_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  CandLaunch c{};
+  c.B = B; c.H = H; c.max_hist = max_hist; c.max_cand = max_cand;
+  c.total_hist = total_hist;
+  c.total_cand = total_cand;
+  c.workspace = workspace;
+  c.hist_offsets = hist_offsets; c.cand_offsets = cand_offsets;
+  c.q = (const bf16*)q_cand; c.kc = (const bf16*)k_cand; c.vc = (const bf16*)v_cand;
+  c.kh = (const bf16*)k_hist; c.vh = (const bf16*)v_hist;
+  c.q_stride = q_stride; c.kc_stride = k_cand_stride; c.vc_stride = v_cand_stride;
+  c.kh_stride = k_hist_stride; c.vh_stride = v_hist_stride;
+  c.o = (bf16*)o; c.bias = ba; c.cand_ts = cand_timestamps;
+  c.alpha = alpha; c.out_scale = out_scale;
+  return check_hip(launch_attn_candidates_bf16(c, stream), "candidate attention launch");
+}
+
 hstu_status hstu_embed_sum_fwd(int64_t total_tokens, int32_t dim, const void* item_table,
                                int64_t num_items, const void* action_table, int32_t num_actions,
                                const int32_t* item_ids, const int32_t* action_ids, void* x,

@@ -41,43 +41,6 @@ namespace {
 // 8*(r/4) + 4*hf + r%4 of the MFMA output layout.
 __device__ __forceinline__ int acc_key(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
 
-__device__ __forceinline__ int64_t shfl_xor_i64(int64_t v, int m) {
-  int lo = __shfl_xor((int)(uint32_t)(uint64_t)v, m, 64);
-  int hi = __shfl_xor((int)(uint32_t)((uint64_t)v >> 32), m, 64);
-  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
-}
-
-// min / max over each 32-lane half of the wave.
-__device__ __forceinline__ void half_minmax(int64_t& mn, int64_t& mx) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) {
-    int64_t a = shfl_xor_i64(mn, m), b = shfl_xor_i64(mx, m);
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-  }
-}
-
-// Values the whole wave holds in common, moved to scalar registers.
-__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ float uniform_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, v)));
-}
-
-// w(y) = y - y^2 (P0 + P1 y^2 + P2 y^4) on |y| <= kPolyRange (near-minimax fit of the
-// relative error of 1/(1+2^y); the fitting script sits beside this file).
-constexpr float kPolyRange = 2.0f;
-constexpr float kP0 = 0.3463683490f, kP1 = -0.0135027335f, kP2 = 0.0004785898f;
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
 // Cross-lane moves inside a row of 16 lanes (DPP, no LDS round trip).
 
 // Sum over each aligned group of 8 lanes, in all 8 lanes.
@@ -95,9 +58,6 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   auto at = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
   return fmaxf(fmaxf(at(0), at(16)), fmaxf(at(32), at(48)));
 }
-
-constexpr int64_t kTMax = 0x7fffffffffffffffLL;
-constexpr int64_t kTMin = -kTMax - 1;
 
 // ============================================================================================
 // Timestamp statistics: for every 32-token block of a user (blocks start at the user's first
@@ -179,12 +139,6 @@ constexpr int kBR = kWaves * kQW;
 constexpr int kKB = 64;
 constexpr int kD = 64;
 
-// Largest half-width D of a 32x32 tile's y range (y = c + delta, |delta| <= D) for which the
-// second-order Taylor expansion of w around the tile's constant bias c is used: its remainder
-// is at most max|w'''| D^3 / 6 = 0.0521 D^3 <= 8.4e-5 D, below 2^-13 of the tile's largest
-// |w| (which is at least 0.96 D for D this small).
-constexpr float kTaylorD = 0.04f;
-
 // LDS rows of 64 bf16 are padded to 144 bytes: 16 lanes reading the same 16-byte column of 16
 // consecutive rows then hit 16 distinct groups of 4 banks (row * 36 words mod 64 is a
 // permutation of the multiples of 4), and every operand read is one base address per lane
@@ -202,23 +156,6 @@ struct __attribute__((aligned(16))) SmemBf16 {
   float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
   float wtime_lz[32];           // wtime[min(31 - lz, NT - 1)]: time bias by leading zeros of dt + 1
 };
-
-// w(y) = 2y/(1+2^y) and its first two derivatives at c, as the coefficients of the expansion
-// in the raw score s (y = c + cq s): w ~ a0 + a1 s + a2 s^2.  No overflow for any finite c:
-// s = 1/(1+2^c) and o = 1 - s come from 2^-|c|.
-__device__ __forceinline__ void w_taylor_coeffs(float c, float cq, float& a0, float& a1, float& a2) {
-  const float e = exp2f(-fabsf(c));
-  const float inv = 1.0f / (1.0f + e);
-  const float s = c >= 0.f ? e * inv : inv;
-  const float o = c >= 0.f ? inv : e * inv;
-  const float g = s * o;
-  const float w0 = 2.0f * c * s;
-  const float w1 = 2.0f * s - 2.0f * kLn2 * c * g;
-  const float w2 = -4.0f * kLn2 * g + 2.0f * kLn2 * kLn2 * c * g * (o - s);
-  a0 = w0;
-  a1 = w1 * cq;
-  a2 = 0.5f * w2 * cq * cq;
-}
 
 template <int KIND, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) {

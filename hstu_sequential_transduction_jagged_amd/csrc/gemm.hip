@@ -48,21 +48,6 @@ __device__ __forceinline__ int f1_off(int row, int chunk) {
   return row * kF1K + ((chunk ^ ((row >> 2) & 3)) << 3);
 }
 
-// s_waitcnt bounding only the vector-memory counter (loads and LDS transfers still in flight)
-template <int C>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((C & 15) | (7 << 4) | (15 << 8) | ((C >> 4) << 14));
-}
-// workgroup barrier with no compiler reordering of memory operations across it (the LDS
-// transfers it publishes were waited for explicitly)
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // NK: K / 32 when known at compile time (the slice loop is then straight-line code, which keeps
 // the compiler's own waits on the transfers exact), 0 for any K

@@ -20,6 +20,24 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// s_waitcnt bounding only the vector-memory counter (loads and LDS transfers still in flight)
+template <int C>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((C & 15) | (7 << 4) | (15 << 8) | ((C >> 4) << 14));
+}
+
+// workgroup barrier with no compiler reordering of memory operations across it (the LDS
+// transfers it publishes were waited for explicitly)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// destination of a direct global -> LDS transfer (buffer load with the LDS bit)
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
 // Lane moves within a row of 16 lanes (DPP): the value of another lane of the same row.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -29,6 +47,71 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within each 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within each 16 lanes
+
+// ---- wave-wide reductions and SiLU evaluation in base-2 units (attention kernels) ----
+
+__device__ __forceinline__ int64_t shfl_xor_i64(int64_t v, int m) {
+  int lo = __shfl_xor((int)(uint32_t)(uint64_t)v, m, 64);
+  int hi = __shfl_xor((int)(uint32_t)((uint64_t)v >> 32), m, 64);
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
+// min / max over each 32-lane half of the wave.
+__device__ __forceinline__ void half_minmax(int64_t& mn, int64_t& mx) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    int64_t a = shfl_xor_i64(mn, m), b = shfl_xor_i64(mx, m);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+}
+
+// Values the whole wave holds in common, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, v)));
+}
+
+// w(y) = y - y^2 (P0 + P1 y^2 + P2 y^4) on |y| <= kPolyRange (near-minimax fit of the
+// relative error of 1/(1+2^y); the fitting script sits beside the attention kernel).
+constexpr float kPolyRange = 2.0f;
+constexpr float kP0 = 0.3463683490f, kP1 = -0.0135027335f, kP2 = 0.0004785898f;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+constexpr int64_t kTMax = 0x7fffffffffffffffLL;
+constexpr int64_t kTMin = -kTMax - 1;
+
+// Largest half-width D of a 32x32 tile's y range (y = c + delta, |delta| <= D) for which the
+// second-order Taylor expansion of w around the tile's constant bias c is used: its remainder
+// is at most max|w'''| D^3 / 6 = 0.0521 D^3 <= 8.4e-5 D, below 2^-13 of the tile's largest
+// |w| (which is at least 0.96 D for D this small).
+constexpr float kTaylorD = 0.04f;
+
+// w(y) = 2y/(1+2^y) and its first two derivatives at c, as the coefficients of the expansion
+// in the raw score s (y = c + cq s): w ~ a0 + a1 s + a2 s^2.  No overflow for any finite c:
+// s = 1/(1+2^c) and o = 1 - s come from 2^-|c|.
+__device__ __forceinline__ void w_taylor_coeffs(float c, float cq, float& a0, float& a1, float& a2) {
+  const float e = exp2f(-fabsf(c));
+  const float inv = 1.0f / (1.0f + e);
+  const float s = c >= 0.f ? e * inv : inv;
+  const float o = c >= 0.f ? inv : e * inv;
+  const float g = s * o;
+  const float w0 = 2.0f * c * s;
+  const float w1 = 2.0f * s - 2.0f * kLn2 * c * g;
+  const float w2 = -4.0f * kLn2 * g + 2.0f * kLn2 * kLn2 * c * g * (o - s);
+  a0 = w0;
+  a1 = w1 * cq;
+  a2 = 0.5f * w2 * cq * cq;
+}
 
 // One unit of attention work: query tile `qt` of user `b`, head `h`.
 struct WorkItem {
@@ -117,6 +200,24 @@ hipError_t launch_ln_gate_f2(const bf16* o, const f32x2* ostats, const bf16* u,
                              int64_t u_stride, const float* gamma, const float* beta, float eps,
                              const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,
                              int32_t D, int32_t H, int32_t dv, hipStream_t stream);
+// Candidate scoring over a cached history (candidates.hip).
+struct CandLaunch {
+  int32_t B, H, max_hist, max_cand;
+  int64_t total_hist, total_cand;
+  void* workspace;         // cand_workspace_bytes(B, max_hist, total_hist, total_cand, H) bytes
+  const int32_t* hist_offsets;
+  const int32_t* cand_offsets;
+  const bf16 *q, *kc, *vc, *kh, *vh;
+  int64_t q_stride, kc_stride, vc_stride, kh_stride, vh_stride;
+  bf16* o;
+  BiasArgs bias;           // bias.ts: history timestamps
+  const int64_t* cand_ts;  // candidate timestamps
+  float alpha, out_scale;
+};
+hipError_t launch_attn_candidates_bf16(const CandLaunch& c, hipStream_t stream);
+size_t cand_workspace_bytes(int32_t B, int32_t max_hist, int64_t total_hist, int64_t total_cand,
+                            int32_t H);
+
 hipError_t launch_embed_sum(int64_t T, int32_t dim, const bf16* item, int64_t num_items,
                             const bf16* action, int32_t num_actions, const int32_t* ids,
                             const int32_t* aids, bf16* x, hipStream_t stream);

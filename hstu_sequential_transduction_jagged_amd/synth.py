@@ -14,6 +14,8 @@ Workloads (each a function below):
                n ~ U{512..4096}, D=512, H=8, d=64, item ids Zipf(1.1) over 1e6
   stack8       bf16 8-layer stack: D=512, H=8, d=64, B=128,
                n0 = clip(Zipf(1.2), 1, 4096), stochastic length to 1024 w.p. 0.5
+  mfalcon      bf16 candidate scoring: attn_long's users and histories, 1024 candidates
+               per user at the request time (last history event + Exp(mean 3600 s))
 
 Value recipe: Q, K, V, X ~ N(0, 1); weights Xavier-uniform; bias tables
 ~ N(0, 0.02); timestamps = per-user base + floor(cumsum(Exp(mean 3600 s)));
@@ -306,10 +308,88 @@ def stack8(seed=1004, B=128, n_layers=8, hi=4096, cap=1024, randomize_affine=Fal
                       randomize_affine=randomize_affine, **kw)
 
 
+@dataclass
+class CandInputs:
+    """Candidate scoring over a cached history: user b's history rows
+    [hist_offsets[b], hist_offsets[b+1]) of kh, vh, ts_h; its candidates' rows
+    [cand_offsets[b], cand_offsets[b+1]) of qc, kc, vc, ts_c."""
+    name: str
+    seed: int
+    dtype: str
+    B: int
+    H: int
+    d: int
+    hist_offsets: np.ndarray   # int32 [B+1]
+    cand_offsets: np.ndarray   # int32 [B+1]
+    max_hist: int
+    max_cand: int
+    ts_h: np.ndarray           # int64 [Th]
+    ts_c: np.ndarray           # int64 [Tc]
+    qc: np.ndarray             # float32 [Tc, H, d] (exact in dtype)
+    kc: np.ndarray
+    vc: np.ndarray
+    kh: np.ndarray             # float32 [Th, H, d]
+    vh: np.ndarray
+    bias: BiasSpec
+    alpha: float
+    out_scale: float = 1.0
+
+    @property
+    def Th(self):
+        return int(self.hist_offsets[-1])
+
+    @property
+    def Tc(self):
+        return int(self.cand_offsets[-1])
+
+
+def make_candidates(name, seed, dtype, hist_lengths, cand_counts, H, d, alpha,
+                    bias_kind=BIAS_RAB_PT, P=256, NT=32, table_std=0.02, per_head_tables=False,
+                    rng=None, jitter=0, out_scale=1.0):
+    """Histories as in make_attn; each user's candidates carry the request time (last
+    history event + Exp(mean 3600 s)) plus U{0..jitter} seconds each."""
+    rng = rng if rng is not None else np.random.default_rng(seed)
+    hist_lengths = np.asarray(hist_lengths, dtype=np.int64)
+    cand_counts = np.asarray(cand_counts, dtype=np.int64)
+    ho = offsets_from_lengths(hist_lengths)
+    co = offsets_from_lengths(cand_counts)
+    Th, Tc = int(ho[-1]), int(co[-1])
+    ts_h = _timestamps(rng, hist_lengths)
+    ts_c = np.zeros(Tc, np.int64)
+    for b in range(len(hist_lengths)):
+        last = int(ts_h[ho[b + 1] - 1]) if hist_lengths[b] else 1_600_000_000
+        req = last + int(rng.exponential(3600.0))
+        ts_c[co[b]:co[b + 1]] = req + rng.integers(0, jitter + 1, size=int(cand_counts[b]))
+    kh = _store(rng.standard_normal((Th, H, d), dtype=np.float32), dtype)
+    vh = _store(rng.standard_normal((Th, H, d), dtype=np.float32), dtype)
+    qc = _store(rng.standard_normal((Tc, H, d), dtype=np.float32), dtype)
+    kc = _store(rng.standard_normal((Tc, H, d), dtype=np.float32), dtype)
+    vc = _store(rng.standard_normal((Tc, H, d), dtype=np.float32), dtype)
+    bias = BiasSpec(kind=bias_kind)
+    if bias_kind == BIAS_RAB_PT:
+        bias.w_pos, bias.w_time = _tables(rng, P, NT, table_std, H if per_head_tables else None)
+    mh = int(hist_lengths.max()) if len(hist_lengths) else 0
+    mc = int(cand_counts.max()) if len(cand_counts) else 0
+    return CandInputs(name, seed, dtype, len(hist_lengths), H, d, ho, co, mh, mc, ts_h, ts_c,
+                      qc, kc, vc, kh, vh, bias, float(alpha), out_scale)
+
+
+def mfalcon(seed=1005, B=16, n_cand=1024, lo=256, hi=8192, **kw):
+    """bf16 candidate scoring: B=16 users with attn_long's history lengths (lognormal,
+    median 2048, clipped to [256, 8192]), 1024 candidates each, H=8, d=64,
+    alpha = 1/8192, 256 position / 32 time buckets."""
+    rng = np.random.default_rng(seed)
+    lengths = lognormal_lengths(rng, B, lo=lo, hi=hi)
+    kw.setdefault("alpha", 1.0 / 8192)
+    return make_candidates("mfalcon", seed, "bf16", lengths, np.full(B, n_cand), H=8, d=64,
+                           P=256, NT=32, rng=rng, **kw)
+
+
 WORKLOADS = {
     "attn_small": attn_small,
     "layer_small": layer_small,
     "attn_long": attn_long,
     "genrank": genrank,
     "stack8": stack8,
+    "mfalcon": mfalcon,
 }

@@ -156,6 +156,51 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
 void hstu_layer_workspace_offsets(int64_t total_tokens, int32_t H, int32_t d_qk, int32_t d_v,
                                   size_t* z_offset, size_t* o_offset, size_t* attn_offset);
 
+/* Candidate scoring over a cached user history (M-FALCON, "Actions Speak Louder than Words"
+ * reading notes §3.6; candidates of one request share one position, GenRank article part (2)).
+ * User b has n_b history tokens (rows [hist_offsets[b], hist_offsets[b+1]) of k_hist, v_hist and
+ * the bias timestamps) and m_b candidates (rows [cand_offsets[b], cand_offsets[b+1]) of q_cand,
+ * k_cand, v_cand and cand_timestamps).  Every candidate c sits at position n_b and sees the
+ * whole history and itself, no other candidate:
+ *   O[c] = out_scale * ( sum_{j < n_b} SiLU(alpha <q_c, k_j> + rab(n_b - j, t_c - t_j)) v_j
+ *                        + SiLU(alpha <q_c, k_c> + rab(0, 0)) v_c )
+ * which is the row eq. (2) gives c appended alone after the history.  The history's K, V are
+ * the cache: score candidates in micro-batches by calling once per batch.
+ *  dt        HSTU_DTYPE_BF16 only; d_qk = d_v = 64
+ *  hist_offsets, cand_offsets  device int32 [B + 1] (jagged, as for the attention); every
+ *            n_b <= max_hist and m_b <= max_cand; total_hist = hist_offsets[B],
+ *            total_cand = cand_offsets[B]
+ *  q_cand, k_cand, v_cand  device bf16 [total_cand, H, 64] rows with the given strides
+ *  k_hist, v_hist          device bf16 [total_hist, H, 64] rows with the given strides
+ *  bias      as for hstu_attn_fwd; bias->timestamps are the history's [total_hist]
+ *  cand_timestamps  device int64 [total_cand] (RAB_PT only, else may be NULL)
+ *  o         device bf16 [total_cand, H, 64]
+ *  workspace device, >= hstu_attn_candidates_workspace_bytes(B, H, max_hist, total_hist,
+ *            total_cand) bytes, 256-byte aligned.  Histories longer than 1024 keys are scored
+ *            in chunks of 1024 whose fp32 sums it holds; they are added in chunk order.  It
+ *            also holds the list of (user, head, chunk) work units and per-32-key timestamp
+ *            extremes of the history (position + time bias).  Contents need no initialisation
+ *            and are scratch after the call; calls sharing a workspace must not overlap.
+ * Errors as for hstu_attn_fwd. */
+hstu_status hstu_attn_candidates_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                                     const int32_t* hist_offsets, int32_t max_hist,
+                                     int64_t total_hist, const int32_t* cand_offsets,
+                                     int32_t max_cand, int64_t total_cand, const void* q_cand,
+                                     int64_t q_stride,
+                                     const void* k_cand, int64_t k_cand_stride,
+                                     const void* v_cand, int64_t v_cand_stride,
+                                     const void* k_hist, int64_t k_hist_stride,
+                                     const void* v_hist, int64_t v_hist_stride,
+                                     const hstu_bias* bias, const int64_t* cand_timestamps,
+                                     float alpha, float out_scale, void* o, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace hstu_attn_candidates_fwd needs: each part rounded up to 256,
+ * 4 x 64 x H x total_cand x ceil(max_hist / 1024) when max_hist > 1024 (else 0),
+ * + 16 x total_hist + 4 x total_hist, + 256 + 4 x B x H x max(ceil(max_hist / 1024), 1). */
+size_t hstu_attn_candidates_workspace_bytes(int32_t B, int32_t H, int32_t max_hist,
+                                            int64_t total_hist, int64_t total_cand);
+
 /* GenRank action-oriented tokens (GenRank article, part (1)): x[t] = item_table[item_ids[t]]
  * + action_table[action_ids[t]], bf16 in and out, fp32 add.  ids are device int32 [T];
  * an id outside [0, num_items) or [0, num_actions) contributes a zero row.  dim % 8 == 0. */

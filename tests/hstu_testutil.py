@@ -104,6 +104,33 @@ def oracle_attn_rows(inp: synth.AttnInputs, tokens, heads):
                                  inp.out_scale)
 
 
+class DevCand:
+    """Device copies of a CandInputs case (bf16)."""
+
+    def __init__(self, inp: synth.CandInputs, device="cuda"):
+        bf = torch.bfloat16
+        self.inp = inp
+        self.qc, self.kc, self.vc = (to_dev(a, bf, device) for a in (inp.qc, inp.kc, inp.vc))
+        self.kh, self.vh = to_dev(inp.kh, bf, device), to_dev(inp.vh, bf, device)
+        self.ho = to_dev(inp.hist_offsets.astype(np.int32), device=device)
+        self.co = to_dev(inp.cand_offsets.astype(np.int32), device=device)
+        self.ts_h = to_dev(inp.ts_h.astype(np.int64), device=device)
+        self.ts_c = to_dev(inp.ts_c.astype(np.int64), device=device)
+        self.bias = device_bias(inp.bias, self.ts_h, device)
+
+    def run(self, **kw):
+        i = self.inp
+        return binding.hstu_attn_candidates_fwd(self.qc, self.kc, self.vc, self.co, i.max_cand,
+                                                self.kh, self.vh, self.ho, i.max_hist, self.bias,
+                                                self.ts_c, i.alpha, i.out_scale, **kw)
+
+
+def oracle_cand(inp: synth.CandInputs):
+    return oracle.attention_candidates(inp.hist_offsets, inp.cand_offsets, inp.qc, inp.kc, inp.vc,
+                                       inp.kh, inp.vh, oracle_bias(inp.bias, inp.ts_h, inp.H),
+                                       inp.ts_c, inp.alpha, inp.out_scale)
+
+
 class DevLayer:
     """Device copies of a LayerInputs case (one or more layers)."""
 

@@ -99,6 +99,25 @@ def test_host_side_errors_need_no_gpu():
     assert L.hstu_layer_fwd(1, 1, 256, 4, 64, 64, None, 8, 8, None, None, None, None, None, 0.0,
                             None, None, None, 1.0, 0, None, None, 0, None) == -1
     assert L.hstu_embed_sum_fwd(4, 12, None, 1, None, 1, None, None, None, None) == -2
+    # candidate scoring: bf16 and d = 64 only; empty work is OK; strides and pointers checked
+    def cand(dt=1, B=1, H=2, d=64, mh=8, mc=4, tc=4, p=None, s=128, s_h=128, ts=None):
+        return L.hstu_attn_candidates_fwd(dt, B, H, d, d, p, mh, 100, p, mc, tc, p, s, p, s, p, s,
+                                          p, s_h, p, s_h, None, ts, 1.0, 1.0, p, None, 0, None)
+    assert cand(dt=0) == -2
+    assert cand(d=32) == -2
+    assert cand(tc=0) == 0 and cand(mc=0) == 0 and cand(B=0) == 0
+    assert cand() == -1
+    assert cand(p=fake, s=64) == -1                        # stride below H * d
+    assert cand(p=ctypes.c_void_p(0x100008)) == -1         # rows not 16-byte aligned
+    assert cand(p=fake, mh=1 << 20, s_h=1 << 12) == -2     # history past 32-bit offsets
+    assert cand(p=fake, s=132) == -1                       # stride leaves rows misaligned
+    assert cand(p=fake) == -3                              # no workspace
+    ws = L.hstu_attn_candidates_workspace_bytes
+    assert ws(3, 2, 1024, 0, 100) == 256 + 256            # unit list header + 6 entries
+    assert ws(3, 2, 1024, 100, 100) == 1792 + 512 + 256 + 256
+    assert ws(1, 2, 1025, 0, 100) == 2 * 100 * 2 * 64 * 4 + 256 + 256
+    assert ws(16, 8, 8192, 37425, 16384) == \
+        8 * 16384 * 8 * 64 * 4 + 599040 + 149760 + 256 + 4096
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

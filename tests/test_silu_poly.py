@@ -1,6 +1,6 @@
-"""The bf16 attention kernel replaces SiLU by an odd polynomial on tiles where a
+"""The bf16 attention kernels replace SiLU by an odd polynomial on tiles where a
 Cauchy-Schwarz bound keeps |y| (y = -log2(e) x) inside a fixed range.  These host checks
-read the constants from the kernel source and bound the approximation error in fp64
+read the constants from the kernels' shared header and bound the approximation error in fp64
 against the exact SiLU; the kernel's parity tests then check the result end to end."""
 import os
 import re
@@ -8,7 +8,7 @@ import re
 import numpy as np
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "hstu_sequential_transduction_jagged_amd", "csrc", "attention.hip")
+                   "hstu_sequential_transduction_jagged_amd", "csrc", "hstu_internal.h")
 
 
 def _constants():
