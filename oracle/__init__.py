@@ -9,7 +9,7 @@ single line of numpy (the embedding sum and the layer stack loop).
 
 Sources, by page title and section:
   "Actions Speak Louder than Words" reading notes, §3.1 eqs. (1)-(3), §3.2,
-  §3.6 (M-FALCON candidate scoring);
+  §3.6 (M-FALCON candidate scoring); the gradients of eq. (2) (backward pass);
   "4.4 推荐模型的 Scaling", section "HSTU 层" and the toy HSTULayer ("代码");
   GenRank article (joto.ai), "(1) item-action组织" and "(2) 位置 & 时间偏差".
 """
@@ -57,6 +57,9 @@ def _L():
                                                P, P, i32, i64, P, i32, i64, P, f64, f64, i64, P, P,
                                                P]
         _lib.oracle_attention_rows.restype = None
+        _lib.oracle_attention_bwd.argtypes = [i32, i32, i32, i32, P, P, P, P, P, i32, P, P, i32,
+                                              i64, P, i32, i64, P, f64, f64, P, P, P, P, P]
+        _lib.oracle_attention_bwd.restype = None
         _lib.oracle_attention_candidates.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, i32,
                                                      P, P, P, i32, i64, P, i32, i64, P, f64, f64,
                                                      P]
@@ -157,6 +160,28 @@ def attention_rows(offsets, q, k, v, bias: Bias, alpha: float, tokens, heads,
                                _ptr(v), H * dv, *bias.args(), float(alpha), float(out_scale), R,
                                _ptr(tok), _ptr(hd), _ptr(out))
     return out
+
+
+def attention_bwd(offsets, q, k, v, dO, bias: Bias, alpha: float, out_scale: float = 1.0):
+    """Gradients of eq. (2) ("Actions Speak Louder than Words" §3.1 eq. (2)) for the upstream
+    gradient dO: returns (dq, dk, dv, dw_pos, dw_time) in float64; the table gradients have
+    the tables' shapes (None without the position + time bias)."""
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    T, H, dqk = q.shape
+    dv = v.shape[2]
+    B = len(offs) - 1
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    rab = bias.kind == BIAS_RAB_PT
+    dwp = np.zeros_like(bias.w_pos) if rab else np.zeros(1)
+    dwt = np.zeros_like(bias.w_time) if rab else np.zeros(1)
+    if T and B:
+        _L().oracle_attention_bwd(B, H, dqk, dv, _ptr(offs), _ptr(q), _ptr(k), _ptr(v), _ptr(dO),
+                                  *bias.args(), float(alpha), float(out_scale), _ptr(dq), _ptr(dk),
+                                  _ptr(dvv), _ptr(dwp), _ptr(dwt))
+    return dq, dk, dvv, (dwp if rab else None), (dwt if rab else None)
 
 
 def attention_candidates(hist_offsets, cand_offsets, q_c, k_c, v_c, k_h, v_h, bias: Bias,

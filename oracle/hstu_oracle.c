@@ -147,6 +147,81 @@ void oracle_attention_rows(int32_t B, int32_t H, int32_t dqk, int32_t dv, const 
   }
 }
 
+/* Gradients of eq. (2) ("Actions Speak Louder than Words" reading notes §3.1 eq. (2), §3.2)
+ * for an upstream gradient dO of O, by the chain rule on each term a_ij v_j of row i:
+ *   x_ij = alpha <q_i, k_j> + rab(i, j),  a_ij = SiLU(x_ij),  SiLU'(x) = s (1 + x (1 - s)),
+ *   s = 1 / (1 + e^-x)   (product rule on x * s(x));
+ *   dV_j += out_scale a_ij dO_i;   g_ij = out_scale <dO_i, v_j> SiLU'(x_ij);
+ *   dQ_i += alpha g_ij k_j;   dK_j += alpha g_ij q_i;
+ *   d w_pos[h][pos bucket(i, j)] += g_ij;   d w_time[h][time bucket(i, j)] += g_ij   (rab_pt).
+ * dq, dk, dv are [T, H, d] contiguous; dw_pos / dw_time have the tables' shapes (head stride
+ * 0 = one table shared by the heads, which then sums over heads).  All outputs are
+ * overwritten. */
+void oracle_attention_bwd(int32_t B, int32_t H, int32_t dqk, int32_t dv, const int64_t* offsets,
+                          const double* q, const double* k, const double* v, const double* dO,
+                          int32_t bias_kind, const int64_t* ts, const double* w_pos,
+                          int32_t num_pos, int64_t head_stride_pos, const double* w_time,
+                          int32_t num_time, int64_t head_stride_time, const double* slopes,
+                          double alpha, double out_scale, double* dq, double* dk, double* dvo,
+                          double* dw_pos, double* dw_time) {
+  oracle_bias bs = {bias_kind, ts, w_pos, w_time, num_pos, num_time,
+                    head_stride_pos, head_stride_time, slopes};
+  const int64_t T = offsets[B];
+  for (int64_t t = 0; t < T * H * (int64_t)dqk; t++) dq[t] = dk[t] = 0.0;
+  for (int64_t t = 0; t < T * H * (int64_t)dv; t++) dvo[t] = 0.0;
+  const int rab = bias_kind == ORACLE_BIAS_RAB_PT;
+  const int64_t np_tab = rab ? (head_stride_pos ? (int64_t)H * head_stride_pos : num_pos) : 0;
+  const int64_t nt_tab = rab ? (head_stride_time ? (int64_t)H * head_stride_time : num_time) : 0;
+  for (int64_t t = 0; t < np_tab; t++) dw_pos[t] = 0.0;
+  for (int64_t t = 0; t < nt_tab; t++) dw_time[t] = 0.0;
+  /* per-(user, head) partial table gradients, summed serially afterwards (no races) */
+  int64_t n_items = (int64_t)B * H;
+  int64_t per = rab ? (int64_t)num_pos + num_time : 0;
+  double* part = per ? (double*)calloc((size_t)(n_items * per), sizeof(double)) : NULL;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t it = 0; it < n_items; it++) {
+    int32_t b = (int32_t)(it / H), h = (int32_t)(it % H);
+    int64_t base = offsets[b], n = offsets[b + 1] - offsets[b];
+    for (int64_t i = 0; i < n; i++) {
+      const double* qi = q + ((base + i) * H + h) * (int64_t)dqk;
+      const double* doi = dO + ((base + i) * H + h) * (int64_t)dv;
+      double* dqi = dq + ((base + i) * H + h) * (int64_t)dqk;
+      for (int64_t j = 0; j <= i; j++) {
+        const double* kj = k + ((base + j) * H + h) * (int64_t)dqk;
+        const double* vj = v + ((base + j) * H + h) * (int64_t)dv;
+        double s = 0.0, dov = 0.0;
+        for (int c = 0; c < dqk; c++) s += qi[c] * kj[c];
+        for (int c = 0; c < dv; c++) dov += doi[c] * vj[c];
+        double x = alpha * s + bias_value(&bs, h, base, i, j);
+        double sg = 1.0 / (1.0 + exp(-x));
+        double a = x * sg;
+        double g = out_scale * dov * sg * (1.0 + x * (1.0 - sg));
+        double* dvj = dvo + ((base + j) * H + h) * (int64_t)dv;
+        double* dkj = dk + ((base + j) * H + h) * (int64_t)dqk;
+        /* dV_j and dK_j are shared by the rows i >= j of this (user, head) only */
+        for (int c = 0; c < dv; c++) dvj[c] += out_scale * a * doi[c];
+        for (int c = 0; c < dqk; c++) {
+          dqi[c] += alpha * g * kj[c];
+          dkj[c] += alpha * g * qi[c];
+        }
+        if (rab) {
+          part[it * per + oracle_pos_bucket(i - j, num_pos)] += g;
+          part[it * per + num_pos + oracle_time_bucket(ts[base + i] - ts[base + j], num_time)] += g;
+        }
+      }
+    }
+  }
+  if (rab) {
+    for (int64_t it = 0; it < n_items; it++) {
+      int32_t h = (int32_t)(it % H);
+      for (int p = 0; p < num_pos; p++) dw_pos[h * head_stride_pos + p] += part[it * per + p];
+      for (int p = 0; p < num_time; p++)
+        dw_time[h * head_stride_time + p] += part[it * per + num_pos + p];
+    }
+    free(part);
+  }
+}
+
 /* Candidate scoring over a user history [AS §3.6 M-FALCON; GenRank part (2): the candidates of
  * one request share one position].  User b: history rows [hist_off[b], hist_off[b+1]) of
  * k_h, v_h with timestamps ts_h, positions 0 .. n_b - 1; candidate rows [cand_off[b],
