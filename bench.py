@@ -145,6 +145,63 @@ def bench_stack8(args, dev):
         flush=True)
 
 
+def bench_attn_bwd(args, dev):
+    """Gradients of the attention on the attn_long batch (dq, dk, dv and the position / time
+    table gradients for a random upstream gradient); one step = one hstu_attn_bwd call."""
+    import numpy as np
+    import torch
+    from hstu_sequential_transduction_jagged_amd import binding, synth
+    inp = synth.attn_long()
+    bf = torch.bfloat16
+    t = lambda a, d=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev, d) if d else \
+        torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, k, v = t(inp.q, bf), t(inp.k, bf), t(inp.v, bf)
+    rng = np.random.default_rng(9)
+    d_o = t(synth.round_bf16(rng.standard_normal(inp.q.shape).astype(np.float32)), bf)
+    offs = t(inp.offsets.astype(np.int32))
+    bias = binding.make_bias(binding.BIAS_RAB_PT, t(inp.ts), t(inp.bias.w_pos), t(inp.bias.w_time))
+    ws = torch.empty(binding.attn_workspace_bytes(inp.B, inp.H, inp.max_seqlen, inp.T),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.hstu_attn_bwd(q, k, v, d_o, offs, inp.max_seqlen, bias, inp.alpha, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    kms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    k_avg = sum(kms) / len(kms) * 1e-3
+    lengths = np.diff(inp.offsets.astype(np.int64))
+    # algorithmic FLOPs: four products per causal pair (dA = dO V^T, dV, dQ, dK), 2 d each
+    flops = 2.0 * causal_flops(lengths, inp.H, inp.dqk, inp.dv)
+    tf = flops / k_avg / 1e12
+    print(json.dumps({
+        "metric": "HSTU jagged causal attention backward TFLOP/s (4 products per causal pair)",
+        "value": round(flops / step_s / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attn_long backward", "B": inp.B, "H": inp.H, "d_qk": inp.dqk,
+                   "d_v": inp.dv, "T": int(inp.T), "bias": "rab_pt P=256 NT=32",
+                   "alpha": inp.alpha, "seed": inp.seed},
+        "tokens_per_s": round(inp.T / step_s, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bwd_dq_kernel + attn_bwd_dkv_kernel (whole call)",
+                     "call_ms_p10_p50_p90": [round(kms[int(f * (len(kms) - 1))], 4)
+                                             for f in (0.1, 0.5, 0.9)]}}), flush=True)
+
+
 def bench_mfalcon(args, dev):
     """Candidate scoring over cached histories (M-FALCON): 16 users with the attention
     benchmark's history lengths, 1024 candidates each, H=8, d=64, position / time bias; one
@@ -211,10 +268,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8", "mfalcon"],
+    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8", "mfalcon", "attn_bwd"],
                     help="attn_long (the headline attention batch), stack8 (the 8-layer HSTU "
                          "stack forward: f1 GEMM + SiLU, attention, LayerNorm-gate-f2, residual) "
-                         "or mfalcon (1024 candidates per user scored over cached histories)")
+                         "mfalcon (1024 candidates per user scored over cached histories) or "
+                         "attn_bwd (the attention's gradients on the attn_long batch)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the HBM byte counters against a known traffic)")
@@ -250,6 +308,9 @@ def main():
         return
     if args.workload == "mfalcon":
         bench_mfalcon(args, dev)
+        return
+    if args.workload == "attn_bwd":
+        bench_attn_bwd(args, dev)
         return
     inp = synth.attn_long()
     lengths = np.diff(inp.offsets.astype(np.int64))

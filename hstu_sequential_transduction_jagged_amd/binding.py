@@ -40,6 +40,9 @@ SIGNATURES = {
     "hstu_attn_fwd_planned": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P,
                                      _i64, _P, _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P, _P,
                                      _sz, _P]),
+    "hstu_attn_bwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P, _i64, _P,
+                             _i64, _P, _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P, _P, _P, _P,
+                             _P, _P, _sz, _P]),
     "hstu_layer_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
     "hstu_layer_fwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _P, _P, _P,
                               _P, _f32, _P, _P, ctypes.POINTER(HstuBias), _f32, _i32, _P, _P, _sz,
@@ -288,6 +291,42 @@ def hstu_attn_candidates_fwd(q_cand, k_cand, v_cand, cand_offsets, max_cand, k_h
 def candidates_workspace_bytes(B, H, max_hist, total_hist, total_cand):
     return int(lib().hstu_attn_candidates_workspace_bytes(int(B), int(H), int(max_hist),
                                                           int(total_hist), int(total_cand)))
+
+
+def hstu_attn_bwd(q, k, v, d_o, offsets, max_seqlen, bias: Optional[HstuBias] = None, alpha=1.0,
+                  out_scale=1.0, workspace=None):
+    """Gradients of hstu_attn_fwd for the upstream gradient d_o (bf16, d = 64).  Returns
+    (dq, dk, dv, dw_pos, dw_time); the table gradients are fp32 tensors shaped like the bias
+    tables (None without the position + time bias)."""
+    if q.dtype != torch.bfloat16:
+        raise HstuError("the backward pass runs in bf16")
+    qs, H, d = _rows(q, "q")
+    ks, _, _ = _rows(k, "k")
+    vs, _, dv_ = _rows(v, "v")
+    dos, _, _ = _rows(d_o, "d_o")
+    T = q.shape[0]
+    B = offsets.numel() - 1
+    if offsets.dtype != torch.int32:
+        raise HstuError("offsets must be int32")
+    bias = bias if bias is not None else make_bias(BIAS_NONE)
+    dq = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    dk = torch.empty((T, H, d), dtype=q.dtype, device=q.device)
+    dv = torch.empty((T, H, dv_), dtype=q.dtype, device=q.device)
+    dwp = dwt = None
+    if bias.kind == BIAS_RAB_PT:
+        ts, wp, wt = bias._keep
+        dwp = torch.empty(wp.shape, dtype=torch.float32, device=q.device)
+        dwt = torch.empty(wt.shape, dtype=torch.float32, device=q.device)
+    need = attn_workspace_bytes(B, H, max_seqlen, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib().hstu_attn_bwd(DTYPE_BF16, B, H, d, dv_, _ptr(offsets), int(max_seqlen), T, _ptr(q),
+                             qs, _ptr(k), ks, _ptr(v), vs, _ptr(d_o), dos, ctypes.byref(bias),
+                             float(alpha), float(out_scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                             _ptr(dwp), _ptr(dwt), _ptr(workspace), workspace.numel(),
+                             _stream(q.device))
+    _check("hstu_attn_bwd", st)
+    return dq, dk, dv, dwp, dwt
 
 
 def hstu_embed_sum_fwd(item_table, action_table, item_ids, action_ids, out=None):

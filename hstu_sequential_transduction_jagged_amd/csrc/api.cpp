@@ -278,6 +278,65 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
                                out_scale, o, workspace, workspace_bytes, stream);
 }
 
+hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                          const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
+                          const void* q, int64_t q_row_stride, const void* k,
+                          int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                          const void* d_o, int64_t do_row_stride, const hstu_bias* bias,
+                          float alpha, float out_scale, void* dq, void* dk, void* dv,
+                          float* dw_pos, float* dw_time, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (dt != HSTU_DTYPE_BF16) return fail(HSTU_ERR_UNSUPPORTED, "the backward pass runs in bf16 only");
+  if (d_qk != 64 || d_v != 64) return fail(HSTU_ERR_UNSUPPORTED, "the backward pass needs d = 64");
+  int block_rows = 0;
+  hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
+  if (st != HSTU_OK) return st;
+  BiasArgs ba;
+  st = check_bias(bias, H, &ba);
+  if (st != HSTU_OK) return st;
+  if (ba.kind == 1 && (!dw_pos || !dw_time))
+    return fail(HSTU_ERR_INVALID_ARG, "rab_pt bias needs dw_pos and dw_time");
+  if (B == 0 || total_tokens == 0 || max_seqlen == 0) return HSTU_OK;
+  if (!offsets || !q || !k || !v || !d_o || !dq || !dk || !dv || !workspace)
+    return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  const int64_t rowlen = (int64_t)H * d_qk;
+  if (q_row_stride < rowlen || k_row_stride < rowlen || v_row_stride < rowlen ||
+      do_row_stride < rowlen)
+    return fail(HSTU_ERR_INVALID_ARG, "row stride smaller than H*d");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || q_row_stride % 8 || k_row_stride % 8 ||
+      v_row_stride % 8 || do_row_stride % 8)
+    return fail(HSTU_ERR_INVALID_ARG, "rows must be 16-byte aligned");
+  st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen, total_tokens);
+  if (st != HSTU_OK) return st;
+  int64_t max_stride = k_row_stride > v_row_stride ? k_row_stride : v_row_stride;
+  if (q_row_stride > max_stride) max_stride = q_row_stride;
+  if (do_row_stride > max_stride) max_stride = do_row_stride;
+  if ((int64_t)(max_seqlen + 64) * max_stride * 2 >= ((int64_t)1 << 31))
+    return fail(HSTU_ERR_UNSUPPORTED, "max_seqlen x row stride reaches 2 GiB per user");
+  st = hstu_attn_plan(dt, B, H, d_qk, offsets, max_seqlen, workspace, workspace_bytes, stream);
+  if (st != HSTU_OK) return st;
+  BwdArgs a{};
+  a.offsets = offsets;
+  a.work_count = (const int32_t*)workspace;
+  a.work = (const WorkItem*)((const char*)workspace + kHeader);
+  a.q = (const bf16*)q; a.k = (const bf16*)k; a.v = (const bf16*)v; a.dout = (const bf16*)d_o;
+  a.q_stride = q_row_stride; a.k_stride = k_row_stride; a.v_stride = v_row_stride;
+  a.do_stride = do_row_stride;
+  a.H = H;
+  a.bias = ba;
+  a.alpha = alpha;
+  a.out_scale = out_scale;
+  a.dq = (bf16*)dq; a.dk = (bf16*)dk; a.dv = (bf16*)dv;
+  a.dw_pos = dw_pos; a.dw_time = dw_time;
+  const int64_t n_pos = ba.kind == 1 ? (ba.pos_stride ? (int64_t)H * ba.pos_stride : ba.num_pos) : 0;
+  const int64_t n_time = ba.kind == 1 ? (ba.time_stride ? (int64_t)H * ba.time_stride : ba.num_time) : 0;
+  const int64_t grid = (int64_t)B * H * ceil_div(max_seqlen, block_rows);
+  if (grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
+  return check_hip(launch_attn_bwd_bf16(a, (int)grid, n_pos, n_time, stream), "backward launch");
+}
+
 void hstu_layer_workspace_offsets(int64_t total_tokens, int32_t H, int32_t d_qk, int32_t d_v,
                                   size_t* z_offset, size_t* o_offset, size_t* attn_offset) {
   const int64_t N1 = 2LL * H * (d_qk + d_v);

@@ -1,0 +1,521 @@
+// Gradients of the jagged causal pointwise attention ("Actions Speak Louder than Words" reading
+// notes §3.1 eq. (2), §3.2) for bf16, d_qk = d_v = 64:
+//
+//   x_ij = alpha <q_i, k_j> + rab(i, j),  a_ij = SiLU(x_ij),  O_i = out_scale sum_{j <= i} a_ij v_j
+//   dV_j = out_scale sum_{i >= j} a_ij dO_i
+//   g_ij = <dO_i, v_j> SiLU'(x_ij),  SiLU'(x) = s (1 + x (1 - s)),  s = 1 / (1 + e^-x)
+//   dQ_i = alpha out_scale sum_{j <= i} g_ij k_j,   dK_j = alpha out_scale sum_{i >= j} g_ij q_i
+//   dw_pos[h][pos bucket] += out_scale g_ij,  dw_time[h][time bucket] += out_scale g_ij
+//
+// Two kernels over the forward's cost-sorted work list of (user, head, 256-row tile) items:
+//   - attn_bwd_dq_kernel, query-major like the forward: per wave 32 query rows; per 32-key step
+//     S^T = K Q^T and dA^T = V dO^T on v_mfma_f32_32x32x16_bf16 (lane = query, registers = keys),
+//     the weights g in registers become the B operand of dQ^T += K^T G^T, K^T read from the
+//     row-major K tile with transposing LDS reads (as V^T in the forward);
+//   - attn_bwd_dkv_kernel, key-major: per wave 32 key rows held in registers; per 32-query step
+//     S = Q K^T and dA = dO V^T (lane = key, registers = queries), then dV^T += dO^T P and
+//     dK^T += Q^T G with dO^T and Q^T read from the row-major query tiles with transposing LDS
+//     reads; the table gradients are summed per workgroup in LDS and added to the tables with
+//     one global atomic per entry touched (so their summation order varies between runs).
+// SiLU and its derivative are evaluated exactly per element (exp2 and reciprocal); the bias of
+// every element comes from LDS-resident tables.
+#include "hstu_internal.h"
+
+namespace hstu {
+namespace {
+
+constexpr int kBWaves = 8;
+constexpr int kBThreads = 64 * kBWaves;
+constexpr int kBRows = 32 * kBWaves;  // rows of a work item (the forward's tile height)
+constexpr int kBTile = 64;            // keys (dq kernel) or queries (dkv kernel) per LDS tile
+constexpr int kBD = 64;
+constexpr int kBRow = 72;             // padded LDS row (bf16), as in the forward kernel
+
+// accumulator register r of a 32x32 MFMA tile holds row 8 (r / 4) + 4 hf + r % 4
+__device__ __forceinline__ int accrow(int r) { return 8 * (r >> 2) + (r & 3); }
+
+struct __attribute__((aligned(16))) SmemBwd {
+  __attribute__((aligned(16))) bf16 x[2][kBTile * kBRow];  // K (dq kernel) or Q (dkv kernel)
+  __attribute__((aligned(16))) bf16 y[2][kBTile * kBRow];  // V (dq kernel) or dO (dkv kernel)
+  __attribute__((aligned(16))) int64_t t[2][kBTile];       // the tile rows' timestamps
+  float wpos[kMaxPosBuckets];    // w_pos[h]
+  float wtime[kMaxTimeBuckets];  // w_time[h]
+  float gpos[kMaxPosBuckets];    // dkv kernel: this workgroup's position-table gradient
+  float gtime[kMaxTimeBuckets];  // dkv kernel: this workgroup's time-table gradient
+  __attribute__((aligned(16))) int64_t tmm[2][2][2];  // dkv kernel: per 32-row half of a tile: min, max time
+};
+
+// sum over the 64 lanes of a wave, as a wave-uniform value
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppMirror>(v);
+  auto at = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l)); };
+  return (at(0) + at(16)) + (at(32) + at(48));
+}
+
+// s = 1 / (1 + e^-x) and SiLU'(x) = s (1 + x (1 - s)); a = x s
+__device__ __forceinline__ void silu_and_grad(float x, float& a, float& d1) {
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
+  a = x * s;
+  d1 = s * __builtin_fmaf(x, 1.0f - s, 1.0f);
+}
+
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
+
+// bias of pair (i, j) of head h (natural units), from the LDS tables
+template <int KIND>
+__device__ __forceinline__ float pair_bias(const SmemBwd& sm, int di, int64_t dt, int Pm1,
+                                           int NTm1, float slope) {
+  if (KIND == 1) return sm.wpos[max(min(di, Pm1), 0)] + sm.wtime[time_bucket(dt, NTm1)];
+  if (KIND == 2) return -slope * (float)di;
+  return 0.f;
+}
+
+// stage one 64-row tile of two row-major [T, H, 64] bf16 tensors (rows r0 .. r0 + 63 of user
+// base tok0, head h; rows at or past `end` read as zeros) and the rows' timestamps
+struct TileStager {
+  __amdgpu_buffer_rsrc_t xr, yr, tr;
+  uint32_t xs, ys, xoff, yoff;
+  u32x4 xreg, yreg;
+  uint32_t tlo = 0, thi = 0;
+  __device__ void load(int r0, bool with_t, int lane) {
+    xreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (uint32_t)r0 * xs, 0));
+    yreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, yoff, (uint32_t)r0 * ys, 0));
+    if (with_t) {
+      const u32x2 tt = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(tr, 8u * (uint32_t)lane, 8u * (uint32_t)r0, 0));
+      tlo = tt[0];
+      thi = tt[1];
+    }
+  }
+};
+
+template <int KIND>
+__global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
+  __shared__ SmemBwd sm;
+  const int item = blockIdx.x;
+  if (item >= *a.work_count) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const WorkItem wi = a.work[item];
+  const int b = wi.b, h = wi.h, H = a.H;
+  const int64_t tok0 = a.offsets[b];
+  const int n = a.offsets[b + 1] - a.offsets[b];
+  const int q0 = wi.qt * kBRows;
+  if (q0 >= n) return;
+  const int q_end = min(q0 + kBRows, n);
+  const int n_tiles = (q_end + kBTile - 1) / kBTile;
+  const int qw0 = q0 + wave * 32;
+  const int wq_last = min(qw0 + 32, q_end) - 1;
+  const int row = qw0 + l32;
+  const bool qvalid = row <= wq_last;
+  const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
+
+  // query and upstream-gradient rows of this lane (B operands; d = 16 ks + 8 hf .. + 7)
+  bf16x8 qop[4], dop[4];
+  {
+    const bf16* qs = a.q + (tok0 + row) * a.q_stride + (int64_t)h * kBD + 8 * hf;
+    const bf16* ds = a.dout + (tok0 + row) * a.do_stride + (int64_t)h * kBD + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 rq = {0u, 0u, 0u, 0u}, rd = {0u, 0u, 0u, 0u};
+      if (qvalid) {
+        rq = *(const u32x4*)(qs + 16 * ks);
+        rd = *(const u32x4*)(ds + 16 * ks);
+      }
+      qop[ks] = __builtin_bit_cast(bf16x8, rq);
+      dop[ks] = __builtin_bit_cast(bf16x8, rd);
+    }
+  }
+  const int64_t tq = KIND == 1 && qvalid ? a.bias.ts[tok0 + row] : 0;
+  float slope = 0.f;
+  if (KIND == 1) {
+    for (int i = tid; i < a.bias.num_pos; i += kBThreads) sm.wpos[i] = a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i];
+    if (tid < a.bias.num_time) sm.wtime[tid] = a.bias.w_time[(int64_t)h * a.bias.time_stride + tid];
+  } else if (KIND == 2) {
+    slope = a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H);
+  }
+
+  // staging: thread t moves 16-byte chunk t % 8 of row t / 8 of K and V
+  const int srow = tid >> 3, sch = tid & 7;
+  TileStager stg;
+  stg.xs = (uint32_t)a.k_stride * 2u;
+  stg.ys = (uint32_t)a.v_stride * 2u;
+  stg.xr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + tok0 * a.k_stride + (int64_t)h * kBD), (short)0,
+                                             (int)((uint32_t)(q_end - 1) * stg.xs + 2u * kBD), 0x00020000);
+  stg.yr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + tok0 * a.v_stride + (int64_t)h * kBD), (short)0,
+                                             (int)((uint32_t)(q_end - 1) * stg.ys + 2u * kBD), 0x00020000);
+  stg.tr = __builtin_amdgcn_make_buffer_rsrc((void*)(KIND == 1 ? a.bias.ts + tok0 : nullptr), (short)0,
+                                             KIND == 1 ? 8 * q_end : 0, 0x00020000);
+  stg.xoff = (uint32_t)srow * stg.xs + 16u * sch;
+  stg.yoff = (uint32_t)srow * stg.ys + 16u * sch;
+  auto lstore = [&](int buf) {
+    *(u32x4*)(&sm.x[buf][srow * kBRow + 8 * sch]) = stg.xreg;
+    *(u32x4*)(&sm.y[buf][srow * kBRow + 8 * sch]) = stg.yreg;
+    if (KIND == 1 && wave == 0) sm.t[buf][lane] = (int64_t)(((uint64_t)stg.thi << 32) | stg.tlo);
+  };
+  stg.load(0, KIND == 1 && wave == 0, lane);
+  lstore(0);
+  __syncthreads();
+
+  // transposing K reads: lane i of each 16-lane group reads keys 4 hf + (i % 16) / 4 (+ the
+  // group's offset) at d 16 ((lane / 16) % 2) + 4 (lane % 4) .. + 3 (+ 32 db)
+  const int tr_row0 = 4 * hf + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  f32x16 acc[2] = {};
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const bool more = t + 1 < n_tiles;
+    if (more) stg.load((t + 1) * kBTile, KIND == 1 && wave == 0, lane);
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+      const int j0h = t * kBTile + 32 * hk;
+      if (j0h > wq_last || wq_last < qw0) continue;  // past the diagonal, or the wave has no rows
+      bf16x8 kop[4], vop[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        kop[ks] = *(const bf16x8*)(&sm.x[buf][(32 * hk + l32) * kBRow + 16 * ks + 8 * hf]);
+        vop[ks] = *(const bf16x8*)(&sm.y[buf][(32 * hk + l32) * kBRow + 16 * ks + 8 * hf]);
+      }
+      f32x16 s = {}, da = {};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], s, 0, 0, 0);
+        da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[ks], dop[ks], da, 0, 0, 0);
+      }
+      f32x16 g;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jl = 32 * hk + accrow(r) + 4 * hf;  // key within the tile
+        const int j = t * kBTile + jl;
+        const int64_t dt = KIND == 1 ? tq - sm.t[buf][jl] : 0;
+        const float x = __builtin_fmaf(a.alpha, s[r], pair_bias<KIND>(sm, row - j, dt, Pm1, NTm1, slope));
+        float aa, d1;
+        silu_and_grad(x, aa, d1);
+        g[r] = (j <= row && qvalid) ? da[r] * d1 : 0.f;
+      }
+      bf16x8 gop[2];
+      {
+        f32x8 g0, g1;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          g0[r] = g[r];
+          g1[r] = g[r + 8];
+        }
+        gop[0] = __builtin_convertvector(g0, bf16x8);
+        gop[1] = __builtin_convertvector(g1, bf16x8);
+      }
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const bf16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&sm.x[buf][(tr_row0 + 32 * hk + 16 * mm) * kBRow + 32 * db + tr_col]));
+          const bf16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&sm.x[buf][(tr_row0 + 32 * hk + 16 * mm + 8) * kBRow + 32 * db + tr_col]));
+          const bf16x8 ktop = bf16x8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktop, gop[mm], acc[db], 0, 0, 0);
+        }
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // dQ rows: accumulator register 4 g + e holds d = 32 db + 8 g + 4 hf + e of this lane's row
+  if (qvalid) {
+    const float sc = a.alpha * a.out_scale;
+    bf16* op = a.dq + ((tok0 + row) * H + h) * kBD + 4 * hf;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v4[e] = acc[db][4 * g + e] * sc;
+        *(bf16x4*)(op + 32 * db + 8 * g) = __builtin_convertvector(v4, bf16x4);
+      }
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
+  __shared__ SmemBwd sm;
+  const int item = blockIdx.x;
+  if (item >= *a.work_count) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const WorkItem wi = a.work[item];
+  const int b = wi.b, h = wi.h, H = a.H;
+  const int64_t tok0 = a.offsets[b];
+  const int n = a.offsets[b + 1] - a.offsets[b];
+  // the work list orders items by q_tile; this kernel takes key tile (tiles - 1 - q_tile),
+  // whose cost (the query tiles at or after it) is the same q_tile + 1
+  const int tiles = (n + kBRows - 1) / kBRows;
+  if (wi.qt >= tiles) return;
+  const int k0 = (tiles - 1 - wi.qt) * kBRows;
+  const int k_end = min(k0 + kBRows, n);
+  const int kw0 = k0 + wave * 32;
+  const int wk_last = min(kw0 + 32, k_end) - 1;
+  const int key = kw0 + l32;
+  const bool kvalid = key <= wk_last;
+  const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
+
+  // key and value rows of this lane (B operands; d = 16 ks + 8 hf .. + 7)
+  bf16x8 kop[4], vop[4];
+  {
+    const bf16* ks_ = a.k + (tok0 + key) * a.k_stride + (int64_t)h * kBD + 8 * hf;
+    const bf16* vs_ = a.v + (tok0 + key) * a.v_stride + (int64_t)h * kBD + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 rk = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
+      if (kvalid) {
+        rk = *(const u32x4*)(ks_ + 16 * ks);
+        rv = *(const u32x4*)(vs_ + 16 * ks);
+      }
+      kop[ks] = __builtin_bit_cast(bf16x8, rk);
+      vop[ks] = __builtin_bit_cast(bf16x8, rv);
+    }
+  }
+  const int64_t tk = KIND == 1 && kvalid ? a.bias.ts[tok0 + key] : 0;
+  // the extremes of this wave's key times (both lane halves hold the same keys)
+  int64_t tk_min = 0, tk_max = 0;
+  if (KIND == 1) {
+    int64_t mn = kvalid ? tk : kTMax, mx = kvalid ? tk : kTMin;
+    half_minmax(mn, mx);
+    tk_min = uniform_i64(mn);
+    tk_max = uniform_i64(mx);
+  }
+  float slope = 0.f;
+  if (KIND == 1) {
+    for (int i = tid; i < a.bias.num_pos; i += kBThreads) {
+      sm.wpos[i] = a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i];
+      sm.gpos[i] = 0.f;
+    }
+    if (tid < a.bias.num_time) {
+      sm.wtime[tid] = a.bias.w_time[(int64_t)h * a.bias.time_stride + tid];
+      sm.gtime[tid] = 0.f;
+    }
+  } else if (KIND == 2) {
+    slope = a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H);
+  }
+
+  // query tiles from the one holding row k0 to the user's last row
+  const int t0 = k0 / kBTile, t_end = (n + kBTile - 1) / kBTile;
+  const int srow = tid >> 3, sch = tid & 7;
+  TileStager stg;
+  stg.xs = (uint32_t)a.q_stride * 2u;
+  stg.ys = (uint32_t)a.do_stride * 2u;
+  stg.xr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + tok0 * a.q_stride + (int64_t)h * kBD), (short)0,
+                                             (int)((uint32_t)(n - 1) * stg.xs + 2u * kBD), 0x00020000);
+  stg.yr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + tok0 * a.do_stride + (int64_t)h * kBD), (short)0,
+                                             (int)((uint32_t)(n - 1) * stg.ys + 2u * kBD), 0x00020000);
+  stg.tr = __builtin_amdgcn_make_buffer_rsrc((void*)(KIND == 1 ? a.bias.ts + tok0 : nullptr), (short)0,
+                                             KIND == 1 ? 8 * n : 0, 0x00020000);
+  stg.xoff = (uint32_t)srow * stg.xs + 16u * sch;
+  stg.yoff = (uint32_t)srow * stg.ys + 16u * sch;
+  auto lstore = [&](int buf) {
+    *(u32x4*)(&sm.x[buf][srow * kBRow + 8 * sch]) = stg.xreg;
+    *(u32x4*)(&sm.y[buf][srow * kBRow + 8 * sch]) = stg.yreg;
+    if (KIND == 1 && wave == 0) sm.t[buf][lane] = (int64_t)(((uint64_t)stg.thi << 32) | stg.tlo);
+  };
+  // wave 0 also records the extremes of each 32-row half's times (rows at or past n excluded)
+  auto lstore_t = [&](int buf, int r0) {
+    if (KIND == 1 && wave == 0) {
+      const int64_t tt = (int64_t)(((uint64_t)stg.thi << 32) | stg.tlo);
+      const bool ok = r0 + lane < n;
+      int64_t mn = ok ? tt : kTMax, mx = ok ? tt : kTMin;
+      half_minmax(mn, mx);
+      if (l32 == 0) *(i64x2*)(&sm.tmm[buf][hf][0]) = i64x2{mn, mx};
+    }
+  };
+  stg.load(t0 * kBTile, KIND == 1 && wave == 0, lane);
+  lstore(0);
+  lstore_t(0, t0 * kBTile);
+  __syncthreads();
+
+  const int tr_row0 = 4 * hf + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  f32x16 dvacc[2] = {}, dkacc[2] = {};
+  for (int t = t0; t < t_end; ++t) {
+    const int buf = (t - t0) & 1;
+    const bool more = t + 1 < t_end;
+    if (more) stg.load((t + 1) * kBTile, KIND == 1 && wave == 0, lane);
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      const int i0h = t * kBTile + 32 * hq;  // first query of this step
+      if (i0h + 31 < kw0 || i0h >= n || kw0 > wk_last) continue;  // uniform: no pair i >= j
+      bf16x8 qa[4], da_[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        qa[ks] = *(const bf16x8*)(&sm.x[buf][(32 * hq + l32) * kBRow + 16 * ks + 8 * hf]);
+        da_[ks] = *(const bf16x8*)(&sm.y[buf][(32 * hq + l32) * kBRow + 16 * ks + 8 * hf]);
+      }
+      f32x16 s = {}, dd = {};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kop[ks], s, 0, 0, 0);
+        dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da_[ks], vop[ks], dd, 0, 0, 0);
+      }
+      // register r: query i = i0h + accrow(r) + 4 hf of this lane's key
+      f32x16 p, g;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int il = 32 * hq + accrow(r) + 4 * hf;
+        const int i = t * kBTile + il;
+        const int64_t dt = KIND == 1 ? sm.t[buf][il] - tk : 0;
+        const float x = __builtin_fmaf(a.alpha, s[r], pair_bias<KIND>(sm, i - key, dt, Pm1, NTm1, slope));
+        float aa, d1;
+        silu_and_grad(x, aa, d1);
+        const bool ok = i >= key && i < n && kvalid;
+        p[r] = ok ? aa : 0.f;
+        g[r] = ok ? dd[r] * d1 : 0.f;
+      }
+      if (KIND == 1) {
+        // table gradients of this 32x32 tile: one position bucket when i - j >= P - 1 for every
+        // pair, one or two time buckets when the extreme times say so (exactly); then tile
+        // sums, else one LDS add per score
+        const i64x2 qmm = *(const i64x2*)(&sm.tmm[buf][hq][0]);
+        const int64_t qmin = uniform_i64(qmm[0]), qmax = uniform_i64(qmm[1]);
+        const int tlo = time_bucket(qmin - tk_max, NTm1), thi = time_bucket(qmax - tk_min, NTm1);
+        const bool sat = i0h - (kw0 + 31) >= Pm1;
+        float gs = 0.f, ghi = 0.f;
+        const int64_t tlim = tk + (((int64_t)1 << thi) - 1);  // dt >= 2^thi - 1
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          gs += g[r];
+          if (thi == tlo + 1) ghi += sm.t[buf][32 * hq + accrow(r) + 4 * hf] >= tlim ? g[r] : 0.f;
+        }
+        if (sat || thi <= tlo + 1) {
+          const float tot = wave_sum(gs);
+          const float hi = thi == tlo + 1 ? wave_sum(ghi) : 0.f;
+          if (lane == 0) {
+            if (sat) atomicAdd(&sm.gpos[Pm1], tot);
+            if (thi == tlo) {
+              atomicAdd(&sm.gtime[tlo], tot);
+            } else if (thi == tlo + 1) {
+              atomicAdd(&sm.gtime[tlo], tot - hi);
+              atomicAdd(&sm.gtime[thi], hi);
+            }
+          }
+        }
+        if (!sat || thi > tlo + 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int il = 32 * hq + accrow(r) + 4 * hf;
+            const int i = t * kBTile + il;
+            if (i >= key && i < n && kvalid) {
+              if (!sat) atomicAdd(&sm.gpos[min(i - key, Pm1)], g[r]);
+              if (thi > tlo + 1) atomicAdd(&sm.gtime[time_bucket(sm.t[buf][il] - tk, NTm1)], g[r]);
+            }
+          }
+        }
+      }
+      bf16x8 pop[2], gop[2];
+      {
+        f32x8 p0, p1, g0, g1;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          p0[r] = p[r];
+          p1[r] = p[r + 8];
+          g0[r] = g[r];
+          g1[r] = g[r + 8];
+        }
+        pop[0] = __builtin_convertvector(p0, bf16x8);
+        pop[1] = __builtin_convertvector(p1, bf16x8);
+        gop[0] = __builtin_convertvector(g0, bf16x8);
+        gop[1] = __builtin_convertvector(g1, bf16x8);
+      }
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const int r0 = tr_row0 + 32 * hq + 16 * mm, c0 = 32 * db + tr_col;
+          const bf16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&sm.y[buf][r0 * kBRow + c0]));
+          const bf16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&sm.y[buf][(r0 + 8) * kBRow + c0]));
+          const bf16x4 e0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&sm.x[buf][r0 * kBRow + c0]));
+          const bf16x4 e1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)(&sm.x[buf][(r0 + 8) * kBRow + c0]));
+          const bf16x8 dot = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          const bf16x8 qt = bf16x8{e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+          dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pop[mm], dvacc[db], 0, 0, 0);
+          dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, gop[mm], dkacc[db], 0, 0, 0);
+        }
+    }
+    if (more) {
+      lstore(buf ^ 1);
+      lstore_t(buf ^ 1, (t + 1) * kBTile);
+    }
+    __syncthreads();
+  }
+
+  // dK and dV rows: accumulator register 4 g + e holds d = 32 db + 8 g + 4 hf + e of this
+  // lane's key
+  if (kvalid) {
+    const float sv = a.out_scale, sk = a.alpha * a.out_scale;
+    bf16* kp = a.dk + ((tok0 + key) * H + h) * kBD + 4 * hf;
+    bf16* vp = a.dv + ((tok0 + key) * H + h) * kBD + 4 * hf;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 k4, v4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          k4[e] = dkacc[db][4 * g + e] * sk;
+          v4[e] = dvacc[db][4 * g + e] * sv;
+        }
+        *(bf16x4*)(kp + 32 * db + 8 * g) = __builtin_convertvector(k4, bf16x4);
+        *(bf16x4*)(vp + 32 * db + 8 * g) = __builtin_convertvector(v4, bf16x4);
+      }
+  }
+  // table gradients: this workgroup's sums, once per touched entry
+  if (KIND == 1) {
+    for (int i = tid; i < a.bias.num_pos; i += kBThreads) {
+      const float v = sm.gpos[i];
+      if (v != 0.f) atomicAdd(&a.dw_pos[(int64_t)h * a.bias.pos_stride + i], v * a.out_scale);
+    }
+    if (tid < a.bias.num_time) {
+      const float v = sm.gtime[tid];
+      if (v != 0.f) atomicAdd(&a.dw_time[(int64_t)h * a.bias.time_stride + tid], v * a.out_scale);
+    }
+  }
+}
+
+// zero fill of the table gradients (a kernel, not a memset: callers may capture the stream)
+__global__ void zero_f32_kernel(float* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int grid, int64_t n_pos_grad, int64_t n_time_grad,
+                                hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (a.bias.kind == 1) {
+    if (n_pos_grad > 0)
+      hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n_pos_grad + 255) / 256)), dim3(256), 0, stream, a.dw_pos, n_pos_grad);
+    if (n_time_grad > 0)
+      hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)((n_time_grad + 255) / 256)), dim3(256), 0, stream, a.dw_time, n_time_grad);
+  }
+  const dim3 g((unsigned)grid), blk(kBThreads);
+  if (a.bias.kind == 1) {
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<1>, g, blk, 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<1>, g, blk, 0, stream, a);
+  } else if (a.bias.kind == 2) {
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<2>, g, blk, 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<2>, g, blk, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<0>, g, blk, 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<0>, g, blk, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hstu

@@ -200,6 +200,22 @@ hipError_t launch_ln_gate_f2(const bf16* o, const f32x2* ostats, const bf16* u,
                              int64_t u_stride, const float* gamma, const float* beta, float eps,
                              const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,
                              int32_t D, int32_t H, int32_t dv, hipStream_t stream);
+// Gradients of the bf16 d = 64 attention (attention_bwd.hip).
+struct BwdArgs {
+  const int32_t* offsets;
+  const int32_t* work_count;
+  const WorkItem* work;
+  const bf16 *q, *k, *v, *dout;
+  int64_t q_stride, k_stride, v_stride, do_stride;  // elements between tokens
+  int32_t H;
+  BiasArgs bias;
+  float alpha, out_scale;
+  bf16 *dq, *dk, *dv;         // [T, H, 64]
+  float *dw_pos, *dw_time;    // position + time bias: gradients shaped like the tables
+};
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int grid, int64_t n_pos_grad,
+                                int64_t n_time_grad, hipStream_t stream);
+
 // Candidate scoring over a cached history (candidates.hip).
 struct CandLaunch {
   int32_t B, H, max_hist, max_cand;

@@ -132,6 +132,28 @@ int32_t hstu_attn_block_rows(int32_t dt, int32_t d);
 size_t hstu_layer_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_model, int32_t H,
                                   int32_t d_qk, int32_t d_v, int32_t max_seqlen);
 
+/* Gradients of the attention ("Actions Speak Louder than Words" reading notes §3.1 eq. (2),
+ * §3.2) for an upstream gradient dO of O:
+ *   dV_j = out_scale sum_{i >= j} SiLU(x_ij) dO_i,   g_ij = <dO_i, v_j> SiLU'(x_ij),
+ *   dQ_i = alpha out_scale sum_{j <= i} g_ij k_j,    dK_j = alpha out_scale sum_{i >= j} g_ij q_i,
+ *   dw_pos[pos bucket(i, j)] += out_scale g_ij,  dw_time[time bucket(i, j)] += out_scale g_ij
+ * with x_ij = alpha <q_i, k_j> + rab(i, j) and SiLU'(x) = s (1 + x (1 - s)), s = 1/(1+e^-x).
+ *  dt        HSTU_DTYPE_BF16 only; d_qk = d_v = 64
+ *  q, k, v, d_o  device bf16 rows [T, H, 64] with the given row strides (as for hstu_attn_fwd)
+ *  dq, dk, dv    device bf16 [T, H, 64] contiguous, overwritten
+ *  dw_pos, dw_time  rab_pt bias only (else may be NULL): device fp32 shaped like w_pos / w_time
+ *            (H x head stride, or one table when the stride is 0: then it sums over heads),
+ *            overwritten; added to with atomics, so their last bits vary between runs
+ *  workspace as for hstu_attn_fwd (same size); other arguments as for hstu_attn_fwd. */
+hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                          const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
+                          const void* q, int64_t q_row_stride, const void* k,
+                          int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                          const void* d_o, int64_t do_row_stride, const hstu_bias* bias,
+                          float alpha, float out_scale, void* dq, void* dk, void* dv,
+                          float* dw_pos, float* dw_time, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 /* One HSTU layer forward, eqs. (1)-(3), bf16 storage with fp32 accumulation.
  *  x        device bf16 [T, d_model]
  *  w1       device bf16 [2H(d_qk+d_v), d_model] (row n = output feature n), b1 fp32 [2H(d_qk+d_v)] or NULL

@@ -1,0 +1,129 @@
+"""GPU parity of the attention gradients ("Actions Speak Louder than Words" §3.1 eq. (2)) against
+the fp64 oracle, through the C ABI.
+
+dq, dk, dv are bf16 outputs: max_k max(0, |y_k - ref_k| - 2^-8 |ref_k|) / rms(ref) <= 2e-2 as for
+the forward.  The table gradients are fp32 sums of fp32 per-score terms: max-abs error relative
+to their RMS <= 1e-3.  Cases: ragged lengths around the 32/64/256-row tiles, empty and single
+rows, every bias kind in the workload's near-linear regime and a nonlinear one, per-head tables,
+strided views of one projection buffer, and a sampled check at the attn_long batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hstu_sequential_transduction_jagged_amd import binding, synth
+from tests.hstu_testutil import TOL, DevAttn, err_rms, err_stored, oracle_bias, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [0, 1, 2, 31, 32, 33, 63, 64, 65, 255, 256, 257, 700]
+
+
+def _case(lengths, kind=synth.BIAS_RAB_PT, alpha=1.0 / 700, table_std=0.02, H=2, P=256, NT=32,
+          seed=21, per_head=False):
+    return synth.make_attn("bwd", seed, "bf16", lengths, H=H, d=64, alpha=alpha, bias_kind=kind,
+                           P=P, NT=NT, table_std=table_std, per_head_tables=per_head)
+
+
+def _dout(inp, seed=5):
+    rng = np.random.default_rng(seed)
+    return synth.round_bf16(rng.standard_normal((inp.T, inp.H, inp.dv)).astype(np.float32))
+
+
+def _run(inp, dO, d=None):
+    d = d or DevAttn(inp)
+    return binding.hstu_attn_bwd(d.q, d.k, d.v, to_dev(dO, torch.bfloat16), d.offsets,
+                                 inp.max_seqlen, d.bias, inp.alpha, inp.out_scale)
+
+
+def _check(inp, got, dO):
+    torch.cuda.synchronize()
+    ref = oracle.attention_bwd(inp.offsets, inp.q, inp.k, inp.v, dO,
+                               oracle_bias(inp.bias, inp.ts, inp.H), inp.alpha, inp.out_scale)
+    for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+        y = g.float().cpu().numpy().astype(np.float64)
+        e = err_stored(y, r, "bf16")
+        print("%s %s T=%d err=%.3g (without allowance %.3g)" % (inp.name, name, inp.T, e, err_rms(y, r)),
+              flush=True)
+        assert e <= TOL["bf16"], (name, e)
+    for name, g, r in zip(("dw_pos", "dw_time"), got[3:], ref[3:]):
+        if r is None:
+            assert g is None
+            continue
+        y = g.cpu().numpy().astype(np.float64)
+        e = err_rms(y, r)
+        print("%s %s err=%.3g" % (inp.name, name, e), flush=True)
+        assert e <= 1e-3, (name, e)
+
+
+@pytest.mark.parametrize("regime", ["workload", "nonlinear"])
+@pytest.mark.parametrize("kind", [synth.BIAS_RAB_PT, synth.BIAS_ALIBI, synth.BIAS_NONE])
+def test_bwd_ragged(kind, regime):
+    if regime == "workload":
+        inp = _case(RAGGED, kind=kind)
+    else:
+        inp = _case(RAGGED, kind=kind, alpha=1.0 / 8.0, table_std=1.0)
+    dO = _dout(inp)
+    _check(inp, _run(inp, dO), dO)
+
+
+def test_bwd_per_head_tables_small_buckets_out_scale():
+    inp = _case([5, 300, 129, 64], H=3, alpha=0.1, table_std=1.0, P=16, NT=6, per_head=True)
+    inp.out_scale = 1.0 / 300
+    dO = _dout(inp, 6)
+    _check(inp, _run(inp, dO), dO)
+
+
+def test_bwd_strided_views():
+    """q, k, v, dO as column blocks of wider rows (as the layer's projection buffer)."""
+    inp = _case([90, 260, 3], alpha=1.0 / 8, table_std=1.0, seed=22)
+    dO = _dout(inp, 7)
+    d = DevAttn(inp)
+    H, dd = inp.H, 64
+    W = 4 * H * dd + 64
+
+    def wide(*blocks):
+        T = blocks[0].shape[0]
+        z = torch.full((T, W), float("nan"), dtype=torch.bfloat16, device="cuda")
+        out = []
+        for i, blk in enumerate(blocks):
+            z[:, i * H * dd:(i + 1) * H * dd] = blk.reshape(T, H * dd)
+            out.append(z[:, i * H * dd:(i + 1) * H * dd].view(T, H, dd))
+        return out
+
+    q, k, v, g = wide(d.q, d.k, d.v, to_dev(dO, torch.bfloat16))
+    got = binding.hstu_attn_bwd(q, k, v, g, d.offsets, inp.max_seqlen, d.bias, inp.alpha,
+                                inp.out_scale)
+    _check(inp, got, dO)
+
+
+def test_bwd_rejects_bad_arguments():
+    inp = _case([10])
+    d = DevAttn(inp)
+    dO = to_dev(_dout(inp), torch.bfloat16)
+    with pytest.raises(binding.HstuError):
+        binding.hstu_attn_bwd(d.q.float(), d.k, d.v, dO, d.offsets, inp.max_seqlen, d.bias)
+
+
+def test_bwd_attn_long_sampled():
+    """The benchmark batch (16 users up to 8192 rows): gradients checked on sampled users
+    against the oracle run on those users alone (users are independent)."""
+    inp = synth.attn_long()
+    dO = _dout(inp, 8)
+    got = _run(inp, dO)
+    torch.cuda.synchronize()
+    offs = inp.offsets.astype(np.int64)
+    lengths = np.diff(offs)
+    for b in (int(np.argmin(lengths)), 3):
+        s, e = int(offs[b]), int(offs[b + 1])
+        sub = synth.AttnInputs("attn_long_user%d" % b, inp.seed, "bf16", 1, inp.H, inp.dqk, inp.dv,
+                               np.array([0, e - s], np.int32), e - s, inp.ts[s:e], inp.q[s:e],
+                               inp.k[s:e], inp.v[s:e], inp.bias, inp.alpha)
+        ref = oracle.attention_bwd(sub.offsets, sub.q, sub.k, sub.v, dO[s:e],
+                                   oracle_bias(sub.bias, sub.ts, sub.H), sub.alpha)
+        for name, g, r in zip(("dq", "dk", "dv"), got[:3], ref[:3]):
+            y = g[s:e].float().cpu().numpy().astype(np.float64)
+            err = err_stored(y, r, "bf16")
+            print("%s %s n=%d err=%.3g" % (sub.name, name, e - s, err), flush=True)
+            assert err <= TOL["bf16"], (name, err)
