@@ -9,13 +9,15 @@ single line of numpy (the embedding sum and the layer stack loop).
 
 Sources, by page title and section:
   "Actions Speak Louder than Words" reading notes, §3.1 eqs. (1)-(3), §3.2,
-  §3.6 (M-FALCON candidate scoring); the gradients of eq. (2) (backward pass);
+  §3.3 (Stochastic Length), §3.6 (M-FALCON candidate scoring); the gradients of eq. (2)
+  (backward pass);
   "4.4 推荐模型的 Scaling", section "HSTU 层" and the toy HSTULayer ("代码");
   GenRank article (joto.ai), "(1) item-action组织" and "(2) 位置 & 时间偏差".
 """
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 import numpy as np
@@ -229,6 +231,42 @@ def layer(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float, H: 
     if return_intermediates:
         return y, z, o
     return y
+
+
+def sl_length(N_c: int, alpha: float) -> int:
+    """Target length of Stochastic Length ("Actions Speak Louder than Words" §3.3): the
+    subsequence has N_c^(alpha/2) elements, taken as the integer part."""
+    return int(math.floor(float(N_c) ** (alpha / 2.0)))
+
+
+def stochastic_length(offsets, N_c: int, alpha: float, u_user, key_tok):
+    """Stochastic Length ("Actions Speak Louder than Words" §3.3) on a jagged batch.
+
+    For user b with n_b events and L = sl_length(N_c, alpha): n_b <= L keeps the sequence;
+    n_b > L replaces it, with probability 1 - N_c^alpha / n_b^2, by L of its events, else keeps
+    it.  The random draws are inputs: user b is subsampled iff u_user[b] < 1 - N_c^alpha / n_b^2
+    (in float64), and the L events kept are those with the smallest key_tok (ties by lower
+    index), in their original order (a uniform random L-subset when the keys are i.i.d.).
+    Returns (out_offsets int64 [B+1], src_index int64 [T_out]: the input token of each output
+    token)."""
+    offs = np.asarray(offsets, dtype=np.int64)
+    u_user = np.asarray(u_user, dtype=np.float32)
+    key_tok = np.asarray(key_tok, dtype=np.float32)
+    L = sl_length(N_c, alpha)
+    c = float(N_c) ** float(alpha)
+    out_off = [0]
+    src = []
+    for b in range(len(offs) - 1):
+        s, e = int(offs[b]), int(offs[b + 1])
+        n = e - s
+        idx = np.arange(s, e, dtype=np.int64)
+        if n > L and float(u_user[b]) < 1.0 - c / float(n * n):
+            order = np.argsort(key_tok[s:e], kind="stable")[:L]
+            idx = s + np.sort(order).astype(np.int64)
+        src.append(idx)
+        out_off.append(out_off[-1] + len(idx))
+    return (np.asarray(out_off, dtype=np.int64),
+            np.concatenate(src) if src else np.zeros(0, np.int64))
 
 
 def embed_sum(item_table, action_table, item_ids, action_ids):
