@@ -202,6 +202,81 @@ def bench_attn_bwd(args, dev):
                                              for f in (0.1, 0.5, 0.9)]}}), flush=True)
 
 
+def bench_sl(args, dev):
+    """Stochastic Length on the device: the 8-layer stack's batch before subsampling (B=128,
+    lengths clip(Zipf(1.2), 1, 4096), token rows of 512 bf16 + int64 timestamps), N_c = 4096,
+    alpha = 1.6 (target 776 events); one step = select + offsets + gather.  Also reports the
+    share of events removed for alpha in 1.6 .. 2.0 on this batch."""
+    import numpy as np
+    import torch
+    from hstu_sequential_transduction_jagged_amd import binding, synth
+    rng = np.random.default_rng(1004)
+    lengths = synth.zipf_lengths(rng, 128, 1.2, 1, 4096)
+    offs_np = synth.offsets_from_lengths(lengths)
+    T = int(offs_np[-1])
+    D = 512
+    x = torch.from_numpy(synth.round_bf16(rng.standard_normal((T, D)).astype(np.float32))).to(dev, torch.bfloat16)
+    ts = torch.from_numpy(np.arange(T, dtype=np.int64)).to(dev)
+    offs = torch.from_numpy(offs_np.astype(np.int32)).to(dev)
+    u = torch.from_numpy(rng.random(128).astype(np.float32)).to(dev)
+    keys = torch.from_numpy(rng.random(T).astype(np.float32)).to(dev)
+    N_c, alpha = 4096, 1.6
+    max_len = int(lengths.max())
+    out_o = torch.empty(129, dtype=torch.int32, device=dev)
+    src = torch.empty(T, dtype=torch.int32, device=dev)
+    x_out, ts_out = torch.empty_like(x), torch.empty_like(ts)
+    ws = torch.empty(binding.lib().hstu_stochastic_length_workspace_bytes(128, T), dtype=torch.uint8,
+                     device=dev)
+    L = binding.lib()
+    stream = torch.cuda.current_stream(dev)
+    P = binding._ptr
+
+    def step(a=alpha):
+        st = L.hstu_stochastic_length(128, P(offs), max_len, T, N_c, a, P(u), P(keys), P(x), D * 2,
+                                      P(ts), P(out_o), P(src), P(x_out), P(ts_out), P(ws),
+                                      ws.numel(), binding._stream(dev))
+        binding._check("hstu_stochastic_length", st)
+
+    sweep = {}
+    for a in (1.6, 1.7, 1.8, 1.9, 2.0):
+        step(a)
+        torch.cuda.synchronize()
+        sweep[str(a)] = round(1.0 - int(out_o[-1].item()) / T, 4)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    kms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    k_avg = sum(kms) / len(kms) * 1e-3
+    T_out = int(out_o[-1].item())
+    # algorithmic bytes: keys and draws read once, each kept row + timestamp read and written,
+    # one source index written per kept event
+    alg = 4 * T + 4 * 128 + T_out * (2 * D * 2 + 16 + 4) + 8 * 129
+    gbs = alg / k_avg / 1e9
+    print(json.dumps({
+        "metric": "Stochastic Length on device: input tokens/s (select + offsets + row gather)",
+        "value": round(T / step_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u32/bf16 rows", "data": "synthetic",
+        "config": {"workload": "stack8 batch before SL", "B": 128, "T_in": T, "T_out": T_out,
+                   "N_c": N_c, "alpha": alpha, "target_len": int(np.floor(N_c ** (alpha / 2))),
+                   "row_bytes": D * 2},
+        "removed_share_by_alpha": sweep,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 4), "traffic": None,
+                     "kernel": "sl_select + sl_offsets + sl_gather (whole call)",
+                     "call_ms_p10_p50_p90": [round(kms[int(f * (len(kms) - 1))], 4)
+                                             for f in (0.1, 0.5, 0.9)]}}), flush=True)
+
+
 def bench_mfalcon(args, dev):
     """Candidate scoring over cached histories (M-FALCON): 16 users with the attention
     benchmark's history lengths, 1024 candidates each, H=8, d=64, position / time bias; one
@@ -268,11 +343,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8", "mfalcon", "attn_bwd"],
+    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8", "mfalcon", "attn_bwd", "sl"],
                     help="attn_long (the headline attention batch), stack8 (the 8-layer HSTU "
                          "stack forward: f1 GEMM + SiLU, attention, LayerNorm-gate-f2, residual) "
                          "mfalcon (1024 candidates per user scored over cached histories) or "
-                         "attn_bwd (the attention's gradients on the attn_long batch)")
+                         "attn_bwd (the attention's gradients on the attn_long batch) or sl "
+                         "(Stochastic Length on the stack's batch)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the HBM byte counters against a known traffic)")
@@ -311,6 +387,9 @@ def main():
         return
     if args.workload == "attn_bwd":
         bench_attn_bwd(args, dev)
+        return
+    if args.workload == "sl":
+        bench_sl(args, dev)
         return
     inp = synth.attn_long()
     lengths = np.diff(inp.offsets.astype(np.int64))

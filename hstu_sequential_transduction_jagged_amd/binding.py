@@ -54,6 +54,9 @@ SIGNATURES = {
                                         ctypes.POINTER(HstuBias), _P, _f32, _f32, _P, _P, _sz,
                                         _P]),
     "hstu_attn_candidates_workspace_bytes": (_sz, [_i32, _i32, _i32, _i64, _i64]),
+    "hstu_stochastic_length": (_i32, [_i32, _P, _i32, _i64, _i32, ctypes.c_double, _P, _P, _P,
+                                      _i64, _P, _P, _P, _P, _P, _P, _sz, _P]),
+    "hstu_stochastic_length_workspace_bytes": (_sz, [_i32, _i64]),
     "hstu_embed_sum_fwd": (_i32, [_i64, _i32, _P, _i64, _P, _i32, _P, _P, _P, _P]),
     "hstu_validate_offsets": (_i32, [_i32, _P, _i64, _i32, _P, _P]),
     "hstu_debug_buckets": (_i32, [_i32, _P, _P, _i32, _i32, _i64, _P, _P, _P, _P, _P]),
@@ -327,6 +330,27 @@ def hstu_attn_bwd(q, k, v, d_o, offsets, max_seqlen, bias: Optional[HstuBias] = 
                              _stream(q.device))
     _check("hstu_attn_bwd", st)
     return dq, dk, dv, dwp, dwt
+
+
+def hstu_stochastic_length(offsets, max_seqlen, N_c, alpha, u_user, key_tok, x=None, ts=None):
+    """Stochastic Length on the device.  Returns (out_offsets int32 [B+1], src_index int32 [T],
+    x_out, ts_out); outputs are sized like the inputs, the first out_offsets[B] rows valid."""
+    B = offsets.numel() - 1
+    T = key_tok.numel()
+    dev = offsets.device
+    out_offsets = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    src_index = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    x_out = torch.empty_like(x) if x is not None else None
+    ts_out = torch.empty_like(ts) if ts is not None else None
+    row_bytes = x[0].numel() * x.element_size() if x is not None and T else 0
+    ws = torch.empty(max(int(lib().hstu_stochastic_length_workspace_bytes(B, T)), 256),
+                     dtype=torch.uint8, device=dev)
+    st = lib().hstu_stochastic_length(B, _ptr(offsets), int(max_seqlen), T, int(N_c), float(alpha),
+                                      _ptr(u_user), _ptr(key_tok), _ptr(x), row_bytes, _ptr(ts),
+                                      _ptr(out_offsets), _ptr(src_index), _ptr(x_out),
+                                      _ptr(ts_out), _ptr(ws), ws.numel(), _stream(dev))
+    _check("hstu_stochastic_length", st)
+    return out_offsets, src_index[:T], x_out, ts_out
 
 
 def hstu_embed_sum_fwd(item_table, action_table, item_ids, action_ids, out=None):

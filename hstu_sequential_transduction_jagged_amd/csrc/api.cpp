@@ -7,6 +7,8 @@
 #include <cstring>
 
 #include "../../include/hstu.h"
+#include <cmath>
+
 #include "hstu_internal.h"
 
 using namespace hstu;
@@ -476,6 +478,42 @@ hstu_status hstu_attn_candidates_fwd(int32_t dt, int32_t B, int32_t H, int32_t d
   c.o = (bf16*)o; c.bias = ba; c.cand_ts = cand_timestamps;
   c.alpha = alpha; c.out_scale = out_scale;
   return check_hip(launch_attn_candidates_bf16(c, stream), "candidate attention launch");
+}
+
+size_t hstu_stochastic_length_workspace_bytes(int32_t B, int64_t total_tokens) {
+  if (B < 0 || total_tokens < 0) return 0;
+  return sl_workspace_bytes(B, total_tokens);
+}
+
+hstu_status hstu_stochastic_length(int32_t B, const int32_t* offsets, int32_t max_seqlen,
+                                   int64_t total_tokens, int32_t N_c, double alpha,
+                                   const float* u_user, const float* key_tok, const void* x,
+                                   int64_t row_bytes, const int64_t* ts, int32_t* out_offsets,
+                                   int32_t* src_index, void* x_out, int64_t* ts_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (B < 0 || max_seqlen < 0 || total_tokens < 0 || N_c < 1)
+    return fail(HSTU_ERR_INVALID_ARG, "bad sizes");
+  if (!(alpha > 0.0 && alpha <= 2.0)) return fail(HSTU_ERR_INVALID_ARG, "alpha must be in (0, 2]");
+  if (B == 0) return HSTU_OK;
+  if (!offsets || !u_user || !out_offsets || !workspace)
+    return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  if (total_tokens > 0 && (!key_tok || !src_index))
+    return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  if (x && (!x_out || row_bytes <= 0 || row_bytes % 16 || !aligned16(x) || !aligned16(x_out)))
+    return fail(HSTU_ERR_INVALID_ARG, "rows must be 16-byte multiples, 16-byte aligned");
+  if (ts && !ts_out) return fail(HSTU_ERR_INVALID_ARG, "ts_out missing");
+  const size_t need = sl_workspace_bytes(B, total_tokens);
+  if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(HSTU_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  // the target length N_c^(alpha/2) (integer part) and N_c^alpha, in double on the host
+  const int32_t L = (int32_t)floor(pow((double)N_c, alpha / 2.0));
+  const double c = pow((double)N_c, alpha);
+  return check_hip(launch_stochastic_length(B, offsets, max_seqlen, total_tokens, L, c, u_user,
+                                            key_tok, x, row_bytes, ts, out_offsets, src_index,
+                                            x_out, ts_out, workspace, stream),
+                   "stochastic length launch");
 }
 
 hstu_status hstu_embed_sum_fwd(int64_t total_tokens, int32_t dim, const void* item_table,

@@ -216,6 +216,15 @@ struct BwdArgs {
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int grid, int64_t n_pos_grad,
                                 int64_t n_time_grad, hipStream_t stream);
 
+// Stochastic Length (stochastic_length.hip).
+size_t sl_workspace_bytes(int32_t B, int64_t total_tokens);
+hipError_t launch_stochastic_length(int32_t B, const int32_t* offsets, int32_t max_seqlen,
+                                    int64_t total_tokens, int32_t L, double c, const float* u_user,
+                                    const float* key_tok, const void* x, int64_t row_bytes,
+                                    const int64_t* ts, int32_t* out_offsets, int32_t* src_index,
+                                    void* x_out, int64_t* ts_out, void* workspace,
+                                    hipStream_t stream);
+
 // Candidate scoring over a cached history (candidates.hip).
 struct CandLaunch {
   int32_t B, H, max_hist, max_cand;

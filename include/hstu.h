@@ -223,6 +223,29 @@ hstu_status hstu_attn_candidates_fwd(int32_t dt, int32_t B, int32_t H, int32_t d
 size_t hstu_attn_candidates_workspace_bytes(int32_t B, int32_t H, int32_t max_hist,
                                             int64_t total_hist, int64_t total_cand);
 
+/* Stochastic Length ("Actions Speak Louder than Words" reading notes §3.3) of a jagged batch.
+ * With L = floor(N_c^(alpha/2)): a user with n_b <= L events keeps them all; with n_b > L it is
+ * subsampled to L events iff u_user[b] < 1 - N_c^alpha / n_b^2 (in double: probability
+ * 1 - N_c^alpha / n_b^2 for uniform draws), else kept whole.  A subsampled user keeps the L
+ * events with the smallest key_tok (ties by lower index) in their original order (a uniform
+ * random subset for i.i.d. keys; keys must not be NaN).
+ *  offsets   device int32 [B + 1]; lengths <= max_seqlen; total_tokens = offsets[B]
+ *  N_c >= 1, 0 < alpha <= 2 (the pages use alpha in (1, 2]; 2 keeps every sequence)
+ *  u_user    device float [B];  key_tok device float [total_tokens]
+ *  x, row_bytes  optional rows [total_tokens][row_bytes] (row_bytes % 16 == 0) to gather into
+ *            x_out; ts optional int64 [total_tokens] to gather into ts_out
+ *  out_offsets  device int32 [B + 1]: the subsampled batch; out_offsets[B] <= total_tokens and
+ *            every new length <= the old one, so input-sized outputs and max_seqlen bound it
+ *  src_index device int32 [total_tokens]: the input token of each output token
+ *  workspace >= hstu_stochastic_length_workspace_bytes(B, total_tokens), 256-byte aligned. */
+hstu_status hstu_stochastic_length(int32_t B, const int32_t* offsets, int32_t max_seqlen,
+                                   int64_t total_tokens, int32_t N_c, double alpha,
+                                   const float* u_user, const float* key_tok, const void* x,
+                                   int64_t row_bytes, const int64_t* ts, int32_t* out_offsets,
+                                   int32_t* src_index, void* x_out, int64_t* ts_out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t hstu_stochastic_length_workspace_bytes(int32_t B, int64_t total_tokens);
+
 /* GenRank action-oriented tokens (GenRank article, part (1)): x[t] = item_table[item_ids[t]]
  * + action_table[action_ids[t]], bf16 in and out, fp32 add.  ids are device int32 [T];
  * an id outside [0, num_items) or [0, num_actions) contributes a zero row.  dim % 8 == 0. */
