@@ -233,6 +233,55 @@ def layer(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float, H: 
     return y
 
 
+def layer_bwd(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float, H: int,
+              dqk: int, dv: int, dY, residual: bool = False, ln_eps: float = 1e-5):
+    """Gradients of one HSTU layer ("Actions Speak Louder than Words" §3.1 eqs. (1)-(3)) for the
+    upstream gradient dY, by the chain rule through each equation in reverse:
+      eq. (3)  Y = (LN(O) * U) W2^T + b2 (+ X):  dW2 = dY^T G, db2 = sum_t dY, dG = dY W2,
+               dU = dG * LN(O), d(LN) = dG * U, dgamma = sum_t d(LN) * xhat, dbeta = sum_t d(LN),
+               dO = rstd (dxhat - mean(dxhat) - xhat mean(dxhat * xhat)), dxhat = d(LN) * gamma;
+      eq. (2)  attention_bwd (dQ, dK, dV, table gradients);
+      eq. (1)  Z = SiLU(X W1^T + b1), split U | V | Q | K:  dZpre = dZ * SiLU'(Zpre),
+               dW1 = dZpre^T X, db1 = sum_t dZpre, dX = dZpre W1 (+ dY).
+    Returns a dict of float64 arrays: dx, dw1, db1, dgamma, dbeta, dw2, db2, dw_pos, dw_time."""
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    x, w1, b1, w2, b2 = _f64(x), _f64(w1), _f64(b1), _f64(w2), _f64(b2)
+    gamma, beta, dY = _f64(gamma), _f64(beta), _f64(dY)
+    T, D = x.shape
+    HV, HQ = H * dv, H * dqk
+    _, z, o = layer(offs, x, w1, b1, gamma, beta, w2, b2, bias, alpha, H, dqk, dv,
+                    residual=residual, ln_eps=ln_eps, return_intermediates=True)
+    zpre = x @ w1.T + b1
+    U = z[:, :HV]
+    V, Q, K = z[:, HV:2 * HV], z[:, 2 * HV:2 * HV + HQ], z[:, 2 * HV + HQ:]
+    mean = o.mean(axis=1, keepdims=True)
+    xc = o - mean
+    rstd = 1.0 / np.sqrt((xc * xc).mean(axis=1, keepdims=True) + ln_eps)
+    xhat = xc * rstd
+    ln = xhat * gamma + beta
+    G = ln * U
+    dw2 = dY.T @ G
+    db2 = dY.sum(axis=0)
+    dG = dY @ w2
+    dU = dG * ln
+    dln = dG * U
+    dgamma = (dln * xhat).sum(axis=0)
+    dbeta = dln.sum(axis=0)
+    dxhat = dln * gamma
+    dO = rstd * (dxhat - dxhat.mean(axis=1, keepdims=True)
+                 - xhat * (dxhat * xhat).mean(axis=1, keepdims=True))
+    dq, dk, dvv, dwp, dwt = attention_bwd(offs, Q.reshape(T, H, dqk), K.reshape(T, H, dqk),
+                                          V.reshape(T, H, dv), dO.reshape(T, H, dv), bias, alpha)
+    dZ = np.concatenate([dU, dvv.reshape(T, HV), dq.reshape(T, HQ), dk.reshape(T, HQ)], axis=1)
+    sg = 1.0 / (1.0 + np.exp(-zpre))
+    dzpre = dZ * sg * (1.0 + zpre * (1.0 - sg))
+    dw1 = dzpre.T @ x
+    db1 = dzpre.sum(axis=0)
+    dx = dzpre @ w1 + (dY if residual else 0.0)
+    return dict(dx=dx, dw1=dw1, db1=db1, dgamma=dgamma, dbeta=dbeta, dw2=dw2, db2=db2,
+                dw_pos=dwp, dw_time=dwt, dzpre=dzpre, dO=dO, G=G)
+
+
 def sl_length(N_c: int, alpha: float) -> int:
     """Target length of Stochastic Length ("Actions Speak Louder than Words" §3.3): the
     subsequence has N_c^(alpha/2) elements, taken as the integer part."""
