@@ -202,6 +202,75 @@ def bench_attn_bwd(args, dev):
                                              for f in (0.1, 0.5, 0.9)]}}), flush=True)
 
 
+def bench_layer_bwd(args, dev):
+    """Gradients of one layer of the 8-layer stack (D=512, H=8, d=64, B=128 power-law users
+    after stochastic length, residual): one step = hstu_layer_bwd after a forward on the same
+    inputs (the forward is not timed)."""
+    import numpy as np
+    import torch
+    from hstu_sequential_transduction_jagged_amd import binding, synth
+    inp = synth.stack8(n_layers=1)
+    L = inp.layers[0]
+    bf = torch.bfloat16
+    t = lambda a, d=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev, d) if d else \
+        torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x = t(inp.x, bf)
+    offs = t(inp.offsets.astype(np.int32))
+    w1, b1, g, be, w2, b2 = t(L.w1, bf), t(L.b1), t(L.gamma), t(L.beta), t(L.w2, bf), t(L.b2)
+    bias = binding.make_bias(binding.BIAS_RAB_PT, t(inp.ts), t(L.bias.w_pos), t(L.bias.w_time))
+    D, H, T = inp.D, inp.H, inp.T
+    fws = torch.empty(binding.layer_workspace_bytes(inp.B, T, D, H, 64, 64, inp.max_seqlen),
+                      dtype=torch.uint8, device=dev)
+    binding.hstu_layer_fwd(x, offs, inp.max_seqlen, w1, b1, g, be, w2, b2, H, 64, 64, bias,
+                           inp.alpha, True, inp.ln_eps, workspace=fws)
+    rng = np.random.default_rng(11)
+    dy = t(synth.round_bf16(rng.standard_normal((T, D)).astype(np.float32)), bf)
+    bws = torch.empty(int(binding.lib().hstu_layer_bwd_workspace_bytes(inp.B, T, H, 64, 64,
+                                                                      inp.max_seqlen)),
+                      dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.hstu_layer_bwd(x, offs, inp.max_seqlen, w1, b1, g, be, w2, H, 64, 64, bias,
+                               inp.alpha, True, inp.ln_eps, fws, dy, workspace=bws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    kms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    k_avg = sum(kms) / len(kms) * 1e-3
+    lengths = np.diff(inp.offsets.astype(np.int64))
+    N1, HV = 2 * H * 128, H * 64
+    # algorithmic FLOPs: twice the forward's (input and weight gradients of both GEMMs, four
+    # products per causal pair in the attention)
+    flops = 2.0 * (2.0 * T * D * N1 + 2.0 * T * HV * D) + 2.0 * causal_flops(lengths, H, 64, 64)
+    tf = flops / k_avg / 1e12
+    print(json.dumps({
+        "metric": "HSTU layer backward TFLOP/s (2x the forward's GEMM and attention FLOPs)",
+        "value": round(flops / step_s / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "stack8 layer backward", "B": inp.B, "D": D, "H": H, "d_qk": 64,
+                   "d_v": 64, "T": int(T), "bias": "rab_pt P=256 NT=32", "alpha": inp.alpha,
+                   "seed": inp.seed},
+        "tokens_per_s": round(T / step_s, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "hstu_layer_bwd (whole call)",
+                     "call_ms_p10_p50_p90": [round(kms[int(f * (len(kms) - 1))], 4)
+                                             for f in (0.1, 0.5, 0.9)]}}), flush=True)
+
+
 def bench_sl(args, dev):
     """Stochastic Length on the device: the 8-layer stack's batch before subsampling (B=128,
     lengths clip(Zipf(1.2), 1, 4096), token rows of 512 bf16 + int64 timestamps), N_c = 4096,
@@ -343,12 +412,13 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8", "mfalcon", "attn_bwd", "sl"],
+    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8", "mfalcon", "attn_bwd", "sl", "layer_bwd"],
                     help="attn_long (the headline attention batch), stack8 (the 8-layer HSTU "
                          "stack forward: f1 GEMM + SiLU, attention, LayerNorm-gate-f2, residual) "
                          "mfalcon (1024 candidates per user scored over cached histories) or "
-                         "attn_bwd (the attention's gradients on the attn_long batch) or sl "
-                         "(Stochastic Length on the stack's batch)")
+                         "attn_bwd (the attention's gradients on the attn_long batch), sl "
+                         "(Stochastic Length on the stack's batch) or layer_bwd (one stack "
+                         "layer's gradients)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the HBM byte counters against a known traffic)")
@@ -390,6 +460,9 @@ def main():
         return
     if args.workload == "sl":
         bench_sl(args, dev)
+        return
+    if args.workload == "layer_bwd":
+        bench_layer_bwd(args, dev)
         return
     inp = synth.attn_long()
     lengths = np.diff(inp.offsets.astype(np.int64))

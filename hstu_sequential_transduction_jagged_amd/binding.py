@@ -54,6 +54,10 @@ SIGNATURES = {
                                         ctypes.POINTER(HstuBias), _P, _f32, _f32, _P, _P, _sz,
                                         _P]),
     "hstu_attn_candidates_workspace_bytes": (_sz, [_i32, _i32, _i32, _i64, _i64]),
+    "hstu_layer_bwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _P, _P, _P, _P,
+                              _f32, _P, ctypes.POINTER(HstuBias), _f32, _i32, _P, _P, _P, _P, _P,
+                              _P, _P, _P, _P, _P, _P, _P, _sz, _P]),
+    "hstu_layer_bwd_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "hstu_stochastic_length": (_i32, [_i32, _P, _i32, _i64, _i32, ctypes.c_double, _P, _P, _P,
                                       _i64, _P, _P, _P, _P, _P, _P, _sz, _P]),
     "hstu_stochastic_length_workspace_bytes": (_sz, [_i32, _i64]),
@@ -330,6 +334,38 @@ def hstu_attn_bwd(q, k, v, d_o, offsets, max_seqlen, bias: Optional[HstuBias] = 
                              _stream(q.device))
     _check("hstu_attn_bwd", st)
     return dq, dk, dv, dwp, dwt
+
+
+def hstu_layer_bwd(x, offsets, max_seqlen, w1, b1, gamma, beta, w2, H, dqk, dv, bias, alpha,
+                   residual, ln_eps, fwd_workspace, dy, workspace=None):
+    """Gradients of hstu_layer_fwd (called before with the same inputs and fwd_workspace).
+    Returns a dict: dx (bf16), dw1, db1, dgamma, dbeta, dw2, db2, dw_pos, dw_time (fp32)."""
+    T, D = x.shape
+    B = offsets.numel() - 1
+    N1 = w1.shape[0]
+    HV = H * dv
+    dev = x.device
+    f = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    out = dict(dx=torch.empty_like(x), dw1=f(N1, D), db1=f(N1), dgamma=f(HV), dbeta=f(HV),
+               dw2=f(D, HV), db2=f(D), dw_pos=None, dw_time=None)
+    bias = bias if bias is not None else make_bias(BIAS_NONE)
+    if bias.kind == BIAS_RAB_PT:
+        ts, wp, wt = bias._keep
+        out["dw_pos"] = torch.empty(wp.shape, dtype=torch.float32, device=dev)
+        out["dw_time"] = torch.empty(wt.shape, dtype=torch.float32, device=dev)
+    need = int(lib().hstu_layer_bwd_workspace_bytes(B, T, H, dqk, dv, int(max_seqlen)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib().hstu_layer_bwd(DTYPE_BF16, B, D, H, dqk, dv, _ptr(offsets), int(max_seqlen), T,
+                              _ptr(x), _ptr(w1), _ptr(b1), _ptr(gamma), _ptr(beta), float(ln_eps),
+                              _ptr(w2), ctypes.byref(bias), float(alpha), int(bool(residual)),
+                              _ptr(fwd_workspace), _ptr(dy), _ptr(out["dx"]), _ptr(out["dw1"]),
+                              _ptr(out["db1"]), _ptr(out["dgamma"]), _ptr(out["dbeta"]),
+                              _ptr(out["dw2"]), _ptr(out["db2"]), _ptr(out["dw_pos"]),
+                              _ptr(out["dw_time"]), _ptr(workspace), workspace.numel(),
+                              _stream(dev))
+    _check("hstu_layer_bwd", st)
+    return out
 
 
 def hstu_stochastic_length(offsets, max_seqlen, N_c, alpha, u_user, key_tok, x=None, ts=None):

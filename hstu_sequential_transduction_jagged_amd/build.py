@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhstu.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["attention.hip", "attention_bwd.hip", "schedule.hip", "gemm.hip", "candidates.hip", "stochastic_length.hip", "api.cpp"]
+SOURCES = ["attention.hip", "attention_bwd.hip", "schedule.hip", "gemm.hip", "candidates.hip", "stochastic_length.hip", "layer_bwd.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

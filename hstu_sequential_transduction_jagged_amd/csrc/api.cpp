@@ -331,6 +331,7 @@ hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   a.alpha = alpha;
   a.out_scale = out_scale;
   a.dq = (bf16*)dq; a.dk = (bf16*)dk; a.dv = (bf16*)dv;
+  a.dq_stride = a.dk_stride = a.dv_stride = (int64_t)H * 64;
   a.dw_pos = dw_pos; a.dw_time = dw_time;
   const int64_t n_pos = ba.kind == 1 ? (ba.pos_stride ? (int64_t)H * ba.pos_stride : ba.num_pos) : 0;
   const int64_t n_time = ba.kind == 1 ? (ba.time_stride ? (int64_t)H * ba.time_stride : ba.num_time) : 0;
@@ -478,6 +479,118 @@ hstu_status hstu_attn_candidates_fwd(int32_t dt, int32_t B, int32_t H, int32_t d
   c.o = (bf16*)o; c.bias = ba; c.cand_ts = cand_timestamps;
   c.alpha = alpha; c.out_scale = out_scale;
   return check_hip(launch_attn_candidates_bf16(c, stream), "candidate attention launch");
+}
+
+size_t hstu_layer_bwd_workspace_bytes(int32_t B, int64_t total_tokens, int32_t H, int32_t d_qk,
+                                      int32_t d_v, int32_t max_seqlen) {
+  if (B < 0 || total_tokens < 0 || H < 1 || d_qk < 1 || d_v < 1) return 0;
+  const int64_t N1 = 2LL * H * (d_qk + d_v), HV = (int64_t)H * d_v;
+  return 3 * align256((size_t)(total_tokens * HV * 2)) + align256((size_t)(total_tokens * N1 * 2)) +
+         align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens));
+}
+
+hstu_status hstu_layer_bwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,
+                           int32_t d_v, const int32_t* offsets, int32_t max_seqlen,
+                           int64_t total_tokens, const void* x, const void* w1, const float* b1,
+                           const float* ln_gamma, const float* ln_beta, float ln_eps,
+                           const void* w2, const hstu_bias* bias, float alpha, int32_t residual,
+                           const void* fwd_workspace, const void* dy, void* dx, float* dw1,
+                           float* db1, float* dgamma, float* dbeta, float* dw2, float* db2,
+                           float* dw_pos, float* dw_time, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (dt != HSTU_DTYPE_BF16) return fail(HSTU_ERR_UNSUPPORTED, "the layer backward runs in bf16 only");
+  if (d_qk != 64 || d_v != 64) return fail(HSTU_ERR_UNSUPPORTED, "the layer backward needs d = 64");
+  if (B < 0 || H < 1 || d_model < 32 || d_model % 32 || max_seqlen < 0 || total_tokens < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "bad sizes (d_model must be a positive multiple of 32)");
+  if ((int64_t)H * d_v > 2048) return fail(HSTU_ERR_UNSUPPORTED, "H * d_v above 2048");
+  if (!(ln_eps > 0.f)) return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be > 0");
+  BiasArgs ba;
+  hstu_status st = check_bias(bias, H, &ba);
+  if (st != HSTU_OK) return st;
+  if (ba.kind == 1 && (!dw_pos || !dw_time))
+    return fail(HSTU_ERR_INVALID_ARG, "rab_pt bias needs dw_pos and dw_time");
+  if (!dw1 || !db1 || !dgamma || !dbeta || !dw2 || !db2)
+    return fail(HSTU_ERR_INVALID_ARG, "null weight-gradient pointer");
+  const int64_t N1 = 2LL * H * (d_qk + d_v), HV = (int64_t)H * d_v, HQ = (int64_t)H * d_qk;
+  // weight gradients are zeroed first (so an empty batch leaves zeros)
+  st = check_hip(launch_zero_f32(dw1, N1 * d_model, stream), "zero");
+  if (st == HSTU_OK) st = check_hip(launch_zero_f32(db1, N1, stream), "zero");
+  if (st == HSTU_OK) st = check_hip(launch_zero_f32(dgamma, HV, stream), "zero");
+  if (st == HSTU_OK) st = check_hip(launch_zero_f32(dbeta, HV, stream), "zero");
+  if (st == HSTU_OK) st = check_hip(launch_zero_f32(dw2, d_model * HV, stream), "zero");
+  if (st == HSTU_OK) st = check_hip(launch_zero_f32(db2, d_model, stream), "zero");
+  if (st != HSTU_OK) return st;
+  if (ba.kind == 1) {
+    const int64_t np = ba.pos_stride ? (int64_t)H * ba.pos_stride : ba.num_pos;
+    const int64_t nt = ba.time_stride ? (int64_t)H * ba.time_stride : ba.num_time;
+    st = check_hip(launch_zero_f32(dw_pos, np, stream), "zero");
+    if (st == HSTU_OK) st = check_hip(launch_zero_f32(dw_time, nt, stream), "zero");
+    if (st != HSTU_OK) return st;
+  }
+  if (B == 0 || total_tokens == 0 || max_seqlen == 0) return HSTU_OK;
+  if (!offsets || !x || !w1 || !ln_gamma || !ln_beta || !w2 || !fwd_workspace || !dy || !dx ||
+      !workspace)
+    return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(dy) || !aligned16(dx) ||
+      ((uintptr_t)fwd_workspace & 255u))
+    return fail(HSTU_ERR_INVALID_ARG, "tensors must be 16-byte aligned (workspaces 256)");
+  const size_t need = hstu_layer_bwd_workspace_bytes(B, total_tokens, H, d_qk, d_v, max_seqlen);
+  if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(HSTU_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  if ((int64_t)(max_seqlen + 64) * N1 * 2 >= ((int64_t)1 << 31))
+    return fail(HSTU_ERR_UNSUPPORTED, "max_seqlen x row stride reaches 2 GiB per user");
+  size_t z_off = 0, o_off = 0;
+  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, &z_off, &o_off, nullptr);
+  const bf16* Z = (const bf16*)((const char*)fwd_workspace + z_off);
+  const bf16* O = (const bf16*)((const char*)fwd_workspace + o_off);
+  char* ws = (char*)workspace;
+  const size_t hvb = align256((size_t)(total_tokens * HV * 2));
+  bf16* dG = (bf16*)ws;
+  bf16* G = (bf16*)(ws + hvb);
+  bf16* dO = (bf16*)(ws + 2 * hvb);
+  bf16* dZ = (bf16*)(ws + 3 * hvb);
+  void* attn_ws = ws + 3 * hvb + align256((size_t)(total_tokens * N1 * 2));
+  const size_t attn_bytes = hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens);
+
+  LayerBwdLaunch L{};
+  L.T = total_tokens; L.D = d_model; L.HV = (int32_t)HV; L.N1 = (int32_t)N1;
+  L.residual = residual ? 1 : 0; L.eps = ln_eps;
+  L.x = (const bf16*)x; L.w1 = (const bf16*)w1; L.w2 = (const bf16*)w2; L.dy = (const bf16*)dy;
+  L.o = O; L.u = Z; L.u_stride = N1;
+  L.b1 = b1; L.gamma = ln_gamma; L.beta = ln_beta;
+  L.dg = dG; L.g = G; L.dO = dO; L.dz = dZ; L.dx = (bf16*)dx; L.dz_stride = N1;
+  L.dgamma = dgamma; L.dbeta = dbeta; L.dw1 = dw1; L.db1 = db1; L.dw2 = dw2; L.db2 = db2;
+  st = check_hip(launch_layer_bwd_pre(L, stream), "layer backward (LN, f2) launch");
+  if (st != HSTU_OK) return st;
+  // attention gradients straight into dZ's V | Q | K columns
+  st = hstu_attn_plan(dt, B, H, d_qk, offsets, max_seqlen, attn_ws, attn_bytes, stream);
+  if (st != HSTU_OK) return st;
+  int block_rows = 0;
+  st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
+  if (st != HSTU_OK) return st;
+  BwdArgs a{};
+  a.offsets = offsets;
+  a.work_count = (const int32_t*)attn_ws;
+  a.work = (const WorkItem*)((const char*)attn_ws + kHeader);
+  a.v = Z + HV; a.q = Z + 2 * HV; a.k = Z + 2 * HV + HQ; a.dout = dO;
+  a.q_stride = a.k_stride = a.v_stride = N1;
+  a.do_stride = HV;
+  a.H = H;
+  a.bias = ba;
+  a.alpha = alpha;
+  a.out_scale = 1.0f;
+  a.dv = dZ + HV; a.dq = dZ + 2 * HV; a.dk = dZ + 2 * HV + HQ;
+  a.dq_stride = a.dk_stride = a.dv_stride = N1;
+  a.dw_pos = dw_pos; a.dw_time = dw_time;
+  const int64_t n_pos = ba.kind == 1 ? (ba.pos_stride ? (int64_t)H * ba.pos_stride : ba.num_pos) : 0;
+  const int64_t n_time = ba.kind == 1 ? (ba.time_stride ? (int64_t)H * ba.time_stride : ba.num_time) : 0;
+  const int64_t grid = (int64_t)B * H * ceil_div(max_seqlen, block_rows);
+  if (grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
+  st = check_hip(launch_attn_bwd_bf16(a, (int)grid, n_pos, n_time, stream), "attention backward launch");
+  if (st != HSTU_OK) return st;
+  return check_hip(launch_layer_bwd_post(L, stream), "layer backward (f1) launch");
 }
 
 size_t hstu_stochastic_length_workspace_bytes(int32_t B, int64_t total_tokens) {

@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   // dQ rows: accumulator register 4 g + e holds d = 32 db + 8 g + 4 hf + e of this lane's row
   if (qvalid) {
     const float sc = a.alpha * a.out_scale;
-    bf16* op = a.dq + ((tok0 + row) * H + h) * kBD + 4 * hf;
+    bf16* op = a.dq + (tok0 + row) * a.dq_stride + (int64_t)h * kBD + 4 * hf;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -458,8 +458,8 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   // lane's key
   if (kvalid) {
     const float sv = a.out_scale, sk = a.alpha * a.out_scale;
-    bf16* kp = a.dk + ((tok0 + key) * H + h) * kBD + 4 * hf;
-    bf16* vp = a.dv + ((tok0 + key) * H + h) * kBD + 4 * hf;
+    bf16* kp = a.dk + (tok0 + key) * a.dk_stride + (int64_t)h * kBD + 4 * hf;
+    bf16* vp = a.dv + (tok0 + key) * a.dv_stride + (int64_t)h * kBD + 4 * hf;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll

@@ -210,11 +210,28 @@ struct BwdArgs {
   int32_t H;
   BiasArgs bias;
   float alpha, out_scale;
-  bf16 *dq, *dk, *dv;         // [T, H, 64]
+  bf16 *dq, *dk, *dv;         // [T, H, 64] rows with the strides below
+  int64_t dq_stride, dk_stride, dv_stride;
   float *dw_pos, *dw_time;    // position + time bias: gradients shaped like the tables
 };
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int grid, int64_t n_pos_grad,
                                 int64_t n_time_grad, hipStream_t stream);
+
+// Layer backward around the attention (layer_bwd.hip).
+struct LayerBwdLaunch {
+  int64_t T;
+  int32_t D, HV, N1, residual;
+  float eps;
+  const bf16 *x, *w1, *w2, *dy, *o, *u;  // u: Z's U columns, row stride u_stride
+  int64_t u_stride;
+  const float *b1, *gamma, *beta;
+  bf16 *dg, *g, *dO, *dz, *dx;            // dz: [T][N1] rows with stride dz_stride
+  int64_t dz_stride;
+  float *dgamma, *dbeta, *dw1, *db1, *dw2, *db2;
+};
+hipError_t launch_layer_bwd_pre(const LayerBwdLaunch& L, hipStream_t stream);
+hipError_t launch_layer_bwd_post(const LayerBwdLaunch& L, hipStream_t stream);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 
 // Stochastic Length (stochastic_length.hip).
 size_t sl_workspace_bytes(int32_t B, int64_t total_tokens);

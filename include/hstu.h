@@ -174,6 +174,30 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
                            int32_t residual, void* y, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Gradients of one HSTU layer ("Actions Speak Louder than Words" reading notes §3.1 eqs. (1)-(3))
+ * for an upstream gradient dY, after hstu_layer_fwd on the same inputs: fwd_workspace is that
+ * call's workspace, whose Z and O it reads (Zpre = X W1^T + b1 is recomputed).  By the chain
+ * rule through eq. (3) (dG = dY W2, dW2 = dY^T G, db2 = sum dY, the gate and LayerNorm),
+ * eq. (2) (hstu_attn_bwd, out_scale 1) and eq. (1) (dZpre = dZ SiLU'(Zpre), dX = dZpre W1,
+ * dW1 = dZpre^T X, db1 = sum dZpre), plus dY for the residual.
+ *  dt HSTU_DTYPE_BF16; d_qk = d_v = 64; d_model % 32 == 0; H d_v <= 2048
+ *  dy, dx    device bf16 [T, d_model]
+ *  dw1 fp32 [2H(d_qk+d_v), d_model], db1 [2H(d_qk+d_v)], dgamma / dbeta [H d_v],
+ *  dw2 fp32 [d_model, H d_v], db2 [d_model]; dw_pos / dw_time as for hstu_attn_bwd: all
+ *            overwritten (sums over tokens, added with atomics: last bits vary between runs)
+ *  workspace >= hstu_layer_bwd_workspace_bytes(...), 256-byte aligned. */
+hstu_status hstu_layer_bwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,
+                           int32_t d_v, const int32_t* offsets, int32_t max_seqlen,
+                           int64_t total_tokens, const void* x, const void* w1, const float* b1,
+                           const float* ln_gamma, const float* ln_beta, float ln_eps,
+                           const void* w2, const hstu_bias* bias, float alpha, int32_t residual,
+                           const void* fwd_workspace, const void* dy, void* dx, float* dw1,
+                           float* db1, float* dgamma, float* dbeta, float* dw2, float* db2,
+                           float* dw_pos, float* dw_time, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+size_t hstu_layer_bwd_workspace_bytes(int32_t B, int64_t total_tokens, int32_t H, int32_t d_qk,
+                                      int32_t d_v, int32_t max_seqlen);
+
 /* Byte offsets of Z, O and the attention workspace inside the layer workspace. */
 void hstu_layer_workspace_offsets(int64_t total_tokens, int32_t H, int32_t d_qk, int32_t d_v,
                                   size_t* z_offset, size_t* o_offset, size_t* attn_offset);

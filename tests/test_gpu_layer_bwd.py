@@ -1,0 +1,67 @@
+"""GPU gradients of one HSTU layer ("Actions Speak Louder than Words" §3.1 eqs. (1)-(3)) against
+the fp64 oracle, through the C ABI.
+
+The layer stores Z and O in bf16 (the forward's storage format) and the backward keeps dG, G,
+dO and dZ in bf16 between its kernels, so each gradient carries bf16 roundings of those
+intermediates (unit roundoff 2^-8 each), amplified where LayerNorm divides by a row's standard
+deviation.  The oracle alone, with only its Z and O rounded to bf16, already moves dW1, dW2 and
+the table gradients by up to 2.3e-2 and dO by 0.23 (max-abs relative to RMS, on the wide case
+below); the backward's own bf16 intermediates add about as much again.  Bounds (max-abs error
+relative to the RMS of the fp64 reference): 5e-2 for dx, 7.5e-2 for the fp32 weight, bias,
+LayerNorm and table gradients (sums over tokens of products of those intermediates).
+Cases: ragged users (empty, single token, several 32/64/256-row tiles), with and without
+residual, position + time bias and none, and a wider model (D = 512, H = 16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from hstu_sequential_transduction_jagged_amd import binding, synth
+from tests.hstu_testutil import DevLayer, err_rms, oracle_bias, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"dx": 5e-2}
+TOL_SUMS = 7.5e-2
+
+
+def _check(inp, seed=3):
+    rng = np.random.default_rng(seed)
+    dY = synth.round_bf16(rng.standard_normal((inp.T, inp.D)).astype(np.float32))
+    d = DevLayer(inp)
+    L = d.layers[0]
+    ws = torch.empty(binding.layer_workspace_bytes(inp.B, inp.T, inp.D, inp.H, inp.dqk, inp.dv,
+                                                   inp.max_seqlen), dtype=torch.uint8, device="cuda")
+    d.run_layer(d.x, workspace=ws)
+    got = binding.hstu_layer_bwd(d.x, d.offsets, inp.max_seqlen, L["w1"], L["b1"], L["gamma"],
+                                 L["beta"], L["w2"], inp.H, inp.dqk, inp.dv, L["bias"], inp.alpha,
+                                 inp.residual, inp.ln_eps, ws, to_dev(dY, torch.bfloat16))
+    torch.cuda.synchronize()
+    P = inp.layers[0]
+    ref = oracle.layer_bwd(inp.offsets, inp.x, P.w1, P.b1, P.gamma, P.beta, P.w2, P.b2,
+                           oracle_bias(P.bias, inp.ts, inp.H), inp.alpha, inp.H, inp.dqk, inp.dv,
+                           dY, residual=inp.residual, ln_eps=inp.ln_eps)
+    for name in ("dx", "dw1", "db1", "dgamma", "dbeta", "dw2", "db2", "dw_pos", "dw_time"):
+        if ref[name] is None:
+            assert got[name] is None
+            continue
+        y = got[name].float().cpu().numpy().astype(np.float64)
+        e = err_rms(y, ref[name])
+        print("%s %s err=%.3g" % (inp.name, name, e), flush=True)
+        assert e <= TOL.get(name, TOL_SUMS), (name, e)
+
+
+@pytest.mark.parametrize("residual", [False, True])
+@pytest.mark.parametrize("kind", [synth.BIAS_RAB_PT, synth.BIAS_NONE])
+def test_layer_bwd_ragged(kind, residual):
+    inp = synth.make_layer("lbwd", 40, [0, 1, 33, 130, 300], D=256, H=2, d=64, alpha=1.0 / 64,
+                           residual=residual, bias_kind=kind, P=64, NT=16, table_std=0.5,
+                           randomize_affine=True)
+    _check(inp)
+
+
+def test_layer_bwd_wide():
+    inp = synth.make_layer("lbwd_wide", 41, [70, 257], D=512, H=16, d=64, alpha=1.0 / 128,
+                           residual=True, P=128, NT=32, table_std=0.2, randomize_affine=True)
+    _check(inp, seed=4)
