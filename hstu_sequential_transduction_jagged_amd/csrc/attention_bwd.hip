@@ -17,8 +17,10 @@
 //     dK^T += Q^T G with dO^T and Q^T read from the row-major query tiles with transposing LDS
 //     reads; the table gradients are summed per workgroup in LDS and added to the tables with
 //     one global atomic per entry touched (so their summation order varies between runs).
-// SiLU and its derivative are evaluated exactly per element (exp2 and reciprocal); the bias of
-// every element comes from LDS-resident tables.
+// Per 32x32 tile with one bias value (no bias, or saturated position bucket and one time
+// bucket, decided exactly from the tile's extreme times) and |alpha s| <= kTaylorD, SiLU and
+// SiLU' come from second-order expansions in the raw score (four fmas per score); elsewhere they
+// are evaluated exactly (exp2 and reciprocal) with the bias of every element from LDS tables.
 #include "hstu_internal.h"
 
 namespace hstu {
@@ -42,8 +44,50 @@ struct __attribute__((aligned(16))) SmemBwd {
   float wtime[kMaxTimeBuckets];  // w_time[h]
   float gpos[kMaxPosBuckets];    // dkv kernel: this workgroup's position-table gradient
   float gtime[kMaxTimeBuckets];  // dkv kernel: this workgroup's time-table gradient
-  __attribute__((aligned(16))) int64_t tmm[2][2][2];  // dkv kernel: per 32-row half of a tile: min, max time
+  __attribute__((aligned(16))) int64_t tmm[2][2][2];  // per 32-row half of a tile: min, max time
+  // per time bucket, for tiles whose position bucket saturates: the bias c and the Taylor
+  // coefficients of SiLU and SiLU' in the raw score (see silu_taylor)
+  __attribute__((aligned(16))) float tay[kMaxTimeBuckets][8];
 };
+
+// Second-order expansions in the raw score s around the bias c (x = c + alpha s):
+//   SiLU(x)  ~ A0 + A1 s + A2 s^2,   SiLU'(x) ~ B0 + B1 s + B2 s^2
+// with SiLU' = sg + c p, SiLU^(2) = 2 p + c p (1 - 2 sg), SiLU^(3) = 3 p (1 - 2 sg)
+// + c (p (1 - 2 sg)^2 - 2 p^2), sg = 1 / (1 + e^-c), p = sg (1 - sg); sg and 1 - sg from
+// e^-|c| (no overflow).  Used when |alpha s| <= kTaylorD over the tile: the remainders are at
+// most max|SiLU^(3)| kTaylorD^3 / 6 <= 3.3e-6 and max|SiLU^(4)| kTaylorD^3 / 6 <= 5.4e-6
+// (max|SiLU^(3)| = 0.31, max|SiLU^(4)| = 0.5), relative to the value at most ~1e-4 (the linear
+// term is exact where SiLU vanishes).
+__device__ __forceinline__ void silu_taylor(float c, float al, float* o) {
+  const float e = exp2f(-kLog2e * fabsf(c));
+  const float inv = 1.0f / (1.0f + e);
+  const float sg = c >= 0.f ? inv : e * inv;
+  const float om = c >= 0.f ? e * inv : inv;  // 1 - sg
+  const float p = sg * om, d = om - sg;
+  const float f0 = c * sg, f1 = sg + c * p, f2 = 2.0f * p + c * p * d;
+  const float f3 = 3.0f * p * d + c * (p * d * d - 2.0f * p * p);
+  o[0] = c;
+  o[1] = f0;
+  o[2] = al * f1;
+  o[3] = 0.5f * al * al * f2;
+  o[4] = f1;
+  o[5] = al * f2;
+  o[6] = 0.5f * al * al * f3;
+  o[7] = 0.f;
+}
+
+// max over the wave of |x[r]|, as a wave-uniform value
+__device__ __forceinline__ float wave_max_abs16(const f32x16& x) {
+  float m = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(x[r]));
+  m = fmaxf(m, dpp<kDppXor1>(m));
+  m = fmaxf(m, dpp<kDppXor2>(m));
+  m = fmaxf(m, dpp<kDppHalfMirror>(m));
+  m = fmaxf(m, dpp<kDppMirror>(m));
+  auto at = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), l)); };
+  return fmaxf(fmaxf(at(0), at(16)), fmaxf(at(32), at(48)));
+}
 
 // sum over the 64 lanes of a wave, as a wave-uniform value
 __device__ __forceinline__ float wave_sum(float v) {
@@ -130,12 +174,26 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     }
   }
   const int64_t tq = KIND == 1 && qvalid ? a.bias.ts[tok0 + row] : 0;
+  int64_t tq_min = 0, tq_max = 0;
+  if (KIND == 1) {
+    int64_t mn = qvalid ? tq : kTMax, mx = qvalid ? tq : kTMin;
+    half_minmax(mn, mx);
+    tq_min = uniform_i64(mn);
+    tq_max = uniform_i64(mx);
+  }
   float slope = 0.f;
+  float k0c[8];
   if (KIND == 1) {
     for (int i = tid; i < a.bias.num_pos; i += kBThreads) sm.wpos[i] = a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i];
-    if (tid < a.bias.num_time) sm.wtime[tid] = a.bias.w_time[(int64_t)h * a.bias.time_stride + tid];
+    if (tid < a.bias.num_time) {
+      const float wt = a.bias.w_time[(int64_t)h * a.bias.time_stride + tid];
+      sm.wtime[tid] = wt;
+      silu_taylor(a.bias.w_pos[(int64_t)h * a.bias.pos_stride + Pm1] + wt, a.alpha, &sm.tay[tid][0]);
+    }
   } else if (KIND == 2) {
     slope = a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H);
+  } else {
+    silu_taylor(0.f, a.alpha, k0c);
   }
 
   // staging: thread t moves 16-byte chunk t % 8 of row t / 8 of K and V
@@ -151,13 +209,21 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
                                              KIND == 1 ? 8 * q_end : 0, 0x00020000);
   stg.xoff = (uint32_t)srow * stg.xs + 16u * sch;
   stg.yoff = (uint32_t)srow * stg.ys + 16u * sch;
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, int r0) {
     *(u32x4*)(&sm.x[buf][srow * kBRow + 8 * sch]) = stg.xreg;
     *(u32x4*)(&sm.y[buf][srow * kBRow + 8 * sch]) = stg.yreg;
-    if (KIND == 1 && wave == 0) sm.t[buf][lane] = (int64_t)(((uint64_t)stg.thi << 32) | stg.tlo);
+    if (KIND == 1 && wave == 0) {
+      const int64_t tt = (int64_t)(((uint64_t)stg.thi << 32) | stg.tlo);
+      sm.t[buf][lane] = tt;
+      // the extremes of each 32-key half's times (keys at or past q_end excluded)
+      const bool ok = r0 + lane < q_end;
+      int64_t mn = ok ? tt : kTMax, mx = ok ? tt : kTMin;
+      half_minmax(mn, mx);
+      if (l32 == 0) *(i64x2*)(&sm.tmm[buf][hf][0]) = i64x2{mn, mx};
+    }
   };
   stg.load(0, KIND == 1 && wave == 0, lane);
-  lstore(0);
+  lstore(0, 0);
   __syncthreads();
 
   // transposing K reads: lane i of each 16-lane group reads keys 4 hf + (i % 16) / 4 (+ the
@@ -185,16 +251,54 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], s, 0, 0, 0);
         da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[ks], dop[ks], da, 0, 0, 0);
       }
+      // one bias value over the tile (no bias, or saturated position and one time bucket)
+      // and a small score range: SiLU' from its expansion around the bias
+      bool taylor = false;
+      float B0 = 0.f, B1 = 0.f, B2 = 0.f;
+      if (KIND != 2) {
+        const float D = fabsf(a.alpha) * 1.0001f * uniform_f32(wave_max_abs16(s));
+        if (D <= kTaylorD) {
+          if (KIND == 0) {
+            taylor = true;
+            B0 = k0c[4];
+            B1 = k0c[5];
+            B2 = k0c[6];
+          } else {
+            const i64x2 mm = *(const i64x2*)(&sm.tmm[buf][hk][0]);
+            const int64_t kmin = uniform_i64(mm[0]), kmax = uniform_i64(mm[1]);
+            const int tlo = time_bucket(tq_min - kmax, NTm1), thi = time_bucket(tq_max - kmin, NTm1);
+            if (qw0 - (j0h + 31) >= Pm1 && tlo == thi) {
+              taylor = true;
+              const f32x4 bc = *(const f32x4*)(&sm.tay[tlo][4]);
+              B0 = uniform_f32(bc[0]);
+              B1 = uniform_f32(bc[1]);
+              B2 = uniform_f32(bc[2]);
+            }
+          }
+        }
+      }
       f32x16 g;
+      if (taylor) {
+        // keys past the query rows only where the tile crosses the diagonal; keys past n and
+        // rows past the item have zero K / V / dO rows, so their g is 0 already
+        const bool diag = j0h + 31 > qw0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jl = 32 * hk + accrow(r) + 4 * hf;  // key within the tile
-        const int j = t * kBTile + jl;
-        const int64_t dt = KIND == 1 ? tq - sm.t[buf][jl] : 0;
-        const float x = __builtin_fmaf(a.alpha, s[r], pair_bias<KIND>(sm, row - j, dt, Pm1, NTm1, slope));
-        float aa, d1;
-        silu_and_grad(x, aa, d1);
-        g[r] = (j <= row && qvalid) ? da[r] * d1 : 0.f;
+        for (int r = 0; r < 16; ++r) {
+          const float d1 = __builtin_fmaf(__builtin_fmaf(B2, s[r], B1), s[r], B0);
+          const int j = j0h + accrow(r) + 4 * hf;
+          g[r] = (!diag || j <= row) ? da[r] * d1 : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jl = 32 * hk + accrow(r) + 4 * hf;  // key within the tile
+          const int j = t * kBTile + jl;
+          const int64_t dt = KIND == 1 ? tq - sm.t[buf][jl] : 0;
+          const float x = __builtin_fmaf(a.alpha, s[r], pair_bias<KIND>(sm, row - j, dt, Pm1, NTm1, slope));
+          float aa, d1;
+          silu_and_grad(x, aa, d1);
+          g[r] = (j <= row && qvalid) ? da[r] * d1 : 0.f;
+        }
       }
       bf16x8 gop[2];
       {
@@ -219,7 +323,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktop, gop[mm], acc[db], 0, 0, 0);
         }
     }
-    if (more) lstore(buf ^ 1);
+    if (more) lstore(buf ^ 1, (t + 1) * kBTile);
     __syncthreads();
   }
 
@@ -289,17 +393,22 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     tk_max = uniform_i64(mx);
   }
   float slope = 0.f;
+  float k0c[8];
   if (KIND == 1) {
     for (int i = tid; i < a.bias.num_pos; i += kBThreads) {
       sm.wpos[i] = a.bias.w_pos[(int64_t)h * a.bias.pos_stride + i];
       sm.gpos[i] = 0.f;
     }
     if (tid < a.bias.num_time) {
-      sm.wtime[tid] = a.bias.w_time[(int64_t)h * a.bias.time_stride + tid];
+      const float wt = a.bias.w_time[(int64_t)h * a.bias.time_stride + tid];
+      sm.wtime[tid] = wt;
       sm.gtime[tid] = 0.f;
+      silu_taylor(a.bias.w_pos[(int64_t)h * a.bias.pos_stride + Pm1] + wt, a.alpha, &sm.tay[tid][0]);
     }
   } else if (KIND == 2) {
     slope = a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H);
+  } else {
+    silu_taylor(0.f, a.alpha, k0c);
   }
 
   // query tiles from the one holding row k0 to the user's last row
@@ -359,28 +468,64 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kop[ks], s, 0, 0, 0);
         dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da_[ks], vop[ks], dd, 0, 0, 0);
       }
-      // register r: query i = i0h + accrow(r) + 4 hf of this lane's key
-      f32x16 p, g;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int il = 32 * hq + accrow(r) + 4 * hf;
-        const int i = t * kBTile + il;
-        const int64_t dt = KIND == 1 ? sm.t[buf][il] - tk : 0;
-        const float x = __builtin_fmaf(a.alpha, s[r], pair_bias<KIND>(sm, i - key, dt, Pm1, NTm1, slope));
-        float aa, d1;
-        silu_and_grad(x, aa, d1);
-        const bool ok = i >= key && i < n && kvalid;
-        p[r] = ok ? aa : 0.f;
-        g[r] = ok ? dd[r] * d1 : 0.f;
-      }
+      // the tile's bias class: one position bucket when i - j >= P - 1 for every pair, one or
+      // two time buckets when the extreme times say so (exactly)
+      int tlo = 0, thi = 0;
+      bool sat = true;
       if (KIND == 1) {
-        // table gradients of this 32x32 tile: one position bucket when i - j >= P - 1 for every
-        // pair, one or two time buckets when the extreme times say so (exactly); then tile
-        // sums, else one LDS add per score
         const i64x2 qmm = *(const i64x2*)(&sm.tmm[buf][hq][0]);
         const int64_t qmin = uniform_i64(qmm[0]), qmax = uniform_i64(qmm[1]);
-        const int tlo = time_bucket(qmin - tk_max, NTm1), thi = time_bucket(qmax - tk_min, NTm1);
-        const bool sat = i0h - (kw0 + 31) >= Pm1;
+        tlo = time_bucket(qmin - tk_max, NTm1);
+        thi = time_bucket(qmax - tk_min, NTm1);
+        sat = i0h - (kw0 + 31) >= Pm1;
+      }
+      bool taylor = false;
+      float A0 = 0.f, A1 = 0.f, A2 = 0.f, B0 = 0.f, B1 = 0.f, B2 = 0.f;
+      if (KIND != 2 && sat && tlo == thi) {
+        const float D = fabsf(a.alpha) * 1.0001f * uniform_f32(wave_max_abs16(s));
+        if (D <= kTaylorD) {
+          taylor = true;
+          if (KIND == 0) {
+            A0 = k0c[1]; A1 = k0c[2]; A2 = k0c[3]; B0 = k0c[4]; B1 = k0c[5]; B2 = k0c[6];
+          } else {
+            const f32x4 ac = *(const f32x4*)(&sm.tay[tlo][0]);
+            const f32x4 bc = *(const f32x4*)(&sm.tay[tlo][4]);
+            A0 = uniform_f32(ac[1]); A1 = uniform_f32(ac[2]); A2 = uniform_f32(ac[3]);
+            B0 = uniform_f32(bc[0]); B1 = uniform_f32(bc[1]); B2 = uniform_f32(bc[2]);
+          }
+        }
+      }
+      // register r: query i = i0h + accrow(r) + 4 hf of this lane's key
+      f32x16 p, g;
+      if (taylor) {
+        // queries before the key only where the tile crosses the diagonal; rows past n and keys
+        // past the item have zero Q / dO / K / V rows (their g is 0, their P meets zero dO)
+        const bool diag = i0h < kw0 + 31;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float aa = __builtin_fmaf(__builtin_fmaf(A2, s[r], A1), s[r], A0);
+          const float d1 = __builtin_fmaf(__builtin_fmaf(B2, s[r], B1), s[r], B0);
+          const bool ok = !diag || i0h + accrow(r) + 4 * hf >= key;
+          p[r] = ok ? aa : 0.f;
+          g[r] = ok ? dd[r] * d1 : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int il = 32 * hq + accrow(r) + 4 * hf;
+          const int i = t * kBTile + il;
+          const int64_t dt = KIND == 1 ? sm.t[buf][il] - tk : 0;
+          const float x = __builtin_fmaf(a.alpha, s[r], pair_bias<KIND>(sm, i - key, dt, Pm1, NTm1, slope));
+          float aa, d1;
+          silu_and_grad(x, aa, d1);
+          const bool ok = i >= key && i < n && kvalid;
+          p[r] = ok ? aa : 0.f;
+          g[r] = ok ? dd[r] * d1 : 0.f;
+        }
+      }
+      if (KIND == 1) {
+        // table gradients of this tile: tile sums for one position bucket and one or two time
+        // buckets, else one LDS add per score
         float gs = 0.f, ghi = 0.f;
         const int64_t tlim = tk + (((int64_t)1 << thi) - 1);  // dt >= 2^thi - 1
 #pragma unroll
