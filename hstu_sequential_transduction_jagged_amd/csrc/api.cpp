@@ -108,11 +108,18 @@ static size_t tclass_bytes(int32_t B, int32_t max_seqlen, int64_t total_tokens) 
   return (size_t)rows * (size_t)tclass_cols(max_seqlen) * 8;
 }
 
+// per (32-key block, head) key norm bounds, block rows numbered as the tile classes
+static size_t knorm_bytes(int32_t B, int32_t H, int64_t total_tokens) {
+  const int64_t rows = (total_tokens + 31 * (int64_t)B) / 32 + 1;
+  return (size_t)rows * (size_t)H * 4;
+}
+
 size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64_t total_tokens) {
   if (B < 0 || H < 0 || max_seqlen < 0 || total_tokens < 0) return 0;
   return worklist_bytes(B, H, max_seqlen) + align256((size_t)total_tokens * sizeof(TimeStat)) +
          align256((size_t)total_tokens * sizeof(int32_t)) +
-         align256(tclass_bytes(B, max_seqlen, total_tokens));
+         align256(tclass_bytes(B, max_seqlen, total_tokens)) +
+         align256(knorm_bytes(B, H, total_tokens));
 }
 
 int32_t hstu_attn_block_rows(int32_t dt, int32_t d) {
@@ -197,6 +204,12 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   TimeStat* tstat = (TimeStat*)((char*)workspace + worklist_bytes(B, H, max_seqlen));
   int32_t* trel = (int32_t*)((char*)tstat + align256((size_t)total_tokens * sizeof(TimeStat)));
   uint32_t* tclass = (uint32_t*)((char*)trel + align256((size_t)total_tokens * sizeof(int32_t)));
+  float* knorm = (float*)((char*)tclass + align256(tclass_bytes(B, max_seqlen, total_tokens)));
+  if (dt == HSTU_DTYPE_BF16) {
+    st = check_hip(launch_key_norm(B, offsets, max_seqlen, k, k_row_stride, H, knorm, stream),
+                   "key norm launch");
+    if (st != HSTU_OK) return st;
+  }
   if (dt == HSTU_DTYPE_BF16 && ba.kind == 1) {
     st = check_hip(launch_time_stats(B, offsets, ba.ts, max_seqlen, tstat, trel, stream), "time stats launch");
     if (st != HSTU_OK) return st;
@@ -227,6 +240,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   a.alpha = alpha;
   a.out_scale = out_scale;
   a.ostats = ostats;
+  a.knorm = knorm;
   const int64_t grid = (int64_t)B * H * max_tiles;
   if (grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
   hipError_t e = dt == HSTU_DTYPE_BF16 ? launch_attn_bf16(d_qk, a, (int)grid, stream)

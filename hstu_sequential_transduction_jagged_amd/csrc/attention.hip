@@ -128,8 +128,44 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const int32_t* __restri
 }
 
 // ============================================================================================
-// bf16, d = 64: 8 waves x 32 queries = 256 query rows per work item, 64 keys per LDS stage,
-// four waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time tables,
+// Key norm bounds: for every 32-key block of a user (blocks start at the user's first token)
+// and head h, the largest squared norm of the block's key rows, in fp32 from the bf16 keys,
+// at row tclass_row0(tok0, b) + block.  One workgroup per (user, block): thread t takes
+// 16-byte chunk t % 8 of token t / 8's head row.
+// ============================================================================================
+__global__ __launch_bounds__(256) void key_norm_kernel(const int32_t* __restrict__ offsets,
+                                                       const bf16* __restrict__ k, int64_t k_stride,
+                                                       int32_t H, float* __restrict__ knorm) {
+  __shared__ float red[4];
+  const int b = blockIdx.x, blk = blockIdx.y, tid = threadIdx.x;
+  const int64_t tok0 = offsets[b];
+  const int n = offsets[b + 1] - offsets[b];
+  if (32 * blk >= n) return;
+  const int tok = 32 * blk + (tid >> 3);
+  const bool valid = tok < n;
+  float* dst = knorm + (tclass_row0(tok0, b) + blk) * H;
+  for (int h = 0; h < H; ++h) {
+    float acc = 0.f;
+    if (valid) {
+      const bf16x8 kv = *(const bf16x8*)(k + (tok0 + tok) * k_stride + (int64_t)h * 64 + 8 * (tid & 7));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
+        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
+      }
+    }
+    const float m = wave_max_dpp(sum8(acc));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    if (tid == 0) dst[h] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+  }
+}
+
+// ============================================================================================
+// bf16, d = 64: 8 waves x 32 queries = 256 query rows per work item, 64 keys per LDS stage
+// (a ring of three stages filled by direct global -> LDS transfers two tiles ahead), four
+// waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time tables,
 // 2 ALiBi).
 // ============================================================================================
 constexpr int kWaves = 8;
@@ -139,18 +175,22 @@ constexpr int kBR = kWaves * kQW;
 constexpr int kKB = 64;
 constexpr int kD = 64;
 
-// LDS rows of 64 bf16 are padded to 144 bytes: 16 lanes reading the same 16-byte column of 16
-// consecutive rows then hit 16 distinct groups of 4 banks (row * 36 words mod 64 is a
-// permutation of the multiples of 4), and every operand read is one base address per lane
-// plus an immediate offset.
-constexpr int kRow = 72;  // bf16 elements per padded row
-
+// K and V rows of 64 bf16 (128 bytes, eight 16-byte chunks) are stored unpadded with chunk c of
+// row r at position c ^ swz(r), swz(r) = ((r >> 1) & 1) << 2 | ((r >> 2) & 3).  Three access
+// patterns then meet the 64 banks without conflicts: the K operand reads (16 lanes, one chunk of
+// 16 consecutive rows: even and odd rows take the two 64-byte halves and swz is a bijection on
+// each), the transposing V reads (32 lanes, chunks 0..3 or 4..7 of 4 consecutive rows: rows r
+// and r + 2 differ in bit 2 of swz) and the transfers, which write whole rows.
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+struct __attribute__((aligned(16))) Stage {
+  __attribute__((aligned(16))) bf16 k[kKB * kD];   // row = key, swizzled chunks
+  __attribute__((aligned(16))) bf16 v[kKB * kD];
+  __attribute__((aligned(16))) int32_t krel[64];   // key time minus its 32-key block's minimum
+  __attribute__((aligned(16))) uint32_t cls[64];   // tile class entries (block, half, word)
+  __attribute__((aligned(16))) float kn[64];       // [0], [1]: max squared key norm of the halves
+  __attribute__((aligned(16))) float dummy[64];    // target of the transfers that carry nothing
+};
 struct __attribute__((aligned(16))) SmemBf16 {
-  __attribute__((aligned(16))) bf16 k[2][kKB * kRow];   // row = key
-  __attribute__((aligned(16))) bf16 v[2][kKB * kRow];   // row = key
-  __attribute__((aligned(16))) int32_t krel[2][kKB];    // key time minus its 32-key block's minimum
-  __attribute__((aligned(16))) float knorm2[2][kWaves]; // per staging wave: max squared key norm
-  __attribute__((aligned(16))) uint32_t cls[2][kWaves][2][2];  // tile class entries (info, dq)
   __attribute__((aligned(16))) float tay[kMaxTimeBuckets][4];  // per time bucket: c, a0, a1, a2
   float wposx[kMaxPosBuckets + 96];  // -log2(e) * w_pos[h][clamp(i - j, 0, P - 1)] at i - j + 32
   float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
@@ -160,6 +200,7 @@ struct __attribute__((aligned(16))) SmemBf16 {
 template <int KIND, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) {
   __shared__ SmemBf16 sm;
+  __shared__ Stage st0, st1, st2;
   const int item = blockIdx.x;
   if (item >= *a.work_count) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -262,11 +303,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-  // ---- staging: global -> registers -> LDS ----
-  // Thread t stages 16-byte chunk t % 8 of key row t / 8 of both K and V, row-major.  K and V
-  // rows are read through buffer descriptors bounded at the last key row this item needs:
-  // rows at or past q_end read as zeros without a branch.
-  const int krow = tid >> 3, kchunk = tid & 7;
+  // ---- staging: direct global -> LDS transfers into a ring of three stages ----
+  // Wave w's K and V transfers fill key rows 8 w .. 8 w + 7 of a stage: lane p writes row
+  // 8 w + p / 8 at chunk position p % 8, i.e. global chunk (p % 8) ^ swz(row).  Rows at or
+  // past q_end read as zeros (buffer bounds).  One 4-byte transfer per wave: wave 0 the keys'
+  // time offsets, wave 1 the class entries (both position + time bias only), wave 2 the two
+  // halves' key norm bounds, the others nothing (out of range).
   const uint32_t kstride_b = (uint32_t)a.k_stride * 2u, vstride_b = (uint32_t)a.v_stride * 2u;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(kp + tok0 * a.k_stride + (int64_t)h * kD), (short)0,
@@ -274,57 +316,68 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(vp + tok0 * a.v_stride + (int64_t)h * kD), (short)0,
       (int)((uint32_t)(q_end - 1) * vstride_b + 2u * kD), 0x00020000);
-  const uint32_t koff = (uint32_t)krow * kstride_b + 16u * kchunk;
-  const uint32_t voff = (uint32_t)krow * vstride_b + 16u * kchunk;
-  // per tile: wave 0 lane l stages key l's time offset from its block minimum; lanes 0..31 of
-  // the class wave stage the class entries of the tile's (wave, 32-key half) pairs, entry
-  // dword l = (wave l / 4, half (l / 2) % 2, word l % 2)
+  uint32_t kvo, vvo;
+  {
+    const int r = 8 * wave + (lane >> 3);
+    const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ swz(r));
+    kvo = (uint32_t)r * kstride_b + ch;
+    vvo = (uint32_t)r * vstride_b + ch;
+  }
   const int64_t crow = tclass_row0(tok0, b) + q0 / 32;
   const int64_t cbase = crow * a.tclass_cols * 8;  // bytes
+  const int64_t krow0 = tclass_row0(tok0, b);  // the user's first 32-key block row
+  const int nkb = (q_end + 31) / 32;            // key blocks this item reads
   const __amdgpu_buffer_rsrc_t rrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(KIND != 1 ? nullptr
-                        : wave == 0 ? (const void*)(a.trel + tok0)
-                                    : (const void*)((const char*)a.tclass + cbase)),
+      (void*)(wave == 2 ? (const void*)(a.knorm + krow0 * H + h)
+              : KIND != 1 || wave > 2 ? nullptr
+              : wave == 0 ? (const void*)(a.trel + tok0)
+                          : (const void*)((const char*)a.tclass + cbase)),
       (short)0,
-      KIND != 1 ? 0 : wave == 0 ? q_end * 4 : (int)min(a.tclass_bytes - cbase, (int64_t)0x7fffffff),
+      wave == 2 ? (nkb - 1) * H * 4 + 4
+      : KIND != 1 || wave > 2 ? 0
+      : wave == 0 ? q_end * 4 : (int)min(a.tclass_bytes - cbase, (int64_t)0x7fffffff),
       0x00020000);
-  const uint32_t roff = wave == 0 ? 4u * lane : 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3);
-  u32x4 kreg, vreg;
-  int32_t rdw = 0;
-  auto gload = [&](int t) {
-    const int j0 = t * kKB;
-    kreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krsrc, koff, (uint32_t)j0 * kstride_b, 0));
-    vreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrsrc, voff, (uint32_t)j0 * vstride_b, 0));
-    if (KIND == 1 && (wave == 0 || (wave == kClassWave && lane < 32)))
-      rdw = __builtin_amdgcn_raw_buffer_load_b32(rrsrc, roff, wave == 0 ? 4u * (uint32_t)j0 : (uint32_t)j0 / 4u, 0);
+  const uint32_t roff = wave == 0 ? 4u * lane
+                      : wave == 2 ? 4u * (uint32_t)H * (uint32_t)lane
+                                  : 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3);
+  constexpr int kDma = 3;
+  auto dma = [&](Stage& stg, int t) __attribute__((always_inline)) {
+    const bool real = t < n_tiles;
+    const uint32_t j0 = (uint32_t)(t * kKB);
+    const uint32_t ksoff = __builtin_amdgcn_readfirstlane(real ? j0 * kstride_b : 0x7fffffffu);
+    const uint32_t vsoff = __builtin_amdgcn_readfirstlane(real ? j0 * vstride_b : 0x7fffffffu);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_ptr)(stg.k + 512 * wave), 16, kvo, ksoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_ptr)(stg.v + 512 * wave), 16, vvo, vsoff, 0, 0);
+    const uint32_t msoff = __builtin_amdgcn_readfirstlane(
+        !real ? 0x7fffffffu
+        : wave == 2 ? (j0 / 32u) * 4u * (uint32_t)H
+        : (KIND == 1 && wave < 2) ? (wave == 0 ? 4u * j0 : j0 / 4u) : 0x7fffffffu);
+    void* dst = wave == 0 ? (void*)stg.krel : wave == 1 ? (void*)stg.cls
+              : wave == 2 ? (void*)stg.kn : (void*)stg.dummy;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rrsrc, (lds_ptr)dst, 4, roff, msoff, 0, 0);
   };
-  auto lstore = [&](int buf) {
-    *(u32x4*)(&sm.k[buf][krow * kRow + 8 * kchunk]) = kreg;
-    *(u32x4*)(&sm.v[buf][krow * kRow + 8 * kchunk]) = vreg;
-    if (KIND == 1 && wave == 0) sm.krel[buf][lane] = rdw;
-    else if (KIND == 1 && wave == kClassWave && lane < 32) (&sm.cls[buf][0][0][0])[lane] = (uint32_t)rdw;
-    // max squared norm of the staged key rows: 8 threads hold the 8 chunks of a row
-    const bf16x8 kv = __builtin_bit_cast(bf16x8, kreg);
-    float acc = 0.f;
+  // byte offsets of this lane's operand reads within a stage.  The K read of k-step ks takes
+  // chunk 2 ks + hf of row l32 (+ 32 hk), at position (2 ks + hf) ^ swz(l32): kbase ^ (32 ks).
+  // The V reads take chunk 4 db + vtr_col / 8 of row vtr_row0 + 8 e (+ 16 m + 32 hk): vbase[e]
+  // ^ (64 db).  (The XORs touch bits 5 and 6 only, which the row offsets leave zero.)
+  uint32_t kbase, vbase[2];
+  {
+    const int sk = swz(l32);
+    kbase = (uint32_t)(l32 * 128 + 32 * (sk >> 1) + 16 * (hf ^ (sk & 1)));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
-      acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
+    for (int e = 0; e < 2; ++e) {
+      const int r = vtr_row0 + 8 * e, sv = swz(r);
+      vbase[e] = (uint32_t)(r * 128 + 64 * (sv >> 2) + 16 * ((vtr_col >> 3) ^ (sv & 3)) + 2 * (vtr_col & 7));
     }
-    acc = wave_max_dpp(sum8(acc));
-    if (lane == 0) sm.knorm2[buf][wave] = acc;
-  };
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  }
+  dma(st0, 0);
+  dma(st1, 1);
+  // the register loads above have landed once at most the two tiles' transfers are outstanding
+  wait_vm<2 * kDma>();
 
   enum { kExact = 0, kPoly = 1, kTaylor = 2 };
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < n_tiles;
-    if (more) gload(t + 1);
+  auto compute = [&](const Stage& stg, int t) __attribute__((always_inline)) {
     const int j0 = t * kKB;
-    float kn2 = 0.f;
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk) {
       const int j0h = j0 + 32 * hk;
@@ -333,13 +386,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       bf16x8 kop[4], vop[2][2];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        kop[ks] = *(const bf16x8*)(&sm.k[buf][(32 * hk + l32) * kRow + 16 * ks + 8 * hf]);
-      if (hk == 0) {
-        const f32x4 k0 = *(const f32x4*)(&sm.knorm2[buf][0]);
-        const f32x4 k1 = *(const f32x4*)(&sm.knorm2[buf][4]);
-        kn2 = uniform_f32(fmaxf(fmaxf(fmaxf(k0[0], k0[1]), fmaxf(k0[2], k0[3])),
-                                fmaxf(fmaxf(k1[0], k1[1]), fmaxf(k1[2], k1[3]))));
-      }
+        kop[ks] = *(const bf16x8*)((const char*)stg.k + 32 * hk * 128 + (kbase ^ (32u * ks)));
+      const float kn2 = uniform_f32(stg.kn[hk]);
       const bool diag = (j0h + 31) > qw0;
       // i - j of register r = dlt + lv - kc(r): a lane term, a tile term and a constant
       const int dlt = qw0 - j0h;
@@ -356,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
         const float D2 = qbound * qbound * kn2;
         path = D2 <= kTaylorD * kTaylorD ? kTaylor : D2 <= kPolyRange * kPolyRange ? kPoly : kExact;
       } else if (KIND == 1) {
-        const u32x2 e = *(const u32x2*)(&sm.cls[buf][wave][hk][0]);
+        const u32x2 e = *(const u32x2*)(&stg.cls[4 * wave + 2 * hk]);
         const uint32_t info = __builtin_amdgcn_readfirstlane(e[0]);
         dq = (int32_t)__builtin_amdgcn_readfirstlane(e[1]);
         mode = info & 15;
@@ -420,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
           } else if (mode == 2) {
             // two time buckets: dt >= 2^thi - 1  <=>  rel_j <= (t_i - kmin) - (2^thi - 1)
             const int lim = tq_rel + dq - ((1 << thi) - 1);
-            const i32x4 rel4 = *(const i32x4*)(&sm.krel[buf][32 * hk + 8 * g + 4 * hf]);
+            const i32x4 rel4 = *(const i32x4*)(&stg.krel[32 * hk + 8 * g + 4 * hf]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) c4[i] = rel4[i] <= lim ? c1 : c0;
           } else if (mode == 3) {
@@ -428,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
             for (int i = 0; i < 4; ++i) c4[i] = sm.wposx[lv + (dltc - kc(4 * g + i)) + 32] + c0;
           } else if (mode == 4) {
             const int ti1 = tq_rel + dq + 1;
-            const i32x4 rel4 = *(const i32x4*)(&sm.krel[buf][32 * hk + 8 * g + 4 * hf]);
+            const i32x4 rel4 = *(const i32x4*)(&stg.krel[32 * hk + 8 * g + 4 * hf]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int u = max(ti1 - rel4[i], 1);  // max(dt, 0) + 1
@@ -480,9 +528,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           bf16x4 half0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(&sm.v[buf][vtr_row0 * kRow + (32 * hk + 16 * m) * kRow + 32 * db + vtr_col]));
+              (__attribute__((address_space(3))) bf16x4*)((const char*)stg.v + (32 * hk + 16 * m) * 128 + (vbase[0] ^ (64u * db))));
           bf16x4 half1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(&sm.v[buf][vtr_row0 * kRow + (32 * hk + 16 * m + 8) * kRow + 32 * db + vtr_col]));
+              (__attribute__((address_space(3))) bf16x4*)((const char*)stg.v + (32 * hk + 16 * m) * 128 + (vbase[1] ^ (64u * db))));
           vop[db][m] = bf16x8{half0[0], half0[1], half0[2], half0[3], half1[0], half1[1], half1[2], half1[3]};
         }
 #pragma unroll
@@ -491,9 +539,29 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
         for (int db = 0; db < 2; ++db)
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[m], oacc[db], 0, 0, 0);
     }
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
+  };
+  // tile t sits in stage t % 3; at tile t the transfer of tile t + 2 goes into the stage tile
+  // t - 1 left (its readers all passed the last barrier), tile t is multiplied, then this
+  // wave's transfers of tile t + 1 are waited for and the barrier publishes them to all
+  wait_vm<kDma>();
+  lds_barrier();
+  auto step = [&](const Stage& cur, Stage& nxt2, int t) __attribute__((always_inline)) {
+    dma(nxt2, t + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, t);
+    wait_vm<kDma>();
+    lds_barrier();
+  };
+  for (int t = 0; t < n_tiles; t += 3) {
+    step(st0, st2, t);
+    if (t + 1 >= n_tiles) break;
+    step(st1, st0, t + 1);
+    if (t + 2 >= n_tiles) break;
+    step(st2, st1, t + 2);
   }
+  // the transfers past the last tile land before the kernel ends
+  wait_vm<0>();
+
 
   // ---- epilogue: O^T accumulators -> O rows, scaled by -(ln 2 / 2) out_scale ----
   const float osc = -0.5f * kLn2 * a.out_scale;
@@ -740,6 +808,14 @@ hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* t
   if (B <= 0 || max_seqlen <= 0) return hipSuccess;
   hipLaunchKernelGGL(time_stats_kernel, dim3(B, (max_seqlen + 255) / 256), dim3(256), 0, stream,
                      offsets, ts, stats, rel);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int32_t max_seqlen, const void* k,
+                           int64_t k_stride, int32_t H, float* knorm, hipStream_t stream) {
+  if (B <= 0 || max_seqlen <= 0) return hipSuccess;
+  hipLaunchKernelGGL(key_norm_kernel, dim3(B, (max_seqlen + 31) / 32), dim3(256), 0, stream,
+                     offsets, (const bf16*)k, k_stride, H, knorm);
   return hipGetLastError();
 }
 

@@ -151,6 +151,7 @@ struct AttnArgs {
   int64_t tclass_bytes;
   float alpha, out_scale;
   f32x2* ostats;          // bf16 path, optional: per (token, head) mean and M2 of the O row
+  const float* knorm;     // bf16 path: per (32-key block, head) max squared key norm, rows as tclass
 };
 
 // Rows of the tile-class table: user b's query block i sits on row (offsets[b] + 31 b) / 32 + i,
@@ -186,6 +187,8 @@ hipError_t launch_schedule(const int32_t* offsets, int32_t B, int32_t H, int32_t
 hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts,
                              int32_t max_seqlen, TimeStat* stats, int32_t* rel,
                              hipStream_t stream);
+hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int32_t max_seqlen, const void* k,
+                           int64_t k_stride, int32_t H, float* knorm, hipStream_t stream);
 hipError_t launch_tile_class(int32_t B, const int32_t* offsets, const TimeStat* stats,
                              int32_t max_blocks, int32_t num_pos, int32_t num_time,
                              uint32_t* tclass, hipStream_t stream);

@@ -80,8 +80,9 @@ typedef struct {
 } hstu_bias;
 
 /* Bytes of device workspace hstu_attn_fwd needs for B users, H heads, lengths up to
- * max_seqlen and total_tokens tokens (work list of the jagged scheduler, plus per-token
- * timestamp statistics of the relative bias). */
+ * max_seqlen and total_tokens tokens (work list of the jagged scheduler, per-token
+ * timestamp statistics and tile classes of the relative bias, and the bf16 path's
+ * per (32-key block, head) key norm bounds). */
 size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64_t total_tokens);
 
 /* Jagged causal pointwise attention, eq. (2) above.
@@ -98,7 +99,8 @@ size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64
  * Layout of the workspace after the call: int32 item_count at byte 0, then
  * from byte 256 the scheduler's work list, one int32x4 {b, h, q_tile, 0} per
  * item, in launch order (cost = q_tile + 1 descending, then b, h ascending);
- * after it (256-aligned) per-token timestamp statistics of the bias. */
+ * after it (256-aligned) per-token timestamp statistics of the bias, the tile
+ * classes and the key norm bounds. */
 hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
                           const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
                           const void* q, int64_t q_row_stride, const void* k,
