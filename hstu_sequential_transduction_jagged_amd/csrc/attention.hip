@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256) void key_norm_kernel(const int32_t* __restrict
 
 // ============================================================================================
 // bf16, d = 64: 8 waves x 32 queries = 256 query rows per work item, 64 keys per LDS stage
-// (a ring of three stages filled by direct global -> LDS transfers two tiles ahead), four
-// waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time tables,
+// (a ring of four stages filled by direct global -> LDS transfers, one barrier per two tiles),
+// four waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time tables,
 // 2 ALiBi).
 // ============================================================================================
 constexpr int kWaves = 8;
@@ -200,7 +200,7 @@ struct __attribute__((aligned(16))) SmemBf16 {
 template <int KIND, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) {
   __shared__ SmemBf16 sm;
-  __shared__ Stage st0, st1, st2;
+  __shared__ Stage st0, st1, st2, st3;
   const int item = blockIdx.x;
   if (item >= *a.work_count) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -225,6 +225,63 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   const float cq = -a.alpha * kLog2e;
   const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
   constexpr int kClassWave = 1;  // its lanes 0..31 stage the next tile's class entries
+
+  // ---- staging: direct global -> LDS transfers into a ring of four stages ----
+  // Wave w's K and V transfers fill key rows 8 w .. 8 w + 7 of a stage: lane p writes row
+  // 8 w + p / 8 at chunk position p % 8, i.e. global chunk (p % 8) ^ swz(row).  Rows at or
+  // past q_end read as zeros (buffer bounds).  One 4-byte transfer per wave: wave 0 the keys'
+  // time offsets, wave 1 the class entries (both position + time bias only), wave 2 the two
+  // halves' key norm bounds, the others nothing (out of range).
+  const uint32_t kstride_b = (uint32_t)a.k_stride * 2u, vstride_b = (uint32_t)a.v_stride * 2u;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kp + tok0 * a.k_stride + (int64_t)h * kD), (short)0,
+      (int)((uint32_t)(q_end - 1) * kstride_b + 2u * kD), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vp + tok0 * a.v_stride + (int64_t)h * kD), (short)0,
+      (int)((uint32_t)(q_end - 1) * vstride_b + 2u * kD), 0x00020000);
+  uint32_t kvo, vvo;
+  {
+    const int r = 8 * wave + (lane >> 3);
+    const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ swz(r));
+    kvo = (uint32_t)r * kstride_b + ch;
+    vvo = (uint32_t)r * vstride_b + ch;
+  }
+  const int64_t crow = tclass_row0(tok0, b) + q0 / 32;
+  const int64_t cbase = crow * a.tclass_cols * 8;  // bytes
+  const int64_t krow0 = tclass_row0(tok0, b);  // the user's first 32-key block row
+  const int nkb = (q_end + 31) / 32;            // key blocks this item reads
+  const __amdgpu_buffer_rsrc_t rrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wave == 2 ? (const void*)(a.knorm + krow0 * H + h)
+              : KIND != 1 || wave > 2 ? nullptr
+              : wave == 0 ? (const void*)(a.trel + tok0)
+                          : (const void*)((const char*)a.tclass + cbase)),
+      (short)0,
+      wave == 2 ? (nkb - 1) * H * 4 + 4
+      : KIND != 1 || wave > 2 ? 0
+      : wave == 0 ? q_end * 4 : (int)min(a.tclass_bytes - cbase, (int64_t)0x7fffffff),
+      0x00020000);
+  const uint32_t roff = wave == 0 ? 4u * lane
+                      : wave == 2 ? 4u * (uint32_t)H * (uint32_t)lane
+                                  : 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3);
+  auto dma = [&](Stage& stg, int t) __attribute__((always_inline)) {
+    const bool real = t < n_tiles;
+    const uint32_t j0 = (uint32_t)(t * kKB);
+    const uint32_t ksoff = __builtin_amdgcn_readfirstlane(real ? j0 * kstride_b : 0x7fffffffu);
+    const uint32_t vsoff = __builtin_amdgcn_readfirstlane(real ? j0 * vstride_b : 0x7fffffffu);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_ptr)(stg.k + 512 * wave), 16, kvo, ksoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_ptr)(stg.v + 512 * wave), 16, vvo, vsoff, 0, 0);
+    const uint32_t msoff = __builtin_amdgcn_readfirstlane(
+        !real ? 0x7fffffffu
+        : wave == 2 ? (j0 / 32u) * 4u * (uint32_t)H
+        : (KIND == 1 && wave < 2) ? (wave == 0 ? 4u * j0 : j0 / 4u) : 0x7fffffffu);
+    void* dst = wave == 0 ? (void*)stg.krel : wave == 1 ? (void*)stg.cls
+              : wave == 2 ? (void*)stg.kn : (void*)stg.dummy;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rrsrc, (lds_ptr)dst, 4, roff, msoff, 0, 0);
+  };
+  // the first two tiles' transfers go out before the item's register loads, so that their
+  // latencies overlap
+  dma(st0, 0);
+  dma(st1, 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T), unscaled ----
   bf16x8 qop[4];
@@ -303,59 +360,6 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-  // ---- staging: direct global -> LDS transfers into a ring of three stages ----
-  // Wave w's K and V transfers fill key rows 8 w .. 8 w + 7 of a stage: lane p writes row
-  // 8 w + p / 8 at chunk position p % 8, i.e. global chunk (p % 8) ^ swz(row).  Rows at or
-  // past q_end read as zeros (buffer bounds).  One 4-byte transfer per wave: wave 0 the keys'
-  // time offsets, wave 1 the class entries (both position + time bias only), wave 2 the two
-  // halves' key norm bounds, the others nothing (out of range).
-  const uint32_t kstride_b = (uint32_t)a.k_stride * 2u, vstride_b = (uint32_t)a.v_stride * 2u;
-  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(kp + tok0 * a.k_stride + (int64_t)h * kD), (short)0,
-      (int)((uint32_t)(q_end - 1) * kstride_b + 2u * kD), 0x00020000);
-  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(vp + tok0 * a.v_stride + (int64_t)h * kD), (short)0,
-      (int)((uint32_t)(q_end - 1) * vstride_b + 2u * kD), 0x00020000);
-  uint32_t kvo, vvo;
-  {
-    const int r = 8 * wave + (lane >> 3);
-    const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ swz(r));
-    kvo = (uint32_t)r * kstride_b + ch;
-    vvo = (uint32_t)r * vstride_b + ch;
-  }
-  const int64_t crow = tclass_row0(tok0, b) + q0 / 32;
-  const int64_t cbase = crow * a.tclass_cols * 8;  // bytes
-  const int64_t krow0 = tclass_row0(tok0, b);  // the user's first 32-key block row
-  const int nkb = (q_end + 31) / 32;            // key blocks this item reads
-  const __amdgpu_buffer_rsrc_t rrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(wave == 2 ? (const void*)(a.knorm + krow0 * H + h)
-              : KIND != 1 || wave > 2 ? nullptr
-              : wave == 0 ? (const void*)(a.trel + tok0)
-                          : (const void*)((const char*)a.tclass + cbase)),
-      (short)0,
-      wave == 2 ? (nkb - 1) * H * 4 + 4
-      : KIND != 1 || wave > 2 ? 0
-      : wave == 0 ? q_end * 4 : (int)min(a.tclass_bytes - cbase, (int64_t)0x7fffffff),
-      0x00020000);
-  const uint32_t roff = wave == 0 ? 4u * lane
-                      : wave == 2 ? 4u * (uint32_t)H * (uint32_t)lane
-                                  : 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3);
-  constexpr int kDma = 3;
-  auto dma = [&](Stage& stg, int t) __attribute__((always_inline)) {
-    const bool real = t < n_tiles;
-    const uint32_t j0 = (uint32_t)(t * kKB);
-    const uint32_t ksoff = __builtin_amdgcn_readfirstlane(real ? j0 * kstride_b : 0x7fffffffu);
-    const uint32_t vsoff = __builtin_amdgcn_readfirstlane(real ? j0 * vstride_b : 0x7fffffffu);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_ptr)(stg.k + 512 * wave), 16, kvo, ksoff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_ptr)(stg.v + 512 * wave), 16, vvo, vsoff, 0, 0);
-    const uint32_t msoff = __builtin_amdgcn_readfirstlane(
-        !real ? 0x7fffffffu
-        : wave == 2 ? (j0 / 32u) * 4u * (uint32_t)H
-        : (KIND == 1 && wave < 2) ? (wave == 0 ? 4u * j0 : j0 / 4u) : 0x7fffffffu);
-    void* dst = wave == 0 ? (void*)stg.krel : wave == 1 ? (void*)stg.cls
-              : wave == 2 ? (void*)stg.kn : (void*)stg.dummy;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rrsrc, (lds_ptr)dst, 4, roff, msoff, 0, 0);
-  };
   // byte offsets of this lane's operand reads within a stage.  The K read of k-step ks takes
   // chunk 2 ks + hf of row l32 (+ 32 hk), at position (2 ks + hf) ^ swz(l32): kbase ^ (32 ks).
   // The V reads take chunk 4 db + vtr_col / 8 of row vtr_row0 + 8 e (+ 16 m + 32 hk): vbase[e]
@@ -370,10 +374,6 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       vbase[e] = (uint32_t)(r * 128 + 64 * (sv >> 2) + 16 * ((vtr_col >> 3) ^ (sv & 3)) + 2 * (vtr_col & 7));
     }
   }
-  dma(st0, 0);
-  dma(st1, 1);
-  // the register loads above have landed once at most the two tiles' transfers are outstanding
-  wait_vm<2 * kDma>();
 
   enum { kExact = 0, kPoly = 1, kTaylor = 2 };
   auto compute = [&](const Stage& stg, int t) __attribute__((always_inline)) {
@@ -540,24 +540,25 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[m], oacc[db], 0, 0, 0);
     }
   };
-  // tile t sits in stage t % 3; at tile t the transfer of tile t + 2 goes into the stage tile
-  // t - 1 left (its readers all passed the last barrier), tile t is multiplied, then this
-  // wave's transfers of tile t + 1 are waited for and the barrier publishes them to all
-  wait_vm<kDma>();
+  // tiles are taken in pairs, one barrier per pair: tiles t, t + 1 sit in stages t % 4,
+  // (t + 1) % 4; the transfers of tiles t + 2, t + 3 go into the stages of tiles t - 2, t - 1
+  // (their readers all passed the last barrier) while t and t + 1 are multiplied, then this
+  // wave's transfers are waited for and the barrier publishes them to all
+  wait_vm<0>();
   lds_barrier();
-  auto step = [&](const Stage& cur, Stage& nxt2, int t) __attribute__((always_inline)) {
-    dma(nxt2, t + 2);
+  auto pair = [&](const Stage& c0, const Stage& c1, Stage& n0, Stage& n1, int t) __attribute__((always_inline)) {
+    dma(n0, t + 2);
+    dma(n1, t + 3);
     __builtin_amdgcn_sched_barrier(0);
-    compute(cur, t);
-    wait_vm<kDma>();
+    compute(c0, t);
+    if (t + 1 < n_tiles) compute(c1, t + 1);
+    wait_vm<0>();
     lds_barrier();
   };
-  for (int t = 0; t < n_tiles; t += 3) {
-    step(st0, st2, t);
-    if (t + 1 >= n_tiles) break;
-    step(st1, st0, t + 1);
+  for (int t = 0; t < n_tiles; t += 4) {
+    pair(st0, st1, st2, st3, t);
     if (t + 2 >= n_tiles) break;
-    step(st2, st1, t + 2);
+    pair(st2, st3, st0, st1, t + 2);
   }
   // the transfers past the last tile land before the kernel ends
   wait_vm<0>();
