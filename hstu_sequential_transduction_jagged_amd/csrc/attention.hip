@@ -130,35 +130,38 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const int32_t* __restri
 // ============================================================================================
 // Key norm bounds: for every 32-key block of a user (blocks start at the user's first token)
 // and head h, the largest squared norm of the block's key rows, in fp32 from the bf16 keys,
-// at row tclass_row0(tok0, b) + block.  One workgroup per (user, block): thread t takes
-// 16-byte chunk t % 8 of token t / 8's head row.
+// at row tclass_row0(tok0, b) + block.  One workgroup per (user, block) of eight waves; wave w
+// takes heads w, w + 8, ...: lane l sums the squares of half l % 2 of token l / 2's head row,
+// the lane pair adds its halves and the wave's maximum is the bound.  No LDS, no barriers.
 // ============================================================================================
-__global__ __launch_bounds__(256) void key_norm_kernel(const int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict__ offsets,
                                                        const bf16* __restrict__ k, int64_t k_stride,
                                                        int32_t H, float* __restrict__ knorm) {
-  __shared__ float red[4];
-  const int b = blockIdx.x, blk = blockIdx.y, tid = threadIdx.x;
+  const int b = blockIdx.x, blk = blockIdx.y, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t tok0 = offsets[b];
   const int n = offsets[b + 1] - offsets[b];
   if (32 * blk >= n) return;
-  const int tok = 32 * blk + (tid >> 3);
+  const int tok = 32 * blk + (lane >> 1);
   const bool valid = tok < n;
+  const bf16* row = k + (tok0 + tok) * k_stride + 32 * (lane & 1);
   float* dst = knorm + (tclass_row0(tok0, b) + blk) * H;
-  for (int h = 0; h < H; ++h) {
+  for (int h = wave; h < H; h += 8) {
     float acc = 0.f;
     if (valid) {
-      const bf16x8 kv = *(const bf16x8*)(k + (tok0 + tok) * k_stride + (int64_t)h * 64 + 8 * (tid & 7));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
-        acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 kv = *(const bf16x8*)(row + (int64_t)h * 64 + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
+        }
       }
     }
-    const float m = wave_max_dpp(sum8(acc));
-    if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
-    if (tid == 0) dst[h] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
+    acc += __shfl_xor(acc, 1, 64);
+    const float m = wave_max_dpp(acc);
+    if (lane == 0) dst[h] = m;
   }
 }
 
@@ -815,7 +818,7 @@ hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* t
 hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int32_t max_seqlen, const void* k,
                            int64_t k_stride, int32_t H, float* knorm, hipStream_t stream) {
   if (B <= 0 || max_seqlen <= 0) return hipSuccess;
-  hipLaunchKernelGGL(key_norm_kernel, dim3(B, (max_seqlen + 31) / 32), dim3(256), 0, stream,
+  hipLaunchKernelGGL(key_norm_kernel, dim3(B, (max_seqlen + 31) / 32), dim3(512), 0, stream,
                      offsets, (const bf16*)k, k_stride, H, knorm);
   return hipGetLastError();
 }
