@@ -171,6 +171,20 @@ hstu_status hstu_attn_plan(int32_t dt, int32_t B, int32_t H, int32_t d, const in
                    "scheduler launch");
 }
 
+// per 32-token block timestamp statistics for the backward kernels (position + time bias only),
+// in the attention workspace's statistics region
+static hstu_status bwd_time_stats(int32_t B, const int32_t* offsets, int32_t max_seqlen,
+                                  int64_t total_tokens, int32_t H, const BiasArgs& ba,
+                                  void* workspace, const TimeStat** out, hipStream_t stream) {
+  *out = nullptr;
+  if (ba.kind != 1) return HSTU_OK;
+  TimeStat* tstat = (TimeStat*)((char*)workspace + worklist_bytes(B, H, max_seqlen));
+  int32_t* trel = (int32_t*)((char*)tstat + align256((size_t)total_tokens * sizeof(TimeStat)));
+  *out = tstat;
+  return check_hip(launch_time_stats(B, offsets, ba.ts, max_seqlen, tstat, trel, stream),
+                   "time stats launch");
+}
+
 static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
                                 const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
                                 const void* q, int64_t q_row_stride, const void* k,
@@ -347,6 +361,8 @@ hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   a.dq = (bf16*)dq; a.dk = (bf16*)dk; a.dv = (bf16*)dv;
   a.dq_stride = a.dk_stride = a.dv_stride = (int64_t)H * 64;
   a.dw_pos = dw_pos; a.dw_time = dw_time;
+  st = bwd_time_stats(B, offsets, max_seqlen, total_tokens, H, ba, workspace, &a.tstat, stream);
+  if (st != HSTU_OK) return st;
   const int64_t n_pos = ba.kind == 1 ? (ba.pos_stride ? (int64_t)H * ba.pos_stride : ba.num_pos) : 0;
   const int64_t n_time = ba.kind == 1 ? (ba.time_stride ? (int64_t)H * ba.time_stride : ba.num_time) : 0;
   const int64_t grid = (int64_t)B * H * ceil_div(max_seqlen, block_rows);
@@ -598,6 +614,8 @@ hstu_status hstu_layer_bwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   a.dv = dZ + HV; a.dq = dZ + 2 * HV; a.dk = dZ + 2 * HV + HQ;
   a.dq_stride = a.dk_stride = a.dv_stride = N1;
   a.dw_pos = dw_pos; a.dw_time = dw_time;
+  st = bwd_time_stats(B, offsets, max_seqlen, total_tokens, H, ba, attn_ws, &a.tstat, stream);
+  if (st != HSTU_OK) return st;
   const int64_t n_pos = ba.kind == 1 ? (ba.pos_stride ? (int64_t)H * ba.pos_stride : ba.num_pos) : 0;
   const int64_t n_time = ba.kind == 1 ? (ba.time_stride ? (int64_t)H * ba.time_stride : ba.num_time) : 0;
   const int64_t grid = (int64_t)B * H * ceil_div(max_seqlen, block_rows);

@@ -36,19 +36,35 @@ constexpr int kBRow = 72;             // padded LDS row (bf16), as in the forwar
 // accumulator register r of a 32x32 MFMA tile holds row 8 (r / 4) + 4 hf + r % 4
 __device__ __forceinline__ int accrow(int r) { return 8 * (r >> 2) + (r & 3); }
 
-struct __attribute__((aligned(16))) SmemBwd {
-  __attribute__((aligned(16))) bf16 x[2][kBTile * kBRow];  // K (dq kernel) or Q (dkv kernel)
-  __attribute__((aligned(16))) bf16 y[2][kBTile * kBRow];  // V (dq kernel) or dO (dkv kernel)
-  __attribute__((aligned(16))) int64_t t[2][kBTile];       // the tile rows' timestamps
+struct __attribute__((aligned(16))) BwdTables {
   float wpos[kMaxPosBuckets];    // w_pos[h]
   float wtime[kMaxTimeBuckets];  // w_time[h]
   float gpos[kMaxPosBuckets];    // dkv kernel: this workgroup's position-table gradient
   float gtime[kMaxTimeBuckets];  // dkv kernel: this workgroup's time-table gradient
-  __attribute__((aligned(16))) int64_t tmm[2][2][2];  // per 32-row half of a tile: min, max time
   // per time bucket, for tiles whose position bucket saturates: the bias c and the Taylor
   // coefficients of SiLU and SiLU' in the raw score (see silu_taylor)
   __attribute__((aligned(16))) float tay[kMaxTimeBuckets][8];
 };
+// dq kernel: the tables and a double-buffered K / V tile with its rows' timestamps
+struct __attribute__((aligned(16))) SmemBwd : BwdTables {
+  __attribute__((aligned(16))) bf16 x[2][kBTile * kBRow];  // K rows
+  __attribute__((aligned(16))) bf16 y[2][kBTile * kBRow];  // V rows
+  __attribute__((aligned(16))) int64_t t[2][kBTile];       // the tile rows' timestamps
+  __attribute__((aligned(16))) int64_t tmm[2][2][2];  // per 32-row half of a tile: min, max time
+};
+
+// dK/dV kernel ring stage: a 64-row tile of Q and of dO (128-byte rows, 16-byte chunk c of row
+// r at position c ^ bswz(r): the operand reads, the transposing reads and the transfers meet the
+// 64 banks without conflicts), the rows' timestamps and the two 32-row halves' min / max times.
+// A 4-byte transfer fills 256 bytes, hence the sizes of tmm and dummy.
+struct __attribute__((aligned(16))) BStage {
+  __attribute__((aligned(16))) bf16 x[kBTile * kBD];
+  __attribute__((aligned(16))) bf16 y[kBTile * kBD];
+  __attribute__((aligned(16))) int64_t t[kBTile];
+  __attribute__((aligned(16))) int64_t tmm[32];     // [0..3]: min, max of half 0, then half 1
+  __attribute__((aligned(16))) uint32_t dummy[64];  // target of the transfers that carry nothing
+};
+__device__ __forceinline__ int bswz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 // Second-order expansions in the raw score s around the bias c (x = c + alpha s):
 //   SiLU(x)  ~ A0 + A1 s + A2 s^2,   SiLU'(x) ~ B0 + B1 s + B2 s^2
@@ -110,7 +126,7 @@ typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
 // bias of pair (i, j) of head h (natural units), from the LDS tables
 template <int KIND>
-__device__ __forceinline__ float pair_bias(const SmemBwd& sm, int di, int64_t dt, int Pm1,
+__device__ __forceinline__ float pair_bias(const BwdTables& sm, int di, int64_t dt, int Pm1,
                                            int NTm1, float slope) {
   if (KIND == 1) return sm.wpos[max(min(di, Pm1), 0)] + sm.wtime[time_bucket(dt, NTm1)];
   if (KIND == 2) return -slope * (float)di;
@@ -345,7 +361,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 
 template <int KIND>
 __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
-  __shared__ SmemBwd sm;
+  __shared__ BwdTables sm;
   const int item = blockIdx.x;
   if (item >= *a.work_count) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -411,47 +427,64 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     silu_taylor(0.f, a.alpha, k0c);
   }
 
-  // query tiles from the one holding row k0 to the user's last row
+  // query tiles from the one holding row k0 to the user's last row, through a ring of four
+  // stages filled by direct global -> LDS transfers: wave w's Q and dO transfers fill rows
+  // 8 w .. 8 w + 7 (lane p: row 8 w + p / 8 at chunk position p % 8, global chunk
+  // (p % 8) ^ bswz(row)); rows at or past n read as zeros.  One 4-byte transfer per wave: waves
+  // 0, 1 the rows' timestamps (32 each), wave 2 the halves' TimeStat entries, the others
+  // nothing.  Tiles go in pairs, one barrier per pair.
   const int t0 = k0 / kBTile, t_end = (n + kBTile - 1) / kBTile;
-  const int srow = tid >> 3, sch = tid & 7;
-  TileStager stg;
-  stg.xs = (uint32_t)a.q_stride * 2u;
-  stg.ys = (uint32_t)a.do_stride * 2u;
-  stg.xr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + tok0 * a.q_stride + (int64_t)h * kBD), (short)0,
-                                             (int)((uint32_t)(n - 1) * stg.xs + 2u * kBD), 0x00020000);
-  stg.yr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.dout + tok0 * a.do_stride + (int64_t)h * kBD), (short)0,
-                                             (int)((uint32_t)(n - 1) * stg.ys + 2u * kBD), 0x00020000);
-  stg.tr = __builtin_amdgcn_make_buffer_rsrc((void*)(KIND == 1 ? a.bias.ts + tok0 : nullptr), (short)0,
-                                             KIND == 1 ? 8 * n : 0, 0x00020000);
-  stg.xoff = (uint32_t)srow * stg.xs + 16u * sch;
-  stg.yoff = (uint32_t)srow * stg.ys + 16u * sch;
-  auto lstore = [&](int buf) {
-    *(u32x4*)(&sm.x[buf][srow * kBRow + 8 * sch]) = stg.xreg;
-    *(u32x4*)(&sm.y[buf][srow * kBRow + 8 * sch]) = stg.yreg;
-    if (KIND == 1 && wave == 0) sm.t[buf][lane] = (int64_t)(((uint64_t)stg.thi << 32) | stg.tlo);
+  __shared__ BStage st0, st1, st2, st3;
+  const uint32_t xs = (uint32_t)a.q_stride * 2u, ys = (uint32_t)a.do_stride * 2u;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.q + tok0 * a.q_stride + (int64_t)h * kBD), (short)0, (int)((uint32_t)(n - 1) * xs + 2u * kBD), 0x00020000);
+  const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.dout + tok0 * a.do_stride + (int64_t)h * kBD), (short)0, (int)((uint32_t)(n - 1) * ys + 2u * kBD), 0x00020000);
+  uint32_t xo, yo;
+  {
+    const int r = 8 * wave + (lane >> 3);
+    const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ bswz(r));
+    xo = (uint32_t)r * xs + ch;
+    yo = (uint32_t)r * ys + ch;
+  }
+  const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(KIND != 1 || wave > 2 ? nullptr : wave < 2 ? (const void*)(a.bias.ts + tok0) : (const void*)(a.tstat + tok0)),
+      (short)0, KIND != 1 || wave > 2 ? 0 : wave < 2 ? 8 * n : 16 * n, 0x00020000);
+  // waves 0, 1: dword lane of the tile's 256-byte half wave; wave 2: dword lane % 4 of the
+  // TimeStat at the first token of half lane / 4
+  const uint32_t mo = wave < 2 ? 256u * (uint32_t)wave + 4u * lane : 512u * (uint32_t)(lane >> 2) + 4u * (lane & 3);
+  auto dma = [&](BStage& stg, int t) __attribute__((always_inline)) {
+    const bool real = t < t_end;
+    const uint32_t r0 = (uint32_t)(t * kBTile);
+    const uint32_t xsoff = __builtin_amdgcn_readfirstlane(real ? r0 * xs : 0x7fffffffu);
+    const uint32_t ysoff = __builtin_amdgcn_readfirstlane(real ? r0 * ys : 0x7fffffffu);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(stg.x + 512 * wave), 16, xo, xsoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(yr, (lds_ptr)(stg.y + 512 * wave), 16, yo, ysoff, 0, 0);
+    const uint32_t msoff = __builtin_amdgcn_readfirstlane(
+        (real && KIND == 1 && wave < 3) ? (wave < 2 ? 8u * r0 : 16u * r0) : 0x7fffffffu);
+    void* dst = wave < 2 ? (void*)(stg.t + 32 * wave) : wave == 2 ? (void*)stg.tmm : (void*)stg.dummy;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(mr, (lds_ptr)dst, 4, mo, msoff, 0, 0);
   };
-  // wave 0 also records the extremes of each 32-row half's times (rows at or past n excluded)
-  auto lstore_t = [&](int buf, int r0) {
-    if (KIND == 1 && wave == 0) {
-      const int64_t tt = (int64_t)(((uint64_t)stg.thi << 32) | stg.tlo);
-      const bool ok = r0 + lane < n;
-      int64_t mn = ok ? tt : kTMax, mx = ok ? tt : kTMin;
-      half_minmax(mn, mx);
-      if (l32 == 0) *(i64x2*)(&sm.tmm[buf][hf][0]) = i64x2{mn, mx};
-    }
-  };
-  stg.load(t0 * kBTile, KIND == 1 && wave == 0, lane);
-  lstore(0);
-  lstore_t(0, t0 * kBTile);
-  __syncthreads();
+  dma(st0, t0);
+  dma(st1, t0 + 1);
 
+  // byte offsets of this lane's reads within a stage: the operand read of k-step ks at
+  // kbase ^ (32 ks) (row l32 + 32 hq), the transposing reads of column block db at
+  // vbase[e] ^ (64 db) (row tr_row0 + 8 e + 16 mm + 32 hq)
   const int tr_row0 = 4 * hf + ((lane & 15) >> 2);
   const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  uint32_t kbase, vbase[2];
+  {
+    const int sk = bswz(l32);
+    kbase = (uint32_t)(l32 * 128 + 32 * (sk >> 1) + 16 * (hf ^ (sk & 1)));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = tr_row0 + 8 * e, sv = bswz(r);
+      vbase[e] = (uint32_t)(r * 128 + 64 * (sv >> 2) + 16 * ((tr_col >> 3) ^ (sv & 3)) + 2 * (tr_col & 7));
+    }
+  }
   f32x16 dvacc[2] = {}, dkacc[2] = {};
-  for (int t = t0; t < t_end; ++t) {
-    const int buf = (t - t0) & 1;
-    const bool more = t + 1 < t_end;
-    if (more) stg.load((t + 1) * kBTile, KIND == 1 && wave == 0, lane);
+  auto compute = [&](const BStage& stg, int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
       const int i0h = t * kBTile + 32 * hq;  // first query of this step
@@ -459,8 +492,8 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       bf16x8 qa[4], da_[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        qa[ks] = *(const bf16x8*)(&sm.x[buf][(32 * hq + l32) * kBRow + 16 * ks + 8 * hf]);
-        da_[ks] = *(const bf16x8*)(&sm.y[buf][(32 * hq + l32) * kBRow + 16 * ks + 8 * hf]);
+        qa[ks] = *(const bf16x8*)((const char*)stg.x + 32 * hq * 128 + (kbase ^ (32u * ks)));
+        da_[ks] = *(const bf16x8*)((const char*)stg.y + 32 * hq * 128 + (kbase ^ (32u * ks)));
       }
       f32x16 s = {}, dd = {};
 #pragma unroll
@@ -473,7 +506,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       int tlo = 0, thi = 0;
       bool sat = true;
       if (KIND == 1) {
-        const i64x2 qmm = *(const i64x2*)(&sm.tmm[buf][hq][0]);
+        const i64x2 qmm = *(const i64x2*)(&stg.tmm[2 * hq]);
         const int64_t qmin = uniform_i64(qmm[0]), qmax = uniform_i64(qmm[1]);
         tlo = time_bucket(qmin - tk_max, NTm1);
         thi = time_bucket(qmax - tk_min, NTm1);
@@ -514,7 +547,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int il = 32 * hq + accrow(r) + 4 * hf;
           const int i = t * kBTile + il;
-          const int64_t dt = KIND == 1 ? sm.t[buf][il] - tk : 0;
+          const int64_t dt = KIND == 1 ? stg.t[il] - tk : 0;
           const float x = __builtin_fmaf(a.alpha, s[r], pair_bias<KIND>(sm, i - key, dt, Pm1, NTm1, slope));
           float aa, d1;
           silu_and_grad(x, aa, d1);
@@ -531,7 +564,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           gs += g[r];
-          if (thi == tlo + 1) ghi += sm.t[buf][32 * hq + accrow(r) + 4 * hf] >= tlim ? g[r] : 0.f;
+          if (thi == tlo + 1) ghi += stg.t[32 * hq + accrow(r) + 4 * hf] >= tlim ? g[r] : 0.f;
         }
         if (sat || thi <= tlo + 1) {
           const float tot = wave_sum(gs);
@@ -553,7 +586,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
             const int i = t * kBTile + il;
             if (i >= key && i < n && kvalid) {
               if (!sat) atomicAdd(&sm.gpos[min(i - key, Pm1)], g[r]);
-              if (thi > tlo + 1) atomicAdd(&sm.gtime[time_bucket(sm.t[buf][il] - tk, NTm1)], g[r]);
+              if (thi > tlo + 1) atomicAdd(&sm.gtime[time_bucket(stg.t[il] - tk, NTm1)], g[r]);
             }
           }
         }
@@ -577,26 +610,37 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       for (int db = 0; db < 2; ++db)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const int r0 = tr_row0 + 32 * hq + 16 * mm, c0 = 32 * db + tr_col;
+          const int rb = (32 * hq + 16 * mm) * 128;
           const bf16x4 d0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(&sm.y[buf][r0 * kBRow + c0]));
+              (__attribute__((address_space(3))) bf16x4*)((const char*)stg.y + rb + (vbase[0] ^ (64u * db))));
           const bf16x4 d1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(&sm.y[buf][(r0 + 8) * kBRow + c0]));
+              (__attribute__((address_space(3))) bf16x4*)((const char*)stg.y + rb + (vbase[1] ^ (64u * db))));
           const bf16x4 e0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(&sm.x[buf][r0 * kBRow + c0]));
+              (__attribute__((address_space(3))) bf16x4*)((const char*)stg.x + rb + (vbase[0] ^ (64u * db))));
           const bf16x4 e1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (__attribute__((address_space(3))) bf16x4*)(&sm.x[buf][(r0 + 8) * kBRow + c0]));
+              (__attribute__((address_space(3))) bf16x4*)((const char*)stg.x + rb + (vbase[1] ^ (64u * db))));
           const bf16x8 dot = bf16x8{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
           const bf16x8 qt = bf16x8{e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
           dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, pop[mm], dvacc[db], 0, 0, 0);
           dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, gop[mm], dkacc[db], 0, 0, 0);
         }
     }
-    if (more) {
-      lstore(buf ^ 1);
-      lstore_t(buf ^ 1, (t + 1) * kBTile);
-    }
-    __syncthreads();
+  };
+  wait_vm<0>();
+  lds_barrier();
+  auto pair = [&](const BStage& c0, const BStage& c1, BStage& n0, BStage& n1, int t) __attribute__((always_inline)) {
+    dma(n0, t + 2);
+    dma(n1, t + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(c0, t);
+    if (t + 1 < t_end) compute(c1, t + 1);
+    wait_vm<0>();
+    lds_barrier();
+  };
+  for (int t = t0; t < t_end; t += 4) {
+    pair(st0, st1, st2, st3, t);
+    if (t + 2 >= t_end) break;
+    pair(st2, st3, st0, st1, t + 2);
   }
 
   // dK and dV rows: accumulator register 4 g + e holds d = 32 db + 8 g + 4 hf + e of this

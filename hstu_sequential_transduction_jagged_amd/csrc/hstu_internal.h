@@ -216,6 +216,7 @@ struct BwdArgs {
   bf16 *dq, *dk, *dv;         // [T, H, 64] rows with the strides below
   int64_t dq_stride, dk_stride, dv_stride;
   float *dw_pos, *dw_time;    // position + time bias: gradients shaped like the tables
+  const TimeStat* tstat;      // position + time bias: per 32-token block min / max time
 };
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int grid, int64_t n_pos_grad,
                                 int64_t n_time_grad, hipStream_t stream);
