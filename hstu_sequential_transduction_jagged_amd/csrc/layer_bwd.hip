@@ -292,17 +292,35 @@ __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(
   }
 }
 
-// column sums of a bf16 [T][N] matrix (row stride ld) added to out[N]: thread = column, block
-// y = a range of rows
+// column sums of a bf16 [T][N] matrix (row stride ld, N % 8 == 0, 16-byte aligned rows) added
+// to out[N]: a workgroup takes 256 columns of rows_per rows; thread t reads the 16-byte chunk
+// t % 32 (8 columns) of rows t / 32, t / 32 + 8, ..., and the 8 row groups are added in LDS
 __global__ __launch_bounds__(256) void colsum_kernel(const bf16* __restrict__ x, int64_t ld,
                                                      int64_t T, int32_t N, int64_t rows_per,
                                                      float* __restrict__ out) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
+  __shared__ float part[8][257];
+  const int tid = threadIdx.x, c = tid & 31, rg = tid >> 5;
+  const int n0 = blockIdx.x * 256 + 8 * c;
   const int64_t t0 = (int64_t)blockIdx.y * rows_per, t1 = min(T, t0 + rows_per);
-  float s = 0.f;
-  for (int64_t t = t0; t < t1; ++t) s += (float)x[t * ld + n];
-  atomicAdd(&out[n], s);
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (n0 < N) {
+#pragma unroll 4
+    for (int64_t t = t0 + rg; t < t1; t += 8) {
+      const bf16x8 v = *(const bf16x8*)(x + t * ld + n0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += (float)v[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][8 * c + e] = s[e];
+  __syncthreads();
+  const int n = blockIdx.x * 256 + tid;
+  if (n < N) {
+    float v = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) v += part[g][tid];
+    atomicAdd(&out[n], v);
+  }
 }
 
 __global__ void zero_f32_kernel2(float* p, int64_t n) {
