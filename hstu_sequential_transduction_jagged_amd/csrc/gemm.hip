@@ -50,8 +50,10 @@ __device__ __forceinline__ int f1_off(int row, int chunk) {
 
 
 // NK: K / 32 when known at compile time (the slice loop is then straight-line code, which keeps
-// the compiler's own waits on the transfers exact), 0 for any K
-template <int NK>
+// the compiler's own waits on the transfers exact), 0 for any K.  EPI 0: Y = SiLU(acc); EPI 1
+// (the layer's backward): Y holds dZ on entry and dZ * SiLU'(acc) on exit, acc = X W^T + b, with
+// SiLU'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z), the product in fp32 and rounded once.
+template <int NK, int EPI>
 __global__ __launch_bounds__(kF1Threads, 3) void f1_kernel(F1Args g) {
   // stage arrays of their own: the compiler then knows which stage a transfer writes
   __shared__ __attribute__((aligned(16))) bf16 sW0[kF1WElems], sW1[kF1WElems];
@@ -179,10 +181,25 @@ __global__ __launch_bounds__(kF1Threads, 3) void f1_kernel(F1Args g) {
 #pragma unroll
         for (int grp = 0; grp < 4; ++grp) {
           f32x4 v;
+          if (EPI == 0) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = acc[i][2 * p + jj][4 * grp + e];
-            v[e] = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
+            for (int e = 0; e < 4; ++e) {
+              const float x = acc[i][2 * p + jj][4 * grp + e];
+              v[e] = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
+            }
+          } else {
+            // this lane's token 128 wt + 32 j + l32 and features 64 wf + 32 i + 8 grp + 4 hf .. + 3
+            const int64_t tok = 128 * wt + 32 * (2 * p + jj) + l32;
+            f32x4 dz = {0.f, 0.f, 0.f, 0.f};
+            if (tok < rows)
+              dz = __builtin_convertvector(
+                  *(const bf16x4*)(g.Y + (m0 + tok) * N + n0 + 64 * wf + 32 * i + 8 * grp + 4 * hf), f32x4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float x = acc[i][2 * p + jj][4 * grp + e];
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
+              v[e] = dz[e] * (sg * __builtin_fmaf(x, 1.0f - sg, 1.0f));
+            }
           }
           const int q = 8 * wf + 4 * i + grp;
           wtile[r * 32 + 2 * (q ^ (r & 15)) + (hf ^ ((r >> 4) & 1))] =
@@ -457,7 +474,7 @@ __global__ void embed_sum_kernel(int64_t T, int dim, const bf16* __restrict__ it
 }  // namespace
 
 hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, bf16* z, int64_t M,
-                               int32_t N, int32_t K, hipStream_t stream) {
+                               int32_t N, int32_t K, hipStream_t stream, bool silu_bwd) {
   if (N % kF1Feat || K % kF1K || K <= 0) return hipErrorInvalidValue;
   if ((int64_t)kF1Tok * N * 2 > 0x7fffffff) return hipErrorInvalidValue;
   if ((int64_t)kF1Tok * 2 * K > 0x7fffffff || (int64_t)kF1Feat * 2 * K > 0x7fffffff)
@@ -468,9 +485,15 @@ hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, b
   F1Args g{};
   g.X = x; g.W = w1; g.bias = b1; g.Y = z; g.M = M; g.N = N; g.K = K; g.tiles = (int32_t)tiles;
   const unsigned grid = (unsigned)((tiles + 7) / 8 * 8);
-  if (K == 512) hipLaunchKernelGGL(f1_kernel<16>, dim3(grid), dim3(kF1Threads), 0, stream, g);
-  else if (K == 256) hipLaunchKernelGGL(f1_kernel<8>, dim3(grid), dim3(kF1Threads), 0, stream, g);
-  else hipLaunchKernelGGL(f1_kernel<0>, dim3(grid), dim3(kF1Threads), 0, stream, g);
+  if (silu_bwd) {
+    if (K == 512) hipLaunchKernelGGL((f1_kernel<16, 1>), dim3(grid), dim3(kF1Threads), 0, stream, g);
+    else if (K == 256) hipLaunchKernelGGL((f1_kernel<8, 1>), dim3(grid), dim3(kF1Threads), 0, stream, g);
+    else hipLaunchKernelGGL((f1_kernel<0, 1>), dim3(grid), dim3(kF1Threads), 0, stream, g);
+  } else {
+    if (K == 512) hipLaunchKernelGGL((f1_kernel<16, 0>), dim3(grid), dim3(kF1Threads), 0, stream, g);
+    else if (K == 256) hipLaunchKernelGGL((f1_kernel<8, 0>), dim3(grid), dim3(kF1Threads), 0, stream, g);
+    else hipLaunchKernelGGL((f1_kernel<0, 0>), dim3(grid), dim3(kF1Threads), 0, stream, g);
+  }
   return hipGetLastError();
 }
 

@@ -198,7 +198,8 @@ int attn_block_rows_bf16(int d);
 int attn_block_rows_f32(int d);
 
 hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, bf16* z, int64_t M,
-                               int32_t N, int32_t K, hipStream_t stream);
+                               int32_t N, int32_t K, hipStream_t stream,
+                               bool silu_bwd = false);
 hipError_t launch_ln_gate_f2(const bf16* o, const f32x2* ostats, const bf16* u,
                              int64_t u_stride, const float* gamma, const float* beta, float eps,
                              const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,

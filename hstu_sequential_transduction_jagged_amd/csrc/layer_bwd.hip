@@ -16,8 +16,8 @@
 // reads (ds_read_b64_tr_b16), whose k order within a 16-deep step is 4 hf + {0..3},
 // 8 + 4 hf + {0..3}; k-contiguous operands are read in that same order (two 8-byte reads), so
 // the two operands always agree.  Epilogues: bf16 store (optional fp32 column bias and bf16
-// residual), fp32 atomic add (split-k weight gradients), and the SiLU backward
-// dZpre = dZ * SiLU'(acc + b1) written over dZ.
+// residual) and fp32 atomic add (split-k weight gradients).  The recomputed X W1^T + b1 with
+// the SiLU backward dZpre = dZ * SiLU'(.) written over dZ runs on the forward's f1 kernel.
 #include "hstu_internal.h"
 
 namespace hstu {
@@ -34,10 +34,10 @@ struct GemmArgs {
   int64_t lda, ldb;
   int32_t M, N, K, k_split;  // k_split: depth per grid.z slice (multiple of 32)
   // epilogues
-  bf16* c;             // EPI 0: bf16 out [M][ldc]; EPI 2: dZ in / dZpre out [M][ldc]
+  bf16* c;             // EPI 0: bf16 out [M][ldc]
   float* cf;           // EPI 1: fp32 [M][ldc] (added to)
   int64_t ldc;
-  const float* bias;   // EPI 0 / 2: fp32 [N] or null
+  const float* bias;   // EPI 0: fp32 [N] or null
   const bf16* resid;   // EPI 0: bf16 [M][ldr] added, or null
   int64_t ldr;
 };
@@ -156,13 +156,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
           float o = v + bn;
           if (g.resid) o += (float)g.resid[(int64_t)m * g.ldr + n];
           g.c[(int64_t)m * g.ldc + n] = (bf16)o;
-        } else if (EPI == 1) {
-          atomicAdd(&g.cf[(int64_t)m * g.ldc + n], v);
         } else {
-          const float z = v + bn;
-          const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * z));
-          bf16* p = g.c + (int64_t)m * g.ldc + n;
-          *p = (bf16)((float)*p * s * __builtin_fmaf(z, 1.0f - s, 1.0f));
+          atomicAdd(&g.cf[(int64_t)m * g.ldc + n], v);
         }
       }
   }
@@ -372,16 +367,12 @@ hipError_t launch_layer_bwd_post(const LayerBwdLaunch& L, hipStream_t stream) {
   const int64_t T = L.T;
   const int HV = L.HV, D = L.D, N1 = L.N1;
   hipError_t e;
-  // dZpre = dZ * SiLU'(X W1^T + b1), over dZ
-  GemmArgs g{};
-  g.a = L.x; g.lda = D;
-  g.b = L.w1; g.ldb = D;
-  g.M = (int)T; g.N = N1; g.K = D; g.k_split = D;
-  g.c = L.dz; g.ldc = L.dz_stride;
-  g.bias = L.b1;
-  if ((e = gemm<0, 0, 2>(g, 1, stream)) != hipSuccess) return e;
+  // dZpre = dZ * SiLU'(X W1^T + b1), over dZ: the forward's f1 GEMM with a SiLU-backward
+  // epilogue (dZ's rows are N1 wide)
+  if (L.dz_stride != N1) return hipErrorInvalidValue;
+  if ((e = launch_f1_gemm_silu(L.x, L.w1, L.b1, L.dz, T, N1, D, stream, true)) != hipSuccess) return e;
   // dX = dZpre W1 (+ dY)
-  g = GemmArgs{};
+  GemmArgs g{};
   g.a = L.dz; g.lda = L.dz_stride;
   g.b = L.w1; g.ldb = D;
   g.M = (int)T; g.N = D; g.K = N1; g.k_split = N1;
