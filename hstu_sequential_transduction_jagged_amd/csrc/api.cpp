@@ -185,13 +185,19 @@ static hstu_status bwd_time_stats(int32_t B, const int32_t* offsets, int32_t max
                    "time stats launch");
 }
 
+// what attn_planned enqueues: the per-batch prepasses the bf16 kernel reads (timestamp
+// statistics and tile classes of the position + time bias, key norm bounds), the attention
+// kernel, or both
+enum AttnPart { kPrepareAndRun = 0, kPrepareOnly = 1, kRunOnly = 2 };
+
 static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
                                 const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
                                 const void* q, int64_t q_row_stride, const void* k,
                                 int64_t k_row_stride, const void* v, int64_t v_row_stride,
                                 const hstu_bias* bias, float alpha, float out_scale, void* o,
                                 bool o_f32, f32x2* ostats, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+                                size_t workspace_bytes, hipStream_t stream,
+                                AttnPart part = kPrepareAndRun) {
   int block_rows = 0;
   hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
   if (st != HSTU_OK) return st;
@@ -219,12 +225,12 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   int32_t* trel = (int32_t*)((char*)tstat + align256((size_t)total_tokens * sizeof(TimeStat)));
   uint32_t* tclass = (uint32_t*)((char*)trel + align256((size_t)total_tokens * sizeof(int32_t)));
   float* knorm = (float*)((char*)tclass + align256(tclass_bytes(B, max_seqlen, total_tokens)));
-  if (dt == HSTU_DTYPE_BF16) {
+  if (dt == HSTU_DTYPE_BF16 && part != kRunOnly) {
     st = check_hip(launch_key_norm(B, offsets, max_seqlen, k, k_row_stride, H, knorm, stream),
                    "key norm launch");
     if (st != HSTU_OK) return st;
   }
-  if (dt == HSTU_DTYPE_BF16 && ba.kind == 1) {
+  if (dt == HSTU_DTYPE_BF16 && ba.kind == 1 && part != kRunOnly) {
     st = check_hip(launch_time_stats(B, offsets, ba.ts, max_seqlen, tstat, trel, stream), "time stats launch");
     if (st != HSTU_OK) return st;
     st = check_hip(launch_tile_class(B, offsets, tstat, tclass_cols(max_seqlen), ba.num_pos,
@@ -232,6 +238,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
                    "tile class launch");
     if (st != HSTU_OK) return st;
   }
+  if (part == kPrepareOnly) return HSTU_OK;
   AttnArgs a{};
   a.tstat = tstat;
   a.trel = trel;
@@ -273,6 +280,30 @@ hstu_status hstu_attn_fwd_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk
   return attn_planned(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q, q_row_stride, k,
                       k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, false, nullptr, workspace,
                       workspace_bytes, stream);
+}
+
+hstu_status hstu_attn_prepare(int32_t dt, int32_t B, int32_t H, int32_t d,
+                              const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
+                              const void* k, int64_t k_row_stride, const hstu_bias* bias,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  // q, v and o are not read: K stands in for them so that the shared checks pass
+  return attn_planned(dt, B, H, d, d, offsets, max_seqlen, total_tokens, k, k_row_stride, k,
+                      k_row_stride, k, k_row_stride, bias, 1.0f, 1.0f, (void*)k, false, nullptr,
+                      workspace, workspace_bytes, stream, kPrepareOnly);
+}
+
+hstu_status hstu_attn_fwd_prepared(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                                   const int32_t* offsets, int32_t max_seqlen,
+                                   int64_t total_tokens, const void* q, int64_t q_row_stride,
+                                   const void* k, int64_t k_row_stride, const void* v,
+                                   int64_t v_row_stride, const hstu_bias* bias, float alpha,
+                                   float out_scale, void* o, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  return attn_planned(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q, q_row_stride, k,
+                      k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, false, nullptr,
+                      workspace, workspace_bytes, stream, kRunOnly);
 }
 
 hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,

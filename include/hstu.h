@@ -114,8 +114,8 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
  * (dt, B, H, d, offsets, max_seqlen) into `workspace` (layout as above).
  * hstu_attn_fwd_planned runs the attention only, on a workspace that a completed
  * or earlier-enqueued hstu_attn_plan call with the same dt, B, H, d, offsets and
- * max_seqlen filled (it rewrites only the timestamp statistics after the work
- * list); all other arguments as for hstu_attn_fwd. */
+ * max_seqlen filled (it rewrites only the regions after the work list: timestamp
+ * statistics, tile classes, key norm bounds); all other arguments as for hstu_attn_fwd. */
 hstu_status hstu_attn_plan(int32_t dt, int32_t B, int32_t H, int32_t d, const int32_t* offsets,
                            int32_t max_seqlen, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
@@ -126,6 +126,28 @@ hstu_status hstu_attn_fwd_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk
                                   int64_t v_row_stride, const hstu_bias* bias, float alpha,
                                   float out_scale, void* o, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/* hstu_attn_fwd_planned in two parts, for callers that time or schedule them apart.
+ * hstu_attn_prepare enqueues only the per-batch prepasses the bf16 kernel reads: key norm
+ * bounds (max |k|^2 per 32-key block and head) and, for the position + time bias, the
+ * per-block timestamp statistics and the tile classes; it reads k (rows as for
+ * hstu_attn_fwd), offsets, the bias timestamps and nothing else, writes only the workspace
+ * regions after the work list, and is a no-op for HSTU_DTYPE_F32.
+ * hstu_attn_fwd_prepared enqueues only the attention kernel, on a workspace that
+ * hstu_attn_plan and then hstu_attn_prepare (same dt, B, H, d, offsets, max_seqlen,
+ * total_tokens, k and bias) filled; arguments as for hstu_attn_fwd_planned, whose result it
+ * reproduces bit for bit.  Errors as for hstu_attn_fwd; neither call allocates. */
+hstu_status hstu_attn_prepare(int32_t dt, int32_t B, int32_t H, int32_t d,
+                              const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,
+                              const void* k, int64_t k_row_stride, const hstu_bias* bias,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+hstu_status hstu_attn_fwd_prepared(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                                   const int32_t* offsets, int32_t max_seqlen,
+                                   int64_t total_tokens, const void* q, int64_t q_row_stride,
+                                   const void* k, int64_t k_row_stride, const void* v,
+                                   int64_t v_row_stride, const hstu_bias* bias, float alpha,
+                                   float out_scale, void* o, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /* Query rows per work item (q_tile granularity) of the attention kernel for a dtype/d. */
 int32_t hstu_attn_block_rows(int32_t dt, int32_t d);

@@ -102,6 +102,13 @@ def test_host_side_errors_need_no_gpu():
     assert _attn(offsets=fake, q=fake, k=fake, v=fake, o=fake, ws=fake, wsb=1 << 20, qs=100) == -1
     assert _attn(offsets=fake, q=fake, k=fake, v=fake, o=fake, ws=ctypes.c_void_p(0x100010),
                  wsb=1 << 20) == -3
+    # the forward in parts: same checks, no launches without work
+    assert L.hstu_attn_prepare(7, 2, 2, 64, None, 16, 20, None, 128, None, None, 0, None) == -1
+    assert L.hstu_attn_prepare(1, 0, 2, 64, None, 16, 20, None, 128, None, None, 0, None) == 0
+    assert L.hstu_attn_prepare(1, 2, 2, 64, None, 16, 20, None, 128, None, None, 0, None) == -1
+    assert L.hstu_attn_prepare(1, 2, 2, 64, fake, 16, 20, fake, 128, None, fake, 16, None) == -3
+    assert L.hstu_attn_fwd_prepared(1, 2, 2, 64, 32, None, 16, 20, None, 128, None, 128, None,
+                                    128, None, 1.0, 1.0, None, None, 0, None) == -2
     assert L.hstu_layer_fwd(0, 1, 256, 4, 64, 64, None, 8, 8, None, None, None, None, None, 1e-5,
                             None, None, None, 1.0, 0, None, None, 0, None) == -2
     assert L.hstu_layer_fwd(1, 1, 256, 4, 64, 64, None, 8, 8, None, None, None, None, None, 0.0,

@@ -187,6 +187,25 @@ def test_gpu_repeat_calls_identical():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("kind", [synth.BIAS_RAB_PT, synth.BIAS_NONE, synth.BIAS_ALIBI])
+def test_gpu_prepare_then_prepared_equals_one_call(kind):
+    # hstu_attn_plan + hstu_attn_prepare + hstu_attn_fwd_prepared is hstu_attn_fwd in parts
+    inp = _case("bf16", RAGGED, kind=kind, alpha=0.05, table_std=0.5)
+    d = DevAttn(inp)
+    ref = d.run().clone()
+    ws = torch.empty(binding.attn_workspace_bytes(inp.B, inp.H, inp.max_seqlen, inp.T),
+                     dtype=torch.uint8, device="cuda")
+    binding.hstu_attn_plan(binding.DTYPE_BF16, inp.B, inp.H, inp.dqk, d.offsets, inp.max_seqlen, ws)
+    binding.hstu_attn_prepare(d.k, d.offsets, inp.max_seqlen, ws, d.bias)
+    o = binding.hstu_attn_fwd_prepared(d.q, d.k, d.v, d.offsets, inp.max_seqlen, ws, d.bias,
+                                       inp.alpha, inp.out_scale)
+    # a second kernel-only call on the same prepared workspace
+    o2 = binding.hstu_attn_fwd_prepared(d.q, d.k, d.v, d.offsets, inp.max_seqlen, ws, d.bias,
+                                        inp.alpha, inp.out_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref) and torch.equal(o2, ref)
+
+
 # ---------------------------------------------------------------------------------------------
 # integer paths: bucket indices and the work list, bit-exact
 
