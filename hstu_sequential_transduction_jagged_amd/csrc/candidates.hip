@@ -18,7 +18,7 @@
 // persistent: each walks a fixed sequence of items and skips the empty ones (chunks past a
 // user's history, candidate tiles past its candidates), so the grid carries no idle
 // workgroups.  Key tiles of 64 are moved global -> LDS directly (buffer loads with the LDS
-// bit) through a ring of 4 stages, 3 tiles ahead of the one being multiplied.  Per tile
+// bit) through a ring of 4 stages, in pairs of tiles with one barrier per pair.  Per tile
 // S^T = K Q^T on v_mfma_f32_32x32x16_bf16, the SiLU weights stay in registers as the B operand
 // of O^T += V^T P^T, V^T is read with transposing LDS reads; the self term is the
 // accumulator's starting value.
@@ -246,11 +246,10 @@ __global__ __launch_bounds__(kCThreads, kCWgPerCu) void attn_cand_bf16_kernel(Ca
     };
     dma(st0, 0);
     dma(st1, 1);
-    dma(st2, 2);
 
-    // ---- per-item constants: the register loads have landed once at most the 3 tiles'
+    // ---- per-item constants: the register loads have landed once at most the 2 tiles'
     // transfers are outstanding ----
-    wait_vm<3 * kDma>();
+    wait_vm<2 * kDma>();
     int64_t tq_min = 0, tq_max = 0;
     float ta0 = 0.f, ta1 = 0.f, ta2 = 0.f, slope_y = 0.f, cself = 0.f;
     if (KIND == 1) {
@@ -417,26 +416,25 @@ __global__ __launch_bounds__(kCThreads, kCWgPerCu) void attn_cand_bf16_kernel(Ca
       }
     };
 
-    // tile t sits in stage t % 4; at tile t the transfer of tile t + 3 goes into the stage tile
-    // t - 1 left (its readers all passed the last barrier), tile t is multiplied, then this
-    // wave's transfers of tile t + 1 are waited for and the barrier publishes them to all
-    wait_vm<2 * kDma>();
+    // tiles are taken in pairs, one barrier per pair: tiles t, t + 1 sit in stages t % 4,
+    // (t + 1) % 4; the transfers of tiles t + 2, t + 3 go into the stages of tiles t - 2, t - 1
+    // (their readers all passed the last barrier) while t and t + 1 are multiplied, then this
+    // wave's transfers are waited for and the barrier publishes them to all
+    wait_vm<0>();
     lds_barrier();
-    auto step = [&](const CandStage& cur, CandStage& nxt3, int t) __attribute__((always_inline)) {
-      dma(nxt3, t + 3);
+    auto pair = [&](const CandStage& c0, const CandStage& c1, CandStage& n0, CandStage& n1, int t) __attribute__((always_inline)) {
+      dma(n0, t + 2);
+      dma(n1, t + 3);
       __builtin_amdgcn_sched_barrier(0);
-      compute(cur, t);
-      wait_vm<2 * kDma>();
+      compute(c0, t);
+      if (t + 1 < n_tiles) compute(c1, t + 1);
+      wait_vm<0>();
       lds_barrier();
     };
     for (int t = 0; t < n_tiles; t += 4) {
-      step(st0, st3, t);
-      if (t + 1 >= n_tiles) break;
-      step(st1, st0, t + 1);
+      pair(st0, st1, st2, st3, t);
       if (t + 2 >= n_tiles) break;
-      step(st2, st1, t + 2);
-      if (t + 3 >= n_tiles) break;
-      step(st3, st2, t + 3);
+      pair(st2, st3, st0, st1, t + 2);
     }
     // the transfers past the last tile land before the stages are reused
     wait_vm<0>();
