@@ -31,7 +31,7 @@ constexpr int kBThreads = 64 * kBWaves;
 constexpr int kBRows = 32 * kBWaves;  // rows of a work item (the forward's tile height)
 constexpr int kBTile = 64;            // keys (dq kernel) or queries (dkv kernel) per LDS tile
 constexpr int kBD = 64;
-constexpr int kBRow = 72;             // padded LDS row (bf16), as in the forward kernel
+constexpr int kBRow = 72;             // dq kernel: padded LDS row (bf16, 144 bytes)
 
 // accumulator register r of a 32x32 MFMA tile holds row 8 (r / 4) + 4 hf + r % 4
 __device__ __forceinline__ int accrow(int r) { return 8 * (r >> 2) + (r & 3); }
