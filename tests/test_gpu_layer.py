@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from hstu_sequential_transduction_jagged_amd import binding, synth
-from tests.hstu_testutil import TOL, DevLayer, err_rms, err_stored, oracle_layer, to_dev
+from tests.hstu_testutil import TOL, DevLayer, err_rms, err_stored, oracle_bias, oracle_layer, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -130,3 +130,28 @@ def test_layer_uneven_widths(D, H):
     print("layer D=%d H=%d err=%.3g (without storage allowance %.3g)" % (D, H, e, err_rms(yy, ref)),
           flush=True)
     assert e <= TOL["bf16"]
+
+
+def test_stack_layer_full_size_sampled_users():
+    """The first layer of the 8-layer stack workload at its full size (128 users, T = 80 405,
+    D = 512, H = 8, position + time bias, residual), in the launch configuration the stack
+    benchmark uses.  A layer acts on each user's rows independently, so the oracle recomputes it
+    for four sampled users (the shortest, a median one, one cut to 1 024 rows by Stochastic
+    Length and the longest, 4 096 rows) and their Y rows are compared with the GPU's."""
+    inp = synth.stack8()
+    d, y = _run_layer(inp)
+    yy = y.float().cpu().numpy()
+    lengths = np.diff(inp.offsets.astype(np.int64))
+    order = np.argsort(lengths, kind="stable")
+    picks = {int(order[0]), int(order[len(order) // 2]), int(np.argmin(np.abs(lengths - 1024))),
+             int(order[-1])}
+    L = inp.layers[0]
+    for b in sorted(picks):
+        s, e = int(inp.offsets[b]), int(inp.offsets[b + 1])
+        ref = oracle.layer(np.array([0, e - s]), inp.x[s:e], L.w1, L.b1, L.gamma, L.beta, L.w2,
+                           L.b2, oracle_bias(L.bias, inp.ts[s:e], inp.H), inp.alpha, inp.H,
+                           inp.dqk, inp.dv, residual=inp.residual, ln_eps=inp.ln_eps)
+        err = err_stored(yy[s:e], ref, "bf16")
+        print("stack8 layer 0, user %d (%d rows): err=%.3g (without storage allowance %.3g)"
+              % (b, e - s, err, err_rms(yy[s:e], ref)), flush=True)
+        assert err <= TOL["bf16"], (b, err)
