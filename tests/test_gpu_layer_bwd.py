@@ -65,3 +65,37 @@ def test_layer_bwd_wide():
     inp = synth.make_layer("lbwd_wide", 41, [70, 257], D=512, H=16, d=64, alpha=1.0 / 128,
                            residual=True, P=128, NT=32, table_std=0.2, randomize_affine=True)
     _check(inp, seed=4)
+
+
+def test_layer_bwd_full_size_sampled_users():
+    """The first layer of the 8-layer stack workload at its full size (128 users, T = 80 405,
+    D = 512, H = 8, position + time bias, residual), forward and backward as the layer benchmark
+    runs them.  dX of a user depends only on that user's rows, so the oracle recomputes it for
+    three sampled users (a median one, one cut to 1 024 rows by Stochastic Length, the longest,
+    4 096 rows); the weight gradients sum over every user and are left to the cases above."""
+    inp = synth.stack8()
+    rng = np.random.default_rng(12)
+    dY = synth.round_bf16(rng.standard_normal((inp.T, inp.D)).astype(np.float32))
+    d = DevLayer(inp)
+    L = d.layers[0]
+    ws = torch.empty(binding.layer_workspace_bytes(inp.B, inp.T, inp.D, inp.H, inp.dqk, inp.dv,
+                                                   inp.max_seqlen), dtype=torch.uint8, device="cuda")
+    d.run_layer(d.x, workspace=ws)
+    got = binding.hstu_layer_bwd(d.x, d.offsets, inp.max_seqlen, L["w1"], L["b1"], L["gamma"],
+                                 L["beta"], L["w2"], inp.H, inp.dqk, inp.dv, L["bias"], inp.alpha,
+                                 inp.residual, inp.ln_eps, ws, to_dev(dY, torch.bfloat16))
+    torch.cuda.synchronize()
+    dx = got["dx"].float().cpu().numpy().astype(np.float64)
+    lengths = np.diff(inp.offsets.astype(np.int64))
+    order = np.argsort(lengths, kind="stable")
+    picks = {int(order[len(order) // 2]), int(np.argmin(np.abs(lengths - 1024))), int(order[-1])}
+    P = inp.layers[0]
+    for b in sorted(picks):
+        s, e = int(inp.offsets[b]), int(inp.offsets[b + 1])
+        ref = oracle.layer_bwd(np.array([0, e - s]), inp.x[s:e], P.w1, P.b1, P.gamma, P.beta,
+                               P.w2, P.b2, oracle_bias(P.bias, inp.ts[s:e], inp.H), inp.alpha,
+                               inp.H, inp.dqk, inp.dv, dY[s:e], residual=inp.residual,
+                               ln_eps=inp.ln_eps)
+        err = err_rms(dx[s:e], ref["dx"])
+        print("stack8 layer 0 backward, user %d (%d rows): dx err=%.3g" % (b, e - s, err), flush=True)
+        assert err <= TOL["dx"], (b, err)
