@@ -226,13 +226,15 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   uint32_t* tclass = (uint32_t*)((char*)trel + align256((size_t)total_tokens * sizeof(int32_t)));
   float* knorm = (float*)((char*)tclass + align256(tclass_bytes(B, max_seqlen, total_tokens)));
   if (dt == HSTU_DTYPE_BF16 && part != kRunOnly) {
-    st = check_hip(launch_key_norm(B, offsets, max_seqlen, k, k_row_stride, H, knorm, stream),
+    // key norm bounds, and for the position + time bias the timestamp statistics with them
+    const bool rab = ba.kind == 1;
+    st = check_hip(launch_key_norm(B, offsets, max_seqlen, k, k_row_stride, H, knorm,
+                                   rab ? ba.ts : nullptr, rab ? tstat : nullptr,
+                                   rab ? trel : nullptr, stream),
                    "key norm launch");
     if (st != HSTU_OK) return st;
   }
   if (dt == HSTU_DTYPE_BF16 && ba.kind == 1 && part != kRunOnly) {
-    st = check_hip(launch_time_stats(B, offsets, ba.ts, max_seqlen, tstat, trel, stream), "time stats launch");
-    if (st != HSTU_OK) return st;
     st = check_hip(launch_tile_class(B, offsets, tstat, tclass_cols(max_seqlen), ba.num_pos,
                                      ba.num_time, tclass, stream),
                    "tile class launch");

@@ -133,10 +133,15 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const int32_t* __restri
 // at row tclass_row0(tok0, b) + block.  One workgroup per (user, block) of eight waves; wave w
 // takes heads w, w + 8, ...: lane l sums the squares of half l % 2 of token l / 2's head row,
 // the lane pair adds its halves and the wave's maximum is the bound.  No LDS, no barriers.
+// With timestamps, wave 7 also writes the block's timestamp statistics exactly as
+// time_stats_kernel does (one launch fewer for the position + time bias).
 // ============================================================================================
 __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict__ offsets,
                                                        const bf16* __restrict__ k, int64_t k_stride,
-                                                       int32_t H, float* __restrict__ knorm) {
+                                                       int32_t H, float* __restrict__ knorm,
+                                                       const int64_t* __restrict__ ts,
+                                                       TimeStat* __restrict__ stats,
+                                                       int32_t* __restrict__ rel) {
   const int b = blockIdx.x, blk = blockIdx.y, lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t tok0 = offsets[b];
@@ -162,6 +167,18 @@ __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict
     acc += __shfl_xor(acc, 1, 64);
     const float m = wave_max_dpp(acc);
     if (lane == 0) dst[h] = m;
+  }
+  if (ts && wave == 7) {
+    const int j = 32 * blk + (lane & 31);
+    const bool ok = j < n;
+    const int64_t t = ok ? ts[tok0 + j] : 0;
+    int64_t mn = ok ? t : kTMax, mx = ok ? t : kTMin;
+    half_minmax(mn, mx);
+    if (ok && lane < 32) {
+      const int64_t d = t - mn;
+      rel[tok0 + j] = d > 0x7fffffffLL ? 0x7fffffff : (int32_t)d;
+      if (lane == 0) stats[tok0 + j] = TimeStat{mn, mx};
+    }
   }
 }
 
@@ -816,10 +833,11 @@ hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* t
 }
 
 hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int32_t max_seqlen, const void* k,
-                           int64_t k_stride, int32_t H, float* knorm, hipStream_t stream) {
+                           int64_t k_stride, int32_t H, float* knorm, const int64_t* ts,
+                           TimeStat* stats, int32_t* rel, hipStream_t stream) {
   if (B <= 0 || max_seqlen <= 0) return hipSuccess;
   hipLaunchKernelGGL(key_norm_kernel, dim3(B, (max_seqlen + 31) / 32), dim3(512), 0, stream,
-                     offsets, (const bf16*)k, k_stride, H, knorm);
+                     offsets, (const bf16*)k, k_stride, H, knorm, ts, stats, rel);
   return hipGetLastError();
 }
 
