@@ -228,7 +228,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   if (dt == HSTU_DTYPE_BF16 && part != kRunOnly) {
     // key norm bounds, and for the position + time bias the timestamp statistics with them
     const bool rab = ba.kind == 1;
-    st = check_hip(launch_key_norm(B, offsets, max_seqlen, k, k_row_stride, H, knorm,
+    st = check_hip(launch_key_norm(B, offsets, total_tokens, k, k_row_stride, H, knorm,
                                    rab ? ba.ts : nullptr, rab ? tstat : nullptr,
                                    rab ? trel : nullptr, stream),
                    "key norm launch");

@@ -130,27 +130,40 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const int32_t* __restri
 // ============================================================================================
 // Key norm bounds: for every 32-key block of a user (blocks start at the user's first token)
 // and head h, the largest squared norm of the block's key rows, in fp32 from the bf16 keys,
-// at row tclass_row0(tok0, b) + block.  One workgroup per (user, block) of eight waves; wave w
+// at row tclass_row0(tok0, b) + block.  One workgroup per row of eight waves (the row's user is
+// found by bisection over the offsets; rows between users exit at once); wave w
 // takes heads w, w + 8, ...: lane l sums the squares of half l % 2 of token l / 2's head row,
 // the lane pair adds its halves and the wave's maximum is the bound.  No LDS, no barriers.
 // With timestamps, wave 7 also writes the block's timestamp statistics exactly as
 // time_stats_kernel does (one launch fewer for the position + time bias).
 // ============================================================================================
 __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict__ offsets,
-                                                       const bf16* __restrict__ k, int64_t k_stride,
-                                                       int32_t H, float* __restrict__ knorm,
+                                                       int32_t B, const bf16* __restrict__ k,
+                                                       int64_t k_stride, int32_t H,
+                                                       float* __restrict__ knorm,
                                                        const int64_t* __restrict__ ts,
                                                        TimeStat* __restrict__ stats,
                                                        int32_t* __restrict__ rel) {
-  const int b = blockIdx.x, blk = blockIdx.y, lane = threadIdx.x & 63;
+  const int64_t r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the last user whose first row is at or before r (first rows never decrease with b)
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tclass_row0(offsets[mid], mid) <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo;
   const int64_t tok0 = offsets[b];
   const int n = offsets[b + 1] - offsets[b];
-  if (32 * blk >= n) return;
+  const int64_t blk64 = r - tclass_row0(tok0, b);
+  if (blk64 < 0 || 32 * blk64 >= n) return;
+  const int blk = (int)blk64;
   const int tok = 32 * blk + (lane >> 1);
   const bool valid = tok < n;
   const bf16* row = k + (tok0 + tok) * k_stride + 32 * (lane & 1);
-  float* dst = knorm + (tclass_row0(tok0, b) + blk) * H;
+  float* dst = knorm + r * H;
   for (int h = wave; h < H; h += 8) {
     float acc = 0.f;
     if (valid) {
@@ -832,12 +845,14 @@ hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* t
   return hipGetLastError();
 }
 
-hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int32_t max_seqlen, const void* k,
-                           int64_t k_stride, int32_t H, float* knorm, const int64_t* ts,
-                           TimeStat* stats, int32_t* rel, hipStream_t stream) {
-  if (B <= 0 || max_seqlen <= 0) return hipSuccess;
-  hipLaunchKernelGGL(key_norm_kernel, dim3(B, (max_seqlen + 31) / 32), dim3(512), 0, stream,
-                     offsets, (const bf16*)k, k_stride, H, knorm, ts, stats, rel);
+hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int64_t total_tokens,
+                           const void* k, int64_t k_stride, int32_t H, float* knorm,
+                           const int64_t* ts, TimeStat* stats, int32_t* rel, hipStream_t stream) {
+  if (B <= 0 || total_tokens <= 0) return hipSuccess;
+  const int64_t rows = (total_tokens + 31 * (int64_t)B) / 32 + 1;
+  if (rows > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(key_norm_kernel, dim3((unsigned)rows), dim3(512), 0, stream, offsets, B,
+                     (const bf16*)k, k_stride, H, knorm, ts, stats, rel);
   return hipGetLastError();
 }
 

@@ -188,9 +188,9 @@ hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* t
                              int32_t max_seqlen, TimeStat* stats, int32_t* rel,
                              hipStream_t stream);
 // key norm bounds; with ts non-null also the timestamp statistics of launch_time_stats
-hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int32_t max_seqlen, const void* k,
-                           int64_t k_stride, int32_t H, float* knorm, const int64_t* ts,
-                           TimeStat* stats, int32_t* rel, hipStream_t stream);
+hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int64_t total_tokens,
+                           const void* k, int64_t k_stride, int32_t H, float* knorm,
+                           const int64_t* ts, TimeStat* stats, int32_t* rel, hipStream_t stream);
 hipError_t launch_tile_class(int32_t B, const int32_t* offsets, const TimeStat* stats,
                              int32_t max_blocks, int32_t num_pos, int32_t num_time,
                              uint32_t* tclass, hipStream_t stream);
