@@ -38,6 +38,7 @@ struct F1Args {
   const bf16* W;       // [N][K]
   const float* bias;   // [N] or null
   bf16* Y;             // [M][N]
+  const bf16* R;       // EPI 2: [M][N] added before the rounding, or null
   int64_t M;
   int32_t N, K, tiles;
 };
@@ -52,7 +53,8 @@ __device__ __forceinline__ int f1_off(int row, int chunk) {
 // NK: K / 32 when known at compile time (the slice loop is then straight-line code, which keeps
 // the compiler's own waits on the transfers exact), 0 for any K.  EPI 0: Y = SiLU(acc); EPI 1
 // (the layer's backward): Y holds dZ on entry and dZ * SiLU'(acc) on exit, acc = X W^T + b, with
-// SiLU'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z), the product in fp32 and rounded once.
+// SiLU'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z), the product in fp32 and rounded once;
+// EPI 2: Y = acc (+ R), rounded once (the layer backward's dX = dZpre W1 + dY).
 template <int NK, int EPI>
 __global__ __launch_bounds__(kF1Threads, 3) void f1_kernel(F1Args g) {
   // stage arrays of their own: the compiler then knows which stage a transfer writes
@@ -190,15 +192,20 @@ __global__ __launch_bounds__(kF1Threads, 3) void f1_kernel(F1Args g) {
           } else {
             // this lane's token 128 wt + 32 j + l32 and features 64 wf + 32 i + 8 grp + 4 hf .. + 3
             const int64_t tok = 128 * wt + 32 * (2 * p + jj) + l32;
+            const bf16* src = EPI == 1 ? g.Y : g.R;
             f32x4 dz = {0.f, 0.f, 0.f, 0.f};
-            if (tok < rows)
+            if (tok < rows && src)
               dz = __builtin_convertvector(
-                  *(const bf16x4*)(g.Y + (m0 + tok) * N + n0 + 64 * wf + 32 * i + 8 * grp + 4 * hf), f32x4);
+                  *(const bf16x4*)(src + (m0 + tok) * N + n0 + 64 * wf + 32 * i + 8 * grp + 4 * hf), f32x4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float x = acc[i][2 * p + jj][4 * grp + e];
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
-              v[e] = dz[e] * (sg * __builtin_fmaf(x, 1.0f - sg, 1.0f));
+              if (EPI == 1) {
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
+                v[e] = dz[e] * (sg * __builtin_fmaf(x, 1.0f - sg, 1.0f));
+              } else {
+                v[e] = x + dz[e];
+              }
             }
           }
           const int q = 8 * wf + 4 * i + grp;
@@ -474,7 +481,8 @@ __global__ void embed_sum_kernel(int64_t T, int dim, const bf16* __restrict__ it
 }  // namespace
 
 hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, bf16* z, int64_t M,
-                               int32_t N, int32_t K, hipStream_t stream, bool silu_bwd) {
+                               int32_t N, int32_t K, hipStream_t stream, bool silu_bwd,
+                               const bf16* resid, bool plain) {
   if (N % kF1Feat || K % kF1K || K <= 0) return hipErrorInvalidValue;
   if ((int64_t)kF1Tok * N * 2 > 0x7fffffff) return hipErrorInvalidValue;
   if ((int64_t)kF1Tok * 2 * K > 0x7fffffff || (int64_t)kF1Feat * 2 * K > 0x7fffffff)
@@ -483,9 +491,12 @@ hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, b
   const int64_t tiles = (int64_t)(N / kF1Feat) * ((M + kF1Tok - 1) / kF1Tok);
   if (tiles > 0x7ffffff0) return hipErrorInvalidValue;
   F1Args g{};
-  g.X = x; g.W = w1; g.bias = b1; g.Y = z; g.M = M; g.N = N; g.K = K; g.tiles = (int32_t)tiles;
+  g.X = x; g.W = w1; g.bias = b1; g.Y = z; g.R = resid; g.M = M; g.N = N; g.K = K;
+  g.tiles = (int32_t)tiles;
   const unsigned grid = (unsigned)((tiles + 7) / 8 * 8);
-  if (silu_bwd) {
+  if (plain) {
+    hipLaunchKernelGGL((f1_kernel<0, 2>), dim3(grid), dim3(kF1Threads), 0, stream, g);
+  } else if (silu_bwd) {
     if (K == 512) hipLaunchKernelGGL((f1_kernel<16, 1>), dim3(grid), dim3(kF1Threads), 0, stream, g);
     else if (K == 256) hipLaunchKernelGGL((f1_kernel<8, 1>), dim3(grid), dim3(kF1Threads), 0, stream, g);
     else hipLaunchKernelGGL((f1_kernel<0, 1>), dim3(grid), dim3(kF1Threads), 0, stream, g);
@@ -494,6 +505,28 @@ hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, b
     else if (K == 256) hipLaunchKernelGGL((f1_kernel<8, 0>), dim3(grid), dim3(kF1Threads), 0, stream, g);
     else hipLaunchKernelGGL((f1_kernel<0, 0>), dim3(grid), dim3(kF1Threads), 0, stream, g);
   }
+  return hipGetLastError();
+}
+
+// dst[c][r] = src[r][c] for a bf16 [R][C] matrix (both dense), through 32 x 32 LDS tiles
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16* __restrict__ src,
+                                                             bf16* __restrict__ dst, int32_t R,
+                                                             int32_t C) {
+  __shared__ bf16 t[32][33];
+  const int c0 = 32 * blockIdx.x, r0 = 32 * blockIdx.y;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int k = ty; k < 32; k += 8)
+    if (r0 + k < R && c0 + tx < C) t[k][tx] = src[(int64_t)(r0 + k) * C + c0 + tx];
+  __syncthreads();
+  for (int k = ty; k < 32; k += 8)
+    if (c0 + k < C && r0 + tx < R) dst[(int64_t)(c0 + k) * R + r0 + tx] = t[tx][k];
+}
+
+hipError_t launch_transpose_bf16(const bf16* src, bf16* dst, int32_t R, int32_t C,
+                                 hipStream_t stream) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((C + 31) / 32, (R + 31) / 32), dim3(256), 0,
+                     stream, src, dst, R, C);
   return hipGetLastError();
 }
 

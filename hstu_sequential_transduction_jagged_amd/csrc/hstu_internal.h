@@ -187,6 +187,9 @@ hipError_t launch_schedule(const int32_t* offsets, int32_t B, int32_t H, int32_t
 hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts,
                              int32_t max_seqlen, TimeStat* stats, int32_t* rel,
                              hipStream_t stream);
+// dst[c][r] = src[r][c], bf16 [R][C]
+hipError_t launch_transpose_bf16(const bf16* src, bf16* dst, int32_t R, int32_t C,
+                                 hipStream_t stream);
 // key norm bounds; with ts non-null also the timestamp statistics of launch_time_stats
 hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int64_t total_tokens,
                            const void* k, int64_t k_stride, int32_t H, float* knorm,
@@ -201,7 +204,8 @@ int attn_block_rows_f32(int d);
 
 hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, bf16* z, int64_t M,
                                int32_t N, int32_t K, hipStream_t stream,
-                               bool silu_bwd = false);
+                               bool silu_bwd = false, const bf16* resid = nullptr,
+                               bool plain = false);
 hipError_t launch_ln_gate_f2(const bf16* o, const f32x2* ostats, const bf16* u,
                              int64_t u_stride, const float* gamma, const float* beta, float eps,
                              const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,

@@ -371,14 +371,23 @@ hipError_t launch_layer_bwd_post(const LayerBwdLaunch& L, hipStream_t stream) {
   // epilogue (dZ's rows are N1 wide)
   if (L.dz_stride != N1) return hipErrorInvalidValue;
   if ((e = launch_f1_gemm_silu(L.x, L.w1, L.b1, L.dz, T, N1, D, stream, true)) != hipSuccess) return e;
-  // dX = dZpre W1 (+ dY)
+  // dX = dZpre W1 (+ dY): on the f1 kernel with W1^T as its weight operand when the dG buffer
+  // (free once the LayerNorm backward has run) holds W1^T, else on the generic kernel
   GemmArgs g{};
-  g.a = L.dz; g.lda = L.dz_stride;
-  g.b = L.w1; g.ldb = D;
-  g.M = (int)T; g.N = D; g.K = N1; g.k_split = N1;
-  g.c = L.dx; g.ldc = D;
-  g.resid = L.residual ? L.dy : nullptr; g.ldr = D;
-  if ((e = gemm<0, 1, 0>(g, 1, stream)) != hipSuccess) return e;
+  if ((int64_t)D * N1 <= T * HV) {
+    bf16* w1t = (bf16*)L.dg;  // [D][N1]
+    if ((e = launch_transpose_bf16(L.w1, w1t, N1, D, stream)) != hipSuccess) return e;
+    if ((e = launch_f1_gemm_silu(L.dz, w1t, nullptr, L.dx, T, D, N1, stream, false,
+                                 L.residual ? L.dy : nullptr, true)) != hipSuccess)
+      return e;
+  } else {
+    g.a = L.dz; g.lda = L.dz_stride;
+    g.b = L.w1; g.ldb = D;
+    g.M = (int)T; g.N = D; g.K = N1; g.k_split = N1;
+    g.c = L.dx; g.ldc = D;
+    g.resid = L.residual ? L.dy : nullptr; g.ldr = D;
+    if ((e = gemm<0, 1, 0>(g, 1, stream)) != hipSuccess) return e;
+  }
   // weight gradients, split over tokens into slices of `kt` rows
   int64_t kt = ((T + 63) / 64 + 31) / 32 * 32;
   if (kt < 256) kt = 256;

@@ -61,6 +61,18 @@ def test_layer_bwd_ragged(kind, residual):
     _check(inp)
 
 
+@pytest.mark.parametrize("residual", [False, True])
+def test_layer_bwd_enough_tokens_for_the_f1_dx_path(residual):
+    # T H d_v >= D N1 (1 306 x 128 >= 256 x 512): dX = dZpre W1 (+ dY) runs on the f1 kernel with
+    # W1^T staged in the freed dG buffer.  No bias here, so every gradient checked depends on the
+    # layer's products alone (the bias tables' gradients are covered by the cases above)
+    inp = synth.make_layer("lbwd_f1dx", 43, [1, 300, 555, 450], D=256, H=2, d=64,
+                           alpha=1.0 / 128, residual=residual, bias_kind=synth.BIAS_NONE,
+                           randomize_affine=True)
+    assert inp.T * inp.H * inp.dv >= inp.D * 2 * inp.H * (inp.dqk + inp.dv)
+    _check(inp, seed=5)
+
+
 def test_layer_bwd_wide():
     inp = synth.make_layer("lbwd_wide", 41, [70, 257], D=512, H=16, d=64, alpha=1.0 / 128,
                            residual=True, P=128, NT=32, table_std=0.2, randomize_affine=True)
