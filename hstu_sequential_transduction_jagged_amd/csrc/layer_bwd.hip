@@ -353,7 +353,7 @@ hipError_t launch_layer_bwd_pre(const LayerBwdLaunch& L, hipStream_t stream) {
   // LayerNorm and gate backward
   const int nc = (HV / 8 + 63) / 64;
   const int64_t want = (T + 3) / 4;
-  const unsigned blocks = (unsigned)(want < 1 ? 1 : want > 256 ? 256 : want);
+  const unsigned blocks = (unsigned)(want < 1 ? 1 : want > 1024 ? 1024 : want);
   if (nc == 1)
     hipLaunchKernelGGL(ln_gate_bwd_kernel<1>, dim3(blocks), dim3(256), 0, stream, T, HV, L.eps, L.dg, L.o, L.u, L.u_stride, L.gamma, L.beta, L.dz, L.dz_stride, L.g, L.dO, L.dgamma, L.dbeta);
   else if (nc == 2)
