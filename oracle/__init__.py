@@ -55,6 +55,10 @@ def _L():
         _lib.oracle_attention.argtypes = [i32, i32, i32, i32, P, P, i64, P, i64, P, i64, i32, P,
                                           P, i32, i64, P, i32, i64, P, f64, f64, P]
         _lib.oracle_attention.restype = None
+        _lib.oracle_attention_mirror.argtypes = [i32, i32, i32, i32, P, P, i64, P, i64, P, i64,
+                                                 i32, P, P, i32, i64, P, i32, i64, P, f64, f64,
+                                                 f64, P]
+        _lib.oracle_attention_mirror.restype = None
         _lib.oracle_attention_rows.argtypes = [i32, i32, i32, i32, P, P, i64, P, i64, P, i64, i32,
                                                P, P, i32, i64, P, i32, i64, P, f64, f64, i64, P, P,
                                                P]
@@ -69,6 +73,8 @@ def _L():
         _lib.oracle_layer.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, f64, P, P, i32, P,
                                       P, i32, i64, P, i32, i64, P, f64, i32, P, P, P]
         _lib.oracle_layer.restype = None
+        _lib.oracle_bucket_counts.argtypes = [i32, P, P, i32, i32, P, P]
+        _lib.oracle_bucket_counts.restype = None
         _lib.oracle_num_threads.restype = i32
         _lib.oracle_num_threads.argtypes = []
     return _lib
@@ -93,6 +99,21 @@ def pos_bucket(i_minus_j: int, num_pos: int) -> int:
 
 def time_bucket(dt: int, num_time: int) -> int:
     return int(_L().oracle_time_bucket(int(dt), int(num_time)))
+
+
+def bucket_counts(offsets, ts, num_pos: int, num_time: int):
+    """For every row i of every user: how many keys j <= i fall in each position bucket and in
+    each time bucket (the integer part of the bias, as the rab^{p,t} form defines it).
+    Returns int32 arrays [T, num_pos] and [T, num_time]."""
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    ts = np.ascontiguousarray(ts, dtype=np.int64)
+    T = int(offs[-1]) if len(offs) else 0
+    pc = np.zeros((T, num_pos), np.int32)
+    tc = np.zeros((T, num_time), np.int32)
+    if T:
+        _L().oracle_bucket_counts(len(offs) - 1, _ptr(offs), _ptr(ts), int(num_pos),
+                                  int(num_time), _ptr(pc), _ptr(tc))
+    return pc, tc
 
 
 class Bias:
@@ -129,8 +150,11 @@ def alibi_slopes(H: int) -> np.ndarray:
     return np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float64)
 
 
-def attention(offsets, q, k, v, bias: Bias, alpha: float, out_scale: float = 1.0):
-    """Eq. (2) on a jagged batch. q, k: [T, H, dqk]; v: [T, H, dv]. Returns [T, H, dv] fp64."""
+def attention(offsets, q, k, v, bias: Bias, alpha: float, out_scale: float = 1.0,
+              weight_unit: float = 0.0):
+    """Eq. (2) on a jagged batch. q, k: [T, H, dqk]; v: [T, H, dv]. Returns [T, H, dv] fp64.
+    weight_unit != 0 is the mirror mode: every SiLU weight is kept as weight_unit times a bf16
+    value before it multiplies v (a bf16 path's weight operand)."""
     offs = np.ascontiguousarray(offsets, dtype=np.int64)
     q, k, v = _f64(q), _f64(k), _f64(v)
     T, H, dqk = q.shape
@@ -139,8 +163,9 @@ def attention(offsets, q, k, v, bias: Bias, alpha: float, out_scale: float = 1.0
     o = np.zeros((T, H, dv), dtype=np.float64)
     if T == 0 or B == 0:
         return o
-    _L().oracle_attention(B, H, dqk, dv, _ptr(offs), _ptr(q), H * dqk, _ptr(k), H * dqk, _ptr(v),
-                          H * dv, *bias.args(), float(alpha), float(out_scale), _ptr(o))
+    _L().oracle_attention_mirror(B, H, dqk, dv, _ptr(offs), _ptr(q), H * dqk, _ptr(k), H * dqk,
+                                 _ptr(v), H * dv, *bias.args(), float(alpha), float(out_scale),
+                                 float(weight_unit), _ptr(o))
     return o
 
 
@@ -233,8 +258,62 @@ def layer(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float, H: 
     return y
 
 
+def round_bf16(a):
+    """Each value rounded to the nearest bfloat16 (8 significant bits, ties to even), returned
+    as float64.  Used only by the mirror mode of ``layer`` / ``layer_bwd``, which rounds named
+    intermediates to bf16 storage to measure how much of a bf16 path's error its storage
+    format alone explains.  (No bf16 subnormals or overflow: the magnitudes here are moderate.)"""
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)                       # a = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)  # np.rint rounds halves to even
+
+
+# intermediates of the layer a mirror run may round to bf16 (forward, then backward):
+#   Z, G, Y, dG, dO, dZ, dZpre  the tensor, each element to the nearest bf16;
+#   O    each element to the nearest bf16;  Oc  each (token, head) row as its mean plus bf16
+#        deviations from it (a storage form that keeps the row's spread to 8 bits);
+#   P    the attention's SiLU weights, as bf16 multiples of ln(2)/2 (the weights a path that
+#        evaluates SiLU in base-2 units hands to the matrix product).
+MIRROR_POINTS = ("Z", "P", "O", "Oc", "G", "Y", "dG", "dO", "dZ", "dZpre")
+
+
+def _round_rows_centred(o, H):
+    T = o.shape[0]
+    o3 = o.reshape(T, H, -1)
+    m = o3.mean(axis=2, keepdims=True)
+    return (m + round_bf16(o3 - m)).reshape(o.shape)
+
+
+def layer_mirror(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float, H: int,
+                 dqk: int, dv: int, residual: bool = False, ln_eps: float = 1e-5, round_at=()):
+    """``layer`` composed step by step in float64 (eqs. (1)-(3)), with the intermediates named in
+    `round_at` (Z, P, O or Oc, G, Y; see MIRROR_POINTS) rounded where they are formed.  With
+    nothing rounded it is the exact layer.  Returns (y, z, o)."""
+    for p in round_at:
+        assert p in MIRROR_POINTS, p
+    R = lambda name, a: round_bf16(a) if name in round_at else a
+    offs = np.ascontiguousarray(offsets, dtype=np.int64)
+    x, w1, b1, w2, b2 = _f64(x), _f64(w1), _f64(b1), _f64(w2), _f64(b2)
+    gamma, beta = _f64(gamma), _f64(beta)
+    T = x.shape[0]
+    HV, HQ = H * dv, H * dqk
+    zpre = x @ w1.T + b1
+    z = R("Z", zpre / (1.0 + np.exp(-zpre)))
+    V, Q, K = z[:, HV:2 * HV], z[:, 2 * HV:2 * HV + HQ], z[:, 2 * HV + HQ:]
+    o = R("O", attention(offs, Q.reshape(T, H, dqk), K.reshape(T, H, dqk), V.reshape(T, H, dv),
+                         bias, alpha, weight_unit=0.5 * math.log(2.0) if "P" in round_at else 0.0
+                         ).reshape(T, HV))
+    if "Oc" in round_at:
+        o = _round_rows_centred(o, H)
+    xc = o - o.mean(axis=1, keepdims=True)
+    xhat = xc / np.sqrt((xc * xc).mean(axis=1, keepdims=True) + ln_eps)
+    G = R("G", (xhat * gamma + beta) * z[:, :HV])
+    y = R("Y", G @ w2.T + b2 + (x if residual else 0.0))
+    return y, z, o
+
+
 def layer_bwd(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float, H: int,
-              dqk: int, dv: int, dY, residual: bool = False, ln_eps: float = 1e-5):
+              dqk: int, dv: int, dY, residual: bool = False, ln_eps: float = 1e-5, round_at=()):
     """Gradients of one HSTU layer ("Actions Speak Louder than Words" §3.1 eqs. (1)-(3)) for the
     upstream gradient dY, by the chain rule through each equation in reverse:
       eq. (3)  Y = (LN(O) * U) W2^T + b2 (+ X):  dW2 = dY^T G, db2 = sum_t dY, dG = dY W2,
@@ -243,14 +322,24 @@ def layer_bwd(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float,
       eq. (2)  attention_bwd (dQ, dK, dV, table gradients);
       eq. (1)  Z = SiLU(X W1^T + b1), split U | V | Q | K:  dZpre = dZ * SiLU'(Zpre),
                dW1 = dZpre^T X, db1 = sum_t dZpre, dX = dZpre W1 (+ dY).
+    `round_at` (mirror mode, see ``layer_mirror`` and MIRROR_POINTS) rounds the named
+    intermediates where they are formed; empty gives the exact gradients.
     Returns a dict of float64 arrays: dx, dw1, db1, dgamma, dbeta, dw2, db2, dw_pos, dw_time."""
+    for p in round_at:
+        assert p in MIRROR_POINTS, p
+    R = lambda name, a: round_bf16(a) if name in round_at else a
     offs = np.ascontiguousarray(offsets, dtype=np.int64)
     x, w1, b1, w2, b2 = _f64(x), _f64(w1), _f64(b1), _f64(w2), _f64(b2)
     gamma, beta, dY = _f64(gamma), _f64(beta), _f64(dY)
     T, D = x.shape
     HV, HQ = H * dv, H * dqk
-    _, z, o = layer(offs, x, w1, b1, gamma, beta, w2, b2, bias, alpha, H, dqk, dv,
-                    residual=residual, ln_eps=ln_eps, return_intermediates=True)
+    if round_at:
+        _, z, o = layer_mirror(offs, x, w1, b1, gamma, beta, w2, b2, bias, alpha, H, dqk, dv,
+                               residual, ln_eps,
+                               tuple(p for p in round_at if p in ("Z", "P", "O", "Oc")))
+    else:
+        _, z, o = layer(offs, x, w1, b1, gamma, beta, w2, b2, bias, alpha, H, dqk, dv,
+                        residual=residual, ln_eps=ln_eps, return_intermediates=True)
     zpre = x @ w1.T + b1
     U = z[:, :HV]
     V, Q, K = z[:, HV:2 * HV], z[:, 2 * HV:2 * HV + HQ], z[:, 2 * HV + HQ:]
@@ -259,22 +348,23 @@ def layer_bwd(offsets, x, w1, b1, gamma, beta, w2, b2, bias: Bias, alpha: float,
     rstd = 1.0 / np.sqrt((xc * xc).mean(axis=1, keepdims=True) + ln_eps)
     xhat = xc * rstd
     ln = xhat * gamma + beta
-    G = ln * U
+    G = R("G", ln * U)
     dw2 = dY.T @ G
     db2 = dY.sum(axis=0)
-    dG = dY @ w2
+    dG = R("dG", dY @ w2)
     dU = dG * ln
     dln = dG * U
     dgamma = (dln * xhat).sum(axis=0)
     dbeta = dln.sum(axis=0)
     dxhat = dln * gamma
-    dO = rstd * (dxhat - dxhat.mean(axis=1, keepdims=True)
-                 - xhat * (dxhat * xhat).mean(axis=1, keepdims=True))
+    dO = R("dO", rstd * (dxhat - dxhat.mean(axis=1, keepdims=True)
+                         - xhat * (dxhat * xhat).mean(axis=1, keepdims=True)))
     dq, dk, dvv, dwp, dwt = attention_bwd(offs, Q.reshape(T, H, dqk), K.reshape(T, H, dqk),
                                           V.reshape(T, H, dv), dO.reshape(T, H, dv), bias, alpha)
-    dZ = np.concatenate([dU, dvv.reshape(T, HV), dq.reshape(T, HQ), dk.reshape(T, HQ)], axis=1)
+    dZ = R("dZ", np.concatenate([dU, dvv.reshape(T, HV), dq.reshape(T, HQ), dk.reshape(T, HQ)],
+                                axis=1))
     sg = 1.0 / (1.0 + np.exp(-zpre))
-    dzpre = dZ * sg * (1.0 + zpre * (1.0 - sg))
+    dzpre = R("dZpre", dZ * sg * (1.0 + zpre * (1.0 - sg)))
     dw1 = dzpre.T @ x
     db1 = dzpre.sum(axis=0)
     dx = dzpre @ w1 + (dY if residual else 0.0)

@@ -61,6 +61,25 @@ int32_t oracle_time_bucket(int64_t dt, int32_t num_time_buckets) {
   return e;
 }
 
+/* Bucket histograms of every row: for user b's local row i, pos_counts[t][p] and
+ * time_counts[t][k] (t = offsets[b] + i) count the keys j <= i whose position bucket is p and
+ * whose time bucket is k.  Used to check the integer bucket indexing of the attention. */
+void oracle_bucket_counts(int32_t B, const int64_t* offsets, const int64_t* ts, int32_t num_pos,
+                          int32_t num_time, int32_t* pos_counts, int32_t* time_counts) {
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t base = offsets[b], n = offsets[b + 1] - offsets[b];
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t i = 0; i < n; ++i) {
+      int32_t* pc = pos_counts + (base + i) * num_pos;
+      int32_t* tc = time_counts + (base + i) * num_time;
+      for (int64_t j = 0; j <= i; ++j) {
+        pc[oracle_pos_bucket(i - j, num_pos)]++;
+        tc[oracle_time_bucket(ts[base + i] - ts[base + j], num_time)]++;
+      }
+    }
+  }
+}
+
 typedef struct {
   int32_t kind;
   const int64_t* ts;      /* [T] timestamps (RAB_PT)                        */
@@ -87,10 +106,17 @@ static double bias_value(const oracle_bias* bs, int h, int64_t base, int64_t i, 
 /* One output row of eq. (2) for user b, head h, local row i:
  *   O[i,:] = out_scale * sum_{j <= i} SiLU(alpha * <q_i, k_j> + rab(i,j)) * v_j
  * q, k, v are [T, H, d] with token row strides (in elements). */
+/* Mirror mode only: w rounded to the nearest bfloat16 (8 significant bits, ties to even). */
+static double round_bf16(double w) {
+  int e;
+  const double m = frexp(w, &e);
+  return ldexp(nearbyint(m * 256.0), e - 8);
+}
+
 static void attn_row(int64_t base, int h, int64_t i, int H, int dqk, int dv,
                      const double* q, int64_t qs, const double* k, int64_t ks,
                      const double* v, int64_t vs, const oracle_bias* bs,
-                     double alpha, double out_scale, double* out /* [dv] */) {
+                     double alpha, double out_scale, double weight_unit, double* out /* [dv] */) {
   for (int c = 0; c < dv; c++) out[c] = 0.0;
   const double* qi = q + (base + i) * qs + (int64_t)h * dqk;
   for (int64_t j = 0; j <= i; j++) {
@@ -99,19 +125,23 @@ static void attn_row(int64_t base, int h, int64_t i, int H, int dqk, int dv,
     double s = 0.0;
     for (int c = 0; c < dqk; c++) s += qi[c] * kj[c];
     double a = silu(alpha * s + bias_value(bs, h, base, i, j));
+    /* mirror mode: the weight kept as a bf16 multiple of weight_unit */
+    if (weight_unit != 0.0) a = weight_unit * round_bf16(a / weight_unit);
     for (int c = 0; c < dv; c++) out[c] += a * vj[c];
   }
   for (int c = 0; c < dv; c++) out[c] *= out_scale;
   (void)H;
 }
 
-/* Full jagged attention: o is [T, H, dv] contiguous. */
-void oracle_attention(int32_t B, int32_t H, int32_t dqk, int32_t dv, const int64_t* offsets,
-                      const double* q, int64_t q_stride, const double* k, int64_t k_stride,
-                      const double* v, int64_t v_stride, int32_t bias_kind, const int64_t* ts,
-                      const double* w_pos, int32_t num_pos, int64_t head_stride_pos,
-                      const double* w_time, int32_t num_time, int64_t head_stride_time,
-                      const double* slopes, double alpha, double out_scale, double* o) {
+/* Full jagged attention: o is [T, H, dv] contiguous.  weight_unit != 0 is the mirror mode
+ * (each SiLU weight kept as weight_unit times a bf16 value); 0 is the exact definition. */
+void oracle_attention_mirror(int32_t B, int32_t H, int32_t dqk, int32_t dv,
+                             const int64_t* offsets, const double* q, int64_t q_stride,
+                             const double* k, int64_t k_stride, const double* v, int64_t v_stride,
+                             int32_t bias_kind, const int64_t* ts, const double* w_pos,
+                             int32_t num_pos, int64_t head_stride_pos, const double* w_time,
+                             int32_t num_time, int64_t head_stride_time, const double* slopes,
+                             double alpha, double out_scale, double weight_unit, double* o) {
   oracle_bias bs = {bias_kind, ts, w_pos, w_time, num_pos, num_time,
                     head_stride_pos, head_stride_time, slopes};
   int64_t n_items = (int64_t)B * H;
@@ -121,8 +151,19 @@ void oracle_attention(int32_t B, int32_t H, int32_t dqk, int32_t dv, const int64
     int64_t base = offsets[b], n = offsets[b + 1] - offsets[b];
     for (int64_t i = 0; i < n; i++)
       attn_row(base, h, i, H, dqk, dv, q, q_stride, k, k_stride, v, v_stride, &bs, alpha,
-               out_scale, o + ((base + i) * H + h) * (int64_t)dv);
+               out_scale, weight_unit, o + ((base + i) * H + h) * (int64_t)dv);
   }
+}
+
+void oracle_attention(int32_t B, int32_t H, int32_t dqk, int32_t dv, const int64_t* offsets,
+                      const double* q, int64_t q_stride, const double* k, int64_t k_stride,
+                      const double* v, int64_t v_stride, int32_t bias_kind, const int64_t* ts,
+                      const double* w_pos, int32_t num_pos, int64_t head_stride_pos,
+                      const double* w_time, int32_t num_time, int64_t head_stride_time,
+                      const double* slopes, double alpha, double out_scale, double* o) {
+  oracle_attention_mirror(B, H, dqk, dv, offsets, q, q_stride, k, k_stride, v, v_stride,
+                          bias_kind, ts, w_pos, num_pos, head_stride_pos, w_time, num_time,
+                          head_stride_time, slopes, alpha, out_scale, 0.0, o);
 }
 
 /* Selected rows only: rows[r] = (token t, head h); out is [R, dv].
@@ -143,7 +184,7 @@ void oracle_attention_rows(int32_t B, int32_t H, int32_t dqk, int32_t dv, const 
     while (b < B && offsets[b + 1] <= t) b++; /* user that owns token t */
     int64_t base = offsets[b];
     attn_row(base, row_head[r], t - base, H, dqk, dv, q, q_stride, k, k_stride, v, v_stride,
-             &bs, alpha, out_scale, out + r * (int64_t)dv);
+             &bs, alpha, out_scale, 0.0, out + r * (int64_t)dv);
   }
 }
 

@@ -121,3 +121,42 @@ def test_layer_grads_finite_differences():
             arr[idx] = a0
             fd = (lp - lm) / (2 * eps_fd)
             assert abs(fd - got[name][idx]) <= 1e-6 * (1 + abs(fd)), (name, idx, fd, got[name][idx])
+
+
+def test_round_bf16_against_torch_and_ties():
+    """The mirror mode's bf16 rounding: ties go to the even neighbour (1 + 2^-8 lies halfway
+    between 1 and 1 + 2^-7; 1 + 3 2^-8 halfway between 1 + 2^-7 and 1 + 2^-6), and on float32
+    inputs it agrees with torch's own float32 -> bfloat16 conversion."""
+    got = oracle.round_bf16(np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20,
+                                      -(1 + 2.0 ** -8), 0.0]))
+    assert list(got) == [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -1.0, 0.0]
+    rng = np.random.default_rng(70)
+    r = (rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000)).astype(np.float32)
+    ref = torch.from_numpy(r).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(oracle.round_bf16(r.astype(np.float64)), ref)
+
+
+def test_mirror_mode_rounds_only_where_named():
+    """Nothing rounded gives the exact gradients; rounding only G changes only dW2 = dY^T G
+    (G feeds nothing else); rounding Y in the forward is the exact Y rounded once."""
+    D, H, dqk, dv = 6, 2, 3, 4
+    lengths = [5, 7]
+    rng = np.random.default_rng(71)
+    offs = synth.offsets_from_lengths(lengths).astype(np.int64)
+    T = int(offs[-1])
+    x = rng.standard_normal((T, D))
+    ts = np.concatenate([100 + np.cumsum(rng.integers(0, 20, size=n)) for n in lengths])
+    p = _params(72, D, H, dqk, dv)
+    dY = rng.standard_normal((T, D))
+    bias = oracle.Bias(oracle.BIAS_RAB_PT, ts, p["w_pos"], p["w_time"])
+    args = (offs, x, p["w1"], p["b1"], p["gamma"], p["beta"], p["w2"], p["b2"], bias, 0.6, H, dqk,
+            dv)
+    exact = oracle.layer_bwd(*args, dY, residual=True)
+    g = oracle.layer_bwd(*args, dY, residual=True, round_at=("G",))
+    for name in ("dx", "dw1", "db1", "dgamma", "dbeta", "db2", "dw_pos", "dw_time"):
+        np.testing.assert_allclose(g[name], exact[name], rtol=1e-12, atol=1e-12, err_msg=name)
+    assert np.max(np.abs(g["dw2"] - exact["dw2"])) > 0
+    y = oracle.layer(*args, residual=True)
+    ym, _, _ = oracle.layer_mirror(*args, residual=True, round_at=("Y",))
+    np.testing.assert_array_equal(ym, oracle.round_bf16(oracle.layer_mirror(*args, residual=True)[0]))
+    np.testing.assert_allclose(oracle.layer_mirror(*args, residual=True)[0], y, rtol=1e-12, atol=1e-12)

@@ -358,7 +358,7 @@ def test_rows_entry_matches_full():
 # dense brute force on tiny inputs (materialises the n x n score, bias and mask)
 
 
-def _dense(offs, q, k, v, ts, kind, wp, wt, slopes, alpha, out_scale=1.0):
+def _dense(offs, q, k, v, ts, kind, wp, wt, slopes, alpha, out_scale=1.0, weight_unit=0.0):
     T, H, _ = q.shape
     out = np.zeros((T, H, v.shape[2]))
     for b in range(len(offs) - 1):
@@ -382,6 +382,8 @@ def _dense(offs, q, k, v, ts, kind, wp, wt, slopes, alpha, out_scale=1.0):
                 Bm = 0.0
             S = alpha * (q[s:e, h] @ k[s:e, h].T) + Bm
             A = np.where(mask, _silu_t(S), 0.0)
+            if weight_unit:
+                A = weight_unit * torch.from_numpy(A / weight_unit).to(torch.bfloat16).double().numpy()
             out[s:e, h] = out_scale * (A @ v[s:e, h])
     return out
 
@@ -394,6 +396,24 @@ def test_dense_brute_force(kind, seed):
     o = oracle.attention(offs, q, k, v, bias, 0.7, out_scale=0.5)
     ref = _dense(offs, q, k, v, ts, kind, bias.w_pos, bias.w_time, bias.slopes, 0.7, 0.5)
     np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_mirror_weights_against_dense():
+    """The oracle's mirror mode (SiLU weights kept as bf16 multiples of a unit) against the
+    dense brute force with the weights rounded by torch's own bfloat16 conversion, and a unit of
+    0 is the exact result."""
+    lengths = [0, 1, 2, 37, 5]
+    offs, q, k, v, ts, bias = _rand_case(22, lengths, H=2, d=6, dv=3, kind=oracle.BIAS_RAB_PT,
+                                         P=8, NT=12)
+    unit = 0.5 * math.log(2.0)
+    o = oracle.attention(offs, q, k, v, bias, 0.7, weight_unit=unit)
+    ref = _dense(offs, q, k, v, ts, oracle.BIAS_RAB_PT, bias.w_pos, bias.w_time, None, 0.7,
+                 weight_unit=unit)
+    exact = oracle.attention(offs, q, k, v, bias, 0.7)
+    assert np.max(np.abs(o - exact)) > 0
+    np.testing.assert_allclose(o, ref, rtol=1e-6, atol=1e-6 * np.abs(exact).max())
+    np.testing.assert_array_equal(oracle.attention(offs, q, k, v, bias, 0.7, weight_unit=0.0),
+                                  exact)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -481,12 +501,13 @@ def test_layer_split_order_u_v_q_k():
         assert not np.allclose(_oracle_layer(inp, L2), y)
 
 
-def test_toy_semantics_single_user():
-    # The toy HSTULayer ("4.4 推荐模型的 Scaling", "代码"): chunk(4) -> u, v, q, k; per-head
-    # view; scores + dense rab; SiLU; lower-triangular mask; divide by n; LayerNorm; gate;
-    # f2; residual.  Without its input LayerNorm and with a position-only bias it equals the
-    # oracle layer with alpha = 1, out_scale = 1/n and residual, which we check through the
-    # attention entry (out_scale) and the layer's pieces.
+def test_length_normalised_variant_single_user():
+    """The length-normalised variant of the layer: "4.4 推荐模型的 Scaling" (remarks on the HSTU
+    layer) divides each pointwise weight by the sequence length, eqs. (1)-(3) of "Actions Speak
+    Louder than Words" §3.1 otherwise.  Written here as explicit sums over the causal pairs
+    (position-only bias indexed by i - j, residual), it must equal the oracle's attention with
+    alpha = 1 and out_scale = 1/n, and the oracle layer (which has no division) up to the
+    LayerNorm's eps: LN(c o; eps) = LN(o; eps / c^2)."""
     rng = np.random.default_rng(33)
     n, d, h = 12, 8, 2
     dh = d // h
@@ -495,37 +516,43 @@ def test_toy_semantics_single_user():
     b1 = rng.standard_normal(4 * d) * 0.1
     w2 = rng.standard_normal((d, d)) * 0.3
     b2 = rng.standard_normal(d) * 0.1
-    wp = rng.standard_normal(n) * 0.5  # position-only rab, indexed by i - j
-    X = torch.as_tensor(x)
-    u, v, q, k = F.silu(F.linear(X, torch.as_tensor(w1), torch.as_tensor(b1))).chunk(4, dim=-1)
-    sp = lambda t: t.view(n, h, dh).transpose(0, 1)
-    qh, kh, vh = sp(q), sp(k), sp(v)
-    idx = torch.arange(n)
-    rab = torch.as_tensor(wp)[(idx[:, None] - idx[None, :]).clamp(min=0)]
-    scores = qh @ kh.transpose(-1, -2) + rab
-    a = F.silu(scores).masked_fill(~torch.tril(torch.ones(n, n, dtype=torch.bool)), 0.0) / n
-    av = (a @ vh).transpose(0, 1).reshape(n, d)
-    ref = X + F.linear(F.layer_norm(av, (d,)) * u, torch.as_tensor(w2), torch.as_tensor(b2))
-    # oracle: attention on the same q, k, v (as [T, H, dh]) with alpha 1 and out_scale 1/n
+    wp = rng.standard_normal(n) * 0.5
+    # eq. (1): four blocks of d columns of SiLU(x W1^T + b1): gate, values, queries, keys
+    z = x @ w1.T + b1
+    z = z / (1.0 + np.exp(-z))
+    U, V, Q, K = z[:, :d], z[:, d:2 * d], z[:, 2 * d:3 * d], z[:, 3 * d:]
+    # eq. (2), one head (a block of dh columns) and one row at a time, each weight divided by n
+    O = np.zeros((n, d))
+    for hh in range(h):
+        c = slice(hh * dh, (hh + 1) * dh)
+        for i in range(n):
+            for j in range(i + 1):
+                sc = float(Q[i, c] @ K[j, c]) + wp[i - j]
+                O[i, c] += sc / (1.0 + math.exp(-sc)) / n * V[j, c]
+
+    # eq. (3): LayerNorm over the d features (biased variance), gate, f2, residual
+    def out(o_rows, eps):
+        y = np.zeros((n, d))
+        for i in range(n):
+            r = o_rows[i]
+            mu = r.mean()
+            g = (r - mu) / math.sqrt(((r - mu) ** 2).mean() + eps) * U[i]
+            y[i] = x[i] + w2 @ g + b2
+        return y
+
     offs = np.array([0, n])
-    qo = q.numpy().reshape(n, h, dh)
-    ko = k.numpy().reshape(n, h, dh)
-    vo = v.numpy().reshape(n, h, dh)
-    ts = np.zeros(n, np.int64)  # all deltas 0 -> time bucket 0; w_t = 0
-    bias = oracle.Bias(oracle.BIAS_RAB_PT, ts, wp, np.zeros(1))
-    o = oracle.attention(offs, qo, ko, vo, bias, alpha=1.0, out_scale=1.0 / n)
-    np.testing.assert_allclose(o.reshape(n, d), av.numpy(), rtol=1e-12, atol=1e-13)
-    # the layer (no division by n) equals the toy up to LayerNorm's eps, since
-    # LN(c o; eps) = LN(o; eps / c^2): check with eps -> 0 and with eps scaled by n^2
+    sh = lambda a: a.reshape(n, h, dh)
+    bias = oracle.Bias(oracle.BIAS_RAB_PT, np.zeros(n, np.int64), wp, np.zeros(1))
+    o = oracle.attention(offs, sh(Q), sh(K), sh(V), bias, alpha=1.0, out_scale=1.0 / n)
+    np.testing.assert_allclose(o.reshape(n, d), O, rtol=1e-12, atol=1e-13)
+    # no division, eps -> 0: the oracle layer equals the normalised form
     y = oracle.layer(offs, x, w1, b1, np.ones(d), np.zeros(d), w2, b2, bias, 1.0, h, dh, dh,
                      residual=True, ln_eps=1e-30)
-    ref_nodiv = X + F.linear(F.layer_norm(av * n, (d,), eps=1e-30) * u, torch.as_tensor(w2),
-                             torch.as_tensor(b2))
-    np.testing.assert_allclose(y, ref_nodiv.numpy(), rtol=1e-10, atol=1e-10)
-    # the toy's own output differs from this only through eps / n^2 in the LayerNorm
-    y_toy_eps = oracle.layer(offs, x, w1, b1, np.ones(d), np.zeros(d), w2, b2, bias, 1.0, h, dh,
-                             dh, residual=True, ln_eps=1e-5 * n * n)
-    np.testing.assert_allclose(y_toy_eps, ref.numpy(), rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(y, out(O, 1e-30), rtol=1e-10, atol=1e-10)
+    # and with eps scaled by n^2 it equals the normalised form with eps
+    y_eps = oracle.layer(offs, x, w1, b1, np.ones(d), np.zeros(d), w2, b2, bias, 1.0, h, dh, dh,
+                         residual=True, ln_eps=1e-5 * n * n)
+    np.testing.assert_allclose(y_eps, out(O, 1e-5), rtol=1e-10, atol=1e-10)
 
 
 def test_stack_is_composition_of_residual_layers():
@@ -552,3 +579,25 @@ def test_embed_sum():
     x = oracle.embed_sum(it, ac, ids, acts)
     for t in range(20):
         np.testing.assert_array_equal(x[t], it[ids[t]] + ac[acts[t]])
+
+
+def test_bucket_counts_brute_force():
+    """The per-row bucket histograms equal a count over the pairs with the scalar bucket
+    functions (pinned by the golden bucket table), on ragged users with unsorted, equal and
+    far-apart timestamps."""
+    lengths = [0, 1, 7, 40]
+    offs = synth.offsets_from_lengths(lengths).astype(np.int64)
+    rng = np.random.default_rng(80)
+    ts = np.concatenate([np.zeros(0, np.int64), np.array([5], np.int64),
+                         np.array([3, 3, 2, 10, 1 << 33, (1 << 33) + 1, 0], np.int64),
+                         np.cumsum(rng.integers(0, 1 << 12, size=40)).astype(np.int64)])
+    P, NT = 6, 9
+    pc, tc = oracle.bucket_counts(offs, ts, P, NT)
+    for b in range(len(lengths)):
+        s = int(offs[b])
+        for i in range(lengths[b]):
+            ep, et = np.zeros(P, np.int64), np.zeros(NT, np.int64)
+            for j in range(i + 1):
+                ep[oracle.pos_bucket(i - j, P)] += 1
+                et[oracle.time_bucket(int(ts[s + i] - ts[s + j]), NT)] += 1
+            assert np.array_equal(pc[s + i], ep) and np.array_equal(tc[s + i], et), (b, i)
