@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhstu.so")
 
-DTYPE_F32, DTYPE_BF16 = 0, 1
+DTYPE_F32, DTYPE_BF16, DTYPE_BF16_OUT_F32 = 0, 1, 2
 BIAS_NONE, BIAS_RAB_PT, BIAS_ALIBI = 0, 1, 2
 
 _P = ctypes.c_void_p
@@ -53,7 +53,8 @@ SIGNATURES = {
                               _P, _f32, _P, _P, ctypes.POINTER(HstuBias), _f32, _i32, _P, _P, _sz,
                               _P]),
     "hstu_layer_workspace_offsets": (None, [_i64, _i32, _i32, _i32, ctypes.POINTER(_sz),
-                                            ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+                                            ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                            ctypes.POINTER(_sz)]),
     "hstu_attn_candidates_fwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i32,
                                         _i64, _P, _i64, _P, _i64, _P, _i64, _P, _i64, _P, _i64,
                                         ctypes.POINTER(HstuBias), _P, _f32, _f32, _P, _P, _sz,
@@ -168,12 +169,17 @@ def _rows(t: torch.Tensor, name: str):
 
 
 def hstu_attn_fwd(q, k, v, offsets, max_seqlen, bias: Optional[HstuBias] = None, alpha=1.0,
-                  out_scale=1.0, out=None, workspace=None):
+                  out_scale=1.0, out=None, workspace=None, out_f32=False):
     """Jagged causal pointwise attention.  q, k, v: [T, H, d] device tensors (bf16 or fp32,
-    row-strided views allowed); offsets: int32 [B+1] on the device.  Returns o [T, H, d]."""
+    row-strided views allowed); offsets: int32 [B+1] on the device.  Returns o [T, H, d]
+    (fp32 when out_f32 is set for bf16 inputs)."""
     if not q.is_cuda:
         raise HstuError("inputs must be device tensors")
     dt = _dtype_code(q)
+    if out_f32:
+        if dt != DTYPE_BF16:
+            raise HstuError("out_f32 needs bf16 inputs")
+        dt = DTYPE_BF16_OUT_F32
     qs, H, d = _rows(q, "q")
     ks, _, _ = _rows(k, "k")
     vs, _, dv = _rows(v, "v")
@@ -182,7 +188,8 @@ def hstu_attn_fwd(q, k, v, offsets, max_seqlen, bias: Optional[HstuBias] = None,
     if offsets.dtype != torch.int32:
         raise HstuError("offsets must be int32")
     if out is None:
-        out = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+        out = torch.empty((T, H, dv), dtype=torch.float32 if out_f32 else q.dtype,
+                          device=q.device)
     need = attn_workspace_bytes(B, H, max_seqlen, T)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -250,10 +257,12 @@ def layer_workspace_bytes(B, T, D, H, dqk, dv, max_seqlen):
 
 
 def layer_workspace_offsets(T, H, dqk, dv):
-    z, o, a = _sz(), _sz(), _sz()
+    """Byte offsets of Z, O, the O statistics and the attention workspace in the layer
+    workspace."""
+    z, o, st, a = _sz(), _sz(), _sz(), _sz()
     lib().hstu_layer_workspace_offsets(T, H, dqk, dv, ctypes.byref(z), ctypes.byref(o),
-                                       ctypes.byref(a))
-    return z.value, o.value, a.value
+                                       ctypes.byref(st), ctypes.byref(a))
+    return z.value, o.value, st.value, a.value
 
 
 def hstu_layer_fwd(x, offsets, max_seqlen, w1, b1, ln_gamma, ln_beta, w2, b2, H, dqk, dv,

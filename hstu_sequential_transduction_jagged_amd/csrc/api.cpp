@@ -122,7 +122,14 @@ size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64
          align256(knorm_bytes(B, H, total_tokens));
 }
 
+// bf16 inputs with an fp32 output run the bf16 kernels; *o_f32 says which output
+static int32_t input_dtype(int32_t dt, bool* o_f32) {
+  if (o_f32) *o_f32 = dt == HSTU_DTYPE_BF16_OUT_F32;
+  return dt == HSTU_DTYPE_BF16_OUT_F32 ? (int32_t)HSTU_DTYPE_BF16 : dt;
+}
+
 int32_t hstu_attn_block_rows(int32_t dt, int32_t d) {
+  dt = input_dtype(dt, nullptr);
   if (dt == HSTU_DTYPE_BF16) return attn_block_rows_bf16(d);
   if (dt == HSTU_DTYPE_F32) return attn_block_rows_f32(d);
   return 0;
@@ -158,6 +165,7 @@ hstu_status hstu_attn_plan(int32_t dt, int32_t B, int32_t H, int32_t d, const in
                            int32_t max_seqlen, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
   g_last_error[0] = 0;
+  dt = input_dtype(dt, nullptr);
   int block_rows = 0;
   hstu_status st = attn_check(dt, B, H, d, d, max_seqlen, 0, &block_rows);
   if (st != HSTU_OK) return st;
@@ -195,7 +203,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
                                 const void* q, int64_t q_row_stride, const void* k,
                                 int64_t k_row_stride, const void* v, int64_t v_row_stride,
                                 const hstu_bias* bias, float alpha, float out_scale, void* o,
-                                bool o_f32, f32x2* ostats, void* workspace,
+                                bool o_f32, f32x4* ostats, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream,
                                 AttnPart part = kPrepareAndRun) {
   int block_rows = 0;
@@ -215,6 +223,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
     return fail(HSTU_ERR_INVALID_ARG, "q/k/v/o rows must be 16-byte aligned");
   st = workspace_check(workspace, workspace_bytes, B, H, max_seqlen, total_tokens);
   if (st != HSTU_OK) return st;
+  if (o_f32 && dt != HSTU_DTYPE_BF16) return fail(HSTU_ERR_INVALID_ARG, "fp32 output needs bf16 inputs");
   // the bf16 kernel addresses one user's K and V rows with 32-bit byte offsets
   const int64_t max_stride = k_row_stride > v_row_stride ? k_row_stride : v_row_stride;
   if (dt == HSTU_DTYPE_BF16 && (int64_t)max_seqlen * max_stride * 2 >= ((int64_t)1 << 31))
@@ -250,6 +259,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   a.offsets = offsets;
   a.work_count = (const int32_t*)workspace;
   a.work = (const WorkItem*)((const char*)workspace + kHeader);
+  a.queue = (int32_t*)workspace + 4;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -266,7 +276,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   a.knorm = knorm;
   const int64_t grid = (int64_t)B * H * max_tiles;
   if (grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
-  hipError_t e = dt == HSTU_DTYPE_BF16 ? launch_attn_bf16(d_qk, a, (int)grid, stream)
+  hipError_t e = dt == HSTU_DTYPE_BF16 ? launch_attn_bf16(d_qk, a, grid, stream)
                                        : launch_attn_f32(d_qk, a, (int)grid, stream);
   return check_hip(e, "attention launch");
 }
@@ -279,9 +289,11 @@ hstu_status hstu_attn_fwd_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk
                                   float out_scale, void* o, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
+  bool of32 = false;
+  dt = input_dtype(dt, &of32);
   return attn_planned(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q, q_row_stride, k,
-                      k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, false, nullptr, workspace,
-                      workspace_bytes, stream);
+                      k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, of32, nullptr,
+                      workspace, workspace_bytes, stream);
 }
 
 hstu_status hstu_attn_prepare(int32_t dt, int32_t B, int32_t H, int32_t d,
@@ -289,6 +301,7 @@ hstu_status hstu_attn_prepare(int32_t dt, int32_t B, int32_t H, int32_t d,
                               const void* k, int64_t k_row_stride, const hstu_bias* bias,
                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
+  dt = input_dtype(dt, nullptr);
   // q, v and o are not read: K stands in for them so that the shared checks pass
   return attn_planned(dt, B, H, d, d, offsets, max_seqlen, total_tokens, k, k_row_stride, k,
                       k_row_stride, k, k_row_stride, bias, 1.0f, 1.0f, (void*)k, false, nullptr,
@@ -303,8 +316,10 @@ hstu_status hstu_attn_fwd_prepared(int32_t dt, int32_t B, int32_t H, int32_t d_q
                                    float out_scale, void* o, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
+  bool of32 = false;
+  dt = input_dtype(dt, &of32);
   return attn_planned(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q, q_row_stride, k,
-                      k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, false, nullptr,
+                      k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, of32, nullptr,
                       workspace, workspace_bytes, stream, kRunOnly);
 }
 
@@ -315,6 +330,8 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
                           const hstu_bias* bias, float alpha, float out_scale, void* o,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
+  const int32_t dt_call = dt;
+  dt = input_dtype(dt, nullptr);
   int block_rows = 0;
   hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
   if (st != HSTU_OK) return st;
@@ -336,7 +353,7 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   if (st != HSTU_OK) return st;
   st = hstu_attn_plan(dt, B, H, d_qk, offsets, max_seqlen, workspace, workspace_bytes, stream);
   if (st != HSTU_OK) return st;
-  return hstu_attn_fwd_planned(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q,
+  return hstu_attn_fwd_planned(dt_call, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q,
                                q_row_stride, k, k_row_stride, v, v_row_stride, bias, alpha,
                                out_scale, o, workspace, workspace_bytes, stream);
 }
@@ -403,23 +420,26 @@ hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   return check_hip(launch_attn_bwd_bf16(a, (int)grid, n_pos, n_time, stream), "backward launch");
 }
 
+// layer workspace: Z | O | per (token, head) O statistics (4 fp32) | attention workspace
 void hstu_layer_workspace_offsets(int64_t total_tokens, int32_t H, int32_t d_qk, int32_t d_v,
-                                  size_t* z_offset, size_t* o_offset, size_t* attn_offset) {
+                                  size_t* z_offset, size_t* o_offset, size_t* stats_offset,
+                                  size_t* attn_offset) {
   const int64_t N1 = 2LL * H * (d_qk + d_v);
   const size_t z_bytes = align256((size_t)(total_tokens * N1 * 2));
   const size_t o_bytes = align256((size_t)(total_tokens * H * d_v * 2));
+  const size_t s_bytes = align256((size_t)(total_tokens * H * 16));
   if (z_offset) *z_offset = 0;
   if (o_offset) *o_offset = z_bytes;
-  if (attn_offset) *attn_offset = z_bytes + o_bytes;
+  if (stats_offset) *stats_offset = z_bytes + o_bytes;
+  if (attn_offset) *attn_offset = z_bytes + o_bytes + s_bytes;
 }
 
 size_t hstu_layer_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_model, int32_t H,
                                   int32_t d_qk, int32_t d_v, int32_t max_seqlen) {
   if (B < 0 || total_tokens < 0 || d_model < 1 || H < 1 || d_qk < 1 || d_v < 1) return 0;
   size_t attn_off = 0;
-  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, nullptr, nullptr, &attn_off);
-  return attn_off + align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens)) +
-         align256((size_t)total_tokens * H * 8);
+  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, nullptr, nullptr, nullptr, &attn_off);
+  return attn_off + align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens));
 }
 
 hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,
@@ -453,13 +473,13 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
     return fail(HSTU_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
                 workspace_bytes);
-  size_t zo, oo, ao;
-  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, &zo, &oo, &ao);
+  size_t zo, oo, so, ao;
+  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, &zo, &oo, &so, &ao);
   bf16* z = (bf16*)((char*)workspace + zo);
   bf16* obuf = (bf16*)((char*)workspace + oo);
+  f32x4* ostats = (f32x4*)((char*)workspace + so);  // per (token, head) offset, mean, M2 of O
   void* aws = (char*)workspace + ao;
   const size_t aws_bytes = align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens));
-  f32x2* ostats = (f32x2*)((char*)aws + aws_bytes);  // per (token, head) mean and M2 of O
 
   st = check_hip(launch_f1_gemm_silu((const bf16*)x, (const bf16*)w1, b1, z, total_tokens, N1,
                                      d_model, stream),
@@ -548,7 +568,7 @@ size_t hstu_layer_bwd_workspace_bytes(int32_t B, int64_t total_tokens, int32_t H
                                       int32_t d_v, int32_t max_seqlen) {
   if (B < 0 || total_tokens < 0 || H < 1 || d_qk < 1 || d_v < 1) return 0;
   const int64_t N1 = 2LL * H * (d_qk + d_v), HV = (int64_t)H * d_v;
-  return 3 * align256((size_t)(total_tokens * HV * 2)) + align256((size_t)(total_tokens * N1 * 2)) +
+  return 4 * align256((size_t)(total_tokens * HV * 2)) + align256((size_t)(total_tokens * N1 * 2)) +
          align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens));
 }
 
@@ -604,26 +624,28 @@ hstu_status hstu_layer_bwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
                 workspace_bytes);
   if ((int64_t)(max_seqlen + 64) * N1 * 2 >= ((int64_t)1 << 31))
     return fail(HSTU_ERR_UNSUPPORTED, "max_seqlen x row stride reaches 2 GiB per user");
-  size_t z_off = 0, o_off = 0;
-  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, &z_off, &o_off, nullptr);
+  size_t z_off = 0, o_off = 0, s_off = 0;
+  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, &z_off, &o_off, &s_off, nullptr);
   const bf16* Z = (const bf16*)((const char*)fwd_workspace + z_off);
   const bf16* O = (const bf16*)((const char*)fwd_workspace + o_off);
+  const f32x4* ostats = (const f32x4*)((const char*)fwd_workspace + s_off);
   char* ws = (char*)workspace;
   const size_t hvb = align256((size_t)(total_tokens * HV * 2));
   bf16* dG = (bf16*)ws;
   bf16* G = (bf16*)(ws + hvb);
   bf16* dO = (bf16*)(ws + 2 * hvb);
-  bf16* dZ = (bf16*)(ws + 3 * hvb);
-  void* attn_ws = ws + 3 * hvb + align256((size_t)(total_tokens * N1 * 2));
+  bf16* dO_lo = (bf16*)(ws + 3 * hvb);
+  bf16* dZ = (bf16*)(ws + 4 * hvb);
+  void* attn_ws = ws + 4 * hvb + align256((size_t)(total_tokens * N1 * 2));
   const size_t attn_bytes = hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens);
 
   LayerBwdLaunch L{};
   L.T = total_tokens; L.D = d_model; L.HV = (int32_t)HV; L.N1 = (int32_t)N1;
   L.residual = residual ? 1 : 0; L.eps = ln_eps;
   L.x = (const bf16*)x; L.w1 = (const bf16*)w1; L.w2 = (const bf16*)w2; L.dy = (const bf16*)dy;
-  L.o = O; L.u = Z; L.u_stride = N1;
+  L.o = O; L.ostats = ostats; L.dvh = d_v; L.u = Z; L.u_stride = N1;
   L.b1 = b1; L.gamma = ln_gamma; L.beta = ln_beta;
-  L.dg = dG; L.g = G; L.dO = dO; L.dz = dZ; L.dx = (bf16*)dx; L.dz_stride = N1;
+  L.dg = dG; L.g = G; L.dO = dO; L.dO_lo = dO_lo; L.dz = dZ; L.dx = (bf16*)dx; L.dz_stride = N1;
   L.dgamma = dgamma; L.dbeta = dbeta; L.dw1 = dw1; L.db1 = db1; L.dw2 = dw2; L.db2 = db2;
   st = check_hip(launch_layer_bwd_pre(L, stream), "layer backward (LN, f2) launch");
   if (st != HSTU_OK) return st;
@@ -637,7 +659,7 @@ hstu_status hstu_layer_bwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   a.offsets = offsets;
   a.work_count = (const int32_t*)attn_ws;
   a.work = (const WorkItem*)((const char*)attn_ws + kHeader);
-  a.v = Z + HV; a.q = Z + 2 * HV; a.k = Z + 2 * HV + HQ; a.dout = dO;
+  a.v = Z + HV; a.q = Z + 2 * HV; a.k = Z + 2 * HV + HQ; a.dout = dO; a.dout_lo = dO_lo;
   a.q_stride = a.k_stride = a.v_stride = N1;
   a.do_stride = HV;
   a.H = H;

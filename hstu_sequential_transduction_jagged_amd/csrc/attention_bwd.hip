@@ -60,6 +60,7 @@ struct __attribute__((aligned(16))) SmemBwd : BwdTables {
 struct __attribute__((aligned(16))) BStage {
   __attribute__((aligned(16))) bf16 x[kBTile * kBD];
   __attribute__((aligned(16))) bf16 y[kBTile * kBD];
+  __attribute__((aligned(16))) bf16 z[kBTile * kBD];  // dkv kernel: dO's bf16 remainder, if given
   __attribute__((aligned(16))) int64_t t[kBTile];
   __attribute__((aligned(16))) int64_t tmm[32];     // [0..3]: min, max of half 0, then half 1
   __attribute__((aligned(16))) uint32_t dummy[64];  // target of the transfers that carry nothing
@@ -440,6 +441,11 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       (void*)(a.q + tok0 * a.q_stride + (int64_t)h * kBD), (short)0, (int)((uint32_t)(n - 1) * xs + 2u * kBD), 0x00020000);
   const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.dout + tok0 * a.do_stride + (int64_t)h * kBD), (short)0, (int)((uint32_t)(n - 1) * ys + 2u * kBD), 0x00020000);
+  // dO's remainder (same rows and stride as dO), when the caller keeps dO to about 16 bits
+  const bool lo = a.dout_lo != nullptr;
+  const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(lo ? a.dout_lo + tok0 * a.do_stride + (int64_t)h * kBD : nullptr), (short)0,
+      lo ? (int)((uint32_t)(n - 1) * ys + 2u * kBD) : 0, 0x00020000);
   uint32_t xo, yo;
   {
     const int r = 8 * wave + (lane >> 3);
@@ -460,6 +466,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     const uint32_t ysoff = __builtin_amdgcn_readfirstlane(real ? r0 * ys : 0x7fffffffu);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(stg.x + 512 * wave), 16, xo, xsoff, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(yr, (lds_ptr)(stg.y + 512 * wave), 16, yo, ysoff, 0, 0);
+    if (lo) __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (lds_ptr)(stg.z + 512 * wave), 16, yo, ysoff, 0, 0);
     const uint32_t msoff = __builtin_amdgcn_readfirstlane(
         (real && KIND == 1 && wave < 3) ? (wave < 2 ? 8u * r0 : 16u * r0) : 0x7fffffffu);
     void* dst = wave < 2 ? (void*)(stg.t + 32 * wave) : wave == 2 ? (void*)stg.tmm : (void*)stg.dummy;
@@ -500,6 +507,14 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       for (int ks = 0; ks < 4; ++ks) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kop[ks], s, 0, 0, 0);
         dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da_[ks], vop[ks], dd, 0, 0, 0);
+      }
+      if (lo) {
+        // dA from dO's remainder too: dA and the table gradients see dO to about 16 bits
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 dl = *(const bf16x8*)((const char*)stg.z + 32 * hq * 128 + (kbase ^ (32u * ks)));
+          dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dl, vop[ks], dd, 0, 0, 0);
+        }
       }
       // the tile's bias class: one position bucket when i - j >= P - 1 for every pair, one or
       // two time buckets when the extreme times say so (exactly)

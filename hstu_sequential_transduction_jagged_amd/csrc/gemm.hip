@@ -245,7 +245,8 @@ constexpr int kF2Threads = 256;
 
 struct F2Args {
   const bf16* O;        // attention output [M][HV]
-  const f32x2* ostats;  // [M][H]: mean and M2 of each head's d_v values of O
+  const f32x4* ostats;  // [M][H]: offset m, mean and M2 of each head's d_v values of O
+                        // (O holds the bf16 deviations from m)
   const bf16* U;        // gate, row stride u_stride
   int64_t u_stride;
   const float* gamma;   // [HV] or null
@@ -284,18 +285,21 @@ __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
   {
     const int64_t t = m0 + srow;
     const int H = g.H;
-    const f32x2* st = g.ostats + (t < M ? t : 0) * H;
+    const f32x4* st = g.ostats + (t < M ? t : 0) * H;
     float hq = 0.f, sm = 0.f;
     for (int hh = 0; hh < H; ++hh) {
-      const f32x2 v = st[hh];
-      sm += v[0];
-      hq += v[1];
+      const f32x4 v = st[hh];
+      sm += v[1];
+      hq += v[2];
     }
     mean = sm / (float)H;
     float dev = 0.f;
-    for (int hh = 0; hh < H; ++hh) dev += (st[hh][0] - mean) * (st[hh][0] - mean);
+    for (int hh = 0; hh < H; ++hh) dev += (st[hh][1] - mean) * (st[hh][1] - mean);
     rstd = 1.0f / sqrtf((hq + (float)g.dv * dev) / (float)HV + g.eps);
   }
+  // each head's offset m (O stores value - m), read per slice: slice kt lies in head kt kF2K / dv
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.ostats + m0 * g.H), (short)0, (int)(nrow * g.H * 16), 0x00020000);
   // O and U rows through descriptors bounded at the block's last token (zeros past M)
   const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.O + m0 * HV), (short)0, (int)(nrow * kb), 0x00020000);
@@ -320,7 +324,10 @@ __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
         (void*)(g.W + (int64_t)n0 * HV), (short)0, (int)(CH * kb), 0x00020000);
     const int nk = HV / kF2K;
     u32x4 wr[2 * NI], orr, urr;
+    float moff = 0.f;
     auto gload = [&](int kt) {
+      moff = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+          srs, 16u * (uint32_t)(srow * g.H + (kt * kF2K) / g.dv), 0, 0));
       const uint32_t k0 = 2u * (uint32_t)kt * kF2K;
 #pragma unroll
       for (int u = 0; u < 2 * NI; ++u)
@@ -342,11 +349,12 @@ __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
       for (int u = 0; u < 2 * NI; ++u) *(u32x4*)(sw(buf) + lofs + 64 * u * kF2K) = wr[u];
       const bf16x8 o8 = __builtin_bit_cast(bf16x8, orr);
       const bf16x8 u8 = __builtin_bit_cast(bf16x8, urr);
+      const float shift = moff - mean;
       f32x8 y;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float gm = has_gamma ? gr[e >> 2][e & 3] : 1.0f;
-        y[e] = (((float)o8[e] - mean) * rstd * gm + br[e >> 2][e & 3]) * (float)u8[e];
+        y[e] = (((float)o8[e] + shift) * rstd * gm + br[e >> 2][e & 3]) * (float)u8[e];
       }
       *(bf16x8*)(sa(buf) + lofs) = __builtin_convertvector(y, bf16x8);
     };
@@ -530,7 +538,7 @@ hipError_t launch_transpose_bf16(const bf16* src, bf16* dst, int32_t R, int32_t 
   return hipGetLastError();
 }
 
-hipError_t launch_ln_gate_f2(const bf16* o, const f32x2* ostats, const bf16* u,
+hipError_t launch_ln_gate_f2(const bf16* o, const f32x4* ostats, const bf16* u,
                              int64_t u_stride, const float* gamma, const float* beta, float eps,
                              const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,
                              int32_t D, int32_t H, int32_t dv, hipStream_t stream) {

@@ -136,6 +136,9 @@ struct AttnArgs {
   const int32_t* offsets;
   const int32_t* work_count;
   const WorkItem* work;
+  int32_t* queue;         // bf16 path: 8 item-queue counters and a finished-workgroup counter,
+                          // zero between launches (the scheduler zeroes them, the last
+                          // workgroup of each launch resets them)
   const void* q;
   const void* k;
   const void* v;
@@ -150,7 +153,8 @@ struct AttnArgs {
   int32_t tclass_cols;    // entries per query-block row of tclass (= blocks of the longest user)
   int64_t tclass_bytes;
   float alpha, out_scale;
-  f32x2* ostats;          // bf16 path, optional: per (token, head) mean and M2 of the O row
+  f32x4* ostats;          // bf16 path, optional (layer mode): per (token, head) offset m,
+                          // mean and M2 of the O row stored as m + bf16 deviations
   const float* knorm;     // bf16 path: per (32-key block, head) max squared key norm, rows as tclass
 };
 
@@ -197,7 +201,7 @@ hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int64_t total_toke
 hipError_t launch_tile_class(int32_t B, const int32_t* offsets, const TimeStat* stats,
                              int32_t max_blocks, int32_t num_pos, int32_t num_time,
                              uint32_t* tclass, hipStream_t stream);
-hipError_t launch_attn_bf16(int d, const AttnArgs& a, int grid, hipStream_t stream);
+hipError_t launch_attn_bf16(int d, const AttnArgs& a, int64_t max_items, hipStream_t stream);
 hipError_t launch_attn_f32(int d, const AttnArgs& a, int grid, hipStream_t stream);
 int attn_block_rows_bf16(int d);
 int attn_block_rows_f32(int d);
@@ -206,7 +210,7 @@ hipError_t launch_f1_gemm_silu(const bf16* x, const bf16* w1, const float* b1, b
                                int32_t N, int32_t K, hipStream_t stream,
                                bool silu_bwd = false, const bf16* resid = nullptr,
                                bool plain = false);
-hipError_t launch_ln_gate_f2(const bf16* o, const f32x2* ostats, const bf16* u,
+hipError_t launch_ln_gate_f2(const bf16* o, const f32x4* ostats, const bf16* u,
                              int64_t u_stride, const float* gamma, const float* beta, float eps,
                              const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,
                              int32_t D, int32_t H, int32_t dv, hipStream_t stream);
@@ -216,6 +220,7 @@ struct BwdArgs {
   const int32_t* work_count;
   const WorkItem* work;
   const bf16 *q, *k, *v, *dout;
+  const bf16* dout_lo;  // optional: bf16 remainder of dO (rows as dout), added in the dO V^T product
   int64_t q_stride, k_stride, v_stride, do_stride;  // elements between tokens
   int32_t H;
   BiasArgs bias;
@@ -234,9 +239,11 @@ struct LayerBwdLaunch {
   int32_t D, HV, N1, residual;
   float eps;
   const bf16 *x, *w1, *w2, *dy, *o, *u;  // u: Z's U columns, row stride u_stride
+  const f32x4* ostats;                    // the forward's per (token, head) O statistics
+  int32_t dvh;                            // d_v (features per head of O)
   int64_t u_stride;
   const float *b1, *gamma, *beta;
-  bf16 *dg, *g, *dO, *dz, *dx;            // dz: [T][N1] rows with stride dz_stride
+  bf16 *dg, *g, *dO, *dO_lo, *dz, *dx;    // dz: [T][N1] rows with stride dz_stride
   int64_t dz_stride;
   float *dgamma, *dbeta, *dw1, *db1, *dw2, *db2;
 };

@@ -171,9 +171,10 @@ constexpr int kMaxHV = 2048;
 template <int NC>
 __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(
     int64_t T, int32_t HV, float eps, const bf16* __restrict__ dG, const bf16* __restrict__ O,
-    const bf16* __restrict__ U, int64_t u_stride, const float* __restrict__ gamma,
-    const float* __restrict__ beta, bf16* __restrict__ dU, int64_t du_stride, bf16* __restrict__ G,
-    bf16* __restrict__ dO, float* __restrict__ dgamma, float* __restrict__ dbeta) {
+    const f32x4* __restrict__ ostats, int32_t dvh, const bf16* __restrict__ U, int64_t u_stride,
+    const float* __restrict__ gamma, const float* __restrict__ beta, bf16* __restrict__ dU,
+    int64_t du_stride, bf16* __restrict__ G, bf16* __restrict__ dO, bf16* __restrict__ dOlo,
+    float* __restrict__ dgamma, float* __restrict__ dbeta) {
   __shared__ float red_g[kMaxHV], red_b[kMaxHV];
   for (int i = threadIdx.x; i < HV; i += 256) red_g[i] = red_b[i] = 0.f;
   __syncthreads();
@@ -193,20 +194,23 @@ __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(
     }
   }
   const float inv = 1.0f / (float)HV;
+  const int H = HV / dvh;
   for (int64_t t = wave; t < T; t += nwaves) {
     float o[NC][8], dg[NC][8], u[NC][8];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int ch = lane + 64 * c;
       bf16x8 ov = {}, gv = {}, uv = {};
+      float moff = 0.f;  // the head's offset: O stores the deviations from it
       if (ch < nch) {
         ov = *(const bf16x8*)(O + t * HV + 8 * ch);
         gv = *(const bf16x8*)(dG + t * HV + 8 * ch);
         uv = *(const bf16x8*)(U + t * u_stride + 8 * ch);
+        moff = ostats[t * H + (8 * ch) / dvh][0];
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        o[c][e] = (float)ov[e];
+        o[c][e] = (float)ov[e] + moff;
         dg[c][e] = (float)gv[e];
         u[c][e] = (float)uv[e];
       }
@@ -263,10 +267,19 @@ __global__ __launch_bounds__(256) void ln_gate_bwd_kernel(
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int ch = lane + 64 * c;
-      bf16x8 dov;
+      // dO in bf16, and (for the attention's dO V^T product) the bf16 rounding of what that
+      // leaves, so hi + lo carries dO to about 16 bits
+      bf16x8 dov, dol;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dov[e] = (bf16)(rstd * (dxh[c][e] - s1 - xh[c][e] * s2));
-      if (ch < nch) *(bf16x8*)(dO + t * HV + 8 * ch) = dov;
+      for (int e = 0; e < 8; ++e) {
+        const float full = rstd * (dxh[c][e] - s1 - xh[c][e] * s2);
+        dov[e] = (bf16)full;
+        dol[e] = (bf16)(full - (float)dov[e]);
+      }
+      if (ch < nch) {
+        *(bf16x8*)(dO + t * HV + 8 * ch) = dov;
+        if (dOlo) *(bf16x8*)(dOlo + t * HV + 8 * ch) = dol;
+      }
     }
   }
   // the workgroup's four waves into LDS, then one global add per column
@@ -355,11 +368,17 @@ hipError_t launch_layer_bwd_pre(const LayerBwdLaunch& L, hipStream_t stream) {
   const int64_t want = (T + 3) / 4;
   const unsigned blocks = (unsigned)(want < 1 ? 1 : want > 1024 ? 1024 : want);
   if (nc == 1)
-    hipLaunchKernelGGL(ln_gate_bwd_kernel<1>, dim3(blocks), dim3(256), 0, stream, T, HV, L.eps, L.dg, L.o, L.u, L.u_stride, L.gamma, L.beta, L.dz, L.dz_stride, L.g, L.dO, L.dgamma, L.dbeta);
+    hipLaunchKernelGGL(ln_gate_bwd_kernel<1>, dim3(blocks), dim3(256), 0, stream, T, HV, L.eps, L.dg, L.o,
+                       L.ostats, L.dvh, L.u, L.u_stride, L.gamma, L.beta, L.dz, L.dz_stride, L.g, L.dO,
+                       L.dO_lo, L.dgamma, L.dbeta);
   else if (nc == 2)
-    hipLaunchKernelGGL(ln_gate_bwd_kernel<2>, dim3(blocks), dim3(256), 0, stream, T, HV, L.eps, L.dg, L.o, L.u, L.u_stride, L.gamma, L.beta, L.dz, L.dz_stride, L.g, L.dO, L.dgamma, L.dbeta);
+    hipLaunchKernelGGL(ln_gate_bwd_kernel<2>, dim3(blocks), dim3(256), 0, stream, T, HV, L.eps, L.dg, L.o,
+                       L.ostats, L.dvh, L.u, L.u_stride, L.gamma, L.beta, L.dz, L.dz_stride, L.g, L.dO,
+                       L.dO_lo, L.dgamma, L.dbeta);
   else
-    hipLaunchKernelGGL(ln_gate_bwd_kernel<4>, dim3(blocks), dim3(256), 0, stream, T, HV, L.eps, L.dg, L.o, L.u, L.u_stride, L.gamma, L.beta, L.dz, L.dz_stride, L.g, L.dO, L.dgamma, L.dbeta);
+    hipLaunchKernelGGL(ln_gate_bwd_kernel<4>, dim3(blocks), dim3(256), 0, stream, T, HV, L.eps, L.dg, L.o,
+                       L.ostats, L.dvh, L.u, L.u_stride, L.gamma, L.beta, L.dz, L.dz_stride, L.g, L.dO,
+                       L.dO_lo, L.dgamma, L.dbeta);
   return hipGetLastError();
 }
 

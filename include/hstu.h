@@ -56,7 +56,9 @@ typedef enum {
   HSTU_ERR_HIP = -4
 } hstu_status;
 
-typedef enum { HSTU_DTYPE_F32 = 0, HSTU_DTYPE_BF16 = 1 } hstu_dtype;
+/* HSTU_DTYPE_BF16_OUT_F32: bf16 q, k, v with the attention output written in fp32 (before its
+ * bf16 rounding); accepted by the attention entry points, which otherwise treat it as BF16. */
+typedef enum { HSTU_DTYPE_F32 = 0, HSTU_DTYPE_BF16 = 1, HSTU_DTYPE_BF16_OUT_F32 = 2 } hstu_dtype;
 
 typedef enum { HSTU_BIAS_NONE = 0, HSTU_BIAS_RAB_PT = 1, HSTU_BIAS_ALIBI = 2 } hstu_bias_kind;
 
@@ -86,14 +88,15 @@ typedef struct {
 size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64_t total_tokens);
 
 /* Jagged causal pointwise attention, eq. (2) above.
- *  dt          HSTU_DTYPE_BF16 (bf16 in/out, fp32 accumulation) or HSTU_DTYPE_F32.
+ *  dt          HSTU_DTYPE_BF16 (bf16 in/out, fp32 accumulation), HSTU_DTYPE_BF16_OUT_F32
+ *              (bf16 in, fp32 out) or HSTU_DTYPE_F32.
  *  B, H        users and heads; d_qk == d_v in {32, 64} for F32, 64 for BF16.
  *  offsets     device int32 [B+1]; max_seqlen >= every user length, <= 65536.
  *  q, k, v     device [T, H, d] rows with row strides q_row_stride etc.
  *              (elements between consecutive tokens; >= H*d).
  *  bias        host pointer to the bias description (may be NULL = NONE).
  *  alpha       multiplies Q K^T inside the SiLU; out_scale multiplies the sum.
- *  o           device [T, H, d_v] contiguous output.
+ *  o           device [T, H, d_v] contiguous output (fp32 for BF16_OUT_F32).
  *  workspace   device, >= hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens),
  *              256-B aligned.
  * Layout of the workspace after the call: int32 item_count at byte 0, then
@@ -186,10 +189,11 @@ hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
  *  residual nonzero: y = x + f2(...)
  *  y        device bf16 [T, d_model]; may not alias x.
  *  The workspace holds Z = SiLU(x W1^T + b1) as bf16 [T, 2H(d_qk+d_v)] (column blocks
- *  U | V | Q | K) at byte 0, then the attention output O as bf16 [T, H d_v], then the
- *  attention workspace; offsets of each are returned by hstu_layer_workspace_offsets().
- *  The last T H fp32 pairs (256-byte aligned) hold each (token, head)'s mean of O and sum of
- *  squared deviations from it, from which the LayerNorm statistics are combined. */
+ *  U | V | Q | K) at byte 0, then the attention output O as bf16 [T, H d_v] stored relative to
+ *  a per (token, head) offset m (O[t, h, :] = m + stored value), then per (token, head) four
+ *  fp32 values {m, mean of the head's d_v values of O, their sum of squared deviations, 0}
+ *  (the LayerNorm statistics are combined from these), then the attention workspace; offsets
+ *  of each are returned by hstu_layer_workspace_offsets(). */
 hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, int32_t d_qk,
                            int32_t d_v, const int32_t* offsets, int32_t max_seqlen,
                            int64_t total_tokens, const void* x, const void* w1, const float* b1,
@@ -222,9 +226,11 @@ hstu_status hstu_layer_bwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
 size_t hstu_layer_bwd_workspace_bytes(int32_t B, int64_t total_tokens, int32_t H, int32_t d_qk,
                                       int32_t d_v, int32_t max_seqlen);
 
-/* Byte offsets of Z, O and the attention workspace inside the layer workspace. */
+/* Byte offsets of Z, O, the O statistics and the attention workspace inside the layer
+ * workspace (any pointer may be NULL). */
 void hstu_layer_workspace_offsets(int64_t total_tokens, int32_t H, int32_t d_qk, int32_t d_v,
-                                  size_t* z_offset, size_t* o_offset, size_t* attn_offset);
+                                  size_t* z_offset, size_t* o_offset, size_t* stats_offset,
+                                  size_t* attn_offset);
 
 /* Candidate scoring over a cached user history (M-FALCON, "Actions Speak Louder than Words"
  * reading notes §3.6; candidates of one request share one position, GenRank article part (2)).

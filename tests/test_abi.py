@@ -57,12 +57,11 @@ def test_workspace_sizes():
     assert L.hstu_attn_block_rows(1, 64) == 256
     assert L.hstu_attn_block_rows(0, 32) == 128
     assert L.hstu_attn_block_rows(1, 48) == 0
-    z, o, a = binding.layer_workspace_offsets(1000, 4, 64, 64)
-    assert z == 0 and o == 1000 * 1024 * 2 and a == o + 1000 * 256 * 2
-    # Z | O | attention workspace (256-byte aligned) | per (token, head) O statistics (2 fp32)
+    z, o, st, a = binding.layer_workspace_offsets(1000, 4, 64, 64)
+    # Z | O | per (token, head) O statistics (4 fp32) | attention workspace, 256-byte aligned
+    assert z == 0 and o == 1000 * 1024 * 2 and st == o + 1000 * 256 * 2 and a == st + 1000 * 4 * 16
     aw = L.hstu_attn_workspace_bytes(3, 4, 300, 1000)
-    assert L.hstu_layer_workspace_bytes(3, 1000, 384, 4, 64, 64, 300) == \
-        a + (aw + 255) // 256 * 256 + 1000 * 4 * 8
+    assert L.hstu_layer_workspace_bytes(3, 1000, 384, 4, 64, 64, 300) == a + (aw + 255) // 256 * 256
 
 
 def _attn(**kw):

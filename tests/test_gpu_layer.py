@@ -33,8 +33,9 @@ def test_layer_small_workload(affine):
 
 
 def test_layer_intermediates():
-    """Z = SiLU(X W1^T + b1) with its U | V | Q | K blocks, and O (stored in bf16 between the
-    attention and the LayerNorm), checked separately."""
+    """Z = SiLU(X W1^T + b1) with its U | V | Q | K blocks, and O (stored between the attention
+    and the LayerNorm as a per (token, head) fp32 offset plus bf16 deviations), checked
+    separately; the per-head statistics stored with O describe the represented values."""
     inp = synth.make_layer("t", 40, [0, 1, 300, 257, 64], D=256, H=4, d=64, alpha=1.0 / 300,
                            P=128, NT=32, table_std=0.5, randomize_affine=True)
     d = DevLayer(inp)
@@ -42,9 +43,17 @@ def test_layer_intermediates():
                      dtype=torch.uint8, device="cuda")
     y = d.run_layer(d.x, workspace=ws)
     torch.cuda.synchronize()
-    zo, oo, _ = binding.layer_workspace_offsets(inp.T, 4, 64, 64)
+    zo, oo, so, _ = binding.layer_workspace_offsets(inp.T, 4, 64, 64)
     z = ws[zo:zo + inp.T * 1024 * 2].view(torch.bfloat16).view(inp.T, 1024).float().cpu().numpy()
-    o = ws[oo:oo + inp.T * 256 * 2].view(torch.bfloat16).view(inp.T, 256).float().cpu().numpy()
+    # O is stored per (token, head) as an fp32 offset (first of four statistics) + bf16 values
+    dev = ws[oo:oo + inp.T * 256 * 2].view(torch.bfloat16).view(inp.T, 4, 64).float().cpu().numpy()
+    st = ws[so:so + inp.T * 4 * 16].view(torch.float32).view(inp.T, 4, 4).cpu().numpy()
+    o = (dev.astype(np.float64) + st[:, :, :1]).reshape(inp.T, 256)
+    o3 = o.reshape(inp.T, 4, 64)
+    mean = o3.mean(axis=2)
+    np.testing.assert_allclose(st[:, :, 1], mean, rtol=0, atol=1e-6 * np.abs(o3).max())
+    np.testing.assert_allclose(st[:, :, 2], ((o3 - mean[:, :, None]) ** 2).sum(axis=2), rtol=1e-4,
+                               atol=1e-6 * (o3 ** 2).sum(axis=2).max())
     yr, zr, orf = oracle_layer(inp, return_intermediates=True)
     for name, a, r in [("U", z[:, :256], zr[:, :256]), ("V", z[:, 256:512], zr[:, 256:512]),
                        ("Q", z[:, 512:768], zr[:, 512:768]), ("K", z[:, 768:], zr[:, 768:]),
