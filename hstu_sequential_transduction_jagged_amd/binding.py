@@ -35,6 +35,9 @@ SIGNATURES = {
     "hstu_attn_workspace_bytes": (_sz, [_i32, _i32, _i32, _i64]),
     "hstu_attn_fwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P, _i64, _P,
                              _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P, _P, _sz, _P]),
+    "hstu_attn_fwd_noalloc": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P,
+                                     _i64, _P, _i64, ctypes.POINTER(HstuBias), _f32, _f32, _P,
+                                     _P]),
     "hstu_attn_block_rows": (_i32, [_i32, _i32]),
     "hstu_attn_plan": (_i32, [_i32, _i32, _i32, _i32, _P, _i32, _P, _sz, _P]),
     "hstu_attn_fwd_planned": (_i32, [_i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _i64, _P,
@@ -199,6 +202,29 @@ def hstu_attn_fwd(q, k, v, offsets, max_seqlen, bias: Optional[HstuBias] = None,
                              float(out_scale), _ptr(out), _ptr(workspace), workspace.numel(),
                              _stream(q.device))
     _check("hstu_attn_fwd", st)
+    return out
+
+
+def hstu_attn_fwd_noalloc(q, k, v, offsets, max_seqlen, out, bias: Optional[HstuBias] = None,
+                          alpha=1.0, out_scale=1.0):
+    """hstu_attn_fwd without a workspace argument (the library's static device scratch); the
+    caller passes the output tensor."""
+    if not q.is_cuda or not out.is_cuda:
+        raise HstuError("inputs and output must be device tensors")
+    dt = _dtype_code(q)
+    if out.dtype == torch.float32 and dt == DTYPE_BF16:
+        dt = DTYPE_BF16_OUT_F32
+    qs, H, d = _rows(q, "q")
+    ks, _, _ = _rows(k, "k")
+    vs, _, dv = _rows(v, "v")
+    if offsets.dtype != torch.int32:
+        raise HstuError("offsets must be int32")
+    bias = bias if bias is not None else make_bias(BIAS_NONE)
+    st = lib().hstu_attn_fwd_noalloc(dt, offsets.numel() - 1, H, d, dv, _ptr(offsets),
+                                     int(max_seqlen), q.shape[0], _ptr(q), qs, _ptr(k), ks,
+                                     _ptr(v), vs, ctypes.byref(bias), float(alpha),
+                                     float(out_scale), _ptr(out), _stream(q.device))
+    _check("hstu_attn_fwd_noalloc", st)
     return out
 
 

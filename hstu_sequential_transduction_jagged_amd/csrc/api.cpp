@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/hstu.h"
 #include <cmath>
@@ -356,6 +357,51 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   return hstu_attn_fwd_planned(dt_call, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q,
                                q_row_stride, k, k_row_stride, v, v_row_stride, bias, alpha,
                                out_scale, o, workspace, workspace_bytes, stream);
+}
+
+// ---- the attention forward without allocation ----
+// Its workspace is a file-scope device array; each device holds its own copy, whose device
+// address hipGetSymbolAddress gives once per device (the array's name is only a host-side
+// stand-in).  Every call on a device shares that device's copy.
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+}  // namespace
+
+hstu_status hstu_attn_fwd_noalloc(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                                  const int32_t* offsets, int32_t max_seqlen,
+                                  int64_t total_tokens, const void* q, int64_t q_row_stride,
+                                  const void* k, int64_t k_row_stride, const void* v,
+                                  int64_t v_row_stride, const hstu_bias* bias, float alpha,
+                                  float out_scale, void* o, hipStream_t stream) {
+  g_last_error[0] = 0;
+  const size_t need = hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens);
+  if (need > kNoAllocScratchBytes)
+    return fail(HSTU_ERR_UNSUPPORTED,
+                "this batch needs %zu bytes of attention workspace; the no-allocation entry point "
+                "has %zu (use hstu_attn_fwd with a workspace)",
+                need, kNoAllocScratchBytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return check_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HSTU_ERR_UNSUPPORTED, "device %d above %d", dev, kMaxDevices);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return check_hip(e, "hipGetSymbolAddress(scratch)");
+      g_scratch_ptr[dev] = p;
+    }
+    ws = g_scratch_ptr[dev];
+  }
+  return hstu_attn_fwd(dt, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, q, q_row_stride, k,
+                       k_row_stride, v, v_row_stride, bias, alpha, out_scale, o, ws,
+                       kNoAllocScratchBytes, stream);
 }
 
 hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,

@@ -111,6 +111,22 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
                           const hstu_bias* bias, float alpha, float out_scale, void* o,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* hstu_attn_fwd for callers that cannot allocate or pass device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same computation with
+ * the same arguments minus the workspace, which is instead a 32 MiB static device array that
+ * the library holds on each device it runs on until the process ends.  Batches whose
+ * hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens) exceeds 32 MiB are rejected with
+ * HSTU_ERR_UNSUPPORTED before anything is enqueued.  Allocates nothing (no hipMalloc, no
+ * library allocation); the first call on a device looks up that device's array address.
+ * Every call on one device uses the same array, so calls that overlap on one device (two
+ * streams, two host threads) race; calls on one stream are ordered and safe. */
+hstu_status hstu_attn_fwd_noalloc(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
+                                  const int32_t* offsets, int32_t max_seqlen,
+                                  int64_t total_tokens, const void* q, int64_t q_row_stride,
+                                  const void* k, int64_t k_row_stride, const void* v,
+                                  int64_t v_row_stride, const hstu_bias* bias, float alpha,
+                                  float out_scale, void* o, hipStream_t stream);
+
 /* The two halves of hstu_attn_fwd, for callers that run several attentions over one
  * jagged batch (a layer stack) or time the kernels apart.
  * hstu_attn_plan runs the jagged scheduler only: it writes the work list for

@@ -139,3 +139,16 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="libhstu.so not found"):
         binding.lib()
+
+
+def test_noalloc_rejects_batches_beyond_its_scratch():
+    """The no-allocation attention (a 32 MiB static workspace) refuses, before anything is
+    enqueued, a batch whose workspace would exceed it: one user of 65 536 rows needs tile
+    classes of (65 536 / 32 + 1) x 2 048 x 8 bytes alone."""
+    L = binding.lib()
+    need = L.hstu_attn_workspace_bytes(1, 1, 65536, 65536)
+    assert need > 32 << 20
+    st = L.hstu_attn_fwd_noalloc(1, 1, 1, 64, 64, None, 65536, 65536, None, 64, None, 64, None,
+                                 64, None, 1.0, 1.0, None, None)
+    assert st == -2
+    assert b"no-allocation" in L.hstu_last_error()
