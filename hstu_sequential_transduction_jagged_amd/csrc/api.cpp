@@ -260,7 +260,6 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   a.offsets = offsets;
   a.work_count = (const int32_t*)workspace;
   a.work = (const WorkItem*)((const char*)workspace + kHeader);
-  a.queue = (int32_t*)workspace + 4;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -277,7 +276,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   a.knorm = knorm;
   const int64_t grid = (int64_t)B * H * max_tiles;
   if (grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
-  hipError_t e = dt == HSTU_DTYPE_BF16 ? launch_attn_bf16(d_qk, a, grid, stream)
+  hipError_t e = dt == HSTU_DTYPE_BF16 ? launch_attn_bf16(d_qk, a, (int)grid, stream)
                                        : launch_attn_f32(d_qk, a, (int)grid, stream);
   return check_hip(e, "attention launch");
 }

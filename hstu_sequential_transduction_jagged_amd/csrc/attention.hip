@@ -196,17 +196,10 @@ __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict
 }
 
 // ============================================================================================
-// bf16, d = 64: a persistent grid (two workgroups per CU) of 8 waves x 32 queries; a work item is
-// 256 query rows of one (user, head), 64 keys per LDS stage (a ring of four stages filled by
-// direct global -> LDS transfers, one barrier per two tiles), four waves per SIMD.  Workgroups
-// pop items from the cost-sorted list: list index i belongs to queue i % 8, a workgroup serves
-// the queue of its XCD (workgroup w runs on XCD w % 8) first and then the others, so that with
-// H = 8 every item of head h runs on one XCD and its keys and values are cached in one L2.  The
-// bias tables are staged into LDS once per workgroup (again only when per-head tables change
-// head).  Per-tile metadata (bias class, key norm bound) is read with scalar loads and the
-// Taylor test is an integer compare of float bit patterns, so the common tile spends its vector
-// instructions on the scores alone.  One instantiation per bias kind (0 none, 1 position + time
-// tables, 2 ALiBi).
+// bf16, d = 64: 8 waves x 32 queries = 256 query rows per work item, 64 keys per LDS stage
+// (a ring of four stages filled by direct global -> LDS transfers, one barrier per two tiles),
+// four waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time tables,
+// 2 ALiBi).
 // ============================================================================================
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -214,7 +207,6 @@ constexpr int kQW = 32;
 constexpr int kBR = kWaves * kQW;
 constexpr int kKB = 64;
 constexpr int kD = 64;
-constexpr int kQueues = 8;
 
 // K and V rows of 64 bf16 (128 bytes, eight 16-byte chunks) are stored unpadded with chunk c of
 // row r at position c ^ swz(r), swz(r) = ((r >> 1) & 1) << 2 | ((r >> 2) & 3).  Three access
@@ -223,484 +215,453 @@ constexpr int kQueues = 8;
 // each), the transposing V reads (32 lanes, chunks 0..3 or 4..7 of 4 consecutive rows: rows r
 // and r + 2 differ in bit 2 of swz) and the transfers, which write whole rows.
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
-
-// wave-uniform metadata is read through the constant address space (scalar loads)
-typedef __attribute__((address_space(4))) const uint32_t cu32_t;
-typedef __attribute__((address_space(4))) const float cf32_t;
-__device__ __forceinline__ const cu32_t* scalar_u32(const void* p) { return (const cu32_t*)(uintptr_t)p; }
-__device__ __forceinline__ const cf32_t* scalar_f32(const void* p) { return (const cf32_t*)(uintptr_t)p; }
-
-struct __attribute__((aligned(16))) KVStage {
+struct __attribute__((aligned(16))) Stage {
   __attribute__((aligned(16))) bf16 k[kKB * kD];   // row = key, swizzled chunks
   __attribute__((aligned(16))) bf16 v[kKB * kD];
+  __attribute__((aligned(16))) int32_t krel[64];   // key time minus its 32-key block's minimum
+  __attribute__((aligned(16))) uint32_t cls[64];   // tile class entries (block, half, word)
+  __attribute__((aligned(16))) float kn[64];       // [0], [1]: max squared key norm of the halves
+  __attribute__((aligned(16))) float dummy[64];    // target of the transfers that carry nothing
 };
 struct __attribute__((aligned(16))) SmemBf16 {
-  KVStage st[4];                 // first 64 KB: every operand read has an immediate offset
-  __attribute__((aligned(16))) int32_t krel[4][64];  // per stage: key time minus its block minimum
   __attribute__((aligned(16))) float tay[kMaxTimeBuckets][4];  // per time bucket: c, a0, a1, a2
   float wposx[kMaxPosBuckets + 96];  // -log2(e) * w_pos[h][clamp(i - j, 0, P - 1)] at i - j + 32
-  float wtime[kMaxTimeBuckets];  // -log2(e) * w_time[h]
-  float wtime_lz[32];            // wtime[min(31 - lz, NT - 1)]: time bias by leading zeros of dt + 1
-  float tabmax;                  // log2(e) (max |w_pos| + max |w_time|)
-  int32_t next_item;
+  float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
+  float wtime_lz[32];           // wtime[min(31 - lz, NT - 1)]: time bias by leading zeros of dt + 1
 };
 
 template <int KIND, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) {
   __shared__ SmemBf16 sm;
+  __shared__ Stage st0, st1, st2, st3;
+  const int item = blockIdx.x;
+  if (item >= *a.work_count) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int count = (int)*scalar_u32(a.work_count);
-  const int H = a.H;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const WorkItem wi = a.work[item];
+  const int b = wi.b, h = wi.h, H = a.H;
+  const int64_t tok0 = a.offsets[b];
+  const int n = a.offsets[b + 1] - a.offsets[b];
+  const int q0 = wi.qt * kBR;
+  if (q0 >= n) return;
+  const int q_end = min(q0 + kBR, n);
+  const int n_tiles = (q_end + kKB - 1) / kKB;
+  const int qw0 = q0 + wave * kQW;                // first query row of this wave
+  const int wq_last = min(qw0 + kQW, q_end) - 1;  // < qw0 when the wave has no rows
+
+  const bf16* __restrict__ qp = (const bf16*)a.q;
+  const bf16* __restrict__ kp = (const bf16*)a.k;
+  const bf16* __restrict__ vp = (const bf16*)a.v;
+  const int64_t* __restrict__ ts = a.bias.ts;
+  const TimeStat* __restrict__ tstat = a.tstat;
   const float cq = -a.alpha * kLog2e;
   const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
-  const bool head_tables = KIND == 1 && (a.bias.pos_stride != 0 || a.bias.time_stride != 0);
+  constexpr int kClassWave = 1;  // its lanes 0..31 stage the next tile's class entries
 
-  // the next item for this workgroup: its XCD's queue first, then the others (thread 0 only)
-  const int own_q = (int)(blockIdx.x % kQueues);
-  int tried = 0;
-  auto pop = [&]() -> int {
-    while (tried < kQueues) {
-      const int x = (own_q + tried) % kQueues;
-      const int idx = x + kQueues * atomicAdd(&a.queue[x], 1);
-      if (idx < count) return idx;
-      ++tried;
-    }
-    return count;
+  // ---- staging: direct global -> LDS transfers into a ring of four stages ----
+  // Wave w's K and V transfers fill key rows 8 w .. 8 w + 7 of a stage: lane p writes row
+  // 8 w + p / 8 at chunk position p % 8, i.e. global chunk (p % 8) ^ swz(row).  Rows at or
+  // past q_end read as zeros (buffer bounds).  One 4-byte transfer per wave: wave 0 the keys'
+  // time offsets, wave 1 the class entries (both position + time bias only), wave 2 the two
+  // halves' key norm bounds, the others nothing (out of range).
+  const uint32_t kstride_b = (uint32_t)a.k_stride * 2u, vstride_b = (uint32_t)a.v_stride * 2u;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(kp + tok0 * a.k_stride + (int64_t)h * kD), (short)0,
+      (int)((uint32_t)(q_end - 1) * kstride_b + 2u * kD), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(vp + tok0 * a.v_stride + (int64_t)h * kD), (short)0,
+      (int)((uint32_t)(q_end - 1) * vstride_b + 2u * kD), 0x00020000);
+  uint32_t kvo, vvo;
+  {
+    const int r = 8 * wave + (lane >> 3);
+    const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ swz(r));
+    kvo = (uint32_t)r * kstride_b + ch;
+    vvo = (uint32_t)r * vstride_b + ch;
+  }
+  const int64_t crow = tclass_row0(tok0, b) + q0 / 32;
+  const int64_t cbase = crow * a.tclass_cols * 8;  // bytes
+  const int64_t krow0 = tclass_row0(tok0, b);  // the user's first 32-key block row
+  const int nkb = (q_end + 31) / 32;            // key blocks this item reads
+  const __amdgpu_buffer_rsrc_t rrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wave == 2 ? (const void*)(a.knorm + krow0 * H + h)
+              : KIND != 1 || wave > 2 ? nullptr
+              : wave == 0 ? (const void*)(a.trel + tok0)
+                          : (const void*)((const char*)a.tclass + cbase)),
+      (short)0,
+      wave == 2 ? (nkb - 1) * H * 4 + 4
+      : KIND != 1 || wave > 2 ? 0
+      : wave == 0 ? q_end * 4 : (int)min(a.tclass_bytes - cbase, (int64_t)0x7fffffff),
+      0x00020000);
+  const uint32_t roff = wave == 0 ? 4u * lane
+                      : wave == 2 ? 4u * (uint32_t)H * (uint32_t)lane
+                                  : 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3);
+  auto dma = [&](Stage& stg, int t) __attribute__((always_inline)) {
+    const bool real = t < n_tiles;
+    const uint32_t j0 = (uint32_t)(t * kKB);
+    const uint32_t ksoff = __builtin_amdgcn_readfirstlane(real ? j0 * kstride_b : 0x7fffffffu);
+    const uint32_t vsoff = __builtin_amdgcn_readfirstlane(real ? j0 * vstride_b : 0x7fffffffu);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_ptr)(stg.k + 512 * wave), 16, kvo, ksoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_ptr)(stg.v + 512 * wave), 16, vvo, vsoff, 0, 0);
+    const uint32_t msoff = __builtin_amdgcn_readfirstlane(
+        !real ? 0x7fffffffu
+        : wave == 2 ? (j0 / 32u) * 4u * (uint32_t)H
+        : (KIND == 1 && wave < 2) ? (wave == 0 ? 4u * j0 : j0 / 4u) : 0x7fffffffu);
+    void* dst = wave == 0 ? (void*)stg.krel : wave == 1 ? (void*)stg.cls
+              : wave == 2 ? (void*)stg.kn : (void*)stg.dummy;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rrsrc, (lds_ptr)dst, 4, roff, msoff, 0, 0);
   };
-  if (tid == 0) sm.next_item = pop();
+  // the first two tiles' transfers go out before the item's register loads, so that their
+  // latencies overlap
+  dma(st0, 0);
+  dma(st1, 1);
 
-  // Taylor coefficients of the bias-free kernel
-  float ta0 = 0.f, ta1 = 0.f, ta2 = 0.f;
-  if (KIND == 0) w_taylor_coeffs(0.f, cq, ta0, ta1, ta2);
-  int table_h = -1;
-  lds_barrier();
-  int item = __builtin_amdgcn_readfirstlane(sm.next_item);
+  // ---- Q fragments (B operand of S^T = K Q^T), unscaled ----
+  bf16x8 qop[4];
+  const int row = qw0 + l32;
+  const bool qvalid = row <= wq_last;
+  {
+    const bf16* src = qp + (tok0 + row) * a.q_stride + (int64_t)h * kD + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (qvalid) raw = *(const u32x4*)(src + 16 * ks);
+      qop[ks] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+  // |alpha log2 e| times the max norm of the wave's query rows: with a tile's max key norm,
+  // a bound on |y - bias| over the tile (Cauchy-Schwarz)
+  float qbound;
+  {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {qop[ks][2 * e], qop[ks][2 * e + 1]};
+        ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
+      }
+    }
+    ss += __shfl_xor(ss, 32, 64);  // the two lane halves hold the two halves of a row
+    qbound = uniform_f32(fabsf(cq) * 1.0001f * sqrtf(wave_max(ss)));  // margin for rounding
+  }
 
-  while (item < count) {
-    // lane-derived constants, recomputed per item (an opaque copy of the lane index keeps the
-    // compiler from holding them across the whole persistent loop)
-    int lane_i = lane;
-    asm volatile("" : "+v"(lane_i));
-    const int l32 = lane_i & 31, hf = lane_i >> 5;
-    // register r of a 32x32 accumulator holds key acc_key(r, hf) = kc(r) + 4 hf for query l32
-    const int lv = l32 - 4 * hf;
-    // transposing V reads: this lane's source row (key) and column (d) within a 16-key group
-    const int vtr_row0 = 4 * hf + ((lane_i & 15) >> 2);
-    const int vtr_col = 16 * ((lane_i >> 4) & 1) + 4 * (lane_i & 3);
-    // byte offsets of this lane's operand reads within a stage.  The K read of k-step ks takes
-    // chunk 2 ks + hf of row l32 (+ 32 hk), at position (2 ks + hf) ^ swz(l32): kbase ^ (32 ks).
-    // The V reads take chunk 4 db + vtr_col / 8 of row vtr_row0 + 8 e (+ 16 m + 32 hk): vbase[e]
-    // ^ (64 db).  (The XORs touch bits 5 and 6 only, which the row offsets leave zero.)
-    uint32_t kbase, vbase[2];
+  // ---- bias set-up ----
+  float slope_y = 0.f, ta0 = 0.f, ta1 = 0.f, ta2 = 0.f, tabmax = 0.f;
+  int32_t tq_rel = 0;  // query time minus the wave's block minimum (32-bit paths)
+  if (KIND == 1) {
+    const float* wp = a.bias.w_pos + (int64_t)h * a.bias.pos_stride;
+    const float* wt = a.bias.w_time + (int64_t)h * a.bias.time_stride;
+    for (int i = tid; i < a.bias.num_pos + 96; i += kThreads) sm.wposx[i] = -kLog2e * wp[min(max(i - 32, 0), Pm1)];
+    if (tid < a.bias.num_time) {
+      // per time bucket: the bias of a tile with saturated position bucket, and its Taylor
+      // coefficients
+      const float c = -kLog2e * (wp[Pm1] + wt[tid]);
+      float x0, x1, x2;
+      w_taylor_coeffs(c, cq, x0, x1, x2);
+      *(f32x4*)(&sm.tay[tid][0]) = f32x4{c, x0, x1, x2};
+      sm.wtime[tid] = -kLog2e * wt[tid];
+    }
+    if (tid < 32) sm.wtime_lz[tid] = -kLog2e * wt[min(31 - tid, NTm1)];
     {
-      const int sk = swz(l32);
-      kbase = (uint32_t)(l32 * 128 + 32 * (sk >> 1) + 16 * (hf ^ (sk & 1)));
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int r = vtr_row0 + 8 * e, sv = swz(r);
-        vbase[e] = (uint32_t)(r * 128 + 64 * (sv >> 2) + 16 * ((vtr_col >> 3) ^ (sv & 3)) + 2 * (vtr_col & 7));
-      }
+      float mp = 0.f, mt = 0.f;
+      for (int i = lane; i < a.bias.num_pos; i += 64) mp = fmaxf(mp, fabsf(wp[i]));
+      for (int i = lane; i < a.bias.num_time; i += 64) mt = fmaxf(mt, fabsf(wt[i]));
+      tabmax = uniform_f32(kLog2e * (wave_max(mp) + wave_max(mt)));
     }
-    // this lane's K / V transfer offsets: wave w fills key rows 8 w .. 8 w + 7, lane p row
-    // 8 w + p / 8 at chunk position p % 8, i.e. global chunk (p % 8) ^ swz(row)
-    const int xrow = 8 * wave + (lane_i >> 3);
-    const uint32_t xch = 16u * (uint32_t)((lane_i & 7) ^ swz(xrow));
-    const uint32_t kstride_b = (uint32_t)a.k_stride * 2u, vstride_b = (uint32_t)a.v_stride * 2u;
-    const uint32_t kvo = (uint32_t)xrow * kstride_b + xch, vvo = (uint32_t)xrow * vstride_b + xch;
-
-    const cu32_t* wp = scalar_u32(a.work + item);
-    const int b = (int)wp[0], h = (int)wp[1], qt = (int)wp[2];
-    const int64_t tok0 = (int32_t)scalar_u32(a.offsets)[b];
-    const int n = (int32_t)scalar_u32(a.offsets)[b + 1] - (int)tok0;
-    const int q0 = qt * kBR;
-    const int q_end = min(q0 + kBR, n);
-    const int n_tiles = (q_end + kKB - 1) / kKB;
-    const int qw0 = q0 + wave * kQW;                // first query row of this wave
-    const int wq_last = min(qw0 + kQW, q_end) - 1;  // < qw0 when the wave has no rows
-
-    // ---- bias tables: once per workgroup, or per head for per-head tables ----
-    const int th = head_tables ? h : 0;
-    if (KIND == 1 && th != table_h) {
-      const float* wpt = a.bias.w_pos + (int64_t)th * a.bias.pos_stride;
-      const float* wtt = a.bias.w_time + (int64_t)th * a.bias.time_stride;
-      for (int i = tid; i < a.bias.num_pos + 96; i += kThreads) sm.wposx[i] = -kLog2e * wpt[min(max(i - 32, 0), Pm1)];
-      if (tid < a.bias.num_time) {
-        // per time bucket: the bias of a tile with saturated position bucket, and its Taylor
-        // coefficients
-        const float c = -kLog2e * (wpt[Pm1] + wtt[tid]);
-        float x0, x1, x2;
-        w_taylor_coeffs(c, cq, x0, x1, x2);
-        *(f32x4*)(&sm.tay[tid][0]) = f32x4{c, x0, x1, x2};
-        sm.wtime[tid] = -kLog2e * wtt[tid];
-      }
-      if (tid < 32) sm.wtime_lz[tid] = -kLog2e * wtt[min(31 - tid, NTm1)];
-      if (wave == 7) {
-        float mp = 0.f, mt = 0.f;
-        for (int i = lane; i < a.bias.num_pos; i += 64) mp = fmaxf(mp, fabsf(wpt[i]));
-        for (int i = lane; i < a.bias.num_time; i += 64) mt = fmaxf(mt, fabsf(wtt[i]));
-        const float m = kLog2e * (wave_max_dpp(mp) + wave_max_dpp(mt));
-        if (lane == 0) sm.tabmax = m;
-      }
-      table_h = th;
+    int64_t tmin = 0;
+    if (qw0 <= wq_last) tmin = tstat[tok0 + qw0].mn;
+    if (qvalid) {
+      const int64_t d = ts[tok0 + row] - tmin;
+      tq_rel = d > 0x7fffffffLL ? 0x7fffffff : (int32_t)d;
     }
+  } else if (KIND == 0) {
+    w_taylor_coeffs(0.f, cq, ta0, ta1, ta2);
+  } else {
+    slope_y = kLog2e * (a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H));
+  }
+  // register r of a 32x32 accumulator holds key acc_key(r, hf) = kc(r) + 4 hf for query l32
+  const int lv = l32 - 4 * hf;
+  // transposing V reads: this lane's source row (key) and column (d) within a 16-key group
+  const int vtr_row0 = 4 * hf + ((lane & 15) >> 2);
+  const int vtr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const float neg_slope_y = -slope_y, alibi_lane = slope_y * (float)lv;
 
-    // ---- staging: direct global -> LDS transfers; rows at or past q_end read as zeros ----
-    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const bf16*)a.k + tok0 * a.k_stride + (int64_t)h * kD), (short)0,
-        (int)((uint32_t)(q_end - 1) * kstride_b + 2u * kD), 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const bf16*)a.v + tok0 * a.v_stride + (int64_t)h * kD), (short)0,
-        (int)((uint32_t)(q_end - 1) * vstride_b + 2u * kD), 0x00020000);
-    // wave 0 also brings the keys' 32-bit time offsets (position + time bias)
-    const __amdgpu_buffer_rsrc_t rrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(KIND == 1 ? (const void*)(a.trel + tok0) : nullptr), (short)0,
-        KIND == 1 ? q_end * 4 : 0, 0x00020000);
-    auto dma = [&](int s, int t) __attribute__((always_inline)) {
-      const bool real = t < n_tiles;
-      const uint32_t j0 = (uint32_t)(t * kKB);
-      const uint32_t ksoff = real ? j0 * kstride_b : 0x7fffffffu;
-      const uint32_t vsoff = real ? j0 * vstride_b : 0x7fffffffu;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_ptr)(sm.st[s].k + 512 * wave), 16, kvo, ksoff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_ptr)(sm.st[s].v + 512 * wave), 16, vvo, vsoff, 0, 0);
-      if (KIND == 1 && wave == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rrsrc, (lds_ptr)sm.krel[s], 4, 4u * lane,
-                                                 real ? 4u * j0 : 0x7fffffffu, 0, 0);
-    };
-    // the first two tiles' transfers go out before the item's register loads
-    dma(0, 0);
-    dma(1, 1);
-
-    // ---- Q fragments (B operand of S^T = K Q^T), unscaled ----
-    bf16x8 qop[4];
-    const int row = qw0 + l32;
-    const bool qvalid = row <= wq_last;
-    {
-      const bf16* src = (const bf16*)a.q + (tok0 + row) * a.q_stride + (int64_t)h * kD + 8 * hf;
+  f32x16 oacc[2];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 raw = {0u, 0u, 0u, 0u};
-        if (qvalid) raw = *(const u32x4*)(src + 16 * ks);
-        qop[ks] = __builtin_bit_cast(bf16x8, raw);
-      }
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+
+  // byte offsets of this lane's operand reads within a stage.  The K read of k-step ks takes
+  // chunk 2 ks + hf of row l32 (+ 32 hk), at position (2 ks + hf) ^ swz(l32): kbase ^ (32 ks).
+  // The V reads take chunk 4 db + vtr_col / 8 of row vtr_row0 + 8 e (+ 16 m + 32 hk): vbase[e]
+  // ^ (64 db).  (The XORs touch bits 5 and 6 only, which the row offsets leave zero.)
+  uint32_t kbase, vbase[2];
+  {
+    const int sk = swz(l32);
+    kbase = (uint32_t)(l32 * 128 + 32 * (sk >> 1) + 16 * (hf ^ (sk & 1)));
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int r = vtr_row0 + 8 * e, sv = swz(r);
+      vbase[e] = (uint32_t)(r * 128 + 64 * (sv >> 2) + 16 * ((vtr_col >> 3) ^ (sv & 3)) + 2 * (vtr_col & 7));
     }
-    // |alpha log2 e|^2 times the largest squared norm of the wave's query rows: with a key
-    // block's squared norm bound kn, D^2 = qb2 kn bounds (y - bias)^2 over the tile
-    // (Cauchy-Schwarz).  Taylor needs D <= kTaylorD, i.e. kn <= kTaylorD^2 / qb2, an order of
-    // non-negative floats that their bit patterns keep: tay_kn is compared as an integer.
-    float qb2;
-    uint32_t tay_kn;
-    {
-      float ss = 0.f;
+  }
+
+  enum { kExact = 0, kPoly = 1, kTaylor = 2 };
+  auto compute = [&](const Stage& stg, int t) __attribute__((always_inline)) {
+    const int j0 = t * kKB;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+    for (int hk = 0; hk < 2; ++hk) {
+      const int j0h = j0 + 32 * hk;
+      if (j0h > wq_last || wq_last < qw0) continue;  // past the diagonal, or the wave has no rows
+      // K operands of this 32-key step (V operands are read after the SiLU)
+      bf16x8 kop[4], vop[2][2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 pr = {qop[ks][2 * e], qop[ks][2 * e + 1]};
-          ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
-        }
+      for (int ks = 0; ks < 4; ++ks)
+        kop[ks] = *(const bf16x8*)((const char*)stg.k + 32 * hk * 128 + (kbase ^ (32u * ks)));
+      const float kn2 = uniform_f32(stg.kn[hk]);
+      const bool diag = (j0h + 31) > qw0;
+      // i - j of register r = dlt + lv - kc(r): a lane term, a tile term and a constant
+      const int dlt = qw0 - j0h;
+      auto kc = [](int r) { return 8 * (r >> 2) + (r & 3); };
+      // dlt capped where every position bucket of the tile saturates: then i - j + 32 indexes
+      // the extended position table within its P + 96 entries
+      const int dltc = min(dlt, Pm1 + 33);
+
+      // ---- this tile's bias mode and SiLU evaluation ----
+      int mode, path, thi = 0, dq = 0;
+      float c0 = 0.f, c1 = 0.f, A0 = ta0, A1 = ta1, A2 = ta2;
+      if (KIND == 0) {
+        mode = diag ? 3 : 1;
+        const float D2 = qbound * qbound * kn2;
+        path = D2 <= kTaylorD * kTaylorD ? kTaylor : D2 <= kPolyRange * kPolyRange ? kPoly : kExact;
+      } else if (KIND == 1) {
+        const u32x2 e = *(const u32x2*)(&stg.cls[4 * wave + 2 * hk]);
+        const uint32_t info = __builtin_amdgcn_readfirstlane(e[0]);
+        dq = (int32_t)__builtin_amdgcn_readfirstlane(e[1]);
+        mode = info & 15;
+        const int tlo = (info >> 4) & 255;
+        thi = info >> 12;
+        const f32x4 lo = *(const f32x4*)(&sm.tay[tlo][0]);
+        c0 = uniform_f32(mode == 3 ? sm.wtime[tlo] : lo[0]);
+        c1 = uniform_f32(sm.tay[thi][0]);
+        A0 = uniform_f32(lo[1]);
+        A1 = uniform_f32(lo[2]);
+        A2 = uniform_f32(lo[3]);
+        // |y - bias| <= D = qbound * knorm; Taylor iff the bias is one value and D <= kTaylorD,
+        // polynomial iff D + max|bias| <= kPolyRange
+        const float cabs = mode == 1 ? fabsf(c0) : mode == 2 ? fmaxf(fabsf(c0), fabsf(c1)) : tabmax;
+        const float D2 = qbound * qbound * kn2;
+        const float room = kPolyRange - cabs;
+        path = (mode == 1 && D2 <= kTaylorD * kTaylorD) ? kTaylor
+             : (room >= 0.f && D2 <= room * room) ? kPoly : kExact;
+      } else {
+        mode = 3;
+        const float room = kPolyRange - slope_y * (float)max(qw0 + 31 - j0h, 0);
+        path = (room >= 0.f && qbound * qbound * kn2 <= room * room) ? kPoly : kExact;
       }
-      ss += __shfl_xor(ss, 32, 64);  // the two lane halves hold the two halves of a row
-      qb2 = uniform_f32(cq * cq * 1.0002f * wave_max_dpp(ss));  // margin for rounding
-      const float lim = qb2 > 0.f ? (kTaylorD * kTaylorD) / qb2 : __builtin_huge_valf();
-      tay_kn = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, lim));
-    }
 
-    // ---- per-item bias state ----
-    float slope_y = 0.f;
-    int32_t tq_rel = 0;  // query time minus the wave's block minimum (32-bit paths)
-    if (KIND == 1) {
-      int64_t tmin = 0;
-      if (qw0 <= wq_last) tmin = a.tstat[tok0 + qw0].mn;
-      if (qvalid) {
-        const int64_t d = a.bias.ts[tok0 + row] - tmin;
-        tq_rel = d > 0x7fffffffLL ? 0x7fffffff : (int32_t)d;
-      }
-    } else if (KIND == 2) {
-      slope_y = kLog2e * (a.bias.slopes ? a.bias.slopes[h] : default_alibi_slope(h, H));
-    }
-    const float neg_slope_y = -slope_y, alibi_lane = slope_y * (float)lv;
-    // this wave's row of tile classes and the user's key norm bounds (scalar loads)
-    const int64_t krow0 = tclass_row0(tok0, b);  // the user's first 32-key block row
-    const cu32_t* cls_row = scalar_u32(a.tclass) + 2 * ((krow0 + qw0 / 32) * a.tclass_cols);
-    const cf32_t* kn_col = scalar_f32(a.knorm) + krow0 * H + h;
+      // S^T tile: rows = keys, columns = this wave's queries
+      f32x16 sacc = {};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], sacc, 0, 0, 0);
 
-    f32x16 oacc[2];
+      // y = -log2(e) (alpha s + bias); w(y) = 2 y / (1 + 2^y) = -(2 / ln 2) SiLU(alpha s + bias)
+      auto w_exact = [&](float y) {
+        return y * __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(y), 0.5f, 0.5f));
+      };
+      auto w_poly = [&](float y) {
+        const float u = y * y;
+        return __builtin_fmaf(-u, __builtin_fmaf(__builtin_fmaf(kP2, u, kP1), u, kP0), y);
+      };
+      f32x16 w;
+      if (path == kTaylor && (mode == 1 || KIND == 0)) {
+        // the common case: constant bias, small |delta|
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+        for (int r = 0; r < 16; ++r) w[r] = __builtin_fmaf(__builtin_fmaf(A2, sacc[r], A1), sacc[r], A0);
+      } else if (mode == 1 || KIND == 0) {
+        if (path == kPoly) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-
-    enum { kExact = 0, kPoly = 1, kTaylor = 2 };
-    auto compute = [&](int s, int t) __attribute__((always_inline)) {
-      const KVStage& stg = sm.st[s];
-      const int j0 = t * kKB;
-#pragma unroll
-      for (int hk = 0; hk < 2; ++hk) {
-        const int j0h = j0 + 32 * hk;
-        if (j0h > wq_last || wq_last < qw0) continue;  // past the diagonal, or the wave has no rows
-        const int kb = j0h / 32;
-        // K operands of this 32-key step (V operands are read after the SiLU)
-        bf16x8 kop[4], vop[2][2];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kop[ks] = *(const bf16x8*)((const char*)stg.k + 32 * hk * 128 + (kbase ^ (32u * ks)));
-        const uint32_t knb = __builtin_bit_cast(uint32_t, kn_col[(int64_t)kb * H]);
-        const bool diag = (j0h + 31) > qw0;
-        // i - j of register r = dlt + lv - kc(r): a lane term, a tile term and a constant
-        const int dlt = qw0 - j0h;
-        auto kc = [](int r) { return 8 * (r >> 2) + (r & 3); };
-        // dlt capped where every position bucket of the tile saturates: then i - j + 32 indexes
-        // the extended position table within its P + 96 entries
-        const int dltc = min(dlt, Pm1 + 33);
-
-        // ---- this tile's bias mode and SiLU evaluation ----
-        int mode, path, thi = 0, dq = 0;
-        f32x4 A = {0.f, ta0, ta1, ta2};  // bias, Taylor a0, a1, a2 (wave-uniform, in registers)
-        float c1 = 0.f;
-        if (KIND == 0) {
-          mode = diag ? 3 : 1;
-          path = knb <= tay_kn ? kTaylor
-               : __builtin_bit_cast(float, knb) * qb2 <= kPolyRange * kPolyRange ? kPoly : kExact;
-        } else if (KIND == 1) {
-          const uint32_t info = cls_row[2 * kb];
-          dq = (int32_t)cls_row[2 * kb + 1];
-          mode = info & 15;
-          const int tlo = (info >> 4) & 255;
-          thi = info >> 12;
-          A = *(const f32x4*)(&sm.tay[tlo][0]);
-          if (mode == 1 && knb <= tay_kn) {
-            path = kTaylor;
-          } else {
-            // polynomial iff D + max|bias| <= kPolyRange
-            if (mode == 3) A[0] = sm.wtime[tlo];
-            c1 = sm.tay[thi][0];
-            const float cabs = mode == 1 ? fabsf(A[0]) : mode == 2 ? fmaxf(fabsf(A[0]), fabsf(c1)) : sm.tabmax;
-            const float room = kPolyRange - cabs;
-            const float D2 = qb2 * __builtin_bit_cast(float, knb);
-            path = (room >= 0.f && D2 <= room * room) ? kPoly : kExact;
-            path = __builtin_amdgcn_readfirstlane(path);
-          }
+          for (int r = 0; r < 16; ++r) w[r] = w_poly(__builtin_fmaf(sacc[r], cq, c0));
         } else {
-          mode = 3;
-          const float room = kPolyRange - slope_y * (float)max(qw0 + 31 - j0h, 0);
-          path = (room >= 0.f && qb2 * __builtin_bit_cast(float, knb) <= room * room) ? kPoly : kExact;
-          path = __builtin_amdgcn_readfirstlane(path);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) w[r] = w_exact(__builtin_fmaf(sacc[r], cq, c0));
         }
-
-        // S^T tile: rows = keys, columns = this wave's queries
-        f32x16 sacc = {};
+      } else {
+        // per-element bias (y units), four registers at a time
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], sacc, 0, 0, 0);
-
-        // y = -log2(e) (alpha s + bias); w(y) = 2 y / (1 + 2^y) = -(2 / ln 2) SiLU(alpha s + bias)
-        auto w_exact = [&](float y) {
-          return y * __builtin_amdgcn_rcpf(__builtin_fmaf(__builtin_amdgcn_exp2f(y), 0.5f, 0.5f));
-        };
-        auto w_poly = [&](float y) {
-          const float u = y * y;
-          return __builtin_fmaf(-u, __builtin_fmaf(__builtin_fmaf(kP2, u, kP1), u, kP0), y);
-        };
-        // the weights w overwrite the scores in place
-        if (path == kTaylor && (mode == 1 || KIND == 0)) {
-          // the common case: constant bias, small |delta|
+        for (int g = 0; g < 4; ++g) {
+          f32x4 c4;
+          if (KIND == 2) {
+            const float base = alibi_lane + slope_y * (float)dlt;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[r] = __builtin_fmaf(__builtin_fmaf(A[3], sacc[r], A[2]), sacc[r], A[1]);
-        } else if (mode == 1 || KIND == 0) {
+            for (int i = 0; i < 4; ++i) c4[i] = __builtin_fmaf(neg_slope_y, (float)kc(4 * g + i), base);
+          } else if (mode == 2) {
+            // two time buckets: dt >= 2^thi - 1  <=>  rel_j <= (t_i - kmin) - (2^thi - 1)
+            const int lim = tq_rel + dq - ((1 << thi) - 1);
+            const i32x4 rel4 = *(const i32x4*)(&stg.krel[32 * hk + 8 * g + 4 * hf]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c4[i] = rel4[i] <= lim ? c1 : c0;
+          } else if (mode == 3) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c4[i] = sm.wposx[lv + (dltc - kc(4 * g + i)) + 32] + c0;
+          } else if (mode == 4) {
+            const int ti1 = tq_rel + dq + 1;
+            const i32x4 rel4 = *(const i32x4*)(&stg.krel[32 * hk + 8 * g + 4 * hf]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int u = max(ti1 - rel4[i], 1);  // max(dt, 0) + 1
+              c4[i] = sm.wposx[lv + (dltc - kc(4 * g + i)) + 32] + sm.wtime_lz[__builtin_clz((uint32_t)u)];
+            }
+          } else {
+            // timestamps spread beyond 2^30 within the tile (rare): exact 64-bit deltas from
+            // global memory
+            const int64_t tq = ts[tok0 + min(row, n - 1)];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * g + i;
+              const int64_t tk = ts[tok0 + min(j0h + kc(r) + 4 * hf, n - 1)];
+              c4[i] = sm.wposx[pos_bucket(lv + (dlt - kc(r)), Pm1) + 32] + sm.wtime[time_bucket(tq - tk, NTm1)];
+            }
+          }
           if (path == kPoly) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[r] = w_poly(__builtin_fmaf(sacc[r], cq, A[0]));
+            for (int i = 0; i < 4; ++i) w[4 * g + i] = w_poly(__builtin_fmaf(sacc[4 * g + i], cq, c4[i]));
           } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[r] = w_exact(__builtin_fmaf(sacc[r], cq, A[0]));
+            for (int i = 0; i < 4; ++i) w[4 * g + i] = w_exact(__builtin_fmaf(sacc[4 * g + i], cq, c4[i]));
           }
-        } else {
-          // per-element bias (y units), four registers at a time
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 c4;
-            if (KIND == 2) {
-              const float base = alibi_lane + slope_y * (float)dlt;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) c4[i] = __builtin_fmaf(neg_slope_y, (float)kc(4 * g + i), base);
-            } else if (mode == 2) {
-              // two time buckets: dt >= 2^thi - 1  <=>  rel_j <= (t_i - kmin) - (2^thi - 1)
-              const int lim = tq_rel + dq - ((1 << thi) - 1);
-              const i32x4 rel4 = *(const i32x4*)(&sm.krel[s][32 * hk + 8 * g + 4 * hf]);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) c4[i] = rel4[i] <= lim ? c1 : A[0];
-            } else if (mode == 3) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) c4[i] = sm.wposx[lv + (dltc - kc(4 * g + i)) + 32] + A[0];
-            } else if (mode == 4) {
-              const int ti1 = tq_rel + dq + 1;
-              const i32x4 rel4 = *(const i32x4*)(&sm.krel[s][32 * hk + 8 * g + 4 * hf]);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int u = max(ti1 - rel4[i], 1);  // max(dt, 0) + 1
-                c4[i] = sm.wposx[lv + (dltc - kc(4 * g + i)) + 32] + sm.wtime_lz[__builtin_clz((uint32_t)u)];
-              }
-            } else {
-              // timestamps spread beyond 2^30 within the tile (rare): exact 64-bit deltas from
-              // global memory (lane terms from an opaque lane copy: computed here, not held)
-              int lx = lane;
-              asm volatile("" : "+v"(lx));
-              const int rowx = qw0 + (lx & 31), hfx = lx >> 5;
-              const int64_t tq = a.bias.ts[tok0 + min(rowx, n - 1)];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int r = 4 * g + i;
-                const int64_t tk = a.bias.ts[tok0 + min(j0h + kc(r) + 4 * hfx, n - 1)];
-                c4[i] = sm.wposx[pos_bucket(lv + (dlt - kc(r)), Pm1) + 32] + sm.wtime[time_bucket(tq - tk, NTm1)];
-              }
-            }
-            if (path == kPoly) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) sacc[4 * g + i] = w_poly(__builtin_fmaf(sacc[4 * g + i], cq, c4[i]));
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) sacc[4 * g + i] = w_exact(__builtin_fmaf(sacc[4 * g + i], cq, c4[i]));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if (diag) {
+      }
+      if (diag) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[r] = lv >= kc(r) - dlt ? sacc[r] : 0.f;
-        }
-        bf16x8 pop8[2];
-        {
-          f32x8 a0, a1;
+        for (int r = 0; r < 16; ++r) w[r] = lv >= kc(r) - dlt ? w[r] : 0.f;
+      }
+      bf16x8 pop[2];
+      {
+        f32x8 a0, a1;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            a0[r] = sacc[r];
-            a1[r] = sacc[r + 8];
-          }
-          pop8[0] = __builtin_convertvector(a0, bf16x8);
-          pop8[1] = __builtin_convertvector(a1, bf16x8);
+        for (int r = 0; r < 8; ++r) {
+          a0[r] = w[r];
+          a1[r] = w[r + 8];
         }
-        // V^T operands straight from the row-major V tile with transposing LDS reads: in each
-        // 16-lane group, source lane j points at keys (row j / 4) and d (4 (j % 4) .. +3); lane i
-        // of the group then holds d = i for 4 consecutive keys.  Two reads give the 8 keys of
-        // k-slots 8 hf .. 8 hf + 7, in the key order of the Pt registers: 4 hf + {0..3} and
-        // 8 + 4 hf + {0..3} within the 16-key group m.
+        pop[0] = __builtin_convertvector(a0, bf16x8);
+        pop[1] = __builtin_convertvector(a1, bf16x8);
+      }
+      // V^T operands straight from the row-major V tile with transposing LDS reads: in each
+      // 16-lane group, source lane j points at keys (row j / 4) and d (4 (j % 4) .. +3); lane i
+      // of the group then holds d = i for 4 consecutive keys.  Two reads give the 8 keys of
+      // k-slots 8 hf .. 8 hf + 7, in the key order of the Pt registers: 4 hf + {0..3} and
+      // 8 + 4 hf + {0..3} within the 16-key group m.
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          bf16x4 half0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)((const char*)stg.v + (32 * hk + 16 * m) * 128 + (vbase[0] ^ (64u * db))));
+          bf16x4 half1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (__attribute__((address_space(3))) bf16x4*)((const char*)stg.v + (32 * hk + 16 * m) * 128 + (vbase[1] ^ (64u * db))));
+          vop[db][m] = bf16x8{half0[0], half0[1], half0[2], half0[3], half1[0], half1[1], half1[2], half1[3]};
+        }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            bf16x4 half0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4*)((const char*)stg.v + (32 * hk + 16 * m) * 128 + (vbase[0] ^ (64u * db))));
-            bf16x4 half1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4*)((const char*)stg.v + (32 * hk + 16 * m) * 128 + (vbase[1] ^ (64u * db))));
-            vop[db][m] = bf16x8{half0[0], half0[1], half0[2], half0[3], half1[0], half1[1], half1[2], half1[3]};
-          }
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int db = 0; db < 2; ++db)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop8[m], oacc[db], 0, 0, 0);
-      }
-    };
-    // tiles are taken in pairs, one barrier per pair: tiles t, t + 1 sit in stages t % 4,
-    // (t + 1) % 4; the transfers of tiles t + 2, t + 3 go into the stages of tiles t - 2, t - 1
-    // (their readers all passed the last barrier) while t and t + 1 are multiplied, then this
-    // wave's transfers are waited for and the barrier publishes them to all.  The first barrier
-    // also publishes the bias tables; after it thread 0 pops the workgroup's next item.
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[m], oacc[db], 0, 0, 0);
+    }
+  };
+  // tiles are taken in pairs, one barrier per pair: tiles t, t + 1 sit in stages t % 4,
+  // (t + 1) % 4; the transfers of tiles t + 2, t + 3 go into the stages of tiles t - 2, t - 1
+  // (their readers all passed the last barrier) while t and t + 1 are multiplied, then this
+  // wave's transfers are waited for and the barrier publishes them to all
+  wait_vm<0>();
+  lds_barrier();
+  auto pair = [&](const Stage& c0, const Stage& c1, Stage& n0, Stage& n1, int t) __attribute__((always_inline)) {
+    dma(n0, t + 2);
+    dma(n1, t + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(c0, t);
+    if (t + 1 < n_tiles) compute(c1, t + 1);
     wait_vm<0>();
     lds_barrier();
-    if (tid == 0) sm.next_item = pop();
-    auto pair = [&](int c0, int c1, int n0, int n1, int t) __attribute__((always_inline)) {
-      dma(n0, t + 2);
-      dma(n1, t + 3);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(c0, t);
-      if (t + 1 < n_tiles) compute(c1, t + 1);
-      wait_vm<0>();
-      lds_barrier();
-    };
-    for (int t = 0; t < n_tiles; t += 4) {
-      pair(0, 1, 2, 3, t);
-      if (t + 2 >= n_tiles) break;
-      pair(2, 3, 0, 1, t + 2);
-    }
-    // (the transfers past the last tile were waited for before the last barrier, which also
-    // published the next item; an item of an empty user, which the scheduler never lists, has
-    // no tiles and so one barrier here)
-    if (n_tiles == 0) lds_barrier();
-    item = __builtin_amdgcn_readfirstlane(sm.next_item);
+  };
+  for (int t = 0; t < n_tiles; t += 4) {
+    pair(st0, st1, st2, st3, t);
+    if (t + 2 >= n_tiles) break;
+    pair(st2, st3, st0, st1, t + 2);
+  }
+  // the transfers past the last tile land before the kernel ends
+  wait_vm<0>();
 
-    // ---- epilogue: O^T accumulators -> O rows, scaled by -(ln 2 / 2) out_scale ----
-    const float osc = -0.5f * kLn2 * a.out_scale;
-    f32x4 ov[2][4];
+
+  // ---- epilogue: O^T accumulators -> O rows, scaled by -(ln 2 / 2) out_scale ----
+  const float osc = -0.5f * kLn2 * a.out_scale;
+  f32x4 ov[2][4];
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[db][g][e] = oacc[db][4 * g + e] * osc;
+  const int64_t obase = ((tok0 + row) * H + h) * kD;
+  if (a.ostats && !OUT_F32) {
+    // layer mode: each head row is stored as its fp32 mean m plus bf16 deviations from m, so
+    // the rounding error scales with the row's spread, not its magnitude (a LayerNorm over the
+    // heads divides by that spread); the statistics entry holds m, the mean of the
+    // represented values m + dev and their sum of squared deviations (lanes l and l + 32 hold
+    // the two halves)
+    float sum = 0.f;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[db][g][e] = oacc[db][4 * g + e] * osc;
-    const int64_t obase = ((tok0 + row) * H + h) * kD;
-    if (a.ostats && !OUT_F32) {
-      // layer mode: each head row is stored as its fp32 mean m plus bf16 deviations from m, so
-      // the rounding error scales with the row's spread, not its magnitude (a LayerNorm over the
-      // heads divides by that spread); the statistics entry holds m, the mean of the
-      // represented values m + dev and their sum of squared deviations (lanes l and l + 32 hold
-      // the two halves)
-      float sum = 0.f;
+        for (int e = 0; e < 4; ++e) sum += ov[db][g][e];
+    sum += __shfl_xor(sum, 32, 64);
+    const float m = sum * (1.0f / kD);
+    bf16x4 dv[2][4];
+    float ds = 0.f;
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sum += ov[db][g][e];
-      sum += __shfl_xor(sum, 32, 64);
-      const float m = sum * (1.0f / kD);
-      bf16x4 dv[2][4];
-      float ds = 0.f;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          dv[db][g] = __builtin_convertvector(ov[db][g] - m, bf16x4);
-          const f32x4 back = __builtin_convertvector(dv[db][g], f32x4);
-          ov[db][g] = back;
-          ds += back[0] + back[1] + back[2] + back[3];
-        }
-      ds += __shfl_xor(ds, 32, 64);
-      const float md = ds * (1.0f / kD);
-      float q = 0.f;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q += (ov[db][g][e] - md) * (ov[db][g][e] - md);
-      q += __shfl_xor(q, 32, 64);
-      if (qvalid) {
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *(bf16x4*)((bf16*)a.o + obase + 32 * db + 8 * g + 4 * hf) = dv[db][g];
-        if (hf == 0) a.ostats[(tok0 + row) * H + h] = f32x4{m, m + md, q, 0.f};
+      for (int g = 0; g < 4; ++g) {
+        dv[db][g] = __builtin_convertvector(ov[db][g] - m, bf16x4);
+        const f32x4 back = __builtin_convertvector(dv[db][g], f32x4);
+        ov[db][g] = back;
+        ds += back[0] + back[1] + back[2] + back[3];
       }
-    } else if (qvalid) {
+    ds += __shfl_xor(ds, 32, 64);
+    const float md = ds * (1.0f / kD);
+    float q = 0.f;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q += (ov[db][g][e] - md) * (ov[db][g][e] - md);
+    q += __shfl_xor(q, 32, 64);
+    if (qvalid) {
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = 32 * db + 8 * g + 4 * hf;
-          if (OUT_F32)
-            *(f32x4*)((float*)a.o + obase + d0) = ov[db][g];
-          else
-            *(bf16x4*)((bf16*)a.o + obase + d0) = __builtin_convertvector(ov[db][g], bf16x4);
-        }
+        for (int g = 0; g < 4; ++g)
+          *(bf16x4*)((bf16*)a.o + obase + 32 * db + 8 * g + 4 * hf) = dv[db][g];
+      if (hf == 0) a.ostats[(tok0 + row) * H + h] = f32x4{m, m + md, q, 0.f};
     }
-  }
-  // the last workgroup to finish leaves the queue counters at zero for the next launch
-  if (tid == 0 && atomicAdd(&a.queue[kQueues], 1) == (int)gridDim.x - 1) {
+  } else if (qvalid) {
 #pragma unroll
-    for (int x = 0; x <= kQueues; ++x) atomicExch(&a.queue[x], 0);
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * hf;
+        if (OUT_F32)
+          *(f32x4*)((float*)a.o + obase + d0) = ov[db][g];
+        else
+          *(bf16x4*)((bf16*)a.o + obase + d0) = __builtin_convertvector(ov[db][g], bf16x4);
+      }
   }
 }
 
@@ -923,17 +884,10 @@ hipError_t launch_tile_class(int32_t B, const int32_t* offsets, const TimeStat* 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16(int d, const AttnArgs& a, int64_t max_items, hipStream_t stream) {
+hipError_t launch_attn_bf16(int d, const AttnArgs& a, int grid, hipStream_t stream) {
   if (d != 64) return hipErrorInvalidValue;
-  if (max_items <= 0) return hipSuccess;
-  // a persistent grid: two workgroups per compute unit (LDS and registers allow two), never
-  // more than there can be items
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return hipErrorInvalidDevice;
-  const int64_t want = 2 * (int64_t)cus;
-  const dim3 g((unsigned)(max_items < want ? max_items : want)), blk(kThreads);
+  if (grid <= 0) return hipSuccess;
+  const dim3 g(grid), blk(kThreads);
   switch (a.bias.kind * 2 + (a.o_f32 ? 1 : 0)) {
     case 0: hipLaunchKernelGGL((attn_bf16_d64_kernel<0, false>), g, blk, 0, stream, a); break;
     case 1: hipLaunchKernelGGL((attn_bf16_d64_kernel<0, true>), g, blk, 0, stream, a); break;

@@ -136,9 +136,6 @@ struct AttnArgs {
   const int32_t* offsets;
   const int32_t* work_count;
   const WorkItem* work;
-  int32_t* queue;         // bf16 path: 8 item-queue counters and a finished-workgroup counter,
-                          // zero between launches (the scheduler zeroes them, the last
-                          // workgroup of each launch resets them)
   const void* q;
   const void* k;
   const void* v;
@@ -201,7 +198,7 @@ hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int64_t total_toke
 hipError_t launch_tile_class(int32_t B, const int32_t* offsets, const TimeStat* stats,
                              int32_t max_blocks, int32_t num_pos, int32_t num_time,
                              uint32_t* tclass, hipStream_t stream);
-hipError_t launch_attn_bf16(int d, const AttnArgs& a, int64_t max_items, hipStream_t stream);
+hipError_t launch_attn_bf16(int d, const AttnArgs& a, int grid, hipStream_t stream);
 hipError_t launch_attn_f32(int d, const AttnArgs& a, int grid, hipStream_t stream);
 int attn_block_rows_bf16(int d);
 int attn_block_rows_f32(int d);

@@ -45,8 +45,6 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
     }
     *count_out = pos;
   }
-  // the persistent attention kernel's item-queue counters (header words 4 .. 12)
-  if (tid < 9) count_out[4 + tid] = 0;
   __syncthreads();
   const int n_waves = kSchedThreads / 64;
   for (int c = max_tiles - wave; c >= 1; c -= n_waves) {
