@@ -145,6 +145,82 @@ def bench_stack8(args, dev):
         flush=True)
 
 
+def bench_genrank(args, dev):
+    """The GenRank action-oriented layer at its full size: tokens = item_emb[id] + action_emb[a]
+    (10^6 items, Zipf(1.1) ids, 4 action types, rows of 512 bf16), then one HSTU layer with the
+    ALiBi bias (D = 512, H = 8, d = 64, B = 64 users of 512..4096 events).  One step = the
+    token gather-sum + the layer (f1 GEMM + SiLU + split, attention, LayerNorm-gate-f2)."""
+    import numpy as np
+    import torch
+    from hstu_sequential_transduction_jagged_amd import binding, synth
+    g = synth.genrank()
+    L = g.layers[0]
+    bf = torch.bfloat16
+    t = lambda a, d=None: torch.from_numpy(np.ascontiguousarray(a)).to(dev, d) if d else \
+        torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    item_table = t(g.item_table, bf)
+    action_table = t(g.action_table, bf)
+    ids = t(g.item_ids.astype(np.int32))
+    aids = t(g.action_ids.astype(np.int32))
+    offs = t(g.offsets.astype(np.int32))
+    w1, w2 = t(L.w1, bf), t(L.w2, bf)
+    b1, b2, gamma, beta = t(L.b1), t(L.b2), t(L.gamma), t(L.beta)
+    bias = binding.make_bias(binding.BIAS_ALIBI)
+    D, T = g.D, int(g.T)
+    x = torch.empty((T, D), dtype=bf, device=dev)
+    y = torch.empty((T, D), dtype=bf, device=dev)
+    ws = torch.empty(binding.layer_workspace_bytes(g.B, T, D, g.H, g.dqk, g.dv, g.max_seqlen),
+                     dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        binding.hstu_embed_sum_fwd(item_table, action_table, ids, aids, out=x)
+        if ev is not None:
+            ev[1].record()
+        binding.hstu_layer_fwd(x, offs, g.max_seqlen, w1, b1, gamma, beta, w2, b2, g.H, g.dqk,
+                               g.dv, bias, g.alpha, False, g.ln_eps, out=y, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    emb_s = float(np.mean([a.elapsed_time(b) for a, b, _ in evs])) / 1e3
+    layer_s = float(np.mean([b.elapsed_time(c) for _, b, c in evs])) / 1e3
+    lengths = np.diff(g.offsets.astype(np.int64))
+    N1 = 2 * g.H * (g.dqk + g.dv)
+    attn = causal_flops(lengths, g.H, g.dqk, g.dv)
+    gemm = 2.0 * T * D * N1 + 2.0 * T * g.H * g.dv * D
+    flops = attn + gemm
+    # token construction: the item row read, the output row written, two int32 ids per token
+    # (the four action rows stay in cache)
+    emb_bytes = T * (D * 2 + D * 2 + 8)
+    print(json.dumps({
+        "metric": "GenRank layer forward TFLOP/s (attention causal FLOPs + f1/f2 GEMM FLOPs)",
+        "value": round(flops / step_s / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "genrank", "B": g.B, "D": D, "H": g.H, "d_qk": g.dqk,
+                   "d_v": g.dv, "T": T, "max_len": int(lengths.max()), "n_items": 1000000,
+                   "n_actions": 4, "bias": "alibi slopes 2^(-8(h+1)/H)", "alpha": g.alpha,
+                   "seed": g.seed},
+        "tokens_per_s": round(T / step_s, 1),
+        "pct_of_bf16_peak": round(100.0 * flops / step_s / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "layer_ms": round(layer_s * 1e3, 4),
+        "embed_sum": {"ms": round(emb_s * 1e3, 4), "bytes": emb_bytes,
+                      "GB_per_s": round(emb_bytes / emb_s / 1e9, 1),
+                      "frac_of_hbm_peak": round(emb_bytes / emb_s / 8e12, 4)},
+        "attention_causal_flop": attn, "gemm_flop": gemm}), flush=True)
+
+
 def bench_attn_bwd(args, dev):
     """Gradients of the attention on the attn_long batch (dq, dk, dv and the position / time
     table gradients for a random upstream gradient); one step = one hstu_attn_bwd call."""
@@ -412,13 +488,14 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8", "mfalcon", "attn_bwd", "sl", "layer_bwd"],
+    ap.add_argument("--workload", default="attn_long", choices=["attn_long", "stack8", "mfalcon", "attn_bwd", "sl", "layer_bwd", "genrank"],
                     help="attn_long (the headline attention batch), stack8 (the 8-layer HSTU "
                          "stack forward: f1 GEMM + SiLU, attention, LayerNorm-gate-f2, residual) "
                          "mfalcon (1024 candidates per user scored over cached histories) or "
                          "attn_bwd (the attention's gradients on the attn_long batch), sl "
-                         "(Stochastic Length on the stack's batch) or layer_bwd (one stack "
-                         "layer's gradients)")
+                         "(Stochastic Length on the stack's batch), layer_bwd (one stack "
+                         "layer's gradients) or genrank (item + action tokens and one ALiBi "
+                         "layer at the GenRank size)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the HBM byte counters against a known traffic)")
@@ -463,6 +540,9 @@ def main():
         return
     if args.workload == "layer_bwd":
         bench_layer_bwd(args, dev)
+        return
+    if args.workload == "genrank":
+        bench_genrank(args, dev)
         return
     inp = synth.attn_long()
     lengths = np.diff(inp.offsets.astype(np.int64))

@@ -228,6 +228,7 @@ struct __attribute__((aligned(16))) SmemBf16 {
   float wposx[kMaxPosBuckets + 96];  // -log2(e) * w_pos[h][clamp(i - j, 0, P - 1)] at i - j + 32
   float wtime[kMaxTimeBuckets]; // -log2(e) * w_time[h]
   float wtime_lz[32];           // wtime[min(31 - lz, NT - 1)]: time bias by leading zeros of dt + 1
+  int32_t need[kWaves];         // ALiBi: the lowest 32-key block each wave still needs
 };
 
 template <int KIND, bool OUT_F32>
@@ -296,8 +297,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   const uint32_t roff = wave == 0 ? 4u * lane
                       : wave == 2 ? 4u * (uint32_t)H * (uint32_t)lane
                                   : 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3);
-  auto dma = [&](Stage& stg, int t) __attribute__((always_inline)) {
-    const bool real = t < n_tiles;
+  // tiles are visited in steps k = 0, 1, ..., n_loop - 1: upwards from the first key tile, or,
+  // with ALiBi, downwards from the diagonal (so that the far tiles, whose weights the bias
+  // drives below any fp32 resolution, come last and can be cut off; see kAlibiFarY)
+  int n_loop = n_tiles;
+  auto tix = [&](int k) { return KIND == 2 ? n_tiles - 1 - k : k; };
+  auto dma = [&](Stage& stg, int k) __attribute__((always_inline)) {
+    const bool real = k < n_loop;
+    const int t = tix(real ? k : 0);
     const uint32_t j0 = (uint32_t)(t * kKB);
     const uint32_t ksoff = __builtin_amdgcn_readfirstlane(real ? j0 * kstride_b : 0x7fffffffu);
     const uint32_t vsoff = __builtin_amdgcn_readfirstlane(real ? j0 * vstride_b : 0x7fffffffu);
@@ -386,6 +393,31 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   const int vtr_row0 = 4 * hf + ((lane & 15) >> 2);
   const int vtr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const float neg_slope_y = -slope_y, alibi_lane = slope_y * (float)lv;
+  if (KIND == 2) {
+    // The far cut.  With y = slope_y (i - j) - log2(e) alpha s and |log2(e) alpha s| <= D_w =
+    // qbound max|k| (max over the user's key blocks up to the item's last row), every pair of
+    // this wave at distance i - j >= L_w = (kAlibiFarY + D_w) / slope_y has y >= kAlibiFarY.
+    // The wave's lowest needed 32-key block is the first whose nearest pair is closer than L_w.
+    int need = 0x7fffffff;  // a wave without rows needs nothing
+    if (qw0 <= wq_last) {
+      need = 0;
+      if (slope_y > 0.f) {
+        float km = 0.f;
+        const int nkb = (q_end + 31) / 32;
+        const int64_t krow0 = tclass_row0(tok0, b);
+        for (int jb = lane; jb < nkb; jb += 64) km = fmaxf(km, a.knorm[(krow0 + jb) * H + h]);
+        const float dw = qbound * sqrtf(wave_max(km)) * 1.0001f;
+        const float lf = (kAlibiFarY + dw) / slope_y;
+        if (lf < (float)(qw0 - 31)) {
+          // blocks jb with qw0 - (32 jb + 31) >= L_w are cut: jb <= (qw0 - 31 - L_w) / 32
+          const int lcut = (int)ceilf(lf * 1.0001f) + 1;
+          const int jcut = qw0 - 31 - lcut;
+          need = jcut >= 0 ? jcut / 32 + 1 : 0;
+        }
+      }
+    }
+    if (lane == 0) sm.need[wave] = uniform_i32(need);
+  }
 
   f32x16 oacc[2];
 #pragma unroll
@@ -415,12 +447,17 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
     for (int hk = 0; hk < 2; ++hk) {
       const int j0h = j0 + 32 * hk;
       if (j0h > wq_last || wq_last < qw0) continue;  // past the diagonal, or the wave has no rows
+      const float kn2 = uniform_f32(stg.kn[hk]);
+      if (KIND == 2) {
+        // far tile: y >= slope_y (qw0 - j0h - 31) - qbound |k| >= kAlibiFarY for every pair
+        const float room = slope_y * (float)(qw0 - j0h - 31) - kAlibiFarY;
+        if (room > 0.f && room * room >= 1.0002f * qbound * qbound * kn2) continue;
+      }
       // K operands of this 32-key step (V operands are read after the SiLU)
       bf16x8 kop[4], vop[2][2];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         kop[ks] = *(const bf16x8*)((const char*)stg.k + 32 * hk * 128 + (kbase ^ (32u * ks)));
-      const float kn2 = uniform_f32(stg.kn[hk]);
       const bool diag = (j0h + 31) > qw0;
       // i - j of register r = dlt + lv - kc(r): a lane term, a tile term and a constant
       const int dlt = qw0 - j0h;
@@ -458,7 +495,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
              : (room >= 0.f && D2 <= room * room) ? kPoly : kExact;
       } else {
         mode = 3;
-        const float room = kPolyRange - slope_y * (float)max(qw0 + 31 - j0h, 0);
+        // |bias| <= |slope_y| (i - j) <= |slope_y| (qw0 + 31 - j0h) over the tile (any sign of slope)
+        const float room = kPolyRange - fabsf(slope_y) * (float)max(qw0 + 31 - j0h, 0);
         path = (room >= 0.f && qbound * qbound * kn2 <= room * room) ? kPoly : kExact;
       }
 
@@ -579,19 +617,27 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   // wave's transfers are waited for and the barrier publishes them to all
   wait_vm<0>();
   lds_barrier();
-  auto pair = [&](const Stage& c0, const Stage& c1, Stage& n0, Stage& n1, int t) __attribute__((always_inline)) {
-    dma(n0, t + 2);
-    dma(n1, t + 3);
+  if (KIND == 2) {
+    // the workgroup stops below the lowest block any wave needs (64-key tile = two blocks)
+    int nb = sm.need[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) nb = min(nb, sm.need[w]);
+    const int t_low = min(nb / 2, n_tiles);
+    n_loop = uniform_i32(n_tiles - t_low);
+  }
+  auto pair = [&](const Stage& c0, const Stage& c1, Stage& n0, Stage& n1, int k) __attribute__((always_inline)) {
+    dma(n0, k + 2);
+    dma(n1, k + 3);
     __builtin_amdgcn_sched_barrier(0);
-    compute(c0, t);
-    if (t + 1 < n_tiles) compute(c1, t + 1);
+    compute(c0, tix(k));
+    if (k + 1 < n_loop) compute(c1, tix(k + 1));
     wait_vm<0>();
     lds_barrier();
   };
-  for (int t = 0; t < n_tiles; t += 4) {
-    pair(st0, st1, st2, st3, t);
-    if (t + 2 >= n_tiles) break;
-    pair(st2, st3, st0, st1, t + 2);
+  for (int k = 0; k < n_loop; k += 4) {
+    pair(st0, st1, st2, st3, k);
+    if (k + 2 >= n_loop) break;
+    pair(st2, st3, st0, st1, k + 2);
   }
   // the transfers past the last tile land before the kernel ends
   wait_vm<0>();

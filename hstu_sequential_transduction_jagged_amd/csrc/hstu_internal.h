@@ -72,6 +72,7 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
+__device__ __forceinline__ int uniform_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ float uniform_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(uint32_t, v)));
 }
@@ -95,6 +96,12 @@ constexpr int64_t kTMin = -kTMax - 1;
 // is at most max|w'''| D^3 / 6 = 0.0521 D^3 <= 8.4e-5 D, below 2^-13 of the tile's largest
 // |w| (which is at least 0.96 D for D this small).
 constexpr float kTaylorD = 0.04f;
+
+// ALiBi far cut: pairs whose base-2 SiLU argument is provably y >= kAlibiFarY are skipped.  w(y)
+// decreases for y > 1 / ln 2, so each skipped weight is below w(64) = 128 / (1 + 2^64) < 7e-18
+// (SiLU below 2.5e-18): a user of n keys loses at most 2.5e-18 n max|v| per output, far below
+// the fp32 resolution of any output that a key within reach contributes to.
+constexpr float kAlibiFarY = 64.0f;
 
 // w(y) = 2y/(1+2^y) and its first two derivatives at c, as the coefficients of the expansion
 // in the raw score s (y = c + cq s): w ~ a0 + a1 s + a2 s^2.  No overflow for any finite c:

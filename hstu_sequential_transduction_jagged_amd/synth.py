@@ -37,12 +37,20 @@ def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns
     float32 values that are exactly representable in bfloat16."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    nan = np.isnan(a)
-    out = r.astype(np.uint32).view(np.float32).copy()
-    out[nan] = np.nan
+    out = np.empty_like(a)
+    u = a.reshape(-1).view(np.uint32)
+    o = out.reshape(-1).view(np.uint32)
+    step = 1 << 22
+    for s in range(0, u.size, step):
+        x = u[s:s + step]
+        # add 0x7FFF plus the lowest kept bit, then clear the low half: nearest, ties to even.
+        # In uint32 this wraps only for bit patterns of negative NaNs, which are reset below.
+        r = (x >> 16) & 1
+        r += 0x7FFF
+        r += x
+        r &= 0xFFFF0000
+        o[s:s + step] = r
+    out[np.isnan(a)] = np.nan
     return out
 
 

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from hstu_sequential_transduction_jagged_amd import binding, synth
 from tests.hstu_testutil import (TOL, DevAttn, err_rms, err_stored, oracle_attn, oracle_attn_rows,
                                  run_attn, schedule_reference, to_dev)
@@ -89,6 +90,39 @@ def test_bf16_unsorted_timestamps_and_huge_gaps():
     inp.ts = ts
     _check(inp)
 
+
+
+@pytest.mark.parametrize("slopes", ["default", "mixed"])
+@pytest.mark.parametrize("alpha", [1.0 / 4096, 1.0 / 8.0])
+def test_bf16_alibi_far_cut(alpha, slopes):
+    """ALiBi with users long enough that most key blocks lie where the bias alone puts the
+    base-2 SiLU argument beyond 64 (the kernel skips those pairs: each weighs < 7e-18).  The
+    nonlinear alpha makes the score part of the bound large (D up to ~20), so a cut that ignored
+    it would drop pairs that matter; the mixed slopes include 0 and a negative slope (nothing may
+    be cut), 2 and 4 (everything beyond ~45 / ~23 keys is cut).  A quarter of the keys carry
+    values 8 times the others', so a pair cut too early shows in the output.
+    Bound: 2e-2 for the default slopes; with a zero or negative slope thousands of same-sign
+    weights of order one add up, and rounding the weights alone to bf16 (the matrix cores'
+    operand) costs more than 2e-2, so the mixed case is held to max(2e-2, 1.5 e_m), e_m the
+    error of the oracle with only its weights rounded so (oracle.attention(weight_unit=...))."""
+    inp = _case("bf16", [1200, 700, 300, 65, 1] if slopes == "mixed" else [3000, 1500, 700, 65, 1],
+                H=8, kind=synth.BIAS_ALIBI, alpha=alpha)
+    rng = np.random.default_rng(11)
+    inp.v = synth.round_bf16(inp.v * rng.choice([1.0, 8.0], size=(inp.T, 1, 1)).astype(np.float32))
+    if slopes == "default":
+        _check(inp)
+        return
+    inp.bias.slopes = np.array([4.0, 0.5, 0.0, -0.002, 2.0, 0.03, 1.0, 0.125], np.float32)
+    o = run_attn(inp)
+    ref = oracle_attn(inp)
+    b = oracle.Bias(oracle.BIAS_ALIBI, slopes=inp.bias.slopes)
+    mir = oracle.attention(inp.offsets, inp.q, inp.k, inp.v, b, inp.alpha,
+                           weight_unit=-np.log(2.0) / 2.0)
+    e, em = err_stored(o, ref, "bf16"), err_stored(mir, ref, "bf16")
+    bound = max(TOL["bf16"], 1.5 * em)
+    print("alibi mixed slopes T=%d err=%.3g (bf16 weights alone %.3g, bound %.3g)"
+          % (inp.T, e, em, bound), flush=True)
+    assert e <= bound, (e, bound)
 
 def test_attn_long_workload_sampled_rows():
     """The long-sequence bf16 workload at full size (16 users up to 8192 tokens, H=8), checked

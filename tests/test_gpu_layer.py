@@ -108,6 +108,43 @@ def test_genrank_layer_small():
     assert e <= TOL["bf16"]
 
 
+
+def test_genrank_full_size_sampled_users():
+    """The GenRank configuration at its full size, as its benchmark runs it: 64 users of
+    512..4096 events, tokens = item_emb[id] + action_emb[a] over 10^6 items (Zipf(1.1) ids) and
+    4 actions, rows of 512; then one layer with the ALiBi bias (D = 512, H = 8, d = 64).  The
+    token sums are compared bit for bit on every row with the fp32 sum of the two bf16 rows
+    rounded once; the layer output on three users (the shortest, a median one, the longest)
+    with the oracle run on those users alone (a layer acts on each user independently)."""
+    g = synth.genrank(randomize_affine=True)
+    it = to_dev(g.item_table, torch.bfloat16)
+    ac = to_dev(g.action_table, torch.bfloat16)
+    x = binding.hstu_embed_sum_fwd(it, ac, to_dev(g.item_ids.astype(np.int32)),
+                                   to_dev(g.action_ids.astype(np.int32)))
+    d = DevLayer(g)
+    y = d.run_layer(x)
+    torch.cuda.synchronize()
+    xs = (torch.from_numpy(g.item_table[g.item_ids]) +
+          torch.from_numpy(g.action_table[g.action_ids])).to(torch.bfloat16)
+    assert torch.equal(x.cpu(), xs)
+    print("genrank tokens: %d x %d bit-exact" % tuple(xs.shape), flush=True)
+    xr = xs.float().numpy()
+    del it, xs
+    yy = y.float().cpu().numpy()
+    lengths = np.diff(g.offsets.astype(np.int64))
+    order = np.argsort(lengths, kind="stable")
+    L = g.layers[0]
+    for b in sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])}):
+        s, e = int(g.offsets[b]), int(g.offsets[b + 1])
+        ref = oracle.layer(np.array([0, e - s]), xr[s:e], L.w1, L.b1, L.gamma, L.beta, L.w2,
+                           L.b2, oracle_bias(L.bias, g.ts[s:e], g.H), g.alpha, g.H, g.dqk, g.dv,
+                           residual=g.residual, ln_eps=g.ln_eps)
+        err = err_stored(yy[s:e], ref, "bf16")
+        print("genrank user %d (%d rows): err=%.3g (without storage allowance %.3g)"
+              % (b, e - s, err, err_rms(yy[s:e], ref)), flush=True)
+        assert err <= TOL["bf16"], (b, err)
+
+
 def test_stack_small():
     inp = synth.stack8(B=12, n_layers=3, hi=1500, randomize_affine=True)
     d = DevLayer(inp)
