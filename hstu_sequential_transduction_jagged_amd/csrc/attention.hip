@@ -440,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
     }
   }
 
-  enum { kExact = 0, kPoly = 1, kTaylor = 2 };
+  enum { kExact = 0, kPoly = 1, kTaylor = 2, kFar = 3 };
   auto compute = [&](const Stage& stg, int t) __attribute__((always_inline)) {
     const int j0 = t * kKB;
 #pragma unroll
@@ -498,6 +498,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
         // |bias| <= |slope_y| (i - j) <= |slope_y| (qw0 + 31 - j0h) over the tile (any sign of slope)
         const float room = kPolyRange - fabsf(slope_y) * (float)max(qw0 + 31 - j0h, 0);
         path = (room >= 0.f && qbound * qbound * kn2 <= room * room) ? kPoly : kExact;
+        // far from the diagonal with a positive slope: y >= slope_y (qw0 - j0h - 31) - D >= 16,
+        // where with e = 2^-y the exact w = 2 y e / (1 + e) is 2 y e to a relative 2^-16
+        const float fy = slope_y * (float)(qw0 - j0h - 31) - kFarExpY;
+        if (fy > 0.f && fy * fy >= 1.0002f * qbound * qbound * kn2) path = kFar;
       }
 
       // S^T tile: rows = keys, columns = this wave's queries
@@ -527,16 +531,33 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
 #pragma unroll
           for (int r = 0; r < 16; ++r) w[r] = w_exact(__builtin_fmaf(sacc[r], cq, c0));
         }
+      } else if (KIND == 2) {
+        // ALiBi: the bias is slope_y (i - j) = base - slope_y kc(r) per register, computed in place
+        const float base = alibi_lane + slope_y * (float)dlt;
+        if (path == kFar) {
+          // far from the diagonal, in z = 1 - y: 2^z = 2 e and w = 2 y e = (1 - z) 2^z, so
+          // w = fma(-z, 2^z, 2^z)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float z = __builtin_fmaf(sacc[r], -cq, __builtin_fmaf(slope_y, (float)kc(r), 1.0f - base));
+            const float e2 = __builtin_amdgcn_exp2f(z);
+            w[r] = __builtin_fmaf(-z, e2, e2);
+          }
+        } else if (path == kPoly) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            w[r] = w_poly(__builtin_fmaf(sacc[r], cq, __builtin_fmaf(neg_slope_y, (float)kc(r), base)));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            w[r] = w_exact(__builtin_fmaf(sacc[r], cq, __builtin_fmaf(neg_slope_y, (float)kc(r), base)));
+        }
       } else {
         // per-element bias (y units), four registers at a time
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 c4;
-          if (KIND == 2) {
-            const float base = alibi_lane + slope_y * (float)dlt;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) c4[i] = __builtin_fmaf(neg_slope_y, (float)kc(4 * g + i), base);
-          } else if (mode == 2) {
+          if (mode == 2) {
             // two time buckets: dt >= 2^thi - 1  <=>  rel_j <= (t_i - kmin) - (2^thi - 1)
             const int lim = tq_rel + dq - ((1 << thi) - 1);
             const i32x4 rel4 = *(const i32x4*)(&stg.krel[32 * hk + 8 * g + 4 * hf]);

@@ -102,6 +102,9 @@ constexpr float kTaylorD = 0.04f;
 // (SiLU below 2.5e-18): a user of n keys loses at most 2.5e-18 n max|v| per output, far below
 // the fp32 resolution of any output that a key within reach contributes to.
 constexpr float kAlibiFarY = 64.0f;
+// Below kFarExpY the exact w(y) = y / (0.5 + 0.5 2^y) is used; from it on (y >= 16) the form
+// 2 y e, e = 2^-y: its ratio to w is 1 + e, a relative error of at most 2^-16.
+constexpr float kFarExpY = 16.0f;
 
 // w(y) = 2y/(1+2^y) and its first two derivatives at c, as the coefficients of the expansion
 // in the raw score s (y = c + cq s): w ~ a0 + a1 s + a2 s^2.  No overflow for any finite c:

@@ -55,3 +55,28 @@ def test_fit_script_reproduces_constants():
     c, err = m.fit(R)
     assert np.allclose(c, P, rtol=1e-6, atol=1e-9), (c, P)
     assert err < 1e-4
+
+
+def _const(name):
+    text = open(SRC).read()
+    return float(re.search(r"\b%s = (-?[0-9.e+-]+)f" % name, text).group(1))
+
+
+def test_far_form_relative_error_bound():
+    """ALiBi tiles whose bound puts every y at or above kFarExpY use w = 2 y e, e = 2^-y, for the
+    exact w = 2 y e / (1 + e): their ratio is 1 + e, a relative error e <= 2^-16."""
+    y0 = _const("kFarExpY")
+    y = np.linspace(y0, 140.0, 400001)
+    e = 2.0 ** -y
+    exact = 2.0 * y * e / (1.0 + e)
+    rel = np.abs(2.0 * y * e - exact) / exact
+    assert y0 >= 16.0 and rel.max() <= 2.0 ** -16 * (1 + 1e-9), rel.max()
+
+
+def test_far_cut_weight_bound():
+    """Pairs with y >= kAlibiFarY are skipped; w decreases for y > 1/ln 2, so each skipped
+    weight is at most w(kAlibiFarY) < 7e-18."""
+    yc = _const("kAlibiFarY")
+    y = np.linspace(yc, 4 * yc, 100001)
+    w = 2.0 * y / (1.0 + 2.0 ** y)
+    assert np.all(np.diff(w) < 0) and w[0] < 7e-18, w[0]
