@@ -58,9 +58,14 @@ struct CandArgs {
   float alpha, out_scale;
 };
 
-// One ring stage: a 64-key tile of K and V (row = key, 64 bf16; the 16-byte chunk c of row r
-// sits at chunk position c ^ (r % 8), so 8 consecutive rows read at one chunk hit 8 distinct
-// bank groups), the keys' timestamps and the two 32-key halves' timestamp extremes.
+// One ring stage: a 64-key tile of K and V (row = key, 64 bf16, unpadded), the keys'
+// timestamps and the two 32-key halves' timestamp extremes.  The 16-byte chunk c of row r sits
+// at chunk position c ^ cswz_r(r), cswz_r(r) = ((r >> 1) & 1) << 2 | ((r >> 2) & 3), which
+// serves all three access patterns without bank conflicts on the 64 banks: the K operand reads
+// (16 lanes read one chunk of 16 consecutive rows: even and odd rows take the two 64-byte
+// halves and cswz_r is a bijection on each), the transposing V reads (32 lanes read chunks
+// 0..3 or 4..7 of 4 consecutive rows: rows r and r + 2 differ in bit 2 of cswz_r) and the
+// transfers (whole rows).  (A plain c ^ (r % 8) leaves the transposing reads conflicted.)
 struct __attribute__((aligned(16))) CandStage {
   __attribute__((aligned(16))) bf16 k[kCKB * kCD];
   __attribute__((aligned(16))) bf16 v[kCKB * kCD];
@@ -68,8 +73,9 @@ struct __attribute__((aligned(16))) CandStage {
   __attribute__((aligned(16))) uint32_t st[128];  // dwords 0..7: TimeStat of halves 0, 1
 };
 
+__device__ __forceinline__ int cswz_r(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 // element offset of (row, 16-byte chunk) in a swizzled tile
-__device__ __forceinline__ int cswz(int row, int chunk) { return row * kCD + ((chunk ^ (row & 7)) << 3); }
+__device__ __forceinline__ int cswz(int row, int chunk) { return row * kCD + ((chunk ^ cswz_r(row)) << 3); }
 
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
 
@@ -122,12 +128,12 @@ __global__ __launch_bounds__(kCThreads, kCWgPerCu) void attn_cand_bf16_kernel(Ca
   const uint32_t kstride_b = (uint32_t)a.kh_stride * 2u, vstride_b = (uint32_t)a.vh_stride * 2u;
   // lane offsets of the K / V transfers: instruction u of wave w fills rows 8 (w + 4 u) ..
   // + 7; lane p writes row 8 (w + 4 u) + p / 8 at chunk position p % 8, i.e. global chunk
-  // (p % 8) ^ (p / 8)
+  // (p % 8) ^ cswz_r(row)
   uint32_t kvo[2], vvo[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const uint32_t row = 8u * (uint32_t)(wave + 4 * u) + (uint32_t)(lane >> 3);
-    const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
+    const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ cswz_r((int)row));
     kvo[u] = row * kstride_b + ch;
     vvo[u] = row * vstride_b + ch;
   }
