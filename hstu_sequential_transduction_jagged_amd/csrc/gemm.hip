@@ -242,6 +242,7 @@ __global__ __launch_bounds__(kF1Threads, 3) void f1_kernel(F1Args g) {
 constexpr int kF2Tok = 64;
 constexpr int kF2K = 32;
 constexpr int kF2Threads = 256;
+constexpr int kF2MaxHeads = 16;  // heads whose statistics f2 combines (H d_v <= 1024, d_v >= 64)
 
 struct F2Args {
   const bf16* O;        // attention output [M][HV]
@@ -286,15 +287,25 @@ __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
     const int64_t t = m0 + srow;
     const int H = g.H;
     const f32x4* st = g.ostats + (t < M ? t : 0) * H;
+    // all heads' entries in one round of loads (at most kF2MaxHeads), then combined
+    float hm[kF2MaxHeads], h2[kF2MaxHeads];
+#pragma unroll
+    for (int hh = 0; hh < kF2MaxHeads; ++hh) {
+      const f32x4 v = hh < H ? st[hh] : f32x4{0.f, 0.f, 0.f, 0.f};
+      hm[hh] = v[1];
+      h2[hh] = v[2];
+    }
     float hq = 0.f, sm = 0.f;
-    for (int hh = 0; hh < H; ++hh) {
-      const f32x4 v = st[hh];
-      sm += v[1];
-      hq += v[2];
+#pragma unroll
+    for (int hh = 0; hh < kF2MaxHeads; ++hh) {
+      sm += hm[hh];
+      hq += h2[hh];
     }
     mean = sm / (float)H;
     float dev = 0.f;
-    for (int hh = 0; hh < H; ++hh) dev += (st[hh][1] - mean) * (st[hh][1] - mean);
+#pragma unroll
+    for (int hh = 0; hh < kF2MaxHeads; ++hh)
+      if (hh < H) dev += (hm[hh] - mean) * (hm[hh] - mean);
     rstd = 1.0f / sqrtf((hq + (float)g.dv * dev) / (float)HV + g.eps);
   }
   // each head's offset m (O stores value - m), read per slice: slice kt lies in head kt kF2K / dv
@@ -543,7 +554,7 @@ hipError_t launch_ln_gate_f2(const bf16* o, const f32x4* ostats, const bf16* u,
                              const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,
                              int32_t D, int32_t H, int32_t dv, hipStream_t stream) {
   const int32_t HV = H * dv;
-  if (D % 128 || D <= 0 || HV % (2 * kF2K) || HV <= 0 || u_stride % 8 || u_stride < HV)
+  if (D % 128 || D <= 0 || HV % (2 * kF2K) || HV <= 0 || u_stride % 8 || u_stride < HV || H > kF2MaxHeads)
     return hipErrorInvalidValue;
   if ((int64_t)kF2Tok * 2 * u_stride > 0x7fffffff || (int64_t)512 * 2 * HV > 0x7fffffff)
     return hipErrorInvalidValue;
