@@ -105,18 +105,16 @@ def bench_stack8(args, dev):
                            bias=binding.make_bias(binding.BIAS_RAB_PT, ts, t(L.bias.w_pos),
                                                   t(L.bias.w_time))))
     D = x0.shape[1]
-    ws = torch.empty(binding.layer_workspace_bytes(inp.B, inp.T, D, inp.H, inp.dqk, inp.dv,
+    ws = torch.empty(binding.stack_workspace_bytes(inp.B, inp.T, D, inp.H, inp.dqk, inp.dv,
                                                    inp.max_seqlen), dtype=torch.uint8, device=dev)
-    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+    y = torch.empty_like(x0)
 
     def step():
-        h = x0
-        for li, L in enumerate(layers):
-            h = binding.hstu_layer_fwd(h, offs, inp.max_seqlen, L["w1"], L["b1"], L["gamma"],
-                                       L["beta"], L["w2"], L["b2"], inp.H, inp.dqk, inp.dv,
-                                       L["bias"], inp.alpha, True, inp.ln_eps, out=bufs[li % 2],
-                                       workspace=ws)
-        return h
+        # all 8 layers in one call; with --fuse-boundaries each layer's LN-gate-f2 and the next
+        # layer's f1 run as one kernel
+        return binding.hstu_stack_fwd(x0, offs, inp.max_seqlen, layers, inp.H, inp.dqk, inp.dv,
+                                      inp.alpha, True, inp.ln_eps,
+                                      fuse_boundaries=args.fuse_boundaries, out=y, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -137,7 +135,8 @@ def bench_stack8(args, dev):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "stack8", "B": inp.B, "layers": len(layers), "D": D, "H": inp.H,
+        "config": {"workload": "stack8", "fused_boundaries": bool(args.fuse_boundaries),
+                   "B": inp.B, "layers": len(layers), "D": D, "H": inp.H,
                    "d_qk": inp.dqk, "d_v": inp.dv, "T": T, "max_len": int(lengths.max()),
                    "bias": "rab_pt P=256 NT=32", "alpha": inp.alpha, "seed": inp.seed},
         "tokens_per_s": round(T / step_s, 1),
@@ -496,6 +495,9 @@ def main():
                          "(Stochastic Length on the stack's batch), layer_bwd (one stack "
                          "layer's gradients) or genrank (item + action tokens and one ALiBi "
                          "layer at the GenRank size)")
+    ap.add_argument("--fuse-boundaries", action="store_true",
+                    help="stack8: run each layer's LayerNorm-gate-f2 and the next layer's f1 as one "
+                         "kernel (the single-operator form between attentions)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB five times "
                          "(calibrates the HBM byte counters against a known traffic)")

@@ -55,6 +55,9 @@ SIGNATURES = {
     "hstu_layer_fwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _P, _P, _P,
                               _P, _f32, _P, _P, ctypes.POINTER(HstuBias), _f32, _i32, _P, _P, _sz,
                               _P]),
+    "hstu_stack_workspace_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32, _i32]),
+    "hstu_stack_fwd": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _P, _i32, _i64, _P, _P, _P,
+                              _P, _P, _f32, _P, _P, _P, _f32, _i32, _i32, _P, _P, _sz, _P]),
     "hstu_layer_workspace_offsets": (None, [_i64, _i32, _i32, _i32, ctypes.POINTER(_sz),
                                             ctypes.POINTER(_sz), ctypes.POINTER(_sz),
                                             ctypes.POINTER(_sz)]),
@@ -316,6 +319,43 @@ def hstu_layer_fwd(x, offsets, max_seqlen, w1, b1, ln_gamma, ln_beta, w2, b2, H,
                               _ptr(b2), ctypes.byref(bias), float(alpha), int(bool(residual)),
                               _ptr(out), _ptr(workspace), workspace.numel(), _stream(x.device))
     _check("hstu_layer_fwd", st)
+    return out
+
+
+def stack_workspace_bytes(B, T, D, H, dqk, dv, max_seqlen):
+    return int(lib().hstu_stack_workspace_bytes(B, T, D, H, dqk, dv, max_seqlen))
+
+
+def hstu_stack_fwd(x, offsets, max_seqlen, layers, H, dqk, dv, alpha=1.0, residual=False,
+                   ln_eps=1e-5, fuse_boundaries=False, out=None, workspace=None):
+    """A stack of HSTU layers (bf16).  layers: a list of dicts with w1, b1, gamma, beta, w2, b2
+    (device tensors or None as for hstu_layer_fwd) and bias (HstuBias or None).  With
+    fuse_boundaries, each f2 and the next layer's f1 run as one kernel (d_model = 512).
+    Returns y [T, D]."""
+    if x.dtype != torch.bfloat16:
+        raise HstuError("the layer runs in bf16")
+    T, D = x.shape
+    B = offsets.numel() - 1
+    n = len(layers)
+    if out is None:
+        out = torch.empty((T, D), dtype=x.dtype, device=x.device)
+    need = stack_workspace_bytes(B, T, D, H, dqk, dv, max_seqlen)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    biases = [L.get("bias") if L.get("bias") is not None else make_bias(BIAS_NONE) for L in layers]
+    for L in layers:
+        for name in ("w1", "w2", "b1", "b2", "gamma", "beta"):
+            t = L.get(name)
+            if t is not None and not t.is_contiguous():
+                raise HstuError("%s must be contiguous" % name)
+    arr = lambda key: (_P * n)(*[_ptr(L.get(key)) for L in layers])
+    bias_arr = (ctypes.POINTER(HstuBias) * n)(*[ctypes.pointer(b) for b in biases])
+    st = lib().hstu_stack_fwd(DTYPE_BF16, B, n, D, H, dqk, dv, _ptr(offsets), int(max_seqlen), T,
+                              _ptr(x), arr("w1"), arr("b1"), arr("gamma"), arr("beta"),
+                              float(ln_eps), arr("w2"), arr("b2"), bias_arr, float(alpha),
+                              int(bool(residual)), int(bool(fuse_boundaries)), _ptr(out),
+                              _ptr(workspace), workspace.numel(), _stream(x.device))
+    _check("hstu_stack_fwd", st)
     return out
 
 

@@ -358,6 +358,109 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
                                out_scale, o, workspace, workspace_bytes, stream);
 }
 
+// ---- a stack of layers, with the f2 / next f1 boundary fused or not ----
+size_t hstu_stack_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_model, int32_t H,
+                                  int32_t d_qk, int32_t d_v, int32_t max_seqlen) {
+  const size_t lw = hstu_layer_workspace_bytes(B, total_tokens, d_model, H, d_qk, d_v, max_seqlen);
+  if (!lw || total_tokens < 0) return 0;
+  return align256(lw) + 2 * align256((size_t)total_tokens * d_model * 2);
+}
+
+hstu_status hstu_stack_fwd(int32_t dt, int32_t B, int32_t n_layers, int32_t d_model, int32_t H,
+                           int32_t d_qk, int32_t d_v, const int32_t* offsets, int32_t max_seqlen,
+                           int64_t total_tokens, const void* x, const void* const* w1,
+                           const float* const* b1, const float* const* ln_gamma,
+                           const float* const* ln_beta, float ln_eps, const void* const* w2,
+                           const float* const* b2, const hstu_bias* const* bias, float alpha,
+                           int32_t residual, int32_t fuse_boundaries, void* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (n_layers < 1) return fail(HSTU_ERR_INVALID_ARG, "n_layers must be >= 1");
+  if (!w1 || !b1 || !ln_gamma || !ln_beta || !w2 || !b2 || !bias)
+    return fail(HSTU_ERR_INVALID_ARG, "null per-layer argument array");
+  if (dt != HSTU_DTYPE_BF16) return fail(HSTU_ERR_UNSUPPORTED, "the layer runs in bf16 only");
+  if (B < 0 || total_tokens < 0 || d_model < 1 || H < 1 || max_seqlen < 0)
+    return fail(HSTU_ERR_INVALID_ARG, "bad sizes");
+  if (d_qk != d_v || d_qk != 64) return fail(HSTU_ERR_UNSUPPORTED, "layer needs d_qk = d_v = 64");
+  const int32_t N1 = 2 * H * (d_qk + d_v);
+  const int32_t HV = H * d_v;
+  if (d_model % 128 || N1 % 128 || HV % 64 || HV > 1024)
+    return fail(HSTU_ERR_UNSUPPORTED,
+                "layer needs d_model %% 128 == 0, 2H(dqk+dv) %% 128 == 0, H dv <= 1024");
+  if (fuse_boundaries && (d_model != 512 || N1 % 512))
+    return fail(HSTU_ERR_UNSUPPORTED, "the fused boundary needs d_model = 512 and 2H(dqk+dv) %% 512 == 0");
+  if (!(ln_eps > 0.f)) return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be > 0");
+  for (int l = 0; l < n_layers; ++l) {
+    BiasArgs ba;
+    const hstu_status st = check_bias(bias[l], H, &ba);
+    if (st != HSTU_OK) return st;
+    if (!w1[l] || !w2[l]) return fail(HSTU_ERR_INVALID_ARG, "null weight of layer %d", l);
+    if (!aligned16(w1[l]) || !aligned16(w2[l]))
+      return fail(HSTU_ERR_INVALID_ARG, "weights of layer %d must be 16-byte aligned", l);
+  }
+  if (B == 0 || total_tokens == 0) return HSTU_OK;
+  if (!offsets || !x || !y || !workspace) return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(x) || !aligned16(y)) return fail(HSTU_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  if (x == y) return fail(HSTU_ERR_INVALID_ARG, "y may not alias x");
+  const size_t need = hstu_stack_workspace_bytes(B, total_tokens, d_model, H, d_qk, d_v, max_seqlen);
+  if (workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(HSTU_ERR_WORKSPACE, "workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
+                workspace_bytes);
+  const size_t lw = align256(hstu_layer_workspace_bytes(B, total_tokens, d_model, H, d_qk, d_v, max_seqlen));
+  const size_t xb = align256((size_t)total_tokens * d_model * 2);
+  bf16* mid[2] = {(bf16*)((char*)workspace + lw), (bf16*)((char*)workspace + lw + xb)};
+  auto layer_in = [&](int l) -> const bf16* { return l == 0 ? (const bf16*)x : mid[(l - 1) & 1]; };
+  auto layer_out = [&](int l) -> bf16* { return l == n_layers - 1 ? (bf16*)y : mid[l & 1]; };
+  if (!fuse_boundaries) {
+    for (int l = 0; l < n_layers; ++l) {
+      const hstu_status st = hstu_layer_fwd(dt, B, d_model, H, d_qk, d_v, offsets, max_seqlen,
+                                            total_tokens, layer_in(l), w1[l], b1[l], ln_gamma[l],
+                                            ln_beta[l], ln_eps, w2[l], b2[l], bias[l], alpha,
+                                            residual, layer_out(l), workspace, lw, stream);
+      if (st != HSTU_OK) return st;
+    }
+    return HSTU_OK;
+  }
+  size_t zo, oo, so, ao;
+  hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, &zo, &oo, &so, &ao);
+  bf16* z = (bf16*)((char*)workspace + zo);
+  bf16* obuf = (bf16*)((char*)workspace + oo);
+  f32x4* ostats = (f32x4*)((char*)workspace + so);
+  void* aws = (char*)workspace + ao;
+  const size_t aws_bytes = align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens));
+  hstu_status st = check_hip(launch_f1_gemm_silu(layer_in(0), (const bf16*)w1[0], b1[0], z,
+                                                 total_tokens, N1, d_model, stream),
+                             "f1 launch");
+  if (st != HSTU_OK) return st;
+  const bf16* U = z;
+  const bf16* V = z + HV;
+  const bf16* Q = z + 2 * HV;
+  const bf16* K = z + 2 * HV + H * d_qk;
+  st = hstu_attn_plan(HSTU_DTYPE_BF16, B, H, d_qk, offsets, max_seqlen, aws, aws_bytes, stream);
+  if (st != HSTU_OK) return st;
+  for (int l = 0; l < n_layers; ++l) {
+    // the work list depends on the offsets only: planned once; the prepass runs per layer
+    st = attn_planned(HSTU_DTYPE_BF16, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, Q, N1,
+                      K, N1, V, N1, bias[l], alpha, 1.0f, obuf, false, ostats, aws, aws_bytes,
+                      stream);
+    if (st != HSTU_OK) return st;
+    const bf16* res = residual ? layer_in(l) : nullptr;
+    if (l + 1 < n_layers)
+      st = check_hip(launch_ln_gate_f2_f1(obuf, ostats, U, N1, ln_gamma[l], ln_beta[l], ln_eps,
+                                          (const bf16*)w2[l], b2[l], res, layer_out(l),
+                                          (const bf16*)w1[l + 1], b1[l + 1], z, N1, total_tokens,
+                                          d_model, H, d_v, stream),
+                     "fused f2 / f1 launch");
+    else
+      st = check_hip(launch_ln_gate_f2(obuf, ostats, U, N1, ln_gamma[l], ln_beta[l], ln_eps,
+                                       (const bf16*)w2[l], b2[l], res, layer_out(l), total_tokens,
+                                       d_model, H, d_v, stream),
+                     "f2 launch");
+    if (st != HSTU_OK) return st;
+  }
+  return HSTU_OK;
+}
+
 // ---- the attention forward without allocation ----
 // Its workspace is a file-scope device array; each device holds its own copy, whose device
 // address hipGetSymbolAddress gives once per device (the array's name is only a host-side

@@ -260,14 +260,32 @@ struct F2Args {
   int64_t M;
   int32_t N, HV, H, dv;
   int32_t n_begin, n_end;  // output features of this launch, in chunks of 128 NI
+  // fused boundary (FUSE): the next layer's f1, Zn = SiLU(Y W1n^T + b1n) [M][N1n], from the Y
+  // tile kept in LDS
+  const bf16* W1n;      // [N1n][N]
+  const float* b1n;     // [N1n] or null
+  bf16* Zn;
+  int32_t N1n;
 };
 
+// Fused boundary: the Y tile (64 tokens x 512 features, bf16) kept in LDS for the next layer's
+// f1.  16-byte chunk c of row r at c ^ (r & 15), so 16 lanes that read one chunk of 16
+// consecutive rows (1 KiB apart) touch 16 distinct bank groups.
+__device__ __forceinline__ int y_off(int row, int chunk) { return row * 512 + ((chunk ^ (row & 15)) << 3); }
+
 // NI: 32-feature blocks per wave (chunk = 128 NI features)
-template <int NI>
+//
+// FUSE (the single operator between two attentions of a layer stack, NI = 4, N = 512): after Y
+// is stored, the workgroup also keeps its bf16 Y tile in LDS and computes the next layer's
+// Zn = SiLU(Y W1n^T + b1n) for its 64 tokens in 512-feature chunks, streaming W1n through the
+// same staging buffers.  The products run in f1's order (bias first, then 16-deep k-steps in
+// increasing k) and f1's SiLU expression, so Zn is bit-identical to f1 on the stored Y.
+template <int NI, bool FUSE>
 __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
   constexpr int CH = 128 * NI;                  // features per chunk
   constexpr int WEL = CH * kF2K, AEL = kF2Tok * kF2K;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (WEL + AEL)];
+  __shared__ __attribute__((aligned(16))) bf16 sY[FUSE ? kF2Tok * 512 : 8];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int HV = g.HV, N = g.N;
@@ -465,11 +483,121 @@ __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
           v[e] = a0[e] + r8[e];
           v[e + 4] = a1[e] + r8[e + 4];
         }
-        __builtin_amdgcn_raw_buffer_store_b128(
-            __builtin_bit_cast(u32x4, __builtin_convertvector(v, bf16x8)), yrs,
-            (uint32_t)(lr * N + fp + 8 * pc) * 2u, 0, 0);
+        const u32x4 y8 = __builtin_bit_cast(u32x4, __builtin_convertvector(v, bf16x8));
+        __builtin_amdgcn_raw_buffer_store_b128(y8, yrs, (uint32_t)(lr * N + fp + 8 * pc) * 2u, 0, 0);
+        if (FUSE) *(u32x4*)(sY + y_off(lr, (fp >> 3) + pc)) = y8;
       }
       __syncthreads();  // the tile is the next pass's / chunk's staging area
+    }
+  }
+
+  if (FUSE) {
+    // ---- the next layer's f1 on the Y tile: K = 512 in 32-deep slices, W1n through the
+    // staging buffers (rows srow + 64 u, chunk sch), 512 output features per chunk ----
+    constexpr int K1 = 512;
+    const uint32_t kb1 = 2u * K1;
+    const int N1 = g.N1n;
+    const __amdgpu_buffer_rsrc_t b1rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.b1n, (short)0, g.b1n ? 4 * N1 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(g.Zn + m0 * N1), (short)0, (int)min(nrow * N1 * 2, (int64_t)0x7fffffff), 0x00020000);
+    auto sw1 = [&](int buf) { return smem + buf * (WEL + AEL); };
+    for (int n1 = 0; n1 < N1; n1 += CH) {
+      const __amdgpu_buffer_rsrc_t w1rs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(g.W1n + (int64_t)n1 * K1), (short)0, (int)(CH * kb1), 0x00020000);
+      u32x4 wr[2 * NI];
+      auto gload1 = [&](int kt) {
+        const uint32_t k0 = 2u * (uint32_t)kt * kF2K;
+#pragma unroll
+        for (int u = 0; u < 2 * NI; ++u)
+          wr[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                w1rs, (uint32_t)srow * kb1 + 16u * sch + 64u * u * kb1, k0, 0));
+      };
+      auto lstore1 = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < 2 * NI; ++u) *(u32x4*)(sw1(buf) + lofs + 64 * u * kF2K) = wr[u];
+      };
+      // acc[i][j] register r -> feature n1 + 32 NI wave + 32 i + 8 (r / 4) + 4 hf + r % 4, token
+      // 32 j + l32; the accumulators start at the bias
+      f32x16 acc[NI][2];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int grp = 0; grp < 4; ++grp) {
+          const f32x4 b4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+              b1rs, 4u * (uint32_t)(n1 + 32 * NI * wave + 4 * hf), 4u * (32 * i + 8 * grp), 0));
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * grp + e] = b4[e];
+        }
+      auto compute1 = [&](int buf, int kt) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 a[NI], b[2];
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+            a[i] = *(const bf16x8*)(sw1(buf) + f1_off(32 * NI * wave + 32 * i + l32, 2 * ks + hf));
+#pragma unroll
+          for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8*)(sY + y_off(32 * j + l32, 4 * kt + 2 * ks + hf));
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+      };
+      constexpr int nk1 = K1 / kF2K;
+      gload1(0);
+      lstore1(0);
+      __syncthreads();
+      for (int kt = 0; kt < nk1; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk1) gload1(kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute1(buf, kt);
+        if (kt + 1 < nk1) lstore1(buf ^ 1);
+        __syncthreads();
+      }
+      // epilogue: SiLU, rounded once, through the fp32 tile as in the f2 part
+      f32x4* tile = (f32x4*)smem;
+      constexpr int GPR = 16 * NI;
+      constexpr int NPC = 64 * 8 * NI / kF2Threads;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if ((wave >> 1) == p) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int lr = 32 * j + l32;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+              for (int grp = 0; grp < 4; ++grp) {
+                const int q = 8 * NI * (wave & 1) + 8 * i + 2 * grp + hf;
+                f32x4 v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float x = acc[i][j][4 * grp + e];
+                  v[e] = x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
+                }
+                tile[lr * GPR + (q ^ (lr & 15))] = v;
+              }
+          }
+        }
+        __syncthreads();
+        const int fp = n1 + 64 * NI * p;
+#pragma unroll
+        for (int k = 0; k < NPC; ++k) {
+          const int c = tid + kF2Threads * k, lr = c / (8 * NI), pc = c % (8 * NI);
+          const f32x4 a0 = tile[lr * GPR + ((2 * pc) ^ (lr & 15))];
+          const f32x4 a1 = tile[lr * GPR + ((2 * pc + 1) ^ (lr & 15))];
+          const f32x8 v = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(u32x4, __builtin_convertvector(v, bf16x8)), zrs,
+              (uint32_t)(lr * N1 + fp + 8 * pc) * 2u, 0, 0);
+        }
+        __syncthreads();
+      }
     }
   }
 }
@@ -568,16 +696,38 @@ hipError_t launch_ln_gate_f2(const bf16* o, const f32x4* ostats, const bf16* u,
   const int32_t full = D / 512 * 512;
   if (full > 0) {
     g.n_begin = 0; g.n_end = full;
-    hipLaunchKernelGGL(f2_kernel<4>, grid, dim3(kF2Threads), 0, stream, g);
+    hipLaunchKernelGGL((f2_kernel<4, false>), grid, dim3(kF2Threads), 0, stream, g);
   }
   if (D > full) {
     g.n_begin = full; g.n_end = D;
     switch ((D - full) / 128) {
-      case 1: hipLaunchKernelGGL(f2_kernel<1>, grid, dim3(kF2Threads), 0, stream, g); break;
-      case 2: hipLaunchKernelGGL(f2_kernel<2>, grid, dim3(kF2Threads), 0, stream, g); break;
-      default: hipLaunchKernelGGL(f2_kernel<3>, grid, dim3(kF2Threads), 0, stream, g); break;
+      case 1: hipLaunchKernelGGL((f2_kernel<1, false>), grid, dim3(kF2Threads), 0, stream, g); break;
+      case 2: hipLaunchKernelGGL((f2_kernel<2, false>), grid, dim3(kF2Threads), 0, stream, g); break;
+      default: hipLaunchKernelGGL((f2_kernel<3, false>), grid, dim3(kF2Threads), 0, stream, g); break;
     }
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_gate_f2_f1(const bf16* o, const f32x4* ostats, const bf16* u,
+                                int64_t u_stride, const float* gamma, const float* beta, float eps,
+                                const bf16* w2, const float* b2, const bf16* x, bf16* y,
+                                const bf16* w1n, const float* b1n, bf16* zn, int32_t N1n,
+                                int64_t M, int32_t D, int32_t H, int32_t dv, hipStream_t stream) {
+  const int32_t HV = H * dv;
+  if (D != 512 || HV % (2 * kF2K) || HV <= 0 || u_stride % 8 || u_stride < HV || H > kF2MaxHeads ||
+      N1n <= 0 || N1n % 512)
+    return hipErrorInvalidValue;
+  if ((int64_t)kF2Tok * 2 * u_stride > 0x7fffffff || (int64_t)512 * 2 * HV > 0x7fffffff)
+    return hipErrorInvalidValue;
+  if (M <= 0) return hipSuccess;
+  F2Args g{};
+  g.O = o; g.ostats = ostats; g.U = u; g.u_stride = u_stride; g.gamma = gamma; g.beta = beta;
+  g.eps = eps; g.W = w2; g.bias = b2; g.R = x; g.Y = y; g.M = M; g.N = D; g.HV = HV; g.H = H;
+  g.dv = dv; g.n_begin = 0; g.n_end = D;
+  g.W1n = w1n; g.b1n = b1n; g.Zn = zn; g.N1n = N1n;
+  hipLaunchKernelGGL((f2_kernel<4, true>), dim3((unsigned)((M + kF2Tok - 1) / kF2Tok)),
+                     dim3(kF2Threads), 0, stream, g);
   return hipGetLastError();
 }
 

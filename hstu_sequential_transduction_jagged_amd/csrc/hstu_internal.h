@@ -221,6 +221,14 @@ hipError_t launch_ln_gate_f2(const bf16* o, const f32x4* ostats, const bf16* u,
                              int64_t u_stride, const float* gamma, const float* beta, float eps,
                              const bf16* w2, const float* b2, const bf16* x, bf16* y, int64_t M,
                              int32_t D, int32_t H, int32_t dv, hipStream_t stream);
+// The same, fused with the next layer's f1: zn = SiLU(y w1n^T + b1n) [M, N1n] (D = 512,
+// N1n % 512 == 0); zn may be the buffer u lies in (each workgroup reads only its own rows of u
+// before it writes them).
+hipError_t launch_ln_gate_f2_f1(const bf16* o, const f32x4* ostats, const bf16* u,
+                                int64_t u_stride, const float* gamma, const float* beta, float eps,
+                                const bf16* w2, const float* b2, const bf16* x, bf16* y,
+                                const bf16* w1n, const float* b1n, bf16* zn, int32_t N1n,
+                                int64_t M, int32_t D, int32_t H, int32_t dv, hipStream_t stream);
 // Gradients of the bf16 d = 64 attention (attention_bwd.hip).
 struct BwdArgs {
   const int32_t* offsets;

@@ -218,6 +218,31 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
                            int32_t residual, void* y, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* A stack of n_layers HSTU layers (each as hstu_layer_fwd, layer l + 1 taking layer l's y as
+ * its x), the single-operator form of the reading notes' §3.5 available between layers: with
+ * fuse_boundaries nonzero, layer l's LayerNorm, gate, f2 (and residual) and layer l + 1's
+ * f1 + SiLU + split run as one kernel per 64-token tile, the tile's y kept on chip between the
+ * two products (d_model = 512 only; otherwise HSTU_ERR_UNSUPPORTED).  Both forms give identical
+ * bits: the fused kernel takes f1's products in f1's order.  The attention stays a kernel of its
+ * own (it needs every key of a user).
+ *  w1, b1, ln_gamma, ln_beta, w2, b2, bias  host arrays of n_layers per-layer arguments, each
+ *            as for hstu_layer_fwd (device pointers; NULL entries allowed where hstu_layer_fwd
+ *            allows them)
+ *  x, y      device bf16 [T, d_model]; y may not alias x
+ *  workspace >= hstu_stack_workspace_bytes(...), 256-byte aligned: the layer workspace, then two
+ *            bf16 [T, d_model] buffers for the layers in between.
+ *  Errors as for hstu_layer_fwd; n_layers >= 1. */
+size_t hstu_stack_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_model, int32_t H,
+                                  int32_t d_qk, int32_t d_v, int32_t max_seqlen);
+hstu_status hstu_stack_fwd(int32_t dt, int32_t B, int32_t n_layers, int32_t d_model, int32_t H,
+                           int32_t d_qk, int32_t d_v, const int32_t* offsets, int32_t max_seqlen,
+                           int64_t total_tokens, const void* x, const void* const* w1,
+                           const float* const* b1, const float* const* ln_gamma,
+                           const float* const* ln_beta, float ln_eps, const void* const* w2,
+                           const float* const* b2, const hstu_bias* const* bias, float alpha,
+                           int32_t residual, int32_t fuse_boundaries, void* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 /* Gradients of one HSTU layer ("Actions Speak Louder than Words" reading notes §3.1 eqs. (1)-(3))
  * for an upstream gradient dY, after hstu_layer_fwd on the same inputs: fwd_workspace is that
  * call's workspace, whose Z and O it reads (Zpre = X W1^T + b1 is recomputed).  By the chain

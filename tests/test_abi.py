@@ -113,6 +113,23 @@ def test_host_side_errors_need_no_gpu():
     assert L.hstu_layer_fwd(1, 1, 256, 4, 64, 64, None, 8, 8, None, None, None, None, None, 0.0,
                             None, None, None, 1.0, 0, None, None, 0, None) == -1
     assert L.hstu_embed_sum_fwd(4, 12, None, 1, None, 1, None, None, None, None) == -2
+    # the layer stack: per-layer argument arrays required; the fused boundary needs d_model 512
+    P2 = ctypes.c_void_p * 2
+    nul = P2(None, None)
+    bias_none = (ctypes.POINTER(binding.HstuBias) * 2)(ctypes.pointer(binding.make_bias(binding.BIAS_NONE)),
+                                                       ctypes.pointer(binding.make_bias(binding.BIAS_NONE)))
+    def stack(n=2, D=512, fuse=1, arrays=True, w=nul, bias=bias_none, B=1):
+        a = (lambda v: v) if arrays else (lambda v: None)
+        return L.hstu_stack_fwd(1, B, n, D, 8, 64, 64, None, 8, 8, None, a(w), a(nul), a(nul), a(nul),
+                                1e-5, a(w), a(nul), a(bias), 1.0, 1, fuse, None, None, 0, None)
+    assert stack(n=0) == -1
+    assert stack(arrays=False) == -1
+    assert stack(D=256) == -2
+    assert stack(D=256, fuse=0) == -1          # null weights
+    assert stack(w=P2(fake, fake), B=0) == 0   # no work
+    assert stack(w=P2(fake, fake)) == -1       # null x / y / offsets
+    assert L.hstu_stack_workspace_bytes(2, 100, 512, 8, 64, 64, 60) == (
+        L.hstu_layer_workspace_bytes(2, 100, 512, 8, 64, 64, 60) + 2 * 102400)
     # candidate scoring: bf16 and d = 64 only; empty work is OK; strides and pointers checked
     def cand(dt=1, B=1, H=2, d=64, mh=8, mc=4, tc=4, p=None, s=128, s_h=128, ts=None):
         return L.hstu_attn_candidates_fwd(dt, B, H, d, d, p, mh, 100, p, mc, tc, p, s, p, s, p, s,

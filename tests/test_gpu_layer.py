@@ -162,6 +162,49 @@ def test_stack_small():
     assert e <= TOL["bf16"]
 
 
+
+def _stack(d, fuse):
+    inp = d.inp
+    y = binding.hstu_stack_fwd(d.x, d.offsets, inp.max_seqlen, d.layers, inp.H, inp.dqk, inp.dv,
+                               inp.alpha, inp.residual, inp.ln_eps, fuse_boundaries=fuse)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_stack_fused_boundaries_bitwise_and_oracle():
+    """The layer stack entry point with the f2 / next-f1 boundary fused into one kernel
+    ("Actions Speak Louder than Words" reading notes §3.5, the single operator between two
+    attentions): its output equals the three-kernel stack bit for bit (the fused kernel takes
+    f1's products in f1's order) and hstu_layer_fwd applied layer by layer, and is held to the
+    oracle like test_stack_small (3 layers, 12 users with ragged 64-token tiles, residual)."""
+    inp = synth.stack8(B=12, n_layers=3, hi=1500, randomize_affine=True)
+    d = DevLayer(inp)
+    y_fused = _stack(d, True)
+    y_plain = _stack(d, False)
+    h = d.x
+    for li in range(len(inp.layers)):
+        h = d.run_layer(h, li=li)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fused, y_plain)
+    assert torch.equal(y_plain, h)
+    x = inp.x.astype(np.float64)
+    for li in range(len(inp.layers)):
+        x = oracle_layer(inp, x=x, li=li)
+    yy = y_fused.float().cpu().numpy()
+    e = err_stored(yy, x, "bf16")
+    print("fused stack T=%d layers=%d err=%.3g (without storage allowance %.3g)"
+          % (inp.T, len(inp.layers), e, err_rms(yy, x)), flush=True)
+    assert e <= TOL["bf16"]
+
+
+def test_stack8_full_size_fused_equals_unfused():
+    """The 8-layer stack at full size (128 users, T = 80 405): fused and three-kernel boundaries
+    give identical bits."""
+    inp = synth.stack8()
+    d = DevLayer(inp)
+    assert torch.equal(_stack(d, True), _stack(d, False))
+
+
 @pytest.mark.parametrize("D,H", [(640, 12), (384, 2)])
 def test_layer_uneven_widths(D, H):
     """Model widths whose f2 output is not a whole number of 512-feature chunks (640 = 512 + 128,
