@@ -495,6 +495,9 @@ def main():
                          "(Stochastic Length on the stack's batch), layer_bwd (one stack "
                          "layer's gradients) or genrank (item + action tokens and one ALiBi "
                          "layer at the GenRank size)")
+    ap.add_argument("--regime", default="workload", choices=["workload", "nonlinear"],
+                    help="attn_long: the workload's alpha = 1/8192 and tables N(0, 0.02), or "
+                         "alpha = 1/8 with tables N(0, 1) (SiLU far from linear)")
     ap.add_argument("--fuse-boundaries", action="store_true",
                     help="stack8: run each layer's LayerNorm-gate-f2 and the next layer's f1 as one "
                          "kernel (the single-operator form between attentions)")
@@ -546,7 +549,12 @@ def main():
     if args.workload == "genrank":
         bench_genrank(args, dev)
         return
-    inp = synth.attn_long()
+    if args.regime == "nonlinear":
+        # the same batch with alpha = 1/8 and bias tables of std 1: most tiles leave the
+        # two-fma Taylor path for the polynomial or exact SiLU
+        inp = synth.attn_long(alpha=1.0 / 8.0, table_std=1.0)
+    else:
+        inp = synth.attn_long()
     lengths = np.diff(inp.offsets.astype(np.int64))
     bf = torch.bfloat16
     q = torch.from_numpy(inp.q).to(dev, bf)
@@ -610,12 +618,13 @@ def main():
         "config": {"workload": "attn_long", "B": inp.B, "H": inp.H, "d_qk": inp.dqk,
                    "d_v": inp.dv, "N_max": 8192, "max_len": int(lengths.max()), "T": T,
                    "causal_pairs": int(sum(int(n) * (int(n) + 1) // 2 for n in lengths)),
-                   "bias": "rab_pt P=256 NT=32", "alpha": inp.alpha, "seed": inp.seed},
+                   "bias": "rab_pt P=256 NT=32", "alpha": inp.alpha, "seed": inp.seed,
+                   "regime": args.regime},
         "tokens_per_s": round(T / step_s, 1),
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(alg_bytes),
+                     "traffic": traffic_from_profile(alg_bytes) if args.regime == "workload" else None,
                      "kernel": "attn_bf16_d64_kernel", "kernel_ms": round(kern_s * 1e3, 4),
                      "kernel_ms_p10_p50_p90": [round(float(np.percentile(kern_ms, q)), 4)
                                                for q in (10, 50, 90)],
