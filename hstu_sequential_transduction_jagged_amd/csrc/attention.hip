@@ -242,8 +242,8 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   const int l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = a.work[item];
   const int b = wi.b, h = wi.h, H = a.H;
-  const int64_t tok0 = a.offsets[b];
-  const int n = a.offsets[b + 1] - a.offsets[b];
+  const int64_t tok0 = wi.tok0;
+  const int n = wi.n;
   const int q0 = wi.qt * kBR;
   if (q0 >= n) return;
   const int q_end = min(q0 + kBR, n);
@@ -761,8 +761,8 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
   const int l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = a.work[item];
   const int b = wi.b, h = wi.h, H = a.H;
-  const int64_t tok0 = a.offsets[b];
-  const int n = a.offsets[b + 1] - a.offsets[b];
+  const int64_t tok0 = wi.tok0;
+  const int n = wi.n;
   const int q0 = wi.qt * kBRf;
   if (q0 >= n) return;
   const int q_end = min(q0 + kBRf, n);

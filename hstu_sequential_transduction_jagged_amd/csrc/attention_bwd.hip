@@ -162,8 +162,8 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const int l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = a.work[item];
   const int b = wi.b, h = wi.h, H = a.H;
-  const int64_t tok0 = a.offsets[b];
-  const int n = a.offsets[b + 1] - a.offsets[b];
+  const int64_t tok0 = wi.tok0;
+  const int n = wi.n;
   const int q0 = wi.qt * kBRows;
   if (q0 >= n) return;
   const int q_end = min(q0 + kBRows, n);
@@ -370,8 +370,8 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   const int l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = a.work[item];
   const int b = wi.b, h = wi.h, H = a.H;
-  const int64_t tok0 = a.offsets[b];
-  const int n = a.offsets[b + 1] - a.offsets[b];
+  const int64_t tok0 = wi.tok0;
+  const int n = wi.n;
   // the work list orders items by q_tile; this kernel takes key tile (tiles - 1 - q_tile),
   // whose cost (the query tiles at or after it) is the same q_tile + 1
   const int tiles = (n + kBRows - 1) / kBRows;

@@ -124,8 +124,11 @@ __device__ __forceinline__ void w_taylor_coeffs(float c, float cq, float& a0, fl
 }
 
 // One unit of attention work: query tile `qt` of user `b`, head `h`.
+// The user's first token and length ride along, so that a workgroup's first dependent reads
+// (its Q rows, K / V tiles, timestamps) need one round trip to memory, not two.
 struct WorkItem {
-  int32_t b, h, qt, pad;
+  int32_t b, h, qt, n;  // n: the user's length
+  int64_t tok0, pad;    // tok0: the user's first token
 };
 
 struct BiasArgs {

@@ -57,7 +57,8 @@ __global__ __launch_bounds__(kSchedThreads) void schedule_kernel(const int32_t* 
                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
       if (pred) {
         WorkItem* dst = work + start[c] + (int64_t)rank * H;
-        for (int h = 0; h < H; ++h) dst[h] = WorkItem{b, h, c - 1, 0};
+        const int32_t t0 = offsets[b], nb = offsets[b + 1] - t0;
+        for (int h = 0; h < H; ++h) dst[h] = WorkItem{b, h, c - 1, nb, (int64_t)t0, 0};
       }
       count += __popcll(mask);
     }

@@ -100,8 +100,9 @@ size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64
  *  workspace   device, >= hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens),
  *              256-B aligned.
  * Layout of the workspace after the call: int32 item_count at byte 0, then
- * from byte 256 the scheduler's work list, one int32x4 {b, h, q_tile, 0} per
- * item, in launch order (cost = q_tile + 1 descending, then b, h ascending);
+ * from byte 256 the scheduler's work list, one 32-byte entry per item
+ * {int32 b, h, q_tile, n_b (the user's length); int64 first token of user b;
+ * int64 0}, in launch order (cost = q_tile + 1 descending, then b, h ascending);
  * after it (256-aligned) per-token timestamp statistics of the bias, the tile
  * classes and the key norm bounds. */
 hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,

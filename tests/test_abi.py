@@ -36,7 +36,7 @@ def test_status_strings():
 
 def test_workspace_sizes():
     L = binding.lib()
-    # 256-byte header + one 16-byte item per (user, head, 128-row tile), 256-aligned
+    # 256-byte header + one 32-byte item per (user, head, 128-row tile), 256-aligned
     # + per-token timestamp statistics (16 B) and offsets (4 B), each region 256-aligned
     # + tile classes: 8 B per (query block row, key block), (T + 31 B) / 32 + 1 rows of
     #   ceil(max_seqlen / 32) entries
@@ -50,10 +50,10 @@ def test_workspace_sizes():
     def knorm(B, H, T):
         return al(((T + 31 * B) // 32 + 1) * H * 4)
     assert L.hstu_attn_workspace_bytes(16, 8, 8192, 0) == \
-        256 + 16 * 8 * 64 * 16 + tclass(16, 8192, 0) + knorm(16, 8, 0)
+        256 + 16 * 8 * 64 * 32 + tclass(16, 8192, 0) + knorm(16, 8, 0)
     assert L.hstu_attn_workspace_bytes(0, 8, 8192, 0) == 256 + tclass(0, 8192, 0) + knorm(0, 8, 0)
     assert L.hstu_attn_workspace_bytes(16, 8, 8192, 1000) == \
-        256 + 16 * 8 * 64 * 16 + 16128 + 4096 + tclass(16, 8192, 1000) + knorm(16, 8, 1000)
+        256 + 16 * 8 * 64 * 32 + 16128 + 4096 + tclass(16, 8192, 1000) + knorm(16, 8, 1000)
     assert L.hstu_attn_block_rows(1, 64) == 256
     assert L.hstu_attn_block_rows(0, 32) == 128
     assert L.hstu_attn_block_rows(1, 48) == 0

@@ -289,8 +289,13 @@ def test_schedule_bit_exact(dtype, d):
     br = binding.attn_block_rows(binding.DTYPE_BF16 if dtype == "bf16" else binding.DTYPE_F32, d)
     ref = schedule_reference(lengths, H, br, inp.max_seqlen)
     assert count == len(ref)
-    items = w[256:256 + 16 * count].view(np.int32).reshape(count, 4)
+    # 32-byte entries: b, h, q_tile, the user's length (int32), its first token (int64), pad
+    items = w[256:256 + 32 * count].view(np.int32).reshape(count, 8)
     assert [tuple(x[:3]) for x in items] == ref
+    offs = inp.offsets.astype(np.int64)
+    b = items[:, 0]
+    assert np.array_equal(items[:, 3], offs[b + 1] - offs[b])
+    assert np.array_equal(items[:, 4:6].copy().view(np.int64)[:, 0], offs[b])
 
 
 def test_validate_offsets_flags():
