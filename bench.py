@@ -625,7 +625,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(alg_bytes) if args.regime == "workload" else None,
-                     "kernel": "attn_bf16_d64_kernel", "kernel_ms": round(kern_s * 1e3, 4),
+                     "kernel": "attn_bf16_kernel<1, false, 64>", "kernel_ms": round(kern_s * 1e3, 4),
                      "kernel_ms_p10_p50_p90": [round(float(np.percentile(kern_ms, q)), 4)
                                                for q in (10, 50, 90)],
                      "flop_per_launch": flops, "algorithmic_bytes_per_launch": alg_bytes},

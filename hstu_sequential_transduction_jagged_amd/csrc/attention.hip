@@ -132,11 +132,13 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const int32_t* __restri
 // and head h, the largest squared norm of the block's key rows, in fp32 from the bf16 keys,
 // at row tclass_row0(tok0, b) + block.  One workgroup per row of eight waves (the row's user is
 // found by bisection over the offsets; rows between users exit at once); wave w
-// takes heads w, w + 8, ...: lane l sums the squares of half l % 2 of token l / 2's head row,
+// takes heads w, w + 8, ...: lane l sums the squares of half l % 2 of token l / 2's head row
+// (d = 32 or 64 columns),
 // the lane pair adds its halves and the wave's maximum is the bound.  No LDS, no barriers.
 // With timestamps, wave 7 also writes the block's timestamp statistics exactly as
 // time_stats_kernel does (one launch fewer for the position + time bias).
 // ============================================================================================
+template <int D>
 __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict__ offsets,
                                                        int32_t B, const bf16* __restrict__ k,
                                                        int64_t k_stride, int32_t H,
@@ -162,14 +164,14 @@ __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict
   const int blk = (int)blk64;
   const int tok = 32 * blk + (lane >> 1);
   const bool valid = tok < n;
-  const bf16* row = k + (tok0 + tok) * k_stride + 32 * (lane & 1);
+  const bf16* row = k + (tok0 + tok) * k_stride + (D / 2) * (lane & 1);
   float* dst = knorm + r * H;
   for (int h = wave; h < H; h += 8) {
     float acc = 0.f;
     if (valid) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 kv = *(const bf16x8*)(row + (int64_t)h * 64 + 8 * c);
+      for (int c = 0; c < D / 16; ++c) {
+        const bf16x8 kv = *(const bf16x8*)(row + (int64_t)h * D + 8 * c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
@@ -196,10 +198,12 @@ __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict
 }
 
 // ============================================================================================
-// bf16, d = 64: 8 waves x 32 queries = 256 query rows per work item, 64 keys per LDS stage
-// (a ring of four stages filled by direct global -> LDS transfers, one barrier per two tiles),
-// four waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time tables,
-// 2 ALiBi).
+// bf16, d = 32 or 64: 8 waves x 32 queries = 256 query rows per work item, 64 keys per LDS
+// stage (a ring of four stages filled by direct global -> LDS transfers, one barrier per two
+// tiles), four waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time
+// tables, 2 ALiBi), output type and head dim; with d = 32 the stages keep their 128-byte rows
+// and only the first four chunks of each row are fetched and read (two k-steps of the score
+// product, one 32-column block of the output).
 // ============================================================================================
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
@@ -231,8 +235,11 @@ struct __attribute__((aligned(16))) SmemBf16 {
   int32_t need[kWaves];         // ALiBi: the lowest 32-key block each wave still needs
 };
 
-template <int KIND, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) {
+template <int KIND, bool OUT_F32, int D>
+__global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
+  static_assert(D == 32 || D == 64, "head dim");
+  constexpr int NKS = D / 16;  // 16-wide k-steps of the score product
+  constexpr int NDB = D / 32;  // 32-column blocks of the output
   __shared__ SmemBf16 sm;
   __shared__ Stage st0, st1, st2, st3;
   const int item = blockIdx.x;
@@ -268,17 +275,20 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   // halves' key norm bounds, the others nothing (out of range).
   const uint32_t kstride_b = (uint32_t)a.k_stride * 2u, vstride_b = (uint32_t)a.v_stride * 2u;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(kp + tok0 * a.k_stride + (int64_t)h * kD), (short)0,
-      (int)((uint32_t)(q_end - 1) * kstride_b + 2u * kD), 0x00020000);
+      (void*)(kp + tok0 * a.k_stride + (int64_t)h * D), (short)0,
+      (int)((uint32_t)(q_end - 1) * kstride_b + 2u * D), 0x00020000);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(vp + tok0 * a.v_stride + (int64_t)h * kD), (short)0,
-      (int)((uint32_t)(q_end - 1) * vstride_b + 2u * kD), 0x00020000);
+      (void*)(vp + tok0 * a.v_stride + (int64_t)h * D), (short)0,
+      (int)((uint32_t)(q_end - 1) * vstride_b + 2u * D), 0x00020000);
   uint32_t kvo, vvo;
   {
     const int r = 8 * wave + (lane >> 3);
     const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ swz(r));
     kvo = (uint32_t)r * kstride_b + ch;
     vvo = (uint32_t)r * vstride_b + ch;
+    // d = 32: chunks 4..7 of a stage row are never read; their lanes fetch nothing (an offset
+    // past every descriptor's range reads as zeros)
+    if (D == 32 && ch >= 64u) kvo = vvo = 0x80000000u;
   }
   const int64_t crow = tclass_row0(tok0, b) + q0 / 32;
   const int64_t cbase = crow * a.tclass_cols * 8;  // bytes
@@ -324,13 +334,13 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   dma(st1, 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T), unscaled ----
-  bf16x8 qop[4];
+  bf16x8 qop[NKS];
   const int row = qw0 + l32;
   const bool qvalid = row <= wq_last;
   {
-    const bf16* src = qp + (tok0 + row) * a.q_stride + (int64_t)h * kD + 8 * hf;
+    const bf16* src = qp + (tok0 + row) * a.q_stride + (int64_t)h * D + 8 * hf;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
       if (qvalid) raw = *(const u32x4*)(src + 16 * ks);
       qop[ks] = __builtin_bit_cast(bf16x8, raw);
@@ -342,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
   {
     float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bf16x2 pr = {qop[ks][2 * e], qop[ks][2 * e + 1]};
@@ -419,9 +429,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
     if (lane == 0) sm.need[wave] = uniform_i32(need);
   }
 
-  f32x16 oacc[2];
+  f32x16 oacc[NDB];
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
@@ -454,9 +464,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
         if (room > 0.f && room * room >= 1.0002f * qbound * qbound * kn2) continue;
       }
       // K operands of this 32-key step (V operands are read after the SiLU)
-      bf16x8 kop[4], vop[2][2];
+      bf16x8 kop[NKS], vop[NDB][2];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < NKS; ++ks)
         kop[ks] = *(const bf16x8*)((const char*)stg.k + 32 * hk * 128 + (kbase ^ (32u * ks)));
       const bool diag = (j0h + 31) > qw0;
       // i - j of register r = dlt + lv - kc(r): a lane term, a tile term and a constant
@@ -507,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       // S^T tile: rows = keys, columns = this wave's queries
       f32x16 sacc = {};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+      for (int ks = 0; ks < NKS; ++ks)
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks], qop[ks], sacc, 0, 0, 0);
 
       // y = -log2(e) (alpha s + bias); w(y) = 2 y / (1 + 2^y) = -(2 / ln 2) SiLU(alpha s + bias)
@@ -616,7 +626,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
       // k-slots 8 hf .. 8 hf + 7, in the key order of the Pt registers: 4 hf + {0..3} and
       // 8 + 4 hf + {0..3} within the 16-key group m.
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
           bf16x4 half0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -628,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int db = 0; db < 2; ++db)
+        for (int db = 0; db < NDB; ++db)
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[m], oacc[db], 0, 0, 0);
     }
   };
@@ -666,14 +676,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
 
   // ---- epilogue: O^T accumulators -> O rows, scaled by -(ln 2 / 2) out_scale ----
   const float osc = -0.5f * kLn2 * a.out_scale;
-  f32x4 ov[2][4];
+  f32x4 ov[NDB][4];
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int e = 0; e < 4; ++e) ov[db][g][e] = oacc[db][4 * g + e] * osc;
-  const int64_t obase = ((tok0 + row) * H + h) * kD;
+  const int64_t obase = ((tok0 + row) * H + h) * D;
   if (a.ostats && !OUT_F32) {
     // layer mode: each head row is stored as its fp32 mean m plus bf16 deviations from m, so
     // the rounding error scales with the row's spread, not its magnitude (a LayerNorm over the
@@ -682,17 +692,17 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
     // the two halves)
     float sum = 0.f;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sum += ov[db][g][e];
     sum += __shfl_xor(sum, 32, 64);
-    const float m = sum * (1.0f / kD);
-    bf16x4 dv[2][4];
+    const float m = sum * (1.0f / D);
+    bf16x4 dv[NDB][4];
     float ds = 0.f;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         dv[db][g] = __builtin_convertvector(ov[db][g] - m, bf16x4);
@@ -701,10 +711,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
         ds += back[0] + back[1] + back[2] + back[3];
       }
     ds += __shfl_xor(ds, 32, 64);
-    const float md = ds * (1.0f / kD);
+    const float md = ds * (1.0f / D);
     float q = 0.f;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -712,7 +722,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
     q += __shfl_xor(q, 32, 64);
     if (qvalid) {
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           *(bf16x4*)((bf16*)a.o + obase + 32 * db + 8 * g + 4 * hf) = dv[db][g];
@@ -720,7 +730,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_d64_kernel(AttnArgs a) 
     }
   } else if (qvalid) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * db + 8 * g + 4 * hf;
@@ -919,7 +929,7 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
 
 }  // namespace
 
-int attn_block_rows_bf16(int d) { return d == 64 ? kBR : 0; }
+int attn_block_rows_bf16(int d) { return (d == 32 || d == 64) ? kBR : 0; }
 int attn_block_rows_f32(int d) { return (d == 32 || d == 64) ? kBRf : 0; }
 
 hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* ts,
@@ -932,13 +942,19 @@ hipError_t launch_time_stats(int32_t B, const int32_t* offsets, const int64_t* t
 }
 
 hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int64_t total_tokens,
-                           const void* k, int64_t k_stride, int32_t H, float* knorm,
+                           const void* k, int64_t k_stride, int32_t H, int32_t d, float* knorm,
                            const int64_t* ts, TimeStat* stats, int32_t* rel, hipStream_t stream) {
   if (B <= 0 || total_tokens <= 0) return hipSuccess;
   const int64_t rows = (total_tokens + 31 * (int64_t)B) / 32 + 1;
   if (rows > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(key_norm_kernel, dim3((unsigned)rows), dim3(512), 0, stream, offsets, B,
-                     (const bf16*)k, k_stride, H, knorm, ts, stats, rel);
+  if (d == 64)
+    hipLaunchKernelGGL(key_norm_kernel<64>, dim3((unsigned)rows), dim3(512), 0, stream, offsets,
+                       B, (const bf16*)k, k_stride, H, knorm, ts, stats, rel);
+  else if (d == 32)
+    hipLaunchKernelGGL(key_norm_kernel<32>, dim3((unsigned)rows), dim3(512), 0, stream, offsets,
+                       B, (const bf16*)k, k_stride, H, knorm, ts, stats, rel);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -952,18 +968,24 @@ hipError_t launch_tile_class(int32_t B, const int32_t* offsets, const TimeStat* 
 }
 
 hipError_t launch_attn_bf16(int d, const AttnArgs& a, int grid, hipStream_t stream) {
-  if (d != 64) return hipErrorInvalidValue;
+  if (d != 32 && d != 64) return hipErrorInvalidValue;
+  if (a.ostats && d != 64) return hipErrorInvalidValue;  // the layer's O layout is for d = 64
   if (grid <= 0) return hipSuccess;
   const dim3 g(grid), blk(kThreads);
+#define HSTU_ATTN_BF16(K, F)                                                                  \
+  if (d == 64) hipLaunchKernelGGL((attn_bf16_kernel<K, F, 64>), g, blk, 0, stream, a);        \
+  else hipLaunchKernelGGL((attn_bf16_kernel<K, F, 32>), g, blk, 0, stream, a);                \
+  break;
   switch (a.bias.kind * 2 + (a.o_f32 ? 1 : 0)) {
-    case 0: hipLaunchKernelGGL((attn_bf16_d64_kernel<0, false>), g, blk, 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((attn_bf16_d64_kernel<0, true>), g, blk, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((attn_bf16_d64_kernel<1, false>), g, blk, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((attn_bf16_d64_kernel<1, true>), g, blk, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((attn_bf16_d64_kernel<2, false>), g, blk, 0, stream, a); break;
-    case 5: hipLaunchKernelGGL((attn_bf16_d64_kernel<2, true>), g, blk, 0, stream, a); break;
+    case 0: HSTU_ATTN_BF16(0, false)
+    case 1: HSTU_ATTN_BF16(0, true)
+    case 2: HSTU_ATTN_BF16(1, false)
+    case 3: HSTU_ATTN_BF16(1, true)
+    case 4: HSTU_ATTN_BF16(2, false)
+    case 5: HSTU_ATTN_BF16(2, true)
     default: return hipErrorInvalidValue;
   }
+#undef HSTU_ATTN_BF16
   return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ size_t hstu_attn_workspace_bytes(int32_t B, int32_t H, int32_t max_seqlen, int64
 /* Jagged causal pointwise attention, eq. (2) above.
  *  dt          HSTU_DTYPE_BF16 (bf16 in/out, fp32 accumulation), HSTU_DTYPE_BF16_OUT_F32
  *              (bf16 in, fp32 out) or HSTU_DTYPE_F32.
- *  B, H        users and heads; d_qk == d_v in {32, 64} for F32, 64 for BF16.
+ *  B, H        users and heads; d_qk == d_v in {32, 64} (BF16_OUT_F32 included).
  *  offsets     device int32 [B+1]; max_seqlen >= every user length, <= 65536.
  *  q, k, v     device [T, H, d] rows with row strides q_row_stride etc.
  *              (elements between consecutive tokens; >= H*d).

@@ -55,6 +55,7 @@ def test_workspace_sizes():
     assert L.hstu_attn_workspace_bytes(16, 8, 8192, 1000) == \
         256 + 16 * 8 * 64 * 32 + 16128 + 4096 + tclass(16, 8192, 1000) + knorm(16, 8, 1000)
     assert L.hstu_attn_block_rows(1, 64) == 256
+    assert L.hstu_attn_block_rows(1, 32) == 256
     assert L.hstu_attn_block_rows(0, 32) == 128
     assert L.hstu_attn_block_rows(1, 48) == 0
     z, o, st, a = binding.layer_workspace_offsets(1000, 4, 64, 64)
@@ -82,7 +83,8 @@ def test_host_side_errors_need_no_gpu():
     assert _attn(dt=7) == -1
     assert _attn(H=0) == -1
     assert _attn(dqk=64, dv=32) == -2
-    assert _attn(dt=1, dqk=32, dv=32) == -2      # bf16 needs d = 64
+    assert _attn(dt=1, dqk=48, dv=48) == -2      # head dims are 32 and 64
+    assert _attn(dt=1, dqk=32, dv=32) == -1      # d = 32 is supported; null pointers
     assert _attn(max_seqlen=70000) == -2
     bad = binding.HstuBias()
     bad.kind = 9

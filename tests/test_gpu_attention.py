@@ -69,6 +69,53 @@ def test_bf16_ragged(kind, regime):
     _check(inp)
 
 
+@pytest.mark.parametrize("regime", ["workload", "nonlinear"])
+@pytest.mark.parametrize("kind", [synth.BIAS_RAB_PT, synth.BIAS_ALIBI, synth.BIAS_NONE])
+def test_bf16_d32_ragged(kind, regime):
+    # head dim 32 in bf16: two k-steps of the score product and one 32-column output block on
+    # the stages' 128-byte rows; H = 3 so the last head's row ends inside the token's row
+    if regime == "workload":
+        inp = _case("bf16", RAGGED, H=3, d=32, kind=kind, alpha=1.0 / 2048, table_std=0.02)
+    else:
+        inp = _case("bf16", RAGGED, H=3, d=32, kind=kind, alpha=1.0 / np.sqrt(32), table_std=1.0,
+                    P=64, NT=16, per_head=True)
+    _check(inp)
+
+
+def test_bf16_d32_strided_views_bitwise():
+    """Q, K, V as column blocks of one [T, 3 H d + 8] bf16 buffer (row stride 3 H d + 8, as the
+    layer's Z views are) give exactly the contiguous result; the columns between and after the
+    blocks hold large values that must never be read."""
+    inp = _case("bf16", [700, 0, 33, 257], H=3, d=32, alpha=0.05, table_std=0.5)
+    d = DevAttn(inp)
+    ref = d.run()
+    T, H = inp.T, inp.H
+    z = torch.full((T, 3 * H * 32 + 8), 3.0e38, dtype=torch.bfloat16, device="cuda")
+    z[:, 0:H * 32] = d.q.reshape(T, -1)
+    z[:, H * 32:2 * H * 32] = d.k.reshape(T, -1)
+    z[:, 2 * H * 32:3 * H * 32] = d.v.reshape(T, -1)
+    views = [z[:, i * H * 32:(i + 1) * H * 32].view(T, H, 32) for i in range(3)]
+    o = binding.hstu_attn_fwd(views[0], views[1], views[2], d.offsets, inp.max_seqlen, d.bias,
+                              inp.alpha, inp.out_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+    assert torch.isfinite(o.float()).all()
+
+
+def test_bf16_d32_long_users_sampled_rows():
+    """Users of 8 192 and 3 000 rows (every query tile, far key tiles on the Taylor path), H = 4,
+    d = 32, position + time bias; 600 sampled (token, head) rows against the oracle."""
+    inp = _case("bf16", [8192, 3000], H=4, d=32, alpha=1.0 / 8192, table_std=0.02, seed=11)
+    o = run_attn(inp)
+    rng = np.random.default_rng(5)
+    toks = rng.integers(0, inp.T, size=600)
+    heads = rng.integers(0, inp.H, size=600)
+    ref = oracle_attn_rows(inp, toks, heads)
+    e = err_stored(o[toks, heads], ref, "bf16")
+    print("d32 long err=%.3g" % e, flush=True)
+    assert e <= TOL["bf16"], e
+
+
 def test_bf16_per_head_tables_and_small_buckets():
     inp = _case("bf16", [5, 300, 129], H=3, alpha=0.1, table_std=1.0, P=16, NT=6, per_head=True)
     _check(inp)
