@@ -206,7 +206,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
                                 const hstu_bias* bias, float alpha, float out_scale, void* o,
                                 bool o_f32, f32x4* ostats, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream,
-                                AttnPart part = kPrepareAndRun) {
+                                AttnPart part = kPrepareAndRun, bool classes_ready = false) {
   int block_rows = 0;
   hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
   if (st != HSTU_OK) return st;
@@ -244,7 +244,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
                    "key norm launch");
     if (st != HSTU_OK) return st;
   }
-  if (dt == HSTU_DTYPE_BF16 && ba.kind == 1 && part != kRunOnly) {
+  if (dt == HSTU_DTYPE_BF16 && ba.kind == 1 && part != kRunOnly && !classes_ready) {
     st = check_hip(launch_tile_class(B, offsets, tstat, tclass_cols(max_seqlen), ba.num_pos,
                                      ba.num_time, tclass, stream),
                    "tile class launch");
@@ -411,16 +411,9 @@ hstu_status hstu_stack_fwd(int32_t dt, int32_t B, int32_t n_layers, int32_t d_mo
   bf16* mid[2] = {(bf16*)((char*)workspace + lw), (bf16*)((char*)workspace + lw + xb)};
   auto layer_in = [&](int l) -> const bf16* { return l == 0 ? (const bf16*)x : mid[(l - 1) & 1]; };
   auto layer_out = [&](int l) -> bf16* { return l == n_layers - 1 ? (bf16*)y : mid[l & 1]; };
-  if (!fuse_boundaries) {
-    for (int l = 0; l < n_layers; ++l) {
-      const hstu_status st = hstu_layer_fwd(dt, B, d_model, H, d_qk, d_v, offsets, max_seqlen,
-                                            total_tokens, layer_in(l), w1[l], b1[l], ln_gamma[l],
-                                            ln_beta[l], ln_eps, w2[l], b2[l], bias[l], alpha,
-                                            residual, layer_out(l), workspace, lw, stream);
-      if (st != HSTU_OK) return st;
-    }
-    return HSTU_OK;
-  }
+  // The work list depends on the offsets only and the tile classes on the offsets, the
+  // timestamps and the bucket counts: both are computed once and reused by every layer whose
+  // bias still matches; the key norm bounds (and the timestamp statistics) run per layer.
   size_t zo, oo, so, ao;
   hstu_layer_workspace_offsets(total_tokens, H, d_qk, d_v, &zo, &oo, &so, &ao);
   bf16* z = (bf16*)((char*)workspace + zo);
@@ -428,24 +421,36 @@ hstu_status hstu_stack_fwd(int32_t dt, int32_t B, int32_t n_layers, int32_t d_mo
   f32x4* ostats = (f32x4*)((char*)workspace + so);
   void* aws = (char*)workspace + ao;
   const size_t aws_bytes = align256(hstu_attn_workspace_bytes(B, H, max_seqlen, total_tokens));
-  hstu_status st = check_hip(launch_f1_gemm_silu(layer_in(0), (const bf16*)w1[0], b1[0], z,
-                                                 total_tokens, N1, d_model, stream),
-                             "f1 launch");
-  if (st != HSTU_OK) return st;
   const bf16* U = z;
   const bf16* V = z + HV;
   const bf16* Q = z + 2 * HV;
   const bf16* K = z + 2 * HV + H * d_qk;
-  st = hstu_attn_plan(HSTU_DTYPE_BF16, B, H, d_qk, offsets, max_seqlen, aws, aws_bytes, stream);
+  hstu_status st = hstu_attn_plan(HSTU_DTYPE_BF16, B, H, d_qk, offsets, max_seqlen, aws,
+                                  aws_bytes, stream);
   if (st != HSTU_OK) return st;
+  const int64_t* cls_ts = nullptr;  // the bias the tile classes in the workspace were made for
+  int32_t cls_p = -1, cls_nt = -1;
   for (int l = 0; l < n_layers; ++l) {
-    // the work list depends on the offsets only: planned once; the prepass runs per layer
+    if (l == 0 || !fuse_boundaries) {
+      st = check_hip(launch_f1_gemm_silu(layer_in(l), (const bf16*)w1[l], b1[l], z, total_tokens,
+                                         N1, d_model, stream),
+                     "f1 launch");
+      if (st != HSTU_OK) return st;
+    }
+    BiasArgs ba;
+    check_bias(bias[l], H, &ba);  // validated above
+    const bool ready = ba.kind == 1 && ba.ts == cls_ts && ba.num_pos == cls_p && ba.num_time == cls_nt;
     st = attn_planned(HSTU_DTYPE_BF16, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, Q, N1,
                       K, N1, V, N1, bias[l], alpha, 1.0f, obuf, false, ostats, aws, aws_bytes,
-                      stream);
+                      stream, kPrepareAndRun, ready);
     if (st != HSTU_OK) return st;
+    if (ba.kind == 1) {
+      cls_ts = ba.ts;
+      cls_p = ba.num_pos;
+      cls_nt = ba.num_time;
+    }
     const bf16* res = residual ? layer_in(l) : nullptr;
-    if (l + 1 < n_layers)
+    if (fuse_boundaries && l + 1 < n_layers)
       st = check_hip(launch_ln_gate_f2_f1(obuf, ostats, U, N1, ln_gamma[l], ln_beta[l], ln_eps,
                                           (const bf16*)w2[l], b2[l], res, layer_out(l),
                                           (const bf16*)w1[l + 1], b1[l + 1], z, N1, total_tokens,

@@ -225,7 +225,9 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
  * f1 + SiLU + split run as one kernel per 64-token tile, the tile's y kept on chip between the
  * two products (d_model = 512 only; otherwise HSTU_ERR_UNSUPPORTED).  Both forms give identical
  * bits: the fused kernel takes f1's products in f1's order.  The attention stays a kernel of its
- * own (it needs every key of a user).
+ * own (it needs every key of a user).  The jagged work list is made once per call, and the
+ * attention's tile classes once per distinct (timestamps, bucket counts) of the layers'
+ * position + time biases; the output equals hstu_layer_fwd applied layer by layer.
  *  w1, b1, ln_gamma, ln_beta, w2, b2, bias  host arrays of n_layers per-layer arguments, each
  *            as for hstu_layer_fwd (device pointers; NULL entries allowed where hstu_layer_fwd
  *            allows them)

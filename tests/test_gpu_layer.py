@@ -197,6 +197,29 @@ def test_stack_fused_boundaries_bitwise_and_oracle():
     assert e <= TOL["bf16"]
 
 
+def test_stack_mixed_biases_reuses_plan_bitwise():
+    """The stack entry point plans the batch once and keeps the tile classes while the layers'
+    position + time bias keeps its timestamps and bucket counts.  Four layers whose biases are
+    rab (P = 256, NT = 32), ALiBi, rab as the first, and rab with other bucket counts (P = 64,
+    NT = 16: the classes are made again) give, fused and unfused, exactly what hstu_layer_fwd
+    gives layer by layer."""
+    inp = synth.stack8(B=12, n_layers=4, hi=1500, randomize_affine=True)
+    d = DevLayer(inp)
+    d.layers[1]["bias"] = binding.make_bias(binding.BIAS_ALIBI)
+    rng = np.random.default_rng(21)
+    d.layers[3]["bias"] = binding.make_bias(
+        binding.BIAS_RAB_PT, d.ts,
+        to_dev((rng.standard_normal(64) * 0.5).astype(np.float32)),
+        to_dev((rng.standard_normal(16) * 0.5).astype(np.float32)))
+    h = d.x
+    for li in range(len(inp.layers)):
+        h = d.run_layer(h, li=li)
+    torch.cuda.synchronize()
+    assert torch.equal(_stack(d, False), h)
+    assert torch.equal(_stack(d, True), h)
+    assert torch.isfinite(h.float()).all()
+
+
 def test_stack8_full_size_all_layers_sampled_users():
     """The whole 8-layer stack at full size (128 users, T = 80 405, residual, position + time
     bias), fused and three-kernel boundaries giving identical bits, and its output checked on
