@@ -594,15 +594,51 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
             }
           }
         }
-        if (!sat || thi > tlo + 1) {
+        if (!sat) {
+          // position buckets of an unsaturated tile: sums along the tile's diagonals.  Score
+          // (query qo = accrow(r) + 4 hf, key l32) lies on diagonal qo - l32, i.e. i - j =
+          // i0h - kw0 + qo - l32.  For register r, lane (m, hf) takes the score of key
+          // (qo - m) mod 32 of its half: diagonal m when qo >= m, m - 32 otherwise; the two
+          // halves' sums are added and each of lanes 0..31 adds its two diagonals to the table
+          // (scores outside the causal range have g = 0).
+          float dpos = 0.f, dneg = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qo = accrow(r) + 4 * hf;
+            const int src = ((qo - l32) & 31) + 32 * hf;
+            // (__shfl: a __builtin_bit_cast of an ext-vector element, g[r], to feed the raw
+            // ds_bpermute builtin is folded to element 0 by hipcc 7.2)
+            const float v = __shfl(g[r], src, 64);
+            if (qo >= l32) dpos += v;
+            else dneg += v;
+          }
+          dpos += __shfl_xor(dpos, 32, 64);
+          dneg += __shfl_xor(dneg, 32, 64);
+          if (hf == 0) {
+            const int dp = i0h - kw0 + l32;  // i - j of diagonal l32; l32 - 32 is dp - 32
+            if (dp >= 0) atomicAdd(&sm.gpos[min(dp, Pm1)], dpos);
+            if (dp >= 32) atomicAdd(&sm.gpos[min(dp - 32, Pm1)], dneg);
+          }
+        }
+        if (thi > tlo + 1) {
+          // three or more time buckets: per bucket b in [tlo, thi], a wave sum of the scores in
+          // b and one LDS add (per-score adds would put up to 64 lanes on one address).  Every
+          // score's bucket lies in [tlo, thi] (the bucket is monotone in dt); scores outside the
+          // causal range have g = 0, whatever bucket they are counted in.
+          uint32_t pk[4] = {0u, 0u, 0u, 0u};  // bucket - tlo of register r in byte r % 4 of pk[r / 4]
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int il = 32 * hq + accrow(r) + 4 * hf;
-            const int i = t * kBTile + il;
-            if (i >= key && i < n && kvalid) {
-              if (!sat) atomicAdd(&sm.gpos[min(i - key, Pm1)], g[r]);
-              if (thi > tlo + 1) atomicAdd(&sm.gtime[time_bucket(stg.t[il] - tk, NTm1)], g[r]);
-            }
+            const uint32_t k = (uint32_t)(time_bucket(stg.t[il] - tk, NTm1) - tlo) & 255u;
+            pk[r >> 2] |= k << (8 * (r & 3));
+          }
+          for (int b = 0; b <= thi - tlo; ++b) {
+            float v = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              v += ((pk[r >> 2] >> (8 * (r & 3))) & 255u) == (uint32_t)b ? g[r] : 0.f;
+            const float tot = wave_sum(v);
+            if (lane == 0) atomicAdd(&sm.gtime[tlo + b], tot);
           }
         }
       }
