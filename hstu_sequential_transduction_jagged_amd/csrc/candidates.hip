@@ -361,8 +361,27 @@ __global__ __launch_bounds__(kCThreads, kCWgPerCu) void attn_cand_bf16_kernel(Ca
         } else {
           f32x16 cb;
           const int dn = n - j0h - 4 * hf;  // n - j of register 0
+          bool per_key = false;
+          if (KIND == 1 && mode == 3) {
+            // When every key of the half has one time bucket for all of the wave's candidates
+            // (decided exactly from the candidates' extreme times; always so for candidates of
+            // one request time) the bias depends on the key only: lane l computes it for key
+            // j0h + l % 32 and the registers take theirs by lane shuffles.  Keys at or past n
+            // meet zero V rows, whatever their bias.
+            const int64_t tkl = stg.kt[32 * hk + l32];
+            const int blo = time_bucket(tq_min - tkl, NTm1);
+            const bool same = blo == time_bucket(tq_max - tkl, NTm1) || j0h + l32 >= n;
+            per_key = __builtin_amdgcn_ballot_w64(!same) == 0;
+            if (per_key) {
+              const float bk = wpos_s[max(min(n - j0h - l32, Pm1), 0)] + wtime_s[blo];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
+              for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cb[4 * g + e] = __shfl(bk, 8 * g + 4 * hf + e, 64);
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < 4 && !per_key; ++g) {
             const int jl = 32 * hk + 8 * g + 4 * hf;
             if (KIND == 2) {
               const float base = slope_y * (float)(dn - 8 * g);

@@ -54,6 +54,15 @@ def test_ragged(kind, regime):
     _check(inp)
 
 
+@pytest.mark.parametrize("jitter", [0, 40])
+def test_one_request_time_and_small_jitter(jitter):
+    """Candidates of one user at one request time (jitter 0: every key's time bucket is the same
+    for all of them, so the last P - 1 keys take the per-key bias path) or spread over 40 s
+    (the path is taken where no key's bucket changes across the wave's candidates)."""
+    inp = _case(HIST + [2000], CAND + [256], jitter=jitter, table_std=0.5, alpha=1.0 / 64)
+    _check(inp)
+
+
 def test_per_head_tables_small_buckets_and_out_scale():
     inp = _case([5, 300, 129], [40, 7, 130], H=3, alpha=0.1, table_std=1.0, P=16, NT=6,
                 per_head=True, out_scale=1.0 / 300)
