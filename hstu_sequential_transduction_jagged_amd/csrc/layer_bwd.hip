@@ -407,22 +407,29 @@ hipError_t launch_layer_bwd_post(const LayerBwdLaunch& L, hipStream_t stream) {
     g.resid = L.residual ? L.dy : nullptr; g.ldr = D;
     if ((e = gemm<0, 1, 0>(g, 1, stream)) != hipSuccess) return e;
   }
-  // weight gradients, split over tokens into slices of `kt` rows
-  int64_t kt = ((T + 63) / 64 + 31) / 32 * 32;
-  if (kt < 256) kt = 256;
-  const int splits = (int)((T + kt - 1) / kt);
+  // weight gradients, split over tokens into slices of `kt` rows: about 1 024 workgroups per
+  // product (two per CU, twice over), so that the fp32 atomic adds of the partial tiles stay few
+  auto token_split = [&](int32_t m, int32_t n, int* splits) {
+    const int64_t tiles = (int64_t)((m + kGB - 1) / kGB) * ((n + kGB - 1) / kGB);
+    const int64_t want = tiles >= 1024 ? 1 : 1024 / tiles;
+    int64_t kt = ((T + want - 1) / want + 31) / 32 * 32;
+    if (kt < 256) kt = 256;
+    *splits = (int)((T + kt - 1) / kt);
+    return kt;
+  };
+  int splits = 0;
   // dW1 = dZpre^T X  ([N1][D]; both operands row-contiguous in the k = t reduction)
   g = GemmArgs{};
   g.a = L.dz; g.lda = L.dz_stride;
   g.b = L.x; g.ldb = D;
-  g.M = N1; g.N = D; g.K = (int)T; g.k_split = (int)kt;
+  g.M = N1; g.N = D; g.K = (int)T; g.k_split = (int)token_split(N1, D, &splits);
   g.cf = L.dw1; g.ldc = D;
   if ((e = gemm<1, 1, 1>(g, splits, stream)) != hipSuccess) return e;
   // dW2 = dY^T G  ([D][HV])
   g = GemmArgs{};
   g.a = L.dy; g.lda = D;
   g.b = L.g; g.ldb = HV;
-  g.M = D; g.N = HV; g.K = (int)T; g.k_split = (int)kt;
+  g.M = D; g.N = HV; g.K = (int)T; g.k_split = (int)token_split(D, HV, &splits);
   g.cf = L.dw2; g.ldc = HV;
   if ((e = gemm<1, 1, 1>(g, splits, stream)) != hipSuccess) return e;
   // bias gradients
