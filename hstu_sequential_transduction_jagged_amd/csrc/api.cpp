@@ -180,6 +180,18 @@ hstu_status hstu_attn_plan(int32_t dt, int32_t B, int32_t H, int32_t d, const in
                    "scheduler launch");
 }
 
+// the backward kernels' work list: the forward's scheduler at the backward's item height
+static hstu_status bwd_plan(int32_t B, int32_t H, const int32_t* offsets, int32_t max_seqlen,
+                            void* workspace, int64_t* grid, hipStream_t stream) {
+  const int32_t rows = attn_bwd_block_rows();
+  const int32_t max_tiles = (int32_t)ceil_div(max_seqlen, rows);
+  *grid = (int64_t)B * H * max_tiles;
+  if (*grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
+  return check_hip(launch_schedule(offsets, B, H, rows, max_tiles, (int32_t*)workspace,
+                                   (WorkItem*)((char*)workspace + kHeader), stream),
+                   "scheduler launch");
+}
+
 // per 32-token block timestamp statistics for the backward kernels (position + time bias only),
 // in the attention workspace's statistics region
 static hstu_status bwd_time_stats(int32_t B, const int32_t* offsets, int32_t max_seqlen,
@@ -548,7 +560,8 @@ hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   if (do_row_stride > max_stride) max_stride = do_row_stride;
   if ((int64_t)(max_seqlen + 64) * max_stride * 2 >= ((int64_t)1 << 31))
     return fail(HSTU_ERR_UNSUPPORTED, "max_seqlen x row stride reaches 2 GiB per user");
-  st = hstu_attn_plan(dt, B, H, d_qk, offsets, max_seqlen, workspace, workspace_bytes, stream);
+  int64_t grid = 0;
+  st = bwd_plan(B, H, offsets, max_seqlen, workspace, &grid, stream);
   if (st != HSTU_OK) return st;
   BwdArgs a{};
   a.offsets = offsets;
@@ -568,8 +581,6 @@ hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   if (st != HSTU_OK) return st;
   const int64_t n_pos = ba.kind == 1 ? (ba.pos_stride ? (int64_t)H * ba.pos_stride : ba.num_pos) : 0;
   const int64_t n_time = ba.kind == 1 ? (ba.time_stride ? (int64_t)H * ba.time_stride : ba.num_time) : 0;
-  const int64_t grid = (int64_t)B * H * ceil_div(max_seqlen, block_rows);
-  if (grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
   return check_hip(launch_attn_bwd_bf16(a, (int)grid, n_pos, n_time, stream), "backward launch");
 }
 
@@ -803,10 +814,11 @@ hstu_status hstu_layer_bwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   st = check_hip(launch_layer_bwd_pre(L, stream), "layer backward (LN, f2) launch");
   if (st != HSTU_OK) return st;
   // attention gradients straight into dZ's V | Q | K columns
-  st = hstu_attn_plan(dt, B, H, d_qk, offsets, max_seqlen, attn_ws, attn_bytes, stream);
-  if (st != HSTU_OK) return st;
   int block_rows = 0;
   st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
+  if (st != HSTU_OK) return st;
+  int64_t grid = 0;
+  st = bwd_plan(B, H, offsets, max_seqlen, attn_ws, &grid, stream);
   if (st != HSTU_OK) return st;
   BwdArgs a{};
   a.offsets = offsets;
@@ -826,8 +838,6 @@ hstu_status hstu_layer_bwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   if (st != HSTU_OK) return st;
   const int64_t n_pos = ba.kind == 1 ? (ba.pos_stride ? (int64_t)H * ba.pos_stride : ba.num_pos) : 0;
   const int64_t n_time = ba.kind == 1 ? (ba.time_stride ? (int64_t)H * ba.time_stride : ba.num_time) : 0;
-  const int64_t grid = (int64_t)B * H * ceil_div(max_seqlen, block_rows);
-  if (grid > 0x7fffffff) return fail(HSTU_ERR_UNSUPPORTED, "too many work items");
   st = check_hip(launch_attn_bwd_bf16(a, (int)grid, n_pos, n_time, stream), "attention backward launch");
   if (st != HSTU_OK) return st;
   return check_hip(launch_layer_bwd_post(L, stream), "layer backward (f1) launch");

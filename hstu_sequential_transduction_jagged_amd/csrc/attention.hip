@@ -198,14 +198,16 @@ __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict
 }
 
 // ============================================================================================
-// bf16, d = 32 or 64: 8 waves x 32 queries = 256 query rows per work item, 64 keys per LDS
-// stage (a ring of four stages filled by direct global -> LDS transfers, one barrier per two
-// tiles), four waves per SIMD.  One instantiation per bias kind (0 none, 1 position + time
-// tables, 2 ALiBi), output type and head dim; with d = 32 the stages keep their 128-byte rows
+// bf16, d = 32 or 64: 4 waves x 32 queries = 128 query rows per work item, 64 keys per LDS
+// stage (two stages filled by direct global -> LDS transfers, one barrier per tile), four
+// workgroups per CU, so that each SIMD holds one wave of each of four workgroups and a
+// workgroup waiting at its barrier leaves the SIMD to the other three.  One instantiation per
+// bias kind (0 none, 1 position + time tables, 2 ALiBi), output type and head dim; with d = 32
+// the stages keep their 128-byte rows
 // and only the first four chunks of each row are fetched and read (two k-steps of the score
 // product, one 32-column block of the output).
 // ============================================================================================
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQW = 32;
 constexpr int kBR = kWaves * kQW;
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NKS = D / 16;  // 16-wide k-steps of the score product
   constexpr int NDB = D / 32;  // 32-column blocks of the output
   __shared__ SmemBf16 sm;
-  __shared__ Stage st0, st1, st2, st3;
+  __shared__ Stage st0, st1;
   const int item = blockIdx.x;
   if (item >= *a.work_count) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -267,9 +269,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
   const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
   constexpr int kClassWave = 1;  // its lanes 0..31 stage the next tile's class entries
 
-  // ---- staging: direct global -> LDS transfers into a ring of four stages ----
-  // Wave w's K and V transfers fill key rows 8 w .. 8 w + 7 of a stage: lane p writes row
-  // 8 w + p / 8 at chunk position p % 8, i.e. global chunk (p % 8) ^ swz(row).  Rows at or
+  // ---- staging: direct global -> LDS transfers into two stages ----
+  // Wave w's K and V transfers fill key rows 16 w .. 16 w + 15 of a stage, two instructions
+  // each: lane p of instruction u writes row 16 w + 8 u + p / 8 at chunk position p % 8, i.e.
+  // global chunk (p % 8) ^ swz(row).  Rows at or
   // past q_end read as zeros (buffer bounds).  One 4-byte transfer per wave: wave 0 the keys'
   // time offsets, wave 1 the class entries (both position + time bias only), wave 2 the two
   // halves' key norm bounds, the others nothing (out of range).
@@ -280,15 +283,14 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(vp + tok0 * a.v_stride + (int64_t)h * D), (short)0,
       (int)((uint32_t)(q_end - 1) * vstride_b + 2u * D), 0x00020000);
-  uint32_t kvo, vvo;
-  {
-    const int r = 8 * wave + (lane >> 3);
+  uint32_t kvo[2], vvo[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = 16 * wave + 8 * u + (lane >> 3);
     const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ swz(r));
-    kvo = (uint32_t)r * kstride_b + ch;
-    vvo = (uint32_t)r * vstride_b + ch;
-    // d = 32: chunks 4..7 of a stage row are never read; their lanes fetch nothing (an offset
-    // past every descriptor's range reads as zeros)
-    if (D == 32 && ch >= 64u) kvo = vvo = 0x80000000u;
+    kvo[u] = (uint32_t)r * kstride_b + ch;
+    vvo[u] = (uint32_t)r * vstride_b + ch;
+    if (D == 32 && ch >= 64u) kvo[u] = vvo[u] = 0x80000000u;
   }
   const int64_t crow = tclass_row0(tok0, b) + q0 / 32;
   const int64_t cbase = crow * a.tclass_cols * 8;  // bytes
@@ -318,8 +320,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
     const uint32_t j0 = (uint32_t)(t * kKB);
     const uint32_t ksoff = __builtin_amdgcn_readfirstlane(real ? j0 * kstride_b : 0x7fffffffu);
     const uint32_t vsoff = __builtin_amdgcn_readfirstlane(real ? j0 * vstride_b : 0x7fffffffu);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_ptr)(stg.k + 512 * wave), 16, kvo, ksoff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_ptr)(stg.v + 512 * wave), 16, vvo, vsoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_ptr)(stg.k + 1024 * wave), 16, kvo[0], ksoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lds_ptr)(stg.k + 1024 * wave + 512), 16, kvo[1], ksoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_ptr)(stg.v + 1024 * wave), 16, vvo[0], vsoff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lds_ptr)(stg.v + 1024 * wave + 512), 16, vvo[1], vsoff, 0, 0);
     const uint32_t msoff = __builtin_amdgcn_readfirstlane(
         !real ? 0x7fffffffu
         : wave == 2 ? (j0 / 32u) * 4u * (uint32_t)H
@@ -328,10 +332,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
               : wave == 2 ? (void*)stg.kn : (void*)stg.dummy;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rrsrc, (lds_ptr)dst, 4, roff, msoff, 0, 0);
   };
-  // the first two tiles' transfers go out before the item's register loads, so that their
+  // the first tile's transfers go out before the item's register loads, so that their
   // latencies overlap
   dma(st0, 0);
-  dma(st1, 1);
 
   // ---- Q fragments (B operand of S^T = K Q^T), unscaled ----
   bf16x8 qop[NKS];
@@ -642,10 +645,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[db][m], pop[m], oacc[db], 0, 0, 0);
     }
   };
-  // tiles are taken in pairs, one barrier per pair: tiles t, t + 1 sit in stages t % 4,
-  // (t + 1) % 4; the transfers of tiles t + 2, t + 3 go into the stages of tiles t - 2, t - 1
-  // (their readers all passed the last barrier) while t and t + 1 are multiplied, then this
-  // wave's transfers are waited for and the barrier publishes them to all
+  // tile t sits in stage t % 2; the transfers of tile t + 1 go into the stage of tile t - 1
+  // (its readers all passed the last barrier) while t is multiplied, then this wave's
+  // transfers are waited for and the barrier publishes them to all
   wait_vm<0>();
   lds_barrier();
   if (KIND == 2) {
@@ -656,19 +658,17 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
     const int t_low = min(nb / 2, n_tiles);
     n_loop = uniform_i32(n_tiles - t_low);
   }
-  auto pair = [&](const Stage& c0, const Stage& c1, Stage& n0, Stage& n1, int k) __attribute__((always_inline)) {
-    dma(n0, k + 2);
-    dma(n1, k + 3);
+  auto one = [&](const Stage& c, Stage& nx, int k) __attribute__((always_inline)) {
+    dma(nx, k + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(c0, tix(k));
-    if (k + 1 < n_loop) compute(c1, tix(k + 1));
+    compute(c, tix(k));
     wait_vm<0>();
     lds_barrier();
   };
-  for (int k = 0; k < n_loop; k += 4) {
-    pair(st0, st1, st2, st3, k);
-    if (k + 2 >= n_loop) break;
-    pair(st2, st3, st0, st1, k + 2);
+  for (int k = 0; k < n_loop; k += 2) {
+    one(st0, st1, k);
+    if (k + 1 >= n_loop) break;
+    one(st1, st0, k + 1);
   }
   // the transfers past the last tile land before the kernel ends
   wait_vm<0>();

@@ -735,6 +735,8 @@ __global__ void zero_f32_kernel(float* p, int64_t n) {
 
 }  // namespace
 
+int attn_bwd_block_rows() { return kBRows; }
+
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int grid, int64_t n_pos_grad, int64_t n_time_grad,
                                 hipStream_t stream) {
   if (grid <= 0) return hipSuccess;

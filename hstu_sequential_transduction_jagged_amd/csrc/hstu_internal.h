@@ -248,6 +248,8 @@ struct BwdArgs {
   float *dw_pos, *dw_time;    // position + time bias: gradients shaped like the tables
   const TimeStat* tstat;      // position + time bias: per 32-token block min / max time
 };
+// query rows per work item of the backward kernels (their own work list)
+int attn_bwd_block_rows();
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, int grid, int64_t n_pos_grad,
                                 int64_t n_time_grad, hipStream_t stream);
 

@@ -54,8 +54,8 @@ def test_workspace_sizes():
     assert L.hstu_attn_workspace_bytes(0, 8, 8192, 0) == 256 + tclass(0, 8192, 0) + knorm(0, 8, 0)
     assert L.hstu_attn_workspace_bytes(16, 8, 8192, 1000) == \
         256 + 16 * 8 * 64 * 32 + 16128 + 4096 + tclass(16, 8192, 1000) + knorm(16, 8, 1000)
-    assert L.hstu_attn_block_rows(1, 64) == 256
-    assert L.hstu_attn_block_rows(1, 32) == 256
+    assert L.hstu_attn_block_rows(1, 64) == 128
+    assert L.hstu_attn_block_rows(1, 32) == 128
     assert L.hstu_attn_block_rows(0, 32) == 128
     assert L.hstu_attn_block_rows(1, 48) == 0
     z, o, st, a = binding.layer_workspace_offsets(1000, 4, 64, 64)
