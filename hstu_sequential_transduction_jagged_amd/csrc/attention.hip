@@ -341,11 +341,13 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
   const int row = qw0 + l32;
   const bool qvalid = row <= wq_last;
   {
-    const bf16* src = qp + (tok0 + row) * a.q_stride + (int64_t)h * D + 8 * hf;
+    // unconditional loads from a row clamped into the item (a load under a branch would make
+    // the compiler wait for every transfer in flight), zeroed for rows past it
+    const bf16* src = qp + (tok0 + min(row, q_end - 1)) * a.q_stride + (int64_t)h * D + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 raw = {0u, 0u, 0u, 0u};
-      if (qvalid) raw = *(const u32x4*)(src + 16 * ks);
+      u32x4 raw = *(const u32x4*)(src + 16 * ks);
+      if (!qvalid) raw = u32x4{0u, 0u, 0u, 0u};
       qop[ks] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -370,29 +372,40 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
   float slope_y = 0.f, ta0 = 0.f, ta1 = 0.f, ta2 = 0.f, tabmax = 0.f;
   int32_t tq_rel = 0;  // query time minus the wave's block minimum (32-bit paths)
   if (KIND == 1) {
+    // every global read of the set-up goes out before the first of them is used (one memory
+    // round trip instead of one per table and loop step); the tables' largest magnitude is
+    // taken from LDS after the first barrier
     const float* wp = a.bias.w_pos + (int64_t)h * a.bias.pos_stride;
     const float* wt = a.bias.w_time + (int64_t)h * a.bias.time_stride;
-    for (int i = tid; i < a.bias.num_pos + 96; i += kThreads) sm.wposx[i] = -kLog2e * wp[min(max(i - 32, 0), Pm1)];
-    if (tid < a.bias.num_time) {
+    const int nposx = a.bias.num_pos + 96;
+    constexpr int kPX = (kMaxPosBuckets + 96 + kThreads - 1) / kThreads;
+    float px[kPX];
+    // (indices clamped into the tables and the item: unconditional loads)
+#pragma unroll
+    for (int u = 0; u < kPX; ++u) px[u] = wp[min(max(tid + kThreads * u - 32, 0), Pm1)];
+    const bool tb = tid < a.bias.num_time;
+    const float wt_t = wt[min(tid, NTm1)];
+    const float wp_sat = wp[Pm1];
+    const float wt_lz = wt[min(max(31 - tid, 0), NTm1)];
+    const int64_t tmin = tstat[tok0 + min(qw0, q_end - 1)].mn;
+    const int64_t tqv = ts[tok0 + min(row, q_end - 1)];
+#pragma unroll
+    for (int u = 0; u < kPX; ++u) {
+      const int i = tid + kThreads * u;
+      if (i < nposx) sm.wposx[i] = -kLog2e * px[u];
+    }
+    if (tb) {
       // per time bucket: the bias of a tile with saturated position bucket, and its Taylor
       // coefficients
-      const float c = -kLog2e * (wp[Pm1] + wt[tid]);
+      const float c = -kLog2e * (wp_sat + wt_t);
       float x0, x1, x2;
       w_taylor_coeffs(c, cq, x0, x1, x2);
       *(f32x4*)(&sm.tay[tid][0]) = f32x4{c, x0, x1, x2};
-      sm.wtime[tid] = -kLog2e * wt[tid];
+      sm.wtime[tid] = -kLog2e * wt_t;
     }
-    if (tid < 32) sm.wtime_lz[tid] = -kLog2e * wt[min(31 - tid, NTm1)];
-    {
-      float mp = 0.f, mt = 0.f;
-      for (int i = lane; i < a.bias.num_pos; i += 64) mp = fmaxf(mp, fabsf(wp[i]));
-      for (int i = lane; i < a.bias.num_time; i += 64) mt = fmaxf(mt, fabsf(wt[i]));
-      tabmax = uniform_f32(kLog2e * (wave_max(mp) + wave_max(mt)));
-    }
-    int64_t tmin = 0;
-    if (qw0 <= wq_last) tmin = tstat[tok0 + qw0].mn;
+    if (tid < 32) sm.wtime_lz[tid] = -kLog2e * wt_lz;
     if (qvalid) {
-      const int64_t d = ts[tok0 + row] - tmin;
+      const int64_t d = tqv - tmin;
       tq_rel = d > 0x7fffffffLL ? 0x7fffffff : (int32_t)d;
     }
   } else if (KIND == 0) {
@@ -650,6 +663,13 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
   // transfers are waited for and the barrier publishes them to all
   wait_vm<0>();
   lds_barrier();
+  if (KIND == 1) {
+    // log2(e) (max |w_pos| + max |w_time|), from the LDS tables (-log2(e) w each)
+    float mp = 0.f, mt = 0.f;
+    for (int i = lane; i < a.bias.num_pos; i += 64) mp = fmaxf(mp, fabsf(sm.wposx[i + 32]));
+    for (int i = lane; i < a.bias.num_time; i += 64) mt = fmaxf(mt, fabsf(sm.wtime[i]));
+    tabmax = uniform_f32(wave_max(mp) + wave_max(mt));
+  }
   if (KIND == 2) {
     // the workgroup stops below the lowest block any wave needs (64-key tile = two blocks)
     int nb = sm.need[0];
