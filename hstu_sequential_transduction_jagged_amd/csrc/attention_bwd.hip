@@ -26,7 +26,7 @@
 namespace hstu {
 namespace {
 
-constexpr int kBWaves = 8;
+constexpr int kBWaves = 4;
 constexpr int kBThreads = 64 * kBWaves;
 constexpr int kBRows = 32 * kBWaves;  // rows of a work item (the forward's tile height)
 constexpr int kBTile = 64;            // keys (dq kernel) or queries (dkv kernel) per LDS tile
@@ -139,11 +139,14 @@ __device__ __forceinline__ float pair_bias(const BwdTables& sm, int di, int64_t 
 struct TileStager {
   __amdgpu_buffer_rsrc_t xr, yr, tr;
   uint32_t xs, ys, xoff, yoff;
-  u32x4 xreg, yreg;
+  u32x4 xreg[2], yreg[2];
   uint32_t tlo = 0, thi = 0;
   __device__ void load(int r0, bool with_t, int lane) {
-    xreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, (uint32_t)r0 * xs, 0));
-    yreg = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, yoff, (uint32_t)r0 * ys, 0));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      xreg[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff + 32u * u * xs, (uint32_t)r0 * xs, 0));
+      yreg[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, yoff + 32u * u * ys, (uint32_t)r0 * ys, 0));
+    }
     if (with_t) {
       const u32x2 tt = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(tr, 8u * (uint32_t)lane, 8u * (uint32_t)r0, 0));
       tlo = tt[0];
@@ -153,7 +156,7 @@ struct TileStager {
 };
 
 template <int KIND>
-__global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   __shared__ SmemBwd sm;
   const int item = blockIdx.x;
   if (item >= *a.work_count) return;
@@ -227,8 +230,11 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   stg.xoff = (uint32_t)srow * stg.xs + 16u * sch;
   stg.yoff = (uint32_t)srow * stg.ys + 16u * sch;
   auto lstore = [&](int buf, int r0) {
-    *(u32x4*)(&sm.x[buf][srow * kBRow + 8 * sch]) = stg.xreg;
-    *(u32x4*)(&sm.y[buf][srow * kBRow + 8 * sch]) = stg.yreg;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      *(u32x4*)(&sm.x[buf][(srow + 32 * u) * kBRow + 8 * sch]) = stg.xreg[u];
+      *(u32x4*)(&sm.y[buf][(srow + 32 * u) * kBRow + 8 * sch]) = stg.yreg[u];
+    }
     if (KIND == 1 && wave == 0) {
       const int64_t tt = (int64_t)(((uint64_t)stg.thi << 32) | stg.tlo);
       sm.t[buf][lane] = tt;
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 template <int KIND>
-__global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBThreads, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
   __shared__ BwdTables sm;
   const int item = blockIdx.x;
   if (item >= *a.work_count) return;
@@ -435,7 +441,7 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   // 0, 1 the rows' timestamps (32 each), wave 2 the halves' TimeStat entries, the others
   // nothing.  Tiles go in pairs, one barrier per pair.
   const int t0 = k0 / kBTile, t_end = (n + kBTile - 1) / kBTile;
-  __shared__ BStage st0, st1, st2, st3;
+  __shared__ BStage st0, st1;
   const uint32_t xs = (uint32_t)a.q_stride * 2u, ys = (uint32_t)a.do_stride * 2u;
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.q + tok0 * a.q_stride + (int64_t)h * kBD), (short)0, (int)((uint32_t)(n - 1) * xs + 2u * kBD), 0x00020000);
@@ -446,12 +452,13 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(lo ? a.dout_lo + tok0 * a.do_stride + (int64_t)h * kBD : nullptr), (short)0,
       lo ? (int)((uint32_t)(n - 1) * ys + 2u * kBD) : 0, 0x00020000);
-  uint32_t xo, yo;
-  {
-    const int r = 8 * wave + (lane >> 3);
+  uint32_t xo[2], yo[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int r = 16 * wave + 8 * u + (lane >> 3);
     const uint32_t ch = 16u * (uint32_t)((lane & 7) ^ bswz(r));
-    xo = (uint32_t)r * xs + ch;
-    yo = (uint32_t)r * ys + ch;
+    xo[u] = (uint32_t)r * xs + ch;
+    yo[u] = (uint32_t)r * ys + ch;
   }
   const __amdgpu_buffer_rsrc_t mr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(KIND != 1 || wave > 2 ? nullptr : wave < 2 ? (const void*)(a.bias.ts + tok0) : (const void*)(a.tstat + tok0)),
@@ -464,16 +471,18 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     const uint32_t r0 = (uint32_t)(t * kBTile);
     const uint32_t xsoff = __builtin_amdgcn_readfirstlane(real ? r0 * xs : 0x7fffffffu);
     const uint32_t ysoff = __builtin_amdgcn_readfirstlane(real ? r0 * ys : 0x7fffffffu);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(stg.x + 512 * wave), 16, xo, xsoff, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(yr, (lds_ptr)(stg.y + 512 * wave), 16, yo, ysoff, 0, 0);
-    if (lo) __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (lds_ptr)(stg.z + 512 * wave), 16, yo, ysoff, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr)(stg.x + 1024 * wave + 512 * u), 16, xo[u], xsoff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(yr, (lds_ptr)(stg.y + 1024 * wave + 512 * u), 16, yo[u], ysoff, 0, 0);
+      if (lo) __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (lds_ptr)(stg.z + 1024 * wave + 512 * u), 16, yo[u], ysoff, 0, 0);
+    }
     const uint32_t msoff = __builtin_amdgcn_readfirstlane(
         (real && KIND == 1 && wave < 3) ? (wave < 2 ? 8u * r0 : 16u * r0) : 0x7fffffffu);
     void* dst = wave < 2 ? (void*)(stg.t + 32 * wave) : wave == 2 ? (void*)stg.tmm : (void*)stg.dummy;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(mr, (lds_ptr)dst, 4, mo, msoff, 0, 0);
   };
   dma(st0, t0);
-  dma(st1, t0 + 1);
 
   // byte offsets of this lane's reads within a stage: the operand read of k-step ks at
   // kbase ^ (32 ks) (row l32 + 32 hq), the transposing reads of column block db at
@@ -679,19 +688,17 @@ __global__ __launch_bounds__(kBThreads, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   };
   wait_vm<0>();
   lds_barrier();
-  auto pair = [&](const BStage& c0, const BStage& c1, BStage& n0, BStage& n1, int t) __attribute__((always_inline)) {
-    dma(n0, t + 2);
-    dma(n1, t + 3);
+  auto one = [&](const BStage& c, BStage& nx, int t) __attribute__((always_inline)) {
+    dma(nx, t + 1);
     __builtin_amdgcn_sched_barrier(0);
-    compute(c0, t);
-    if (t + 1 < t_end) compute(c1, t + 1);
+    compute(c, t);
     wait_vm<0>();
     lds_barrier();
   };
-  for (int t = t0; t < t_end; t += 4) {
-    pair(st0, st1, st2, st3, t);
-    if (t + 2 >= t_end) break;
-    pair(st2, st3, st0, st1, t + 2);
+  for (int t = t0; t < t_end; t += 2) {
+    one(st0, st1, t);
+    if (t + 1 >= t_end) break;
+    one(st1, st0, t + 1);
   }
 
   // dK and dV rows: accumulator register 4 g + e holds d = 32 db + 8 g + 4 hf + e of this
