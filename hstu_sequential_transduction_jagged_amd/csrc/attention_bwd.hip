@@ -500,6 +500,22 @@ __global__ __launch_bounds__(kBThreads, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
     }
   }
   f32x16 dvacc[2] = {}, dkacc[2] = {};
+  // running per-lane sum of the scores of saturated one-bucket tiles whose time bucket is run_b
+  // (wave-uniform; their position bucket is P - 1): added to the tables when the bucket changes
+  // and after the last tile, instead of one wave sum and LDS add per tile
+  float run_g = 0.f;
+  int run_b = -1;
+  auto flush = [&]() __attribute__((always_inline)) {
+    if (run_b >= 0) {
+      const float tot = wave_sum(run_g);
+      if (lane == 0) {
+        atomicAdd(&sm.gpos[Pm1], tot);
+        atomicAdd(&sm.gtime[run_b], tot);
+      }
+      run_g = 0.f;
+      run_b = -1;
+    }
+  };
   auto compute = [&](const BStage& stg, int t) __attribute__((always_inline)) {
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
@@ -580,7 +596,14 @@ __global__ __launch_bounds__(kBThreads, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
           g[r] = ok ? dd[r] * d1 : 0.f;
         }
       }
-      if (KIND == 1) {
+      if (KIND == 1 && sat && thi == tlo) {
+        if (tlo != run_b) {
+          flush();
+          run_b = tlo;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) run_g += g[r];
+      } else if (KIND == 1) {
         // table gradients of this tile: tile sums for one position bucket and one or two time
         // buckets, else one LDS add per score
         float gs = 0.f, ghi = 0.f;
@@ -723,6 +746,8 @@ __global__ __launch_bounds__(kBThreads, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
   }
   // table gradients: this workgroup's sums, once per touched entry
   if (KIND == 1) {
+    flush();
+    lds_barrier();
     for (int i = tid; i < a.bias.num_pos; i += kBThreads) {
       const float v = sm.gpos[i];
       if (v != 0.f) atomicAdd(&a.dw_pos[(int64_t)h * a.bias.pos_stride + i], v * a.out_scale);
