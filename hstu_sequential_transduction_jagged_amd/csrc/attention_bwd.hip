@@ -633,16 +633,25 @@ __global__ __launch_bounds__(kBThreads, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
           // (qo - m) mod 32 of its half: diagonal m when qo >= m, m - 32 otherwise; the two
           // halves' sums are added and each of lanes 0..31 adds its two diagonals to the table
           // (scores outside the causal range have g = 0).
+          // (in two groups of eight shuffles, each issued before any of them is used)
           float dpos = 0.f, dneg = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qo = accrow(r) + 4 * hf;
-            const int src = ((qo - l32) & 31) + 32 * hf;
-            // (__shfl: a __builtin_bit_cast of an ext-vector element, g[r], to feed the raw
-            // ds_bpermute builtin is folded to element 0 by hipcc 7.2)
-            const float v = __shfl(g[r], src, 64);
-            if (qo >= l32) dpos += v;
-            else dneg += v;
+          for (int h8 = 0; h8 < 2; ++h8) {
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int r = 8 * h8 + q;
+              const int src = ((accrow(r) + 4 * hf - l32) & 31) + 32 * hf;
+              // (__shfl: a __builtin_bit_cast of an ext-vector element, g[r], to feed the raw
+              // ds_bpermute builtin is folded to element 0 by hipcc 7.2)
+              v[q] = __shfl(g[r], src, 64);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const int r = 8 * h8 + q;
+              if (accrow(r) + 4 * hf >= l32) dpos += v[q];
+              else dneg += v[q];
+            }
           }
           dpos += __shfl_xor(dpos, 32, 64);
           dneg += __shfl_xor(dneg, 32, 64);
