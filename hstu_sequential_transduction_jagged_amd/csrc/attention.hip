@@ -130,16 +130,18 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const int32_t* __restri
 // ============================================================================================
 // Key norm bounds: for every 32-key block of a user (blocks start at the user's first token)
 // and head h, the largest squared norm of the block's key rows, in fp32 from the bf16 keys,
-// at row tclass_row0(tok0, b) + block.  One workgroup per row of eight waves (the row's user is
-// found by bisection over the offsets; rows between users exit at once); wave w
-// takes heads w, w + 8, ...: lane l sums the squares of half l % 2 of token l / 2's head row
-// (d = 32 or 64 columns),
-// the lane pair adds its halves and the wave's maximum is the bound.  No LDS, no barriers.
-// With timestamps, wave 7 also writes the block's timestamp statistics exactly as
-// time_stats_kernel does (one launch fewer for the position + time bias).
+// at row tclass_row0(tok0, b) + block.  One workgroup of four waves per row: the row's user is
+// found by a 64-way search over the offsets (one round trip to memory per factor of 64 users;
+// rows between users exit at once); wave w takes heads w, w + 4, ... two at a time, with the
+// loads of both heads in flight together: lane l sums the squares of half l % 2 of token l / 2's
+// head row (d = 32 or 64 columns), the lane pair adds its halves and the wave's maximum is the
+// bound.  No LDS, no barriers.  With timestamps, wave 3 also writes the block's timestamp
+// statistics exactly as time_stats_kernel does (one launch fewer for the position + time bias).
 // ============================================================================================
+constexpr int kNormWaves = 4;
+
 template <int D>
-__global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(64 * kNormWaves) void key_norm_kernel(const int32_t* __restrict__ offsets,
                                                        int32_t B, const bf16* __restrict__ k,
                                                        int64_t k_stride, int32_t H,
                                                        float* __restrict__ knorm,
@@ -149,14 +151,18 @@ __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict
   const int64_t r = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // the last user whose first row is at or before r (first rows never decrease with b)
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tclass_row0(offsets[mid], mid) <= r) lo = mid;
-    else hi = mid - 1;
+  // the last user whose first row is at or before r (first rows never decrease with b; user 0's
+  // is 0): each step probes 64 users evenly spaced over the remaining range
+  int lo = 0, len = B;
+  while (len > 1) {
+    const int step = (len + 63) / 64;
+    const int i = lo + lane * step;
+    const bool ok = lane * step < len && tclass_row0(offsets[i], i) <= r;
+    const int cnt = (int)__popcll(__ballot(ok));  // >= 1: lane 0 probes lo
+    lo += (cnt - 1) * step;
+    len = min(step, len - (cnt - 1) * step);
   }
-  const int b = lo;
+  const int b = __builtin_amdgcn_readfirstlane(lo);
   const int64_t tok0 = offsets[b];
   const int n = offsets[b + 1] - offsets[b];
   const int64_t blk64 = r - tclass_row0(tok0, b);
@@ -164,26 +170,34 @@ __global__ __launch_bounds__(512) void key_norm_kernel(const int32_t* __restrict
   const int blk = (int)blk64;
   const int tok = 32 * blk + (lane >> 1);
   const bool valid = tok < n;
-  const bf16* row = k + (tok0 + tok) * k_stride + (D / 2) * (lane & 1);
+  const bf16* row = k + (tok0 + min(tok, n - 1)) * k_stride + (D / 2) * (lane & 1);
   float* dst = knorm + r * H;
-  for (int h = wave; h < H; h += 8) {
-    float acc = 0.f;
-    if (valid) {
+  for (int h = wave; h < H; h += 2 * kNormWaves) {
+    // heads h and h2 (= h when there is no second head: its result is not stored)
+    const int h2 = h + kNormWaves < H ? h + kNormWaves : h;
+    bf16x8 kv[2][D / 16];
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 kv = *(const bf16x8*)(row + (int64_t)h * D + 8 * c);
+    for (int c = 0; c < D / 16; ++c) {
+      kv[0][c] = *(const bf16x8*)(row + (int64_t)h * D + 8 * c);
+      kv[1][c] = *(const bf16x8*)(row + (int64_t)h2 * D + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bf16x2 pr = {kv[2 * e], kv[2 * e + 1]};
+          const bf16x2 pr = {kv[u][c][2 * e], kv[u][c][2 * e + 1]};
           acc = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, acc, false);
         }
-      }
+      if (!valid) acc = 0.f;
+      acc += __shfl_xor(acc, 1, 64);
+      const float m = wave_max_dpp(acc);
+      if (lane == 0 && (u == 0 || h2 != h)) dst[u == 0 ? h : h2] = m;
     }
-    acc += __shfl_xor(acc, 1, 64);
-    const float m = wave_max_dpp(acc);
-    if (lane == 0) dst[h] = m;
   }
-  if (ts && wave == 7) {
+  if (ts && wave == kNormWaves - 1) {
     const int j = 32 * blk + (lane & 31);
     const bool ok = j < n;
     const int64_t t = ok ? ts[tok0 + j] : 0;
@@ -968,10 +982,10 @@ hipError_t launch_key_norm(int32_t B, const int32_t* offsets, int64_t total_toke
   const int64_t rows = (total_tokens + 31 * (int64_t)B) / 32 + 1;
   if (rows > 0x7fffffff) return hipErrorInvalidValue;
   if (d == 64)
-    hipLaunchKernelGGL(key_norm_kernel<64>, dim3((unsigned)rows), dim3(512), 0, stream, offsets,
+    hipLaunchKernelGGL(key_norm_kernel<64>, dim3((unsigned)rows), dim3(64 * kNormWaves), 0, stream, offsets,
                        B, (const bf16*)k, k_stride, H, knorm, ts, stats, rel);
   else if (d == 32)
-    hipLaunchKernelGGL(key_norm_kernel<32>, dim3((unsigned)rows), dim3(512), 0, stream, offsets,
+    hipLaunchKernelGGL(key_norm_kernel<32>, dim3((unsigned)rows), dim3(64 * kNormWaves), 0, stream, offsets,
                        B, (const bf16*)k, k_stride, H, knorm, ts, stats, rel);
   else
     return hipErrorInvalidValue;

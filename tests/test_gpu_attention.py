@@ -321,6 +321,81 @@ def test_bucket_indices_bit_exact():
             assert tb[r] == oracle.time_bucket(int(ts[ti[r]]) - int(ts[tj[r]]), NT)
 
 
+def test_prepass_key_norms_and_block_time_stats():
+    """The bf16 forward's prepass outputs, read back from the workspace: per (32-key block, head)
+    the largest squared norm of the block's key rows (fp32 sums of the bf16 squares, within 1e-5
+    of the exact value, relative), and for the position + time bias each block's (min, max)
+    timestamp at its first token and every token's time minus its block's minimum (exact
+    integers).  300 users (more than 64: the row-to-user search takes two steps), among them
+    empty, single-token and multi-block ones, and H = 3 (one head pair with a single head)."""
+    rng = np.random.default_rng(21)
+    lengths = rng.integers(0, 90, size=300)
+    lengths[:6] = [0, 1, 32, 33, 700, 0]
+    H = 3
+    inp = _case("bf16", lengths.tolist(), H=H, d=64)
+    dev = DevAttn(inp)
+    B, T, ms = inp.B, inp.T, inp.max_seqlen
+    ws = torch.zeros(binding.attn_workspace_bytes(B, H, ms, T), dtype=torch.uint8, device="cuda")
+    dev.run(workspace=ws)
+    torch.cuda.synchronize()
+    w = ws.cpu().numpy()
+
+    def al(x):
+        return (x + 255) // 256 * 256
+    # regions: header + work list (32 B per item, 128-row tiles), TimeStat x T, int32 x T,
+    # tile classes (8 B per row and column), key norms (4 B per row and head)
+    rows = (T + 31 * B) // 32 + 1
+    p_stats = 256 + al(B * H * ((ms + 127) // 128) * 32)
+    p_rel = p_stats + al(16 * T)
+    p_cls = p_rel + al(4 * T)
+    p_kn = p_cls + al(rows * ((ms + 31) // 32) * 8)
+    stats = w[p_stats:p_stats + 16 * T].view(np.int64).reshape(T, 2)
+    rel = w[p_rel:p_rel + 4 * T].view(np.int32)
+    kn = w[p_kn:p_kn + 4 * rows * H].view(np.float32).reshape(rows, H)
+    offs = inp.offsets.astype(np.int64)
+    k = inp.k.astype(np.float64)
+    n_checked = 0
+    for b in range(B):
+        t0, n = int(offs[b]), int(offs[b + 1] - offs[b])
+        row0 = (t0 + 31 * b) // 32
+        for blk in range((n + 31) // 32):
+            a, e = t0 + 32 * blk, t0 + min(32 * blk + 32, n)
+            exact = np.max(np.sum(k[a:e] ** 2, axis=2), axis=0)  # [H]
+            got = kn[row0 + blk].astype(np.float64)
+            assert np.all(np.abs(got - exact) <= 1e-5 * exact), (b, blk, got, exact)
+            tb = inp.ts[a:e]
+            assert tuple(stats[a]) == (tb.min(), tb.max()), (b, blk)
+            assert np.array_equal(rel[a:e], np.minimum(tb - tb.min(), 0x7fffffff)), (b, blk)
+            n_checked += 1
+    print("prepass: %d blocks of %d users, %d heads" % (n_checked, B, H), flush=True)
+
+
+@pytest.mark.parametrize("B", [300, 5000])
+def test_schedule_many_users_bit_exact(B):
+    """The scheduler alone (hstu_attn_plan) on batches of more than 64 users (several ballot
+    chunks per cost class) and of more than 4 096 (offsets read from global memory instead of
+    LDS), with empty users and users longer than max_seqlen (cut at its tiles)."""
+    rng = np.random.default_rng(B)
+    lengths = rng.integers(0, 1200, size=B)
+    lengths[rng.random(B) < 0.1] = 0
+    lengths[:3] = [5000, 0, 1]
+    ms, H = 1000, 3
+    offs = synth.offsets_from_lengths(lengths)
+    ws = torch.zeros(binding.attn_workspace_bytes(B, H, ms, int(offs[-1])), dtype=torch.uint8,
+                     device="cuda")
+    binding.hstu_attn_plan(binding.DTYPE_BF16, B, H, 64, to_dev(offs), ms, ws)
+    torch.cuda.synchronize()
+    w = ws.cpu().numpy()
+    count = int(w[:4].view(np.int32)[0])
+    ref = schedule_reference(lengths, H, binding.attn_block_rows(binding.DTYPE_BF16, 64), ms)
+    assert count == len(ref)
+    items = w[256:256 + 32 * count].view(np.int32).reshape(count, 8)
+    assert [tuple(x[:3]) for x in items] == ref
+    b = items[:, 0]
+    assert np.array_equal(items[:, 3], offs[b + 1].astype(np.int64) - offs[b])
+    assert np.array_equal(items[:, 4:6].copy().view(np.int64)[:, 0], offs[b])
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 32)])
 def test_schedule_bit_exact(dtype, d):
     lengths = [0, 1, 700, 256, 257, 1500, 3, 128, 129, 1024]
