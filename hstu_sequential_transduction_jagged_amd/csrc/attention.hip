@@ -320,9 +320,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
       : KIND != 1 || wave > 2 ? 0
       : wave == 0 ? q_end * 4 : (int)min(a.tclass_bytes - cbase, (int64_t)0x7fffffff),
       0x00020000);
+  // lanes whose entries no wave reads (class entries of rows past the item's four query blocks,
+  // key norms past the tile's two blocks) fetch nothing: their offsets lie outside every buffer
   const uint32_t roff = wave == 0 ? 4u * lane
-                      : wave == 2 ? 4u * (uint32_t)H * (uint32_t)lane
-                                  : 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3);
+                      : wave == 2 ? (lane < 2 ? 4u * (uint32_t)H * (uint32_t)lane : 0x80000000u)
+                      : lane < 4 * kWaves ? 8u * (uint32_t)a.tclass_cols * (uint32_t)(lane >> 2) + 4u * (lane & 3)
+                                          : 0x80000000u;
   // tiles are visited in steps k = 0, 1, ..., n_loop - 1: upwards from the first key tile, or,
   // with ALiBi, downwards from the diagonal (so that the far tiles, whose weights the bias
   // drives below any fp32 resolution, come last and can be cut off; see kAlibiFarY)
