@@ -286,6 +286,9 @@ __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
   constexpr int WEL = CH * kF2K, AEL = kF2Tok * kF2K;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * (WEL + AEL)];
   __shared__ __attribute__((aligned(16))) bf16 sY[FUSE ? kF2Tok * 512 : 8];
+  // gamma and beta of every feature (1 and 0 when absent), staged once: the slices read them
+  // from LDS instead of waiting on a memory round trip each
+  __shared__ __attribute__((aligned(16))) float sgb[2 * kF2MaxHeads * 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int HV = g.HV, N = g.N;
@@ -336,14 +339,13 @@ __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
       (void*)(g.U + m0 * g.u_stride), (short)0, (int)(nrow * g.u_stride * 2), 0x00020000);
   const uint32_t voff_o = (uint32_t)srow * kb + 16u * sch;
   const uint32_t voff_u = (uint32_t)srow * (uint32_t)g.u_stride * 2u + 16u * sch;
-  // gamma / beta (null: 1 / 0) through descriptors: a null one reads zeros
-  const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.gamma, (short)0, g.gamma ? 4 * HV : 0, 0x00020000);
-  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)g.beta, (short)0, g.beta ? 4 * HV : 0, 0x00020000);
+  for (int i = tid; i < HV; i += kF2Threads) {
+    sgb[2 * i] = g.gamma ? g.gamma[i] : 1.0f;
+    sgb[2 * i + 1] = g.beta ? g.beta[i] : 0.0f;
+  }
+  __syncthreads();
   const __amdgpu_buffer_rsrc_t biasrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)g.bias, (short)0, g.bias ? 4 * N : 0, 0x00020000);
-  const bool has_gamma = g.gamma != nullptr;
 
   auto sw = [&](int buf) { return smem + buf * (WEL + AEL); };
   auto sa = [&](int buf) { return smem + buf * (WEL + AEL) + WEL; };
@@ -365,15 +367,12 @@ __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
       orr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ors, voff_o, k0, 0));
       urr = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(urs, voff_u, k0, 0));
     };
-    // gamma / beta of the slice's 8 k-values of this thread (small, cache-resident)
+    // gamma / beta of the slice's 8 k-values of this thread, as (gamma, beta) pairs from LDS
     auto lstore = [&](int buf, int kt) {
-      const uint32_t kf = 4u * (uint32_t)(kt * kF2K + 8 * sch);
-      f32x4 gr[2], br[2];
+      const f32x4* gb = (const f32x4*)(sgb + 2 * (kt * kF2K + 8 * sch));
+      f32x4 gbv[4];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        gr[h2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(grs, kf + 16u * h2, 0, 0));
-        br[h2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, kf + 16u * h2, 0, 0));
-      }
+      for (int q = 0; q < 4; ++q) gbv[q] = gb[q];
 #pragma unroll
       for (int u = 0; u < 2 * NI; ++u) *(u32x4*)(sw(buf) + lofs + 64 * u * kF2K) = wr[u];
       const bf16x8 o8 = __builtin_bit_cast(bf16x8, orr);
@@ -382,8 +381,8 @@ __global__ __launch_bounds__(kF2Threads, 2) void f2_kernel(F2Args g) {
       f32x8 y;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float gm = has_gamma ? gr[e >> 2][e & 3] : 1.0f;
-        y[e] = (((float)o8[e] + shift) * rstd * gm + br[e >> 2][e & 3]) * (float)u8[e];
+        const float gm = gbv[e >> 1][2 * (e & 1)], bt = gbv[e >> 1][2 * (e & 1) + 1];
+        y[e] = (((float)o8[e] + shift) * rstd * gm + bt) * (float)u8[e];
       }
       *(bf16x8*)(sa(buf) + lofs) = __builtin_convertvector(y, bf16x8);
     };
