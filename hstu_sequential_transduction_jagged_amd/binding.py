@@ -403,10 +403,11 @@ def candidates_workspace_bytes(B, H, max_hist, total_hist, total_cand):
 
 
 def hstu_attn_bwd(q, k, v, d_o, offsets, max_seqlen, bias: Optional[HstuBias] = None, alpha=1.0,
-                  out_scale=1.0, workspace=None):
+                  out_scale=1.0, workspace=None, dw_out=None):
     """Gradients of hstu_attn_fwd for the upstream gradient d_o (bf16, d = 64).  Returns
     (dq, dk, dv, dw_pos, dw_time); the table gradients are fp32 tensors shaped like the bias
-    tables (None without the position + time bias)."""
+    tables (None without the position + time bias), written into dw_out = (dw_pos, dw_time)
+    when given."""
     if q.dtype != torch.bfloat16:
         raise HstuError("the backward pass runs in bf16")
     qs, H, d = _rows(q, "q")
@@ -424,8 +425,14 @@ def hstu_attn_bwd(q, k, v, d_o, offsets, max_seqlen, bias: Optional[HstuBias] = 
     dwp = dwt = None
     if bias.kind == BIAS_RAB_PT:
         ts, wp, wt = bias._keep
-        dwp = torch.empty(wp.shape, dtype=torch.float32, device=q.device)
-        dwt = torch.empty(wt.shape, dtype=torch.float32, device=q.device)
+        if dw_out is not None:
+            dwp, dwt = dw_out
+            if dwp.shape != wp.shape or dwt.shape != wt.shape or dwp.dtype != torch.float32 \
+                    or dwt.dtype != torch.float32:
+                raise HstuError("dw_out must be fp32 tensors shaped like the bias tables")
+        else:
+            dwp = torch.empty(wp.shape, dtype=torch.float32, device=q.device)
+            dwt = torch.empty(wt.shape, dtype=torch.float32, device=q.device)
     need = attn_workspace_bytes(B, H, max_seqlen, T)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)

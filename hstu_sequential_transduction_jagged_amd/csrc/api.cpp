@@ -41,14 +41,15 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-hstu_status check_bias(const hstu_bias* bias, int32_t H, BiasArgs* out) {
+// timestamps may be null only for a batch without tokens (total_tokens 0)
+hstu_status check_bias(const hstu_bias* bias, int32_t H, BiasArgs* out, int64_t total_tokens) {
   *out = BiasArgs{};
   if (!bias || bias->kind == HSTU_BIAS_NONE) {
     out->kind = 0;
     return HSTU_OK;
   }
   if (bias->kind == HSTU_BIAS_RAB_PT) {
-    if (!bias->timestamps || !bias->w_pos || !bias->w_time)
+    if ((!bias->timestamps && total_tokens > 0) || !bias->w_pos || !bias->w_time)
       return fail(HSTU_ERR_INVALID_ARG, "rab_pt bias needs timestamps, w_pos and w_time");
     if (bias->num_pos_buckets < 1 || bias->num_pos_buckets > kMaxPosBuckets)
       return fail(HSTU_ERR_UNSUPPORTED, "num_pos_buckets must be in [1, %d]", kMaxPosBuckets);
@@ -223,7 +224,7 @@ static hstu_status attn_planned(int32_t dt, int32_t B, int32_t H, int32_t d_qk, 
   hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
   if (st != HSTU_OK) return st;
   BiasArgs ba;
-  st = check_bias(bias, H, &ba);
+  st = check_bias(bias, H, &ba, total_tokens);
   if (st != HSTU_OK) return st;
   if (B == 0 || total_tokens == 0 || max_seqlen == 0) return HSTU_OK;
   if (!offsets || !q || !k || !v || !o) return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
@@ -348,7 +349,7 @@ hstu_status hstu_attn_fwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
   if (st != HSTU_OK) return st;
   BiasArgs ba;
-  st = check_bias(bias, H, &ba);
+  st = check_bias(bias, H, &ba, total_tokens);
   if (st != HSTU_OK) return st;
   if (B == 0 || total_tokens == 0 || max_seqlen == 0) return HSTU_OK;
   if (!offsets || !q || !k || !v || !o || !workspace)
@@ -404,7 +405,7 @@ hstu_status hstu_stack_fwd(int32_t dt, int32_t B, int32_t n_layers, int32_t d_mo
   if (!(ln_eps > 0.f)) return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be > 0");
   for (int l = 0; l < n_layers; ++l) {
     BiasArgs ba;
-    const hstu_status st = check_bias(bias[l], H, &ba);
+    const hstu_status st = check_bias(bias[l], H, &ba, total_tokens);
     if (st != HSTU_OK) return st;
     if (!w1[l] || !w2[l]) return fail(HSTU_ERR_INVALID_ARG, "null weight of layer %d", l);
     if (!aligned16(w1[l]) || !aligned16(w2[l]))
@@ -450,7 +451,7 @@ hstu_status hstu_stack_fwd(int32_t dt, int32_t B, int32_t n_layers, int32_t d_mo
       if (st != HSTU_OK) return st;
     }
     BiasArgs ba;
-    check_bias(bias[l], H, &ba);  // validated above
+    check_bias(bias[l], H, &ba, total_tokens);  // validated above
     const bool ready = ba.kind == 1 && ba.ts == cls_ts && ba.num_pos == cls_p && ba.num_time == cls_nt;
     st = attn_planned(HSTU_DTYPE_BF16, B, H, d_qk, d_v, offsets, max_seqlen, total_tokens, Q, N1,
                       K, N1, V, N1, bias[l], alpha, 1.0f, obuf, false, ostats, aws, aws_bytes,
@@ -538,11 +539,20 @@ hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_
   hstu_status st = attn_check(dt, B, H, d_qk, d_v, max_seqlen, total_tokens, &block_rows);
   if (st != HSTU_OK) return st;
   BiasArgs ba;
-  st = check_bias(bias, H, &ba);
+  st = check_bias(bias, H, &ba, total_tokens);
   if (st != HSTU_OK) return st;
   if (ba.kind == 1 && (!dw_pos || !dw_time))
     return fail(HSTU_ERR_INVALID_ARG, "rab_pt bias needs dw_pos and dw_time");
-  if (B == 0 || total_tokens == 0 || max_seqlen == 0) return HSTU_OK;
+  if (B == 0 || total_tokens == 0 || max_seqlen == 0) {
+    // no pairs: the table gradients are sums over nothing
+    if (ba.kind == 1) {
+      const int64_t np = ba.pos_stride ? (int64_t)H * ba.pos_stride : ba.num_pos;
+      const int64_t nt = ba.time_stride ? (int64_t)H * ba.time_stride : ba.num_time;
+      st = check_hip(launch_zero_f32(dw_pos, np, stream), "zero");
+      if (st == HSTU_OK) st = check_hip(launch_zero_f32(dw_time, nt, stream), "zero");
+    }
+    return st;
+  }
   if (!offsets || !q || !k || !v || !d_o || !dq || !dk || !dv || !workspace)
     return fail(HSTU_ERR_INVALID_ARG, "null pointer argument");
   const int64_t rowlen = (int64_t)H * d_qk;
@@ -625,7 +635,7 @@ hstu_status hstu_layer_fwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
                 "layer needs d_model %% 128 == 0, 2H(dqk+dv) %% 128 == 0, H dv <= 1024");
   if (!(ln_eps > 0.f)) return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be > 0");
   BiasArgs ba;
-  hstu_status st = check_bias(bias, H, &ba);
+  hstu_status st = check_bias(bias, H, &ba, total_tokens);
   if (st != HSTU_OK) return st;
   if (B == 0 || total_tokens == 0) return HSTU_OK;
   if (!offsets || !x || !w1 || !w2 || !y || !workspace)
@@ -689,7 +699,7 @@ hstu_status hstu_attn_candidates_fwd(int32_t dt, int32_t B, int32_t H, int32_t d
   if (B < 0 || H < 1 || max_hist < 0 || total_hist < 0 || max_cand < 0 || total_cand < 0)
     return fail(HSTU_ERR_INVALID_ARG, "bad sizes");
   BiasArgs ba;
-  hstu_status st = check_bias(bias, H, &ba);
+  hstu_status st = check_bias(bias, H, &ba, total_hist + total_cand);
   if (st != HSTU_OK) return st;
   if (B == 0 || total_cand == 0 || max_cand == 0) return HSTU_OK;
   if (!hist_offsets || !cand_offsets || !q_cand || !k_cand || !v_cand || !o)
@@ -753,7 +763,7 @@ hstu_status hstu_layer_bwd(int32_t dt, int32_t B, int32_t d_model, int32_t H, in
   if ((int64_t)H * d_v > 2048) return fail(HSTU_ERR_UNSUPPORTED, "H * d_v above 2048");
   if (!(ln_eps > 0.f)) return fail(HSTU_ERR_INVALID_ARG, "ln_eps must be > 0");
   BiasArgs ba;
-  hstu_status st = check_bias(bias, H, &ba);
+  hstu_status st = check_bias(bias, H, &ba, total_tokens);
   if (st != HSTU_OK) return st;
   if (ba.kind == 1 && (!dw_pos || !dw_time))
     return fail(HSTU_ERR_INVALID_ARG, "rab_pt bias needs dw_pos and dw_time");

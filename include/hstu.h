@@ -63,7 +63,7 @@ typedef enum { HSTU_DTYPE_F32 = 0, HSTU_DTYPE_BF16 = 1, HSTU_DTYPE_BF16_OUT_F32 
 typedef enum { HSTU_BIAS_NONE = 0, HSTU_BIAS_RAB_PT = 1, HSTU_BIAS_ALIBI = 2 } hstu_bias_kind;
 
 /* Relative attention bias.  Host struct; the arrays it points to are device memory.
- *  RAB_PT: timestamps [T] int64 (any unit; only differences are used);
+ *  RAB_PT: timestamps [T] int64 (any unit; only differences are used; may be NULL when T = 0);
  *          w_pos [H_tab][pos_head_stride] and w_time [H_tab][time_head_stride] fp32,
  *          with num_pos_buckets in [1, 1024] and num_time_buckets in [1, 64];
  *          a head stride of 0 shares one table across heads.
@@ -187,7 +187,8 @@ size_t hstu_layer_workspace_bytes(int32_t B, int64_t total_tokens, int32_t d_mod
  *  dq, dk, dv    device bf16 [T, H, 64] contiguous, overwritten
  *  dw_pos, dw_time  rab_pt bias only (else may be NULL): device fp32 shaped like w_pos / w_time
  *            (H x head stride, or one table when the stride is 0: then it sums over heads),
- *            overwritten; added to with atomics, so their last bits vary between runs
+ *            overwritten (zeros for an empty batch: B, T or max_seqlen 0); added to with
+ *            atomics, so their last bits vary between runs
  *  workspace as for hstu_attn_fwd (same size); other arguments as for hstu_attn_fwd. */
 hstu_status hstu_attn_bwd(int32_t dt, int32_t B, int32_t H, int32_t d_qk, int32_t d_v,
                           const int32_t* offsets, int32_t max_seqlen, int64_t total_tokens,

@@ -116,6 +116,29 @@ def test_bf16_d32_long_users_sampled_rows():
     assert e <= TOL["bf16"], e
 
 
+@pytest.mark.parametrize("kind", [synth.BIAS_RAB_PT, synth.BIAS_ALIBI])
+def test_bf16_maximum_sizes_sampled_rows(kind):
+    """The largest inputs the entry points accept: a user of 65 536 rows (max_seqlen's limit:
+    512 query tiles, 2 048 key blocks) beside a one-row user, position tables of 1 024 buckets
+    and 64 time buckets (both limits), tables of std 0.5 and alpha = 1/64 so that every SiLU
+    path occurs; 300 sampled (token, head) rows (the last rows, tile and bucket edges, random
+    rows) against the oracle."""
+    inp = _case("bf16", [65536, 1], H=2, d=64, kind=kind, alpha=1.0 / 64, table_std=0.5,
+                P=1024, NT=64, seed=13)
+    o = run_attn(inp)
+    rng = np.random.default_rng(8)
+    toks = [65535, 65534, 65536, 0, 127, 128, 1023, 1024, 1025, 32767, 32768]
+    toks += list(rng.integers(0, inp.T, size=300 - len(toks)))
+    toks = np.array(toks)
+    heads = rng.integers(0, inp.H, size=len(toks))
+    ref = oracle_attn_rows(inp, toks, heads)
+    e = err_stored(o[toks, heads], ref, "bf16")
+    print("max sizes kind=%d err=%.3g (without storage allowance %.3g)"
+          % (kind, e, err_rms(o[toks, heads], ref)), flush=True)
+    assert e <= TOL["bf16"], e
+    assert np.all(np.isfinite(o))
+
+
 def test_bf16_per_head_tables_and_small_buckets():
     inp = _case("bf16", [5, 300, 129], H=3, alpha=0.1, table_std=1.0, P=16, NT=6, per_head=True)
     _check(inp)
@@ -257,6 +280,14 @@ def test_gpu_zero_queries_keys_and_bias():
     inp.q[:] = 0.0
     inp.k[:] = 0.0
     assert np.all(run_attn(inp) == 0.0)
+
+
+@pytest.mark.parametrize("kind", [synth.BIAS_RAB_PT, synth.BIAS_ALIBI, synth.BIAS_NONE])
+def test_gpu_empty_batch(kind):
+    """Three empty users (T = 0, no timestamps): the call succeeds and returns an empty output."""
+    inp = _case("bf16", [0, 0, 0], kind=kind)
+    o = run_attn(inp)
+    assert o.shape == (0, inp.H, inp.dv)
 
 
 def test_gpu_repeat_calls_identical():

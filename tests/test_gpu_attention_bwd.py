@@ -98,6 +98,24 @@ def test_bwd_strided_views():
     _check(inp, got, dO)
 
 
+def test_bwd_empty_batch_table_grads_are_zero():
+    """A batch with no tokens (three empty users) has no pairs: the table gradients, sums over
+    nothing, come back as zeros (the output tables are filled with NaN first), and dQ, dK, dV
+    are empty."""
+    inp = _case([0, 0, 0])
+    d = DevAttn(inp)
+    dO = to_dev(_dout(inp), torch.bfloat16)
+    ts, wp, wt = d.bias._keep
+    dwp = torch.full(wp.shape, float("nan"), dtype=torch.float32, device="cuda")
+    dwt = torch.full(wt.shape, float("nan"), dtype=torch.float32, device="cuda")
+    got = binding.hstu_attn_bwd(d.q, d.k, d.v, dO, d.offsets, inp.max_seqlen, d.bias, inp.alpha,
+                                inp.out_scale, dw_out=(dwp, dwt))
+    torch.cuda.synchronize()
+    assert got[3] is dwp and got[4] is dwt
+    assert torch.all(dwp == 0).item() and torch.all(dwt == 0).item()
+    assert all(g.numel() == 0 for g in got[:3])
+
+
 def test_bwd_rejects_bad_arguments():
     inp = _case([10])
     d = DevAttn(inp)
