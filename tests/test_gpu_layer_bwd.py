@@ -115,6 +115,29 @@ def test_layer_bwd_wide():
     _check(inp, seed=4)
 
 
+def test_layer_empty_batch():
+    """Three empty users (T = 0, no timestamps): the forward returns an empty output and the
+    backward's weight, bias, LayerNorm and table gradients, sums over no tokens, are zeros."""
+    inp = synth.make_layer("lempty", 44, [0, 0, 0], D=256, H=2, d=64, alpha=1.0 / 64,
+                           residual=True, bias_kind=synth.BIAS_RAB_PT, P=64, NT=16,
+                           table_std=0.5, randomize_affine=True)
+    d = DevLayer(inp)
+    L = d.layers[0]
+    ws = torch.empty(max(256, binding.layer_workspace_bytes(inp.B, inp.T, inp.D, inp.H, inp.dqk,
+                                                            inp.dv, inp.max_seqlen)),
+                     dtype=torch.uint8, device="cuda")
+    y = d.run_layer(d.x, workspace=ws)
+    got = binding.hstu_layer_bwd(d.x, d.offsets, inp.max_seqlen, L["w1"], L["b1"], L["gamma"],
+                                 L["beta"], L["w2"], inp.H, inp.dqk, inp.dv, L["bias"], inp.alpha,
+                                 inp.residual, inp.ln_eps, ws,
+                                 torch.empty((0, inp.D), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert y.shape == (0, inp.D)
+    assert got["dx"].shape == (0, inp.D)
+    for name in NAMES[1:]:
+        assert got[name] is not None and torch.all(got[name] == 0).item(), name
+
+
 def test_layer_bwd_full_size_sampled_users():
     """The first layer of the 8-layer stack workload at its full size (128 users, T = 80 405,
     D = 512, H = 8, position + time bias, residual), forward and backward as the layer benchmark
