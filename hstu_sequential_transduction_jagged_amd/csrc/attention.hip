@@ -43,12 +43,6 @@ __device__ __forceinline__ int acc_key(int r, int hf) { return 8 * (r >> 2) + 4 
 
 // Cross-lane moves inside a row of 16 lanes (DPP, no LDS round trip).
 
-// Sum over each aligned group of 8 lanes, in all 8 lanes.
-__device__ __forceinline__ float sum8(float v) {
-  v += dpp<kDppXor1>(v);
-  v += dpp<kDppXor2>(v);
-  return v + dpp<kDppHalfMirror>(v);
-}
 // Max over the 64 lanes of a wave, as a wave-uniform value.
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp<kDppXor1>(v));
@@ -281,7 +275,6 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bf16_kernel(AttnArgs a) {
   const TimeStat* __restrict__ tstat = a.tstat;
   const float cq = -a.alpha * kLog2e;
   const int Pm1 = a.bias.num_pos - 1, NTm1 = a.bias.num_time - 1;
-  constexpr int kClassWave = 1;  // its lanes 0..31 stage the next tile's class entries
 
   // ---- staging: direct global -> LDS transfers into two stages ----
   // Wave w's K and V transfers fill key rows 16 w .. 16 w + 15 of a stage, two instructions
@@ -807,7 +800,7 @@ __global__ __launch_bounds__(256, 2) void attn_f32_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = a.work[item];
-  const int b = wi.b, h = wi.h, H = a.H;
+  const int h = wi.h, H = a.H;
   const int64_t tok0 = wi.tok0;
   const int n = wi.n;
   const int q0 = wi.qt * kBRf;

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kBThreads, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = a.work[item];
-  const int b = wi.b, h = wi.h, H = a.H;
+  const int h = wi.h, H = a.H;
   const int64_t tok0 = wi.tok0;
   const int n = wi.n;
   const int q0 = wi.qt * kBRows;
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(kBThreads, 2) void attn_bwd_dkv_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const WorkItem wi = a.work[item];
-  const int b = wi.b, h = wi.h, H = a.H;
+  const int h = wi.h, H = a.H;
   const int64_t tok0 = wi.tok0;
   const int n = wi.n;
   // the work list orders items by q_tile; this kernel takes key tile (tiles - 1 - q_tile),
